@@ -159,3 +159,28 @@ def test_mxfp4_tie_case_rounds_to_even():
     packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, None, :]
     q, _ = decode_mxfp4_ref(packed, np.full((1, 1, 4), 127, np.uint8))
     assert q[0, 0, 0] == 127 and q[0, 0, 1] == 64
+
+
+@pytest.mark.parametrize("dialect", [OCP, FNUZ])
+def test_subnormal_group_scale_and_clamp(dialect):
+    """Block exponent byte 0 puts group maxima near 2^-136: the float32 scale amax/127 is
+    subnormal with few significant bits, so the argmax need not map to 127. In the fnuz
+    reading the smallest code gives x/scale = 128 exactly, and only the symmetric clamp
+    keeps q at +-127 (never -128)."""
+    w = np.zeros((128, 128), np.uint8)
+    w[0, 0] = 0x81                       # -(smallest subnormal) in both dialects
+    w[0, 1] = 0x01
+    w[1, :3] = [0x02, 0x81, 0x83]
+    bs = np.zeros((1, 1), np.uint8)      # 2^-127
+    Wd = dequant_fp8_block_ref(w, bs, dialect)
+    q, s = decode_fp8_block_ref(w, bs, dialect)
+    for n in (0, 1):
+        qe, se = exact.quant_rule_exact(Wd[n].tolist())
+        assert exact.f32_bits(se) == exact.f32_bits(s[n, 0]) and 0 < s[n, 0] < 1e-38
+        assert q[n].tolist() == qe
+    if dialect == FNUZ:
+        raw = exact.round_f32(exact.F(Wd[0, 0]) / exact.F(s[0, 0]))
+        assert raw == -128.0                  # unclamped value would be -128
+        assert q[0, 0] == -127 and q[0, 1] == 127
+    else:
+        assert q[0, 0] == -126 and q[0, 1] == 126     # scale rounded up: 127*64.5/65
