@@ -1,0 +1,229 @@
+"""ctypes binding of libbsb.so (the gfx950 HIP kernels behind include/bsb.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library. PyTorch provides device memory and the current HIP
+stream; tensors are passed as raw device pointers. There is no fallback: if
+the library is not built, importing this module's functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsb.so")
+
+BSB_OUT_BF16, BSB_OUT_FP32 = 0, 1
+BSB_FP8_OCP, BSB_FP8_FNUZ = 0, 1
+STATUS = {0: "BSB_OK", 1: "BSB_ERR_INVALID_ARG", 2: "BSB_ERR_UNSUPPORTED_DEVICE",
+          3: "BSB_ERR_MISALIGNED", 4: "BSB_ERR_LAUNCH"}
+
+_c_p = ctypes.c_void_p
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+
+_SIGNATURES = {
+    "bsb_quantize_act": [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
+    "bsb_gemm_w8a8_g128": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
+    "bsb_grouped_gemm_w8a8_g128": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
+                                   _c_p, _c_int, _c_p],
+    "bsb_decode_fp8_block": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_p],
+    "bsb_decode_mxfp4": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
+    "bsb_gemm_w8a8_g128_partials": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+}
+EXPORTED = tuple(_SIGNATURES) + ("bsb_status_string", "bsb_abi_version")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbsb.so once (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m block_scaled_bit_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = _c_int
+        L.bsb_status_string.argtypes = [_c_int]
+        L.bsb_status_string.restype = ctypes.c_char_p
+        L.bsb_abi_version.argtypes = []
+        L.bsb_abi_version.restype = _c_int
+        _lib = L
+    return _lib
+
+
+class BsbError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: {lib().bsb_status_string(status).decode()}")
+
+
+def _check(status: int, fn: str) -> None:
+    if status != 0:
+        raise BsbError(status, fn)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtypes, shape=None, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16_BITS = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def quantize_act(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                 sa: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """BF16 activations [M,K] -> (q int8 [M,K], sa float32 [M])."""
+    _need(x, "x", _BF16_BITS)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    dev = x.device
+    q = torch.empty((M, K), dtype=torch.int8, device=dev) if q is None else q
+    sa = torch.empty((M,), dtype=torch.float32, device=dev) if sa is None else sa
+    _need(q, "q", (torch.int8,), (M, K), dev)
+    _need(sa, "sa", (torch.float32,), (M,), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_quantize_act(_ptr(x), M, K, _ptr(q), _ptr(sa), _stream(dev)),
+               "bsb_quantize_act")
+    return q, sa
+
+
+def _out_code(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return BSB_OUT_BF16
+    if dtype == torch.float32:
+        return BSB_OUT_FP32
+    raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+
+
+def gemm_w8a8_g128(q: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                   out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [M,N] = W8A8 per-group-128 GEMM of q [M,K] (scales sa [M]) with qw [N,K] (scales sw [N,K/128])."""
+    _need(q, "q", (torch.int8,))
+    if q.dim() != 2 or qw.dim() != 2:
+        raise ValueError("q [M,K] and qw [N,K] required")
+    M, K = q.shape
+    N = qw.shape[0]
+    dev = q.device
+    _need(qw, "qw", (torch.int8,), (N, K), dev)
+    _need(sa, "sa", (torch.float32,), (M,), dev)
+    _need(sw, "sw", (torch.float32,), (N, K // 128), dev)
+    code = _out_code(out_dtype)
+    out = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", (out_dtype,), (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_gemm_w8a8_g128(_ptr(q), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K,
+                                        _ptr(out), code, _stream(dev)), "bsb_gemm_w8a8_g128")
+    return out
+
+
+def gemm_w8a8_g128_partials(q: torch.Tensor, qw: torch.Tensor,
+                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """INT32 group partials P [M,N,K/128] from the GEMM's own main loop."""
+    _need(q, "q", (torch.int8,))
+    M, K = q.shape
+    N = qw.shape[0]
+    dev = q.device
+    _need(qw, "qw", (torch.int8,), (N, K), dev)
+    out = torch.empty((M, N, K // 128), dtype=torch.int32, device=dev) if out is None else out
+    _need(out, "out", (torch.int32,), (M, N, K // 128), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_gemm_w8a8_g128_partials(_ptr(q), _ptr(qw), M, N, K, _ptr(out),
+                                                 _stream(dev)), "bsb_gemm_w8a8_g128_partials")
+    return out
+
+
+def grouped_gemm_w8a8_g128(q: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                           offsets: torch.Tensor, out_dtype=torch.bfloat16,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MoE form: rows [offsets[e], offsets[e+1]) of q run against expert e's qw [E,N,K] / sw [E,N,K/128].
+
+    R is taken from q's first dimension; offsets must satisfy offsets[0] = 0,
+    non-decreasing, offsets[E] = R (device tensor, not read on the host).
+    """
+    _need(q, "q", (torch.int8,))
+    if q.dim() != 2 or qw.dim() != 3:
+        raise ValueError("q [R,K] and qw [E,N,K] required")
+    R, K = q.shape
+    E, N, _ = qw.shape
+    dev = q.device
+    _need(qw, "qw", (torch.int8,), (E, N, K), dev)
+    _need(sa, "sa", (torch.float32,), (R,), dev)
+    _need(sw, "sw", (torch.float32,), (E, N, K // 128), dev)
+    _need(offsets, "offsets", (torch.int32,), (E + 1,), dev)
+    code = _out_code(out_dtype)
+    out = torch.empty((R, N), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", (out_dtype,), (R, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_grouped_gemm_w8a8_g128(_ptr(q), _ptr(sa), _ptr(qw), _ptr(sw),
+                                                _ptr(offsets), E, R, N, K, _ptr(out), code,
+                                                _stream(dev)), "bsb_grouped_gemm_w8a8_g128")
+    return out
+
+
+def decode_fp8_block(w: torch.Tensor, bs: torch.Tensor, dialect: int,
+                     qw: Optional[torch.Tensor] = None,
+                     sw: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """FP8 e4m3 bytes [N,K] + UE8M0 block exponents [N/128,K/128] -> (qw int8 [N,K], sw [N,K/128])."""
+    _need(w, "w", (torch.uint8,))
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    N, K = w.shape
+    dev = w.device
+    _need(bs, "bs", (torch.uint8,), (N // 128, K // 128), dev)
+    if dialect not in (BSB_FP8_OCP, BSB_FP8_FNUZ):
+        raise ValueError("dialect must be BSB_FP8_OCP or BSB_FP8_FNUZ")
+    qw = torch.empty((N, K), dtype=torch.int8, device=dev) if qw is None else qw
+    sw = torch.empty((N, K // 128), dtype=torch.float32, device=dev) if sw is None else sw
+    _need(qw, "qw", (torch.int8,), (N, K), dev)
+    _need(sw, "sw", (torch.float32,), (N, K // 128), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_decode_fp8_block(_ptr(w), _ptr(bs), N, K, dialect, _ptr(qw), _ptr(sw),
+                                          _stream(dev)), "bsb_decode_fp8_block")
+    return qw, sw
+
+
+def decode_mxfp4(packed: torch.Tensor, scale: torch.Tensor,
+                 qw: Optional[torch.Tensor] = None,
+                 sw: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MXFP4 packed [E,N,K/2] + UE8M0 [E,N,K/32] -> (qw int8 [E,N,K], sw [E,N,K/128])."""
+    _need(packed, "packed", (torch.uint8,))
+    if packed.dim() != 3:
+        raise ValueError("packed must be [E, N, K/2]")
+    E, N, Kh = packed.shape
+    K = 2 * Kh
+    dev = packed.device
+    _need(scale, "scale", (torch.uint8,), (E, N, K // 32), dev)
+    qw = torch.empty((E, N, K), dtype=torch.int8, device=dev) if qw is None else qw
+    sw = torch.empty((E, N, K // 128), dtype=torch.float32, device=dev) if sw is None else sw
+    _need(qw, "qw", (torch.int8,), (E, N, K), dev)
+    _need(sw, "sw", (torch.float32,), (E, N, K // 128), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_decode_mxfp4(_ptr(packed), _ptr(scale), E, N, K, _ptr(qw), _ptr(sw),
+                                      _stream(dev)), "bsb_decode_mxfp4")
+    return qw, sw

@@ -1,0 +1,148 @@
+// C ABI of libbsb: argument validation, device check, dispatch to the gfx950
+// kernels. Every entry point validates before it launches anything and
+// returns a status code; nothing here allocates, synchronises or reads
+// device memory.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/bsb.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch_state[kMaxDevices];
+
+bsb_status check_device() noexcept {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return BSB_ERR_UNSUPPORTED_DEVICE;
+    if (dev >= kMaxDevices) return BSB_ERR_UNSUPPORTED_DEVICE;
+    int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BSB_ERR_UNSUPPORTED_DEVICE;
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? BSB_OK : BSB_ERR_UNSUPPORTED_DEVICE;
+}
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest extents the 32-bit index arithmetic inside the kernels accepts.
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxElems = (int64_t)1 << 36;
+
+inline bool dims_ok(int64_t rows, int64_t N, int64_t K) {
+    return rows >= 0 && N >= 1 && K >= 128 && (K % 128) == 0 && rows < kMaxDim && N < kMaxDim &&
+           K < kMaxDim;
+}
+
+inline bsb_status finish(hipError_t e) noexcept { return e == hipSuccess ? BSB_OK : BSB_ERR_LAUNCH; }
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int bsb_abi_version(void) { return BSB_ABI_VERSION; }
+
+const char *bsb_status_string(bsb_status s) {
+    switch (s) {
+        case BSB_OK: return "BSB_OK";
+        case BSB_ERR_INVALID_ARG: return "BSB_ERR_INVALID_ARG: invalid argument";
+        case BSB_ERR_UNSUPPORTED_DEVICE: return "BSB_ERR_UNSUPPORTED_DEVICE: current device is not gfx950";
+        case BSB_ERR_MISALIGNED: return "BSB_ERR_MISALIGNED: pointer not 16-byte aligned";
+        case BSB_ERR_LAUNCH: return "BSB_ERR_LAUNCH: kernel launch failed";
+    }
+    return "BSB_ERR_UNKNOWN";
+}
+
+bsb_status bsb_quantize_act(const uint16_t *x_bf16, int64_t M, int64_t K, int8_t *q, float *sa,
+                            void *stream) {
+    if (M < 0 || M >= kMaxDim || K < 128 || K % 128 || K >= kMaxDim) return BSB_ERR_INVALID_ARG;
+    if (M == 0) return BSB_OK;
+    if (!x_bf16 || !q || !sa) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(x_bf16) || !aligned16(q) || !aligned16(sa)) return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_quantize_act(x_bf16, M, K, q, sa, as_stream(stream)));
+}
+
+bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
+                              int64_t M, int64_t N, int64_t K, void *y, bsb_out_dtype out,
+                              void *stream) {
+    if (!dims_ok(M, N, K) || N * K > kMaxElems) return BSB_ERR_INVALID_ARG;
+    if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
+    if (M == 0) return BSB_OK;
+    if (!q || !sa || !qw || !sw || !y) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(sa) || !aligned16(qw) || !aligned16(sw) || !aligned16(y))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_gemm(q, sa, qw, sw, M, N, K, y, (int)out, as_stream(stream)));
+}
+
+bsb_status bsb_gemm_w8a8_g128_partials(const int8_t *q, const int8_t *qw, int64_t M, int64_t N,
+                                       int64_t K, int32_t *P, void *stream) {
+    if (!dims_ok(M, N, K) || N * K > kMaxElems || M * N * (K / 128) > kMaxElems)
+        return BSB_ERR_INVALID_ARG;
+    if (M == 0) return BSB_OK;
+    if (!q || !qw || !P) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(qw) || !aligned16(P)) return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_gemm(q, nullptr, qw, nullptr, M, N, K, P, 2, as_stream(stream)));
+}
+
+bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa, const int8_t *qw,
+                                      const float *sw, const int32_t *offsets, int64_t E,
+                                      int64_t R, int64_t N, int64_t K, void *y,
+                                      bsb_out_dtype out, void *stream) {
+    if (!dims_ok(R, N, K) || E < 1 || E >= (1 << 20) || E * N * K > kMaxElems)
+        return BSB_ERR_INVALID_ARG;
+    if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
+    if (R == 0) return BSB_OK;
+    if (!q || !sa || !qw || !sw || !offsets || !y) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(sa) || !aligned16(qw) || !aligned16(sw) ||
+        !aligned16(offsets) || !aligned16(y))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_grouped_gemm(q, sa, qw, sw, offsets, E, R, N, K, y, (int)out,
+                                           as_stream(stream)));
+}
+
+bsb_status bsb_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t N, int64_t K,
+                                bsb_fp8_dialect dialect, int8_t *qw, float *sw, void *stream) {
+    if (N < 128 || N % 128 || K < 128 || K % 128 || N >= kMaxDim || K >= kMaxDim ||
+        N * K >= kMaxElems)
+        return BSB_ERR_INVALID_ARG;
+    if (dialect != BSB_FP8_OCP && dialect != BSB_FP8_FNUZ) return BSB_ERR_INVALID_ARG;
+    if (!w || !bs || !qw || !sw) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(bs) || !aligned16(qw) || !aligned16(sw))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_decode_fp8_block(w, bs, N, K, dialect == BSB_FP8_FNUZ ? 1 : 0, qw,
+                                               sw, as_stream(stream)));
+}
+
+bsb_status bsb_decode_mxfp4(const uint8_t *packed, const uint8_t *scale, int64_t E, int64_t N,
+                            int64_t K, int8_t *qw, float *sw, void *stream) {
+    if (E < 1 || N < 1 || K < 128 || K % 128 || E >= kMaxDim || N >= kMaxDim || K >= kMaxDim ||
+        E * N * K >= kMaxElems)
+        return BSB_ERR_INVALID_ARG;
+    if (!packed || !scale || !qw || !sw) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(packed) || !aligned16(scale) || !aligned16(qw) || !aligned16(sw))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_decode_mxfp4(packed, scale, E, N, K, qw, sw, as_stream(stream)));
+}
+
+}  // extern "C"

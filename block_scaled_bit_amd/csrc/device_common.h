@@ -1,0 +1,64 @@
+// Device helpers shared by the gfx950 kernels of libbsb.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsb {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kGroup = 128;   // K-group width of the weight scales
+constexpr int kWave = 64;     // CDNA wavefront
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) {
+    return __uint_as_float(b16 << 16);
+}
+
+// float32 -> BF16 bits, round to nearest even. Inputs are finite.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t b = __float_as_uint(f);
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// The absmax INT8 rule of [P3] sec. 3.1 for one element, given the row's
+// scale s > 0: clamp(rint(x / s), -127, 127). The division is the IEEE
+// correctly rounded one (the library is built without fast-math), and rint
+// rounds half to even (v_rndne_f32).
+__device__ __forceinline__ int quant_elem(float x, float s) {
+    float t = x / s;
+    t = __builtin_rintf(t);
+    t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
+    return (int)t;
+}
+
+// Scale of the absmax rule: amax / 127 as an IEEE float32 divide.
+__device__ __forceinline__ float absmax_scale(float amax) {
+    return amax / 127.0f;
+}
+
+// Max over the `width` consecutive lanes that share an aligned lane group.
+__device__ __forceinline__ float group_max(float v, int width) {
+    for (int off = width >> 1; off > 0; off >>= 1)
+        v = __builtin_fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v, int width) {
+    for (int off = width >> 1; off > 0; off >>= 1) {
+        uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// Pack four int8 values (each already in [-127, 127]) into one dword.
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) |
+           ((uint32_t)(c & 0xFF) << 16) | ((uint32_t)(d & 0xFF) << 24);
+}
+
+}  // namespace bsb

@@ -1,0 +1,431 @@
+// W8A8 per-group-128 GEMM (dense and grouped/MoE) on gfx950 MFMA.
+//
+// [P3] sec. 3.1: INT8 x INT8 multiply-accumulate into INT32 inside the
+// matmul, the FP32 scales applied last. Per output element:
+//     acc = 0
+//     for g = 0 .. K/128-1:                  (ascending, never split)
+//         P   = sum_{k in group g} q[m,k]*qw[n,k]        (INT32, MFMA)
+//         acc = fmaf((float)P, sw[n,g], acc)             (VALU epilogue)
+//     y = acc * sa[m]  -> BF16 (RNE) or FP32
+//
+// Two kernels share that per-group structure:
+//
+//  * smallm (M <= 64, decode-shaped): the weight matrix is the stream. A
+//    workgroup of 4 waves owns 64 output columns; each wave owns 16 columns
+//    and all M rows (v_mfma_i32_16x16x64_i8, one 16-row block per 16 tokens).
+//    The activation tile of the current group is staged once per workgroup
+//    in LDS (double-buffered); each lane prefetches its weight bytes PF groups
+//    ahead straight into registers, so every weight byte is read from HBM
+//    once with many bytes in flight per wave.
+//
+//  * tile (large M, prefill-shaped, and the grouped MoE kernel): 128x128
+//    output tile per workgroup of 4 waves (2x2, 64x64 per wave, four
+//    v_mfma_i32_32x32x32_i8 blocks). A and B tiles of one K group are staged
+//    through double-buffered LDS (rows padded to 144 B against bank
+//    conflicts), the next group's tiles are loaded into registers while the
+//    current one is multiplied.
+//
+// MFMA operand pairing: lane l supplies 16 bytes of row (l % 16 or l % 32)
+// of A and the same 16 K positions of column (l % 16 or l % 32) of B. Any
+// assignment of K positions to (lane slot, instruction) that is identical for
+// A and B gives the same exact INT32 sum; each lane here owns a contiguous
+// span of the group so its loads are 16-byte aligned and contiguous.
+#include "device_common.h"
+#include "launch.h"
+
+namespace bsb {
+
+namespace {
+
+enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_PARTIALS = 2 };
+
+__device__ __forceinline__ v4i as_v4i(uint4 u) {
+    v4i r;
+    r[0] = (int)u.x; r[1] = (int)u.y; r[2] = (int)u.z; r[3] = (int)u.w;
+    return r;
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
+    if (OUT == OUT_BF16)
+        reinterpret_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
+    else
+        reinterpret_cast<float *>(y)[idx] = v;
+}
+
+// --------------------------------------------------------------------------
+// smallm: M <= 16*MB tokens, weight-streaming.
+// --------------------------------------------------------------------------
+template <int MB, int OUT, int PF>
+__global__ void __launch_bounds__(256)
+gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
+                   const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N,
+                   int K, void *__restrict__ y) {
+    constexpr int ROWS = 16 * MB;
+    constexpr int LDA = kGroup + 16;   // padded LDS row (bytes)
+    __shared__ __align__(16) int8_t As[2][ROWS * LDA];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = K >> 7;
+    const int col = lane & 15;          // B column / A row within a 16-block
+    const int slot = lane >> 4;         // which 32-byte quarter of the group
+    const int n = blockIdx.x * 64 + wave * 16 + col;
+    const bool nvalid = n < N;
+    const int8_t *wrow = qw + (int64_t)(nvalid ? n : 0) * K + slot * 32;
+    const float *swrow = sw + (int64_t)(nvalid ? n : 0) * G;
+
+    // Cooperative A loads: ROWS x 128 B per group = ROWS*8 chunks of 16 B.
+    constexpr int ACH = ROWS * 8;
+    constexpr int APT = (ACH + 255) / 256;   // chunks per thread
+    uint4 areg[APT];
+    auto load_a = [&](int g) {
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int c = tid + 256 * i;
+            const int r = c >> 3, cc = c & 7;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (c < ACH && r < M)
+                v = *reinterpret_cast<const uint4 *>(q + (int64_t)r * K + g * kGroup + cc * 16);
+            areg[i] = v;
+        }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int c = tid + 256 * i;
+            if (c < ACH)
+                *reinterpret_cast<uint4 *>(&As[buf][(c >> 3) * LDA + (c & 7) * 16]) = areg[i];
+        }
+    };
+
+    // Weight prefetch ring: PF groups x 32 bytes per lane, plus the group scale.
+    uint4 breg[PF][2];
+    float sreg[PF];
+    auto load_b = [&](int j, int g) {
+        if (g < G && nvalid) {
+            const uint4 *p = reinterpret_cast<const uint4 *>(wrow + g * kGroup);
+            breg[j][0] = p[0];
+            breg[j][1] = p[1];
+            sreg[j] = swrow[g];
+        } else {
+            breg[j][0] = make_uint4(0u, 0u, 0u, 0u);
+            breg[j][1] = make_uint4(0u, 0u, 0u, 0u);
+            sreg[j] = 0.0f;
+        }
+    };
+
+    float facc[MB][4];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
+
+#pragma unroll
+    for (int j = 0; j < PF; ++j) load_b(j, j);
+    load_a(0);
+    store_a(0);
+    __syncthreads();
+    if (G > 1) load_a(1);
+
+    for (int g0 = 0; g0 < G; g0 += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const int g = g0 + j;
+            if (g >= G) break;
+            const int buf = g & 1;
+            v4i acc[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) acc[i] = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const v4i b = as_v4i(breg[j][t]);
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const v4i a = as_v4i(*reinterpret_cast<const uint4 *>(
+                        &As[buf][(i * 16 + col) * LDA + slot * 32 + t * 16]));
+                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i], 0, 0, 0);
+                }
+            }
+            if (OUT == OUT_PARTIALS) {
+                // C layout of 16x16: lane holds column `col`, rows 4*slot + r.
+                if (nvalid) {
+#pragma unroll
+                    for (int i = 0; i < MB; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int m = i * 16 + slot * 4 + r;
+                            if (m < M)
+                                reinterpret_cast<int32_t *>(y)[((int64_t)m * N + n) * G + g] =
+                                    acc[i][r];
+                        }
+                }
+            } else {
+                const float s = sreg[j];
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        facc[i][r] = __builtin_fmaf((float)acc[i][r], s, facc[i][r]);
+            }
+            load_b(j, g + PF);
+            if (g + 1 < G) {
+                store_a(buf ^ 1);
+                if (g + 2 < G) load_a(g + 2);
+            }
+            __syncthreads();
+        }
+    }
+
+    if (OUT != OUT_PARTIALS && nvalid) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = i * 16 + slot * 4 + r;
+                if (m < M) store_out<OUT>(y, (int64_t)m * N + n, facc[i][r] * sa[m]);
+            }
+    }
+}
+
+// --------------------------------------------------------------------------
+// tile: 128x128 per workgroup, dense or grouped.
+// --------------------------------------------------------------------------
+struct TileArgs {
+    const int8_t *q;
+    const float *sa;
+    const int8_t *qw;
+    const float *sw;
+    const int32_t *offsets;   // grouped only
+    void *y;
+    int M;                    // dense rows, or R for grouped
+    int N, K, E;
+};
+
+constexpr int TBM = 128, TBN = 128, TLD = kGroup + 16;
+
+constexpr int kTileSmem = 2 * (TBM + TBN) * TLD;   // 73728 bytes (gfx950 allows 160 KB)
+
+// Grid: one workgroup per (row tile, column tile), flattened so that
+// consecutive workgroups share a row tile: bm = id / n_tiles, bn = id % n_tiles.
+template <int OUT, bool GROUPED>
+__global__ void __launch_bounds__(256, 2)
+gemm_tile_kernel(TileArgs p, int n_tiles) {
+    __shared__ __align__(16) int8_t smem[kTileSmem];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int N = p.N, K = p.K, G = K >> 7;
+    const int bm = (int)(blockIdx.x / (unsigned)n_tiles);
+    const int n0 = (int)(blockIdx.x - (unsigned)bm * (unsigned)n_tiles) * TBN;
+
+    // Row range of this tile and the weight slice it multiplies.
+    int row0, row_end;
+    const int8_t *qw = p.qw;
+    const float *sw = p.sw;
+    if (GROUPED) {
+        // Tile index -> (expert, row block): walk the expert segments in order.
+        // Segments are clamped to [0, R] so malformed offsets stay in bounds.
+        int t = bm, e = 0;
+        row0 = -1;
+        row_end = 0;
+        for (; e < p.E; ++e) {
+            int lo = p.offsets[e], hi = p.offsets[e + 1];
+            lo = lo < 0 ? 0 : (lo > p.M ? p.M : lo);
+            hi = hi < lo ? lo : (hi > p.M ? p.M : hi);
+            const int nt = (hi - lo + TBM - 1) / TBM;
+            if (t < nt) {
+                row0 = lo + t * TBM;
+                row_end = hi;
+                break;
+            }
+            t -= nt;
+        }
+        if (row0 < 0) return;   // surplus tile of the host-sized grid
+        qw += (int64_t)e * N * K;
+        sw += (int64_t)e * N * G;
+    } else {
+        row0 = bm * TBM;
+        row_end = p.M;
+    }
+
+    // Global -> register staging: 2048 chunks of 16 B per group (A then B).
+    uint4 st[8];
+    auto load_stage = [&](int g) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + 256 * (i & 3);
+            const int r = c >> 3, cc = c & 7;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (i < 4) {
+                if (row0 + r < row_end)
+                    v = *reinterpret_cast<const uint4 *>(p.q + (int64_t)(row0 + r) * K +
+                                                         g * kGroup + cc * 16);
+            } else {
+                if (n0 + r < N)
+                    v = *reinterpret_cast<const uint4 *>(qw + (int64_t)(n0 + r) * K +
+                                                         g * kGroup + cc * 16);
+            }
+            st[i] = v;
+        }
+    };
+    auto store_stage = [&](int buf) {
+        int8_t *base = smem + buf * (TBM + TBN) * TLD;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + 256 * (i & 3);
+            const int r = (c >> 3) + (i < 4 ? 0 : TBM), cc = c & 7;
+            *reinterpret_cast<uint4 *>(base + r * TLD + cc * 16) = st[i];
+        }
+    };
+
+    const int l32 = lane & 31, half = lane >> 5;
+    // Per-lane output columns of the two 32-wide column blocks.
+    int ncol[2];
+    bool nok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        ncol[j] = n0 + wn * 64 + j * 32 + l32;
+        nok[j] = ncol[j] < N;
+    }
+
+    v16f facc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) facc[i][j][r] = 0.0f;
+
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+
+    for (int g = 0; g < G; ++g) {
+        if (g + 1 < G) load_stage(g + 1);
+        float swv[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) swv[j] = nok[j] ? sw[(int64_t)ncol[j] * G + g] : 0.0f;
+
+        const int8_t *As = smem + (g & 1) * (TBM + TBN) * TLD;
+        const int8_t *Bs = As + TBM * TLD;
+        v16i acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            v4i a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = as_v4i(*reinterpret_cast<const uint4 *>(
+                    As + (wm * 64 + i * 32 + l32) * TLD + half * 64 + t * 16));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[j] = as_v4i(*reinterpret_cast<const uint4 *>(
+                    Bs + (wn * 64 + j * 32 + l32) * TLD + half * 64 + t * 16));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+
+        if (OUT == OUT_PARTIALS) {
+            // C layout of 32x32: lane holds column l32, rows 8*(r/4) + 4*half + r%4.
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                        if (m < row_end && nok[j])
+                            reinterpret_cast<int32_t *>(p.y)[((int64_t)m * N + ncol[j]) * G + g] =
+                                acc[i][j][r];
+                    }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        facc[i][j][r] = __builtin_fmaf((float)acc[i][j][r], swv[j], facc[i][j][r]);
+        }
+
+        if (g + 1 < G) store_stage((g + 1) & 1);
+        __syncthreads();
+    }
+
+    if (OUT != OUT_PARTIALS) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (m >= row_end) continue;
+                const float s = p.sa[m];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    if (nok[j]) store_out<OUT>(p.y, (int64_t)m * N + ncol[j], facc[i][j][r] * s);
+            }
+    }
+}
+
+template <int OUT, bool GROUPED>
+hipError_t launch_tile(const TileArgs &a, int64_t row_tiles, hipStream_t stream) {
+    const int64_t n_tiles = (a.N + TBN - 1) / TBN;
+    const int64_t total = row_tiles * n_tiles;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    gemm_tile_kernel<OUT, GROUPED><<<dim3((unsigned)total), 256, 0, stream>>>(a, (int)n_tiles);
+    return hipGetLastError();
+}
+
+constexpr int kSmallPF = 8;
+
+template <int OUT>
+hipError_t launch_smallm(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
+                         int M, int N, int K, void *y, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + 63) / 64));
+    if (M <= 16)
+        gemm_smallm_kernel<1, OUT, kSmallPF><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+    else if (M <= 32)
+        gemm_smallm_kernel<2, OUT, kSmallPF><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+    else
+        gemm_smallm_kernel<4, OUT, kSmallPF><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+    return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
+                        int M, int N, int K, void *y, hipStream_t stream) {
+    if (M <= 64) return launch_smallm<OUT>(q, sa, qw, sw, M, N, K, y, stream);
+    TileArgs a{q, sa, qw, sw, nullptr, y, M, N, K, 0};
+    return launch_tile<OUT, false>(a, (M + TBM - 1) / TBM, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
+                       int64_t M, int64_t N, int64_t K, void *y, int out, hipStream_t stream) {
+    switch (out) {
+        case OUT_BF16: return launch_dense<OUT_BF16>(q, sa, qw, sw, (int)M, (int)N, (int)K, y, stream);
+        case OUT_FP32: return launch_dense<OUT_FP32>(q, sa, qw, sw, (int)M, (int)N, (int)K, y, stream);
+        default: return launch_dense<OUT_PARTIALS>(q, nullptr, qw, nullptr, (int)M, (int)N, (int)K, y, stream);
+    }
+}
+
+hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *qw,
+                               const float *sw, const int32_t *offsets, int64_t E, int64_t R,
+                               int64_t N, int64_t K, void *y, int out, hipStream_t stream) {
+    TileArgs a{q, sa, qw, sw, offsets, y, (int)R, (int)N, (int)K, (int)E};
+    // Upper bound on the row tiles over all segments, from host values only.
+    const int64_t row_tiles = (R + TBM - 1) / TBM + E;
+    if (out == OUT_BF16) return launch_tile<OUT_BF16, true>(a, row_tiles, stream);
+    return launch_tile<OUT_FP32, true>(a, row_tiles, stream);
+}
+
+}  // namespace bsb

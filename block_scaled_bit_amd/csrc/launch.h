@@ -1,0 +1,31 @@
+// Host-side launchers of the gfx950 kernels (internal to libbsb).
+// Arguments have been validated by the C-ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsb {
+
+hipError_t launch_quantize_act(const uint16_t *x, int64_t M, int64_t K, int8_t *q,
+                               float *sa, hipStream_t stream);
+
+hipError_t launch_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t N,
+                                   int64_t K, int fnuz, int8_t *qw, float *sw,
+                                   hipStream_t stream);
+
+hipError_t launch_decode_mxfp4(const uint8_t *packed, const uint8_t *scale, int64_t E,
+                               int64_t N, int64_t K, int8_t *qw, float *sw,
+                               hipStream_t stream);
+
+// out: 0 = BF16, 1 = FP32, 2 = INT32 group partials [M, N, G]
+hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw,
+                       const float *sw, int64_t M, int64_t N, int64_t K, void *y,
+                       int out, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *qw,
+                               const float *sw, const int32_t *offsets, int64_t E,
+                               int64_t R, int64_t N, int64_t K, void *y, int out,
+                               hipStream_t stream);
+
+}  // namespace bsb

@@ -1,0 +1,124 @@
+// Dynamic per-token INT8 quantisation of BF16 activations on gfx950.
+//
+// [P3] sec. 3.1: per-token scales computed at run time from each token's own
+// range. Rule: sa = amax/127 (IEEE float32), q = clamp(rint(x/sa), -127, 127).
+//
+// HBM-bound: 2 bytes in, 1 byte out per element. One workgroup per token row;
+// the row is read once with 16-byte coalesced loads and kept in registers
+// while the workgroup reduces the row maximum, then quantised from registers.
+#include "device_common.h"
+#include "launch.h"
+
+namespace bsb {
+
+namespace {
+
+// Max of the 15-bit BF16 magnitudes in a dword holding two BF16 values. For
+// finite BF16 the unsigned order of |bits| is the order of |values|, so the
+// row maximum is an exact integer max.
+__device__ __forceinline__ uint32_t mag2_max(uint32_t w, uint32_t cur) {
+    uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+    cur = cur > lo ? cur : lo;
+    return cur > hi ? cur : hi;
+}
+
+__device__ __forceinline__ uint32_t row_reduce_max(uint32_t v, uint32_t *red) {
+    v = group_max_u32(v, kWave);
+    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    uint32_t r = red[0];
+    for (int i = 1; i < nw; ++i) r = r > red[i] ? r : red[i];
+    return r;
+}
+
+__device__ __forceinline__ uint2 quant8(uint4 v, float s, bool zero) {
+    if (zero) return make_uint2(0u, 0u);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    int o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = quant_elem(bf16_to_f32(w[i] & 0xFFFFu), s);
+        o[2 * i + 1] = quant_elem(bf16_to_f32(w[i] >> 16), s);
+    }
+    return make_uint2(pack4_i8(o[0], o[1], o[2], o[3]), pack4_i8(o[4], o[5], o[6], o[7]));
+}
+
+// CH 16-byte chunks per thread live in registers (K <= 8 * CH * blockDim).
+template <int CH>
+__global__ void __launch_bounds__(256)
+quantize_act_kernel(const uint16_t *__restrict__ x, int64_t K, int8_t *__restrict__ q,
+                    float *__restrict__ sa) {
+    __shared__ uint32_t red[4];
+    const int64_t m = blockIdx.x;
+    const int nchunk = (int)(K >> 3);
+    const uint4 *xr = reinterpret_cast<const uint4 *>(x + m * K);
+    uint2 *qr = reinterpret_cast<uint2 *>(q + m * K);
+    uint4 v[CH];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = threadIdx.x + c * blockDim.x;
+        v[c] = idx < nchunk ? xr[idx] : make_uint4(0u, 0u, 0u, 0u);
+        amax = mag2_max(v[c].x, amax);
+        amax = mag2_max(v[c].y, amax);
+        amax = mag2_max(v[c].z, amax);
+        amax = mag2_max(v[c].w, amax);
+    }
+    amax = row_reduce_max(amax, red);
+    const float s = absmax_scale(bf16_to_f32(amax));
+    if (threadIdx.x == 0) sa[m] = s;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = threadIdx.x + c * blockDim.x;
+        if (idx < nchunk) qr[idx] = quant8(v[c], s, amax == 0);
+    }
+}
+
+// Rows longer than the register-resident limit: two passes over the row
+// (the second pass re-reads from cache).
+__global__ void __launch_bounds__(256)
+quantize_act_stream_kernel(const uint16_t *__restrict__ x, int64_t K, int8_t *__restrict__ q,
+                           float *__restrict__ sa) {
+    __shared__ uint32_t red[4];
+    const int64_t m = blockIdx.x;
+    const int64_t nchunk = K >> 3;
+    const uint4 *xr = reinterpret_cast<const uint4 *>(x + m * K);
+    uint2 *qr = reinterpret_cast<uint2 *>(q + m * K);
+    uint32_t amax = 0;
+    for (int64_t idx = threadIdx.x; idx < nchunk; idx += blockDim.x) {
+        const uint4 v = xr[idx];
+        amax = mag2_max(v.x, amax);
+        amax = mag2_max(v.y, amax);
+        amax = mag2_max(v.z, amax);
+        amax = mag2_max(v.w, amax);
+    }
+    amax = row_reduce_max(amax, red);
+    const float s = absmax_scale(bf16_to_f32(amax));
+    if (threadIdx.x == 0) sa[m] = s;
+    for (int64_t idx = threadIdx.x; idx < nchunk; idx += blockDim.x)
+        qr[idx] = quant8(xr[idx], s, amax == 0);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_act(const uint16_t *x, int64_t M, int64_t K, int8_t *q, float *sa,
+                               hipStream_t stream) {
+    const int64_t nchunk = K / 8;
+    const int threads = (int)(nchunk >= 256 ? 256 : ((nchunk + 63) / 64) * 64);
+    const int64_t ch = (nchunk + threads - 1) / threads;
+    const dim3 grid((unsigned)M), block((unsigned)threads);
+    if (ch <= 1)
+        quantize_act_kernel<1><<<grid, block, 0, stream>>>(x, K, q, sa);
+    else if (ch <= 2)
+        quantize_act_kernel<2><<<grid, block, 0, stream>>>(x, K, q, sa);
+    else if (ch <= 4)
+        quantize_act_kernel<4><<<grid, block, 0, stream>>>(x, K, q, sa);
+    else if (ch <= 8)
+        quantize_act_kernel<8><<<grid, block, 0, stream>>>(x, K, q, sa);
+    else
+        quantize_act_stream_kernel<<<grid, block, 0, stream>>>(x, K, q, sa);
+    return hipGetLastError();
+}
+
+}  // namespace bsb

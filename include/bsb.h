@@ -1,0 +1,179 @@
+/*
+ * bsb.h — block-scaled INT8 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbsb.so. Sources ("pages"):
+ *   [P1] "Running DeepSeek-V4-Flash-Vision on 4x A800: adaptation"
+ *        (yfxerp.com/news/113390), sec. 1 (constraints table) and sec. 2
+ *        (per-segment re-routing: dequantise / repack onto the INT8 path).
+ *   [P2] "Deploying DeepSeek-V4-Flash on AMD MI300X: a hard-core
+ *        retrospective" (aimsg.uk), sections "FP8 dialect clash",
+ *        "HIP Graphs limits" and "Loose ends".
+ *   [P3] "Hunyuan 770B in INT8 on domestic accelerators"
+ *        (pwwt.cn/news/4495474), sec. 3.1 and sec. 1.3 / 4.4.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a DEVICE pointer into memory the caller
+ *    allocated and owns (PyTorch in the Python binding). The library
+ *    allocates nothing, keeps no pointer after returning, never synchronises
+ *    and never reads device memory on the host. Work is enqueued on `stream`
+ *    (a hipStream_t passed as void*, NULL = the null stream) of the current
+ *    device, so every call can be captured into a HIP graph: launch sizes
+ *    come from the host-side size arguments only, as [P2] "HIP Graphs limits"
+ *    requires of graph-safe kernels (device pointers and sizes, no host reads
+ *    mid-way, no scratch allocation).
+ *  - All matrices are row-major and contiguous. K is the reduction dimension
+ *    and is contiguous in both operands; G = K / 128 is the number of
+ *    128-wide K groups.
+ *  - Sizes: K % 128 == 0 and K > 0; N >= 1; M, R >= 0 (0 rows is a
+ *    successful no-op that launches nothing).
+ *  - Every pointer must be 16-byte aligned (BSB_ERR_MISALIGNED otherwise).
+ *  - Arguments are validated before anything is launched: a NULL pointer
+ *    with a non-empty size, a negative or inconsistent size, or a bad enum
+ *    returns BSB_ERR_INVALID_ARG and launches nothing. Then, on the first
+ *    call per device, the device's architecture is checked: anything other
+ *    than gfx950 returns BSB_ERR_UNSUPPORTED_DEVICE (fail fast instead of
+ *    running a kernel built for another chip, [P1] sec. 3). A launch failure
+ *    reported by hipGetLastError() returns BSB_ERR_LAUNCH. Faults inside a
+ *    kernel surface at the caller's next synchronisation, as usual for HIP.
+ *  - Outputs are written exactly once for every in-range element; nothing
+ *    outside the documented output extents is written.
+ *  - Calls are reentrant; calls on different streams do not share state.
+ *  - No C++ exception crosses this boundary.
+ */
+#ifndef BSB_H
+#define BSB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsb_status {
+    BSB_OK = 0,
+    BSB_ERR_INVALID_ARG = 1,
+    BSB_ERR_UNSUPPORTED_DEVICE = 2,
+    BSB_ERR_MISALIGNED = 3,
+    BSB_ERR_LAUNCH = 4
+} bsb_status;
+
+typedef enum bsb_out_dtype {
+    BSB_OUT_BF16 = 0,   /* uint16 BF16 bits, round to nearest even */
+    BSB_OUT_FP32 = 1    /* IEEE float32 */
+} bsb_out_dtype;
+
+typedef enum bsb_fp8_dialect {
+    BSB_FP8_OCP = 0,    /* E4M3FN:   bias 7, max 448, 0x7F/0xFF NaN, 0x80 = -0 */
+    BSB_FP8_FNUZ = 1    /* E4M3FNUZ: bias 8, max 240, 0x80 NaN, no -0, no inf  */
+} bsb_fp8_dialect;
+
+/*
+ * Dynamic per-token INT8 quantisation of BF16 activations ([P3] sec. 3.1:
+ * per-token scales computed at run time from each token's own range).
+ * For each row m:
+ *     amax  = max_k |x[m,k]|
+ *     sa[m] = amax / 127                     (IEEE float32 divide)
+ *     q[m,k] = clamp(rint(x[m,k] / sa[m]), -127, 127)
+ * with a true IEEE divide by the stored scale and round-half-to-even; an
+ * all-zero row gives sa = 0 and q = 0. Inputs must be finite.
+ *   x_bf16  [M, K] BF16 bits (read)
+ *   q       [M, K] int8      (written)
+ *   sa      [M]    float32   (written)
+ */
+bsb_status bsb_quantize_act(const uint16_t *x_bf16, int64_t M, int64_t K,
+                            int8_t *q, float *sa, void *stream);
+
+/*
+ * W8A8 GEMM with per-(output row, 128-wide K group) weight scales ([P3]
+ * sec. 3.1: INT8 multiply-accumulate into INT32 inside the matmul, FP32
+ * scales applied last):
+ *     P[m,n,g] = sum_{k in group g} q[m,k] * qw[n,k]        (exact INT32)
+ *     acc      = 0; for g = 0..G-1: acc = fmaf((float)P[m,n,g], sw[n,g], acc)
+ *     y[m,n]   = acc * sa[m]        (float32), stored as BF16 (RNE) or FP32
+ * The float32 accumulation runs over g in ascending order for every output
+ * element (no split-K), so results do not depend on the launch shape.
+ *   q   [M, K] int8, sa [M] float32       (output of bsb_quantize_act)
+ *   qw  [N, K] int8, sw [N, G] float32    (weights, [out, in] layout)
+ *   y   [M, N] BF16 bits or float32 per `out`
+ */
+bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa,
+                              const int8_t *qw, const float *sw,
+                              int64_t M, int64_t N, int64_t K,
+                              void *y, bsb_out_dtype out, void *stream);
+
+/*
+ * Grouped (MoE) form: rows are sorted by expert and expert e owns rows
+ * [offsets[e], offsets[e+1]) ([P3] sec. 1.3: experts resident, each token
+ * runs through a few of them). Each segment is multiplied with its expert's
+ * weights by the rule of bsb_gemm_w8a8_g128. Tail rows of a tile are masked
+ * by the segment end, never by a padded bound ([P2] "Loose ends" item 2);
+ * empty experts launch no work and read no weights.
+ *   q       [R, K] int8, sa [R] float32
+ *   qw      [E, N, K] int8, sw [E, N, G] float32
+ *   offsets [E+1] int32, DEVICE memory; preconditions: offsets[0] = 0,
+ *           non-decreasing, offsets[E] = R. The kernel clamps every segment
+ *           to [0, R], so a violated precondition gives unspecified values in
+ *           y but never an out-of-bounds access.
+ *   y       [R, N] BF16 bits or float32
+ * The launch grid is sized from host values only: ceil(R/BM) + E row tiles.
+ */
+bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa,
+                                      const int8_t *qw, const float *sw,
+                                      const int32_t *offsets,
+                                      int64_t E, int64_t R, int64_t N, int64_t K,
+                                      void *y, bsb_out_dtype out, void *stream);
+
+/*
+ * FP8 e4m3 weights with [128,128] UE8M0 block scales ([P1] sec. 1) ->
+ * INT8 per-group-128 ([P1] sec. 2 repack onto the INT8 path). The dialect is
+ * explicit: the same bytes read as OCP are exactly twice their fnuz reading
+ * ([P2] "FP8 dialect clash").
+ *     W[n,k]  = e4m3_dialect(w[n,k]) * 2^(bs[n/128, k/128] - 127)
+ *     then per (n, g) the rule of bsb_quantize_act over W[n, 128g .. 128g+127]
+ *   w   [N, K] uint8 e4m3 bytes; N % 128 == 0
+ *   bs  [N/128, K/128] uint8 UE8M0 exponents (255 = NaN: outside the domain)
+ *   qw  [N, K] int8, sw [N, G] float32 (written)
+ * Bytes that the dialect defines as NaN are outside the domain.
+ */
+bsb_status bsb_decode_fp8_block(const uint8_t *w, const uint8_t *bs,
+                                int64_t N, int64_t K, bsb_fp8_dialect dialect,
+                                int8_t *qw, float *sw, void *stream);
+
+/*
+ * MXFP4 (E2M1 elements, 1x32 UE8M0 block scales along K) experts ([P1]
+ * sec. 1) -> INT8 per-group-128 ([P1] sec. 2).
+ *     W[e,n,k] = E2M1(nibble k of row (e,n)) * 2^(scale[e,n,k/32] - 127)
+ *     then per (e, n, g) the rule of bsb_quantize_act
+ *   packed [E, N, K/2] uint8: element 2j in the low nibble of byte j,
+ *          element 2j+1 in the high nibble
+ *   scale  [E, N, K/32] uint8 UE8M0 exponents
+ *   qw     [E, N, K] int8, sw [E, N, G] float32 (written)
+ */
+bsb_status bsb_decode_mxfp4(const uint8_t *packed, const uint8_t *scale,
+                            int64_t E, int64_t N, int64_t K,
+                            int8_t *qw, float *sw, void *stream);
+
+/*
+ * Inspection form of bsb_gemm_w8a8_g128 for tests: the same kernels and
+ * main loop selected by the same M, with the epilogue replaced by a store of
+ * the exact INT32 group partials ([P3] sec. 3.1 INT32 accumulator).
+ *   P [M, N, G] int32 (written)
+ */
+bsb_status bsb_gemm_w8a8_g128_partials(const int8_t *q, const int8_t *qw,
+                                       int64_t M, int64_t N, int64_t K,
+                                       int32_t *P, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *bsb_status_string(bsb_status s);
+
+/* ABI version of this header; bumped on any incompatible change. */
+int bsb_abi_version(void);
+
+#define BSB_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSB_H */

@@ -1,0 +1,102 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/bsb.h
+declares, and rejects bad arguments before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+import block_scaled_bit_amd as bsb
+from block_scaled_bit_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsb.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED = 0, 1, 2, 3
+A = 0x10000          # fake, 16-byte aligned, never dereferenced
+U = 0x10008          # fake, misaligned
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(bsb_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libbsb.so is not built (python -m block_scaled_bit_amd.build)")
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.bsb_abi_version() == 1
+    for code, name in _lib.STATUS.items():
+        assert L.bsb_status_string(code).decode().startswith(name)
+    assert L.bsb_status_string(99).decode() == "BSB_ERR_UNKNOWN"
+
+
+def test_invalid_sizes_return_invalid_arg(L):
+    # K not a multiple of 128, negative sizes, empty N
+    assert L.bsb_quantize_act(A, 4, 100, A, A, None) == INVALID
+    assert L.bsb_quantize_act(A, -1, 128, A, A, None) == INVALID
+    assert L.bsb_gemm_w8a8_g128(A, A, A, A, 4, 0, 128, A, 0, None) == INVALID
+    assert L.bsb_gemm_w8a8_g128(A, A, A, A, 4, 8, 130, A, 0, None) == INVALID
+    assert L.bsb_gemm_w8a8_g128(A, A, A, A, -4, 8, 128, A, 0, None) == INVALID
+    assert L.bsb_gemm_w8a8_g128_partials(A, A, 4, 8, 0, A, None) == INVALID
+    assert L.bsb_grouped_gemm_w8a8_g128(A, A, A, A, A, 0, 4, 8, 128, A, 0, None) == INVALID
+    assert L.bsb_decode_fp8_block(A, A, 100, 128, 0, A, A, None) == INVALID   # N % 128
+    assert L.bsb_decode_mxfp4(A, A, 1, 8, 96, A, A, None) == INVALID
+
+
+def test_bad_enums_return_invalid_arg(L):
+    assert L.bsb_gemm_w8a8_g128(A, A, A, A, 4, 8, 128, A, 7, None) == INVALID
+    assert L.bsb_grouped_gemm_w8a8_g128(A, A, A, A, A, 2, 4, 8, 128, A, -1, None) == INVALID
+    assert L.bsb_decode_fp8_block(A, A, 128, 128, 2, A, A, None) == INVALID
+
+
+def test_null_pointers_return_invalid_arg(L):
+    assert L.bsb_quantize_act(None, 4, 128, A, A, None) == INVALID
+    assert L.bsb_gemm_w8a8_g128(A, None, A, A, 4, 8, 128, A, 0, None) == INVALID
+    assert L.bsb_grouped_gemm_w8a8_g128(A, A, A, A, None, 2, 4, 8, 128, A, 0, None) == INVALID
+    assert L.bsb_decode_fp8_block(A, A, 128, 128, 0, None, A, None) == INVALID
+    assert L.bsb_decode_mxfp4(A, None, 1, 8, 128, A, A, None) == INVALID
+    assert L.bsb_gemm_w8a8_g128_partials(A, A, 4, 8, 128, None, None) == INVALID
+
+
+def test_misaligned_pointers(L):
+    assert L.bsb_quantize_act(U, 4, 128, A, A, None) == MISALIGNED
+    assert L.bsb_gemm_w8a8_g128(A, A, A, U, 4, 8, 128, A, 1, None) == MISALIGNED
+    assert L.bsb_grouped_gemm_w8a8_g128(A, A, A, A, U, 2, 4, 8, 128, A, 0, None) == MISALIGNED
+    assert L.bsb_decode_mxfp4(A, A, 1, 8, 128, U, A, None) == MISALIGNED
+
+
+def test_empty_rows_are_a_successful_no_op(L):
+    # M = 0 / R = 0: nothing to do, nothing launched, null pointers allowed
+    assert L.bsb_quantize_act(None, 0, 128, None, None, None) == OK
+    assert L.bsb_gemm_w8a8_g128(None, None, None, None, 0, 8, 128, None, 0, None) == OK
+    assert L.bsb_grouped_gemm_w8a8_g128(None, None, None, None, None, 3, 0, 8, 128, None, 0,
+                                        None) == OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_no_gpu_is_unsupported_device(L):
+    # valid arguments, but no gfx950 device is present: fail fast, launch nothing
+    assert L.bsb_quantize_act(A, 4, 128, A, A, None) == UNSUPPORTED
+    assert L.bsb_gemm_w8a8_g128(A, A, A, A, 4, 8, 128, A, 0, None) == UNSUPPORTED
+
+
+def test_python_binding_validates_before_calling():
+    cpu = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bsb.quantize_act(cpu)                      # not on a GPU
+    with pytest.raises(ValueError):
+        bsb.gemm_w8a8_g128(torch.zeros(4, 128, dtype=torch.int8), None, None, None)
