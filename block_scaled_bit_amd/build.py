@@ -45,7 +45,7 @@ def hipcc() -> str:
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]   # src may be absolute
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the GPU target feature; that warning is harmless
     noise = "not a recognized feature for this target"

@@ -62,3 +62,27 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 }
 
 }  // namespace bsb
+
+namespace bsb {
+
+// Raw buffer resource over [base, base + bytes). Loads at offsets >= bytes
+// return zero without touching memory, which lets the kernels issue every
+// prefetch unconditionally (no divergent branches around loads, so the
+// compiler's memory-counter waits stay exact). Word 3 = 0x00020000: the
+// untyped-buffer configuration for CDNA.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+constexpr uint32_t kOOB = 0x80000000u;   // an offset past every resource used here
+
+}  // namespace bsb

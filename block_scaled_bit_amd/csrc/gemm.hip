@@ -56,61 +56,66 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // --------------------------------------------------------------------------
 // smallm: M <= 16*MB tokens, weight-streaming.
 // --------------------------------------------------------------------------
-template <int MB, int OUT, int PF>
+// Workgroup = 4 waves = 64 weight rows (output columns) starting at n0; each
+// wave owns 16 of them. K is processed in super-stages of S groups, double
+// buffered in registers: while super-stage s is multiplied, all loads of
+// super-stage s+1 are in flight (between S and 2S groups per wave). The memory
+// counter completes loads in issue order, so issuing a whole super-stage and
+// then waiting for the previous one gives exact waits with no drain. The S
+// activation tiles of a super-stage go to LDS together (one barrier per
+// super-stage) and are shared by the four waves.
+//
+// All loads are buffer loads whose out-of-range offsets read zero (rows >= M,
+// columns >= N, groups >= G), so no load sits behind a branch. Requires
+// 64*K < 2^31 (checked by the launcher).
+template <int MB, int OUT, int S>
 __global__ void __launch_bounds__(256)
 gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                    const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N,
                    int K, void *__restrict__ y) {
     constexpr int ROWS = 16 * MB;
-    constexpr int LDA = kGroup + 16;   // padded LDS row (bytes)
-    __shared__ __align__(16) int8_t As[2][ROWS * LDA];
+    constexpr int LDA = kGroup + 16;          // padded LDS row (bytes)
+    constexpr int TILE = ROWS * LDA;          // one group's activation tile
+    __shared__ __align__(16) int8_t As[2][S][TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = K >> 7;
     const int col = lane & 15;          // B column / A row within a 16-block
     const int slot = lane >> 4;         // which 32-byte quarter of the group
-    const int n = blockIdx.x * 64 + wave * 16 + col;
-    const bool nvalid = n < N;
-    const int8_t *wrow = qw + (int64_t)(nvalid ? n : 0) * K + slot * 32;
-    const float *swrow = sw + (int64_t)(nvalid ? n : 0) * G;
+    const int n0 = blockIdx.x * 64;
+    const int nrows = min(64, N - n0);
+    const int nl = wave * 16 + col;     // this lane's weight row within the slice
+    const int n = n0 + nl;
+
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw + (int64_t)n0 * K, (uint32_t)(nrows * K));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sw + (int64_t)n0 * G, (uint32_t)(nrows * G * 4));
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(q, (uint32_t)(M * K));
+    const uint32_t woff = (uint32_t)(nl * K + slot * 32);
+    const uint32_t soff = (uint32_t)(nl * G * 4);
 
     // Cooperative A loads: ROWS x 128 B per group = ROWS*8 chunks of 16 B.
     constexpr int ACH = ROWS * 8;
-    constexpr int APT = (ACH + 255) / 256;   // chunks per thread
-    uint4 areg[APT];
-    auto load_a = [&](int g) {
-#pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int c = tid + 256 * i;
-            const int r = c >> 3, cc = c & 7;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (c < ACH && r < M)
-                v = *reinterpret_cast<const uint4 *>(q + (int64_t)r * K + g * kGroup + cc * 16);
-            areg[i] = v;
-        }
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int c = tid + 256 * i;
-            if (c < ACH)
-                *reinterpret_cast<uint4 *>(&As[buf][(c >> 3) * LDA + (c & 7) * 16]) = areg[i];
-        }
-    };
+    constexpr int APT = (ACH + 255) / 256;   // chunks per thread per group
 
-    // Weight prefetch ring: PF groups x 32 bytes per lane, plus the group scale.
-    uint4 breg[PF][2];
-    float sreg[PF];
-    auto load_b = [&](int j, int g) {
-        if (g < G && nvalid) {
-            const uint4 *p = reinterpret_cast<const uint4 *>(wrow + g * kGroup);
-            breg[j][0] = p[0];
-            breg[j][1] = p[1];
-            sreg[j] = swrow[g];
-        } else {
-            breg[j][0] = make_uint4(0u, 0u, 0u, 0u);
-            breg[j][1] = make_uint4(0u, 0u, 0u, 0u);
-            sreg[j] = 0.0f;
+    v4i areg[2][S][APT];
+    v4i breg[2][S][2];
+    float sreg[2][S];
+
+    auto issue = [&](int set, int s0) {      // all loads of the super-stage starting at group s0
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            const int g = s0 + j;
+            const bool in = g < G;
+#pragma unroll
+            for (int i = 0; i < APT; ++i) {
+                const int c = tid + 256 * i;
+                const uint32_t off = (uint32_t)((c >> 3) * K + (c & 7) * 16 + g * kGroup);
+                areg[set][j][i] = buf_load16(ra, (in && c < ACH) ? off : kOOB);
+            }
+            const uint32_t o = in ? woff + (uint32_t)g * kGroup : kOOB;
+            breg[set][j][0] = buf_load16(rw, o);
+            breg[set][j][1] = buf_load16(rw, o + 16);
+            sreg[set][j] = buf_load_f32(rs, in ? soff + (uint32_t)g * 4 : kOOB);
         }
     };
 
@@ -120,35 +125,36 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 #pragma unroll
         for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
 
+    auto consume = [&](int set, int s0) {
 #pragma unroll
-    for (int j = 0; j < PF; ++j) load_b(j, j);
-    load_a(0);
-    store_a(0);
-    __syncthreads();
-    if (G > 1) load_a(1);
-
-    for (int g0 = 0; g0 < G; g0 += PF) {
+        for (int j = 0; j < S; ++j)
 #pragma unroll
-        for (int j = 0; j < PF; ++j) {
-            const int g = g0 + j;
+            for (int i = 0; i < APT; ++i) {
+                const int c = tid + 256 * i;
+                if (ACH % 256 == 0 || c < ACH)
+                    *reinterpret_cast<v4i *>(&As[set][j][(c >> 3) * LDA + (c & 7) * 16]) =
+                        areg[set][j][i];
+            }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            const int g = s0 + j;
             if (g >= G) break;
-            const int buf = g & 1;
             v4i acc[MB];
 #pragma unroll
             for (int i = 0; i < MB; ++i) acc[i] = v4i{0, 0, 0, 0};
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const v4i b = as_v4i(breg[j][t]);
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
-                    const v4i a = as_v4i(*reinterpret_cast<const uint4 *>(
-                        &As[buf][(i * 16 + col) * LDA + slot * 32 + t * 16]));
-                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i], 0, 0, 0);
+                    const v4i a = *reinterpret_cast<const v4i *>(
+                        &As[set][j][(i * 16 + col) * LDA + slot * 32 + t * 16]);
+                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, breg[set][j][t], acc[i], 0, 0, 0);
                 }
             }
             if (OUT == OUT_PARTIALS) {
                 // C layout of 16x16: lane holds column `col`, rows 4*slot + r.
-                if (nvalid) {
+                if (nl < nrows) {
 #pragma unroll
                     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -160,23 +166,25 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                         }
                 }
             } else {
-                const float s = sreg[j];
+                const float s = sreg[set][j];
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         facc[i][r] = __builtin_fmaf((float)acc[i][r], s, facc[i][r]);
             }
-            load_b(j, g + PF);
-            if (g + 1 < G) {
-                store_a(buf ^ 1);
-                if (g + 2 < G) load_a(g + 2);
-            }
-            __syncthreads();
         }
+    };
+
+    issue(0, 0);
+    for (int s0 = 0; s0 < G; s0 += 2 * S) {
+        issue(1, s0 + S);
+        consume(0, s0);
+        issue(0, s0 + 2 * S);
+        consume(1, s0 + S);
     }
 
-    if (OUT != OUT_PARTIALS && nvalid) {
+    if (OUT != OUT_PARTIALS && nl < nrows) {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -384,25 +392,31 @@ hipError_t launch_tile(const TileArgs &a, int64_t row_tiles, hipStream_t stream)
     return hipGetLastError();
 }
 
-constexpr int kSmallPF = 8;
+#ifndef BSB_SMALLM_S
+#define BSB_SMALLM_S 4
+#endif
+constexpr int kSmallS = BSB_SMALLM_S;   // groups per super-stage
 
 template <int OUT>
 hipError_t launch_smallm(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                          int M, int N, int K, void *y, hipStream_t stream) {
     const dim3 grid((unsigned)((N + 63) / 64));
     if (M <= 16)
-        gemm_smallm_kernel<1, OUT, kSmallPF><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+        gemm_smallm_kernel<1, OUT, kSmallS><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
     else if (M <= 32)
-        gemm_smallm_kernel<2, OUT, kSmallPF><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+        gemm_smallm_kernel<2, OUT, kSmallS><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
     else
-        gemm_smallm_kernel<4, OUT, kSmallPF><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+        gemm_smallm_kernel<4, OUT, kSmallS><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
     return hipGetLastError();
 }
 
 template <int OUT>
 hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                         int M, int N, int K, void *y, hipStream_t stream) {
-    if (M <= 64) return launch_smallm<OUT>(q, sa, qw, sw, M, N, K, y, stream);
+    // smallm addresses a 64-row weight slice and the whole activation matrix
+    // with 32-bit buffer offsets
+    if (M <= 64 && (int64_t)64 * K < ((int64_t)1 << 31))
+        return launch_smallm<OUT>(q, sa, qw, sw, M, N, K, y, stream);
     TileArgs a{q, sa, qw, sw, nullptr, y, M, N, K, 0};
     return launch_tile<OUT, false>(a, (M + TBM - 1) / TBM, stream);
 }
