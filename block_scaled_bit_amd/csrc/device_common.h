@@ -85,4 +85,8 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
 
 constexpr uint32_t kOOB = 0x80000000u;   // an offset past every resource used here
 
+// Cache-policy bits of a buffer load: non-temporal (streamed once, do not
+// keep in the caches).
+constexpr int kNonTemporal = 2;
+
 }  // namespace bsb

@@ -56,27 +56,37 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // --------------------------------------------------------------------------
 // smallm: M <= 16*MB tokens, weight-streaming.
 // --------------------------------------------------------------------------
-// Workgroup = 4 waves = 64 weight rows (output columns) starting at n0; each
-// wave owns 16 of them. K is processed in super-stages of S groups, double
-// buffered in registers: while super-stage s is multiplied, all loads of
-// super-stage s+1 are in flight (between S and 2S groups per wave). The memory
-// counter completes loads in issue order, so issuing a whole super-stage and
-// then waiting for the previous one gives exact waits with no drain. The S
-// activation tiles of a super-stage go to LDS together (one barrier per
-// super-stage) and are shared by the four waves.
+// Workgroup = 4 waves = 64 weight rows (output columns) n0 .. n0+63; each
+// wave owns 16 of them (v_mfma_i32_16x16x64_i8, MB 16-token blocks).
 //
-// All loads are buffer loads whose out-of-range offsets read zero (rows >= M,
-// columns >= N, groups >= G), so no load sits behind a branch. Requires
-// 64*K < 2^31 (checked by the launcher).
-template <int MB, int OUT, int S>
+// K is walked in super-stages of S groups. A super-stage's weight tile
+// (64 rows x S*128 B) and activation tile (16*MB rows x S*128 B) are read
+// with fully coalesced 16-byte buffer loads (8 lanes per 128-byte row line,
+// the pattern HBM streams fastest, with the non-temporal hint on the
+// weights, which are touched once) into a ring of D register sets, then
+// written to a double-buffered LDS tile from which every wave reads its MFMA
+// fragments. One barrier per super-stage. The memory counter completes loads
+// in issue order; a set is waited for only after the D-1 younger sets have
+// been issued, so (D-1)*S groups stay in flight without any drain.
+//
+// LDS tile layout: [group][row][8 x 16-byte chunks], chunk j of row r stored
+// at position j ^ ((r >> 1) & 7). Fragment reads (16 rows, one chunk index)
+// and the row-line writes (2 rows x 8 chunks per 16 lanes) both hit 16
+// distinct 16-byte bank groups.
+//
+// Out-of-range rows, columns and groups read zero through the buffer
+// descriptors, so no load sits behind a branch. Requires 64*K < 2^31
+// (checked by the launcher).
+template <int MB, int OUT, int S, int D>
 __global__ void __launch_bounds__(256)
 gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                    const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N,
                    int K, void *__restrict__ y) {
     constexpr int ROWS = 16 * MB;
-    constexpr int LDA = kGroup + 16;          // padded LDS row (bytes)
-    constexpr int TILE = ROWS * LDA;          // one group's activation tile
-    __shared__ __align__(16) int8_t As[2][S][TILE];
+    constexpr int BT = 64 * kGroup;           // one group of the weight tile (bytes)
+    constexpr int AT = ROWS * kGroup;         // one group of the activation tile
+    __shared__ __align__(16) int8_t Bs[2][S * BT];
+    __shared__ __align__(16) int8_t As[2][S * AT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = K >> 7;
@@ -90,32 +100,53 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw + (int64_t)n0 * K, (uint32_t)(nrows * K));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(sw + (int64_t)n0 * G, (uint32_t)(nrows * G * 4));
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(q, (uint32_t)(M * K));
-    const uint32_t woff = (uint32_t)(nl * K + slot * 32);
-    const uint32_t soff = (uint32_t)(nl * G * 4);
 
-    // Cooperative A loads: ROWS x 128 B per group = ROWS*8 chunks of 16 B.
-    constexpr int ACH = ROWS * 8;
-    constexpr int APT = (ACH + 255) / 256;   // chunks per thread per group
+    constexpr int BPT = S * BT / (256 * 16);          // weight chunks per thread per set
+    constexpr int ACH = S * AT / 16;                  // activation chunks per set
+    constexpr int APT = (ACH + 255) / 256;
+    static_assert(BPT * 256 * 16 == S * BT, "weight tile must split evenly");
 
-    v4i areg[2][S][APT];
-    v4i breg[2][S][2];
-    float sreg[2][S];
+    v4i breg[D][BPT];
+    v4i areg[D][APT];
+    float sreg[D][S];
 
-    auto issue = [&](int set, int s0) {      // all loads of the super-stage starting at group s0
+    auto issue = [&](int d, int s0) {   // loads of the super-stage starting at group s0
 #pragma unroll
-        for (int j = 0; j < S; ++j) {
-            const int g = s0 + j;
-            const bool in = g < G;
+        for (int i = 0; i < BPT; ++i) {
+            const int c = tid + 256 * i;
+            const int gl = c >> 9, row = (c >> 3) & 63, j = c & 7;
+            const int g = s0 + gl;
+            const uint32_t off = (uint32_t)(row * K + g * kGroup + j * 16);
+            breg[d][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(g < G ? off : kOOB), 0,
+                                                               kNonTemporal);
+        }
 #pragma unroll
-            for (int i = 0; i < APT; ++i) {
-                const int c = tid + 256 * i;
-                const uint32_t off = (uint32_t)((c >> 3) * K + (c & 7) * 16 + g * kGroup);
-                areg[set][j][i] = buf_load16(ra, (in && c < ACH) ? off : kOOB);
-            }
-            const uint32_t o = in ? woff + (uint32_t)g * kGroup : kOOB;
-            breg[set][j][0] = buf_load16(rw, o);
-            breg[set][j][1] = buf_load16(rw, o + 16);
-            sreg[set][j] = buf_load_f32(rs, in ? soff + (uint32_t)g * 4 : kOOB);
+        for (int i = 0; i < APT; ++i) {
+            const int c = tid + 256 * i;
+            const int gl = c / (ROWS * 8), row = (c >> 3) % ROWS, j = c & 7;
+            const int g = s0 + gl;
+            const uint32_t off = (uint32_t)(row * K + g * kGroup + j * 16);
+            areg[d][i] = buf_load16(ra, (g < G && c < ACH) ? off : kOOB);
+        }
+#pragma unroll
+        for (int j = 0; j < S; ++j)
+            sreg[d][j] = buf_load_f32(rs, s0 + j < G ? (uint32_t)((nl * G + s0 + j) * 4) : kOOB);
+    };
+    auto swz = [](int row, int j) { return (j ^ ((row >> 1) & 7)) * 16; };
+    auto stage = [&](int d, int buf) {
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            const int c = tid + 256 * i;
+            const int gl = c >> 9, row = (c >> 3) & 63, j = c & 7;
+            *reinterpret_cast<v4i *>(&Bs[buf][gl * BT + row * kGroup + swz(row, j)]) = breg[d][i];
+        }
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int c = tid + 256 * i;
+            const int gl = c / (ROWS * 8), row = (c >> 3) % ROWS, j = c & 7;
+            if (ACH % 256 == 0 || c < ACH)
+                *reinterpret_cast<v4i *>(&As[buf][gl * AT + row * kGroup + swz(row, j)]) =
+                    areg[d][i];
         }
     };
 
@@ -125,36 +156,32 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 #pragma unroll
         for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
 
-    auto consume = [&](int set, int s0) {
+    auto compute = [&](const float *scale, int buf, int s0) {
 #pragma unroll
-        for (int j = 0; j < S; ++j)
-#pragma unroll
-            for (int i = 0; i < APT; ++i) {
-                const int c = tid + 256 * i;
-                if (ACH % 256 == 0 || c < ACH)
-                    *reinterpret_cast<v4i *>(&As[set][j][(c >> 3) * LDA + (c & 7) * 16]) =
-                        areg[set][j][i];
-            }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < S; ++j) {
-            const int g = s0 + j;
-            if (g >= G) break;
+        for (int gl = 0; gl < S; ++gl) {
+            // Groups past the end hold zero weights and a zero scale, so they
+            // leave the accumulators unchanged bit for bit (fmaf(+0, 0, acc) ==
+            // acc); running them keeps the step free of branches.
+            const int g = s0 + gl;
             v4i acc[MB];
 #pragma unroll
             for (int i = 0; i < MB; ++i) acc[i] = v4i{0, 0, 0, 0};
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
+                const int j = slot * 2 + t;
+                const v4i b = *reinterpret_cast<const v4i *>(
+                    &Bs[buf][gl * BT + nl * kGroup + swz(nl, j)]);
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
+                    const int ar = i * 16 + col;
                     const v4i a = *reinterpret_cast<const v4i *>(
-                        &As[set][j][(i * 16 + col) * LDA + slot * 32 + t * 16]);
-                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, breg[set][j][t], acc[i], 0, 0, 0);
+                        &As[buf][gl * AT + ar * kGroup + swz(ar, j)]);
+                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i], 0, 0, 0);
                 }
             }
             if (OUT == OUT_PARTIALS) {
                 // C layout of 16x16: lane holds column `col`, rows 4*slot + r.
-                if (nl < nrows) {
+                if (nl < nrows && g < G) {
 #pragma unroll
                     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -166,7 +193,7 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                         }
                 }
             } else {
-                const float s = sreg[set][j];
+                const float s = scale[gl];
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -176,12 +203,30 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         }
     };
 
-    issue(0, 0);
-    for (int s0 = 0; s0 < G; s0 += 2 * S) {
-        issue(1, s0 + S);
-        consume(0, s0);
-        issue(0, s0 + 2 * S);
-        consume(1, s0 + S);
+    // Each step first refills the slot freed by the previous step, then waits
+    // for the oldest slot (D-1 younger sets outstanding: an exact count).
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) {
+        issue(d, d * S);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int s0 = 0; s0 < G; s0 += D * S) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int ss = s0 + d * S;       // may lie past G: loads read zero, compute skips
+            const int buf = (ss / S) & 1;
+            // scheduling fences keep the loads in ring order, which the exact
+            // wait counts rely on
+            __builtin_amdgcn_sched_barrier(0);
+            issue((d + D - 1) % D, ss + (D - 1) * S);
+            __builtin_amdgcn_sched_barrier(0);
+            stage(d, buf);
+            float scale[S];
+#pragma unroll
+            for (int j = 0; j < S; ++j) scale[j] = sreg[d][j];
+            __syncthreads();
+            compute(scale, buf, ss);
+        }
     }
 
     if (OUT != OUT_PARTIALS && nl < nrows) {
@@ -393,20 +438,24 @@ hipError_t launch_tile(const TileArgs &a, int64_t row_tiles, hipStream_t stream)
 }
 
 #ifndef BSB_SMALLM_S
-#define BSB_SMALLM_S 4
+#define BSB_SMALLM_S 2
 #endif
-constexpr int kSmallS = BSB_SMALLM_S;   // groups per super-stage
+#ifndef BSB_SMALLM_D
+#define BSB_SMALLM_D 4
+#endif
+constexpr int kSmallS = BSB_SMALLM_S;   // K groups per super-stage
+constexpr int kSmallD = BSB_SMALLM_D;   // super-stages in flight (register ring depth)
 
 template <int OUT>
 hipError_t launch_smallm(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                          int M, int N, int K, void *y, hipStream_t stream) {
     const dim3 grid((unsigned)((N + 63) / 64));
     if (M <= 16)
-        gemm_smallm_kernel<1, OUT, kSmallS><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+        gemm_smallm_kernel<1, OUT, kSmallS, kSmallD><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
     else if (M <= 32)
-        gemm_smallm_kernel<2, OUT, kSmallS><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+        gemm_smallm_kernel<2, OUT, kSmallS, kSmallD><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
     else
-        gemm_smallm_kernel<4, OUT, kSmallS><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+        gemm_smallm_kernel<4, OUT, kSmallS, kSmallD><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
     return hipGetLastError();
 }
 
