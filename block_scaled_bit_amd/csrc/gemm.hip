@@ -56,11 +56,11 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // --------------------------------------------------------------------------
 // smallm: M <= 16*MB tokens, weight-streaming.
 // --------------------------------------------------------------------------
-// Workgroup = 4 waves = 64 weight rows (output columns) n0 .. n0+63; each
-// wave owns 16 of them (v_mfma_i32_16x16x64_i8, MB 16-token blocks).
+// Workgroup = NW waves = 16*NW weight rows (output columns) n0 .. n0+16*NW-1;
+// each wave owns 16 of them (v_mfma_i32_16x16x64_i8, MB 16-token blocks).
 //
 // K is walked in super-stages of S groups. A super-stage's weight tile
-// (64 rows x S*128 B) and activation tile (16*MB rows x S*128 B) are read
+// (16*NW rows x S*128 B) and activation tile (16*MB rows x S*128 B) are read
 // with fully coalesced 16-byte buffer loads (8 lanes per 128-byte row line,
 // the pattern HBM streams fastest, with the non-temporal hint on the
 // weights, which are touched once) into a ring of D register sets, then
@@ -75,16 +75,18 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // distinct 16-byte bank groups.
 //
 // Out-of-range rows, columns and groups read zero through the buffer
-// descriptors, so no load sits behind a branch. Requires 64*K < 2^31
+// descriptors, so no load sits behind a branch. Requires 16*NW*K < 2^31
 // (checked by the launcher).
-template <int MB, int OUT, int S, int D>
-__global__ void __launch_bounds__(256)
+template <int MB, int NW, int OUT, int S, int D>
+__global__ void __launch_bounds__(64 * NW)
 gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                    const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N,
                    int K, void *__restrict__ y) {
-    constexpr int ROWS = 16 * MB;
-    constexpr int BT = 64 * kGroup;           // one group of the weight tile (bytes)
-    constexpr int AT = ROWS * kGroup;         // one group of the activation tile
+    constexpr int ROWS = 16 * MB;              // activation rows
+    constexpr int WR = 16 * NW;                // weight rows per workgroup
+    constexpr int NT = 64 * NW;                // threads
+    constexpr int BT = WR * kGroup;            // one group of the weight tile (bytes)
+    constexpr int AT = ROWS * kGroup;          // one group of the activation tile
     __shared__ __align__(16) int8_t Bs[2][S * BT];
     __shared__ __align__(16) int8_t As[2][S * AT];
 
@@ -92,8 +94,8 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     const int G = K >> 7;
     const int col = lane & 15;          // B column / A row within a 16-block
     const int slot = lane >> 4;         // which 32-byte quarter of the group
-    const int n0 = blockIdx.x * 64;
-    const int nrows = min(64, N - n0);
+    const int n0 = blockIdx.x * WR;
+    const int nrows = min(WR, N - n0);
     const int nl = wave * 16 + col;     // this lane's weight row within the slice
     const int n = n0 + nl;
 
@@ -101,50 +103,63 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(sw + (int64_t)n0 * G, (uint32_t)(nrows * G * 4));
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(q, (uint32_t)(M * K));
 
-    constexpr int BPT = S * BT / (256 * 16);          // weight chunks per thread per set
+    constexpr int BPT = S * BT / (NT * 16);           // weight chunks per thread per set
     constexpr int ACH = S * AT / 16;                  // activation chunks per set
-    constexpr int APT = (ACH + 255) / 256;
-    static_assert(BPT * 256 * 16 == S * BT, "weight tile must split evenly");
+    constexpr int APT = (ACH + NT - 1) / NT;
+    static_assert(BPT * NT * 16 == S * BT, "weight tile must split evenly");
 
     v4i breg[D][BPT];
     v4i areg[D][APT];
     float sreg[D][S];
 
+    // Per-lane parts of the load offsets are fixed for the whole K walk; the
+    // group offset of a step is wave-uniform and travels in the scalar offset.
+    // Offsets past a resource's end read zero; a group past G is pushed there
+    // through the scalar part (weights, scales) or a select (activations,
+    // whose group within a super-stage can differ across lanes).
+    uint32_t bvo[BPT], avo[APT];
+    int agl[APT];
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        const int c = tid + NT * i;
+        bvo[i] = (uint32_t)(((c >> 3) % WR) * K + (c & 7) * 16);   // group within stage: i*NT/(WR*8)
+    }
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+        const int c = tid + NT * i;
+        agl[i] = c / (ROWS * 8);
+        avo[i] = (c < ACH) ? (uint32_t)(((c >> 3) % ROWS) * K + agl[i] * kGroup + (c & 7) * 16)
+                           : kOOB;
+    }
+    const uint32_t svo = (uint32_t)(nl * G * 4);
+
     auto issue = [&](int d, int s0) {   // loads of the super-stage starting at group s0
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
-            const int c = tid + 256 * i;
-            const int gl = c >> 9, row = (c >> 3) & 63, j = c & 7;
-            const int g = s0 + gl;
-            const uint32_t off = (uint32_t)(row * K + g * kGroup + j * 16);
-            breg[d][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(g < G ? off : kOOB), 0,
-                                                               kNonTemporal);
+            const int g = s0 + (i * NT) / (WR * 8);          // uniform per i
+            breg[d][i] = buf_load16s<kNonTemporal>(rw, bvo[i], g < G ? (uint32_t)g * kGroup : kOOB);
         }
 #pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int c = tid + 256 * i;
-            const int gl = c / (ROWS * 8), row = (c >> 3) % ROWS, j = c & 7;
-            const int g = s0 + gl;
-            const uint32_t off = (uint32_t)(row * K + g * kGroup + j * 16);
-            areg[d][i] = buf_load16(ra, (g < G && c < ACH) ? off : kOOB);
-        }
+        for (int i = 0; i < APT; ++i)
+            areg[d][i] = buf_load16s(ra, (s0 + agl[i] < G) ? avo[i] : kOOB, (uint32_t)s0 * kGroup);
 #pragma unroll
         for (int j = 0; j < S; ++j)
-            sreg[d][j] = buf_load_f32(rs, s0 + j < G ? (uint32_t)((nl * G + s0 + j) * 4) : kOOB);
+            sreg[d][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rs, (int)svo, (int)(s0 + j < G ? (uint32_t)(s0 + j) * 4 : kOOB), 0));
     };
     auto swz = [](int row, int j) { return (j ^ ((row >> 1) & 7)) * 16; };
     auto stage = [&](int d, int buf) {
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
-            const int c = tid + 256 * i;
-            const int gl = c >> 9, row = (c >> 3) & 63, j = c & 7;
+            const int c = tid + NT * i;
+            const int gl = c / (WR * 8), row = (c >> 3) % WR, j = c & 7;
             *reinterpret_cast<v4i *>(&Bs[buf][gl * BT + row * kGroup + swz(row, j)]) = breg[d][i];
         }
 #pragma unroll
         for (int i = 0; i < APT; ++i) {
-            const int c = tid + 256 * i;
+            const int c = tid + NT * i;
             const int gl = c / (ROWS * 8), row = (c >> 3) % ROWS, j = c & 7;
-            if (ACH % 256 == 0 || c < ACH)
+            if (ACH % NT == 0 || c < ACH)
                 *reinterpret_cast<v4i *>(&As[buf][gl * AT + row * kGroup + swz(row, j)]) =
                     areg[d][i];
         }
@@ -203,30 +218,33 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         }
     };
 
-    // Each step first refills the slot freed by the previous step, then waits
-    // for the oldest slot (D-1 younger sets outstanding: an exact count).
+    // One step: refill the slot freed by the previous step, wait for the
+    // oldest slot (D-1 younger sets outstanding), stage it, multiply. The
+    // scheduling fences keep the loads in ring order, which the exact wait
+    // counts rely on.
+    auto step = [&](int d, int ss) {
+        const int buf = (ss / S) & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        issue((d + D - 1) % D, ss + (D - 1) * S);
+        asm volatile("" ::: "memory");   // no IR-level motion of the loads either
+        __builtin_amdgcn_sched_barrier(0);
+        stage(d, buf);
+        float scale[S];                  // take the scales out before the slot is reused
+#pragma unroll
+        for (int j = 0; j < S; ++j) scale[j] = sreg[d][j];
+        __syncthreads();
+        compute(scale, buf, ss);
+    };
+
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) {
         issue(d, d * S);
+        asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     }
     for (int s0 = 0; s0 < G; s0 += D * S) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int ss = s0 + d * S;       // may lie past G: loads read zero, compute skips
-            const int buf = (ss / S) & 1;
-            // scheduling fences keep the loads in ring order, which the exact
-            // wait counts rely on
-            __builtin_amdgcn_sched_barrier(0);
-            issue((d + D - 1) % D, ss + (D - 1) * S);
-            __builtin_amdgcn_sched_barrier(0);
-            stage(d, buf);
-            float scale[S];
-#pragma unroll
-            for (int j = 0; j < S; ++j) scale[j] = sreg[d][j];
-            __syncthreads();
-            compute(scale, buf, ss);
-        }
+        for (int d = 0; d < D; ++d) step(d, s0 + d * S);   // may run past G: zeros
     }
 
     if (OUT != OUT_PARTIALS && nl < nrows) {
@@ -443,28 +461,45 @@ hipError_t launch_tile(const TileArgs &a, int64_t row_tiles, hipStream_t stream)
 #ifndef BSB_SMALLM_D
 #define BSB_SMALLM_D 4
 #endif
-constexpr int kSmallS = BSB_SMALLM_S;   // K groups per super-stage
-constexpr int kSmallD = BSB_SMALLM_D;   // super-stages in flight (register ring depth)
+constexpr int kSmallS = BSB_SMALLM_S;     // K groups per super-stage
+constexpr int kSmallD = BSB_SMALLM_D;     // super-stages in flight (register ring depth)
+
+template <int MB, int NW, int OUT>
+hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
+                            int M, int N, int K, void *y, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW)));
+    gemm_smallm_kernel<MB, NW, OUT, kSmallS, kSmallD>
+        <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+    return hipGetLastError();
+}
+
+// Workgroup width: the widest (fewest activation re-reads) that still gives
+// about one workgroup per CU; never narrower than the activation tile needs.
+template <int MB, int OUT>
+hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
+                            int M, int N, int K, void *y, hipStream_t stream) {
+    constexpr int kMinGrid = 224;
+    if (N >= 16 * 8 * kMinGrid)
+        return launch_smallm_mb<MB, 8, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+    if (MB >= 4 || N >= 16 * 4 * kMinGrid)
+        return launch_smallm_mb<MB, 4, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+    return launch_smallm_mb<MB, 2, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+}
 
 template <int OUT>
 hipError_t launch_smallm(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                          int M, int N, int K, void *y, hipStream_t stream) {
-    const dim3 grid((unsigned)((N + 63) / 64));
-    if (M <= 16)
-        gemm_smallm_kernel<1, OUT, kSmallS, kSmallD><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
-    else if (M <= 32)
-        gemm_smallm_kernel<2, OUT, kSmallS, kSmallD><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
-    else
-        gemm_smallm_kernel<4, OUT, kSmallS, kSmallD><<<grid, 256, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
-    return hipGetLastError();
+    if (M <= 16) return launch_smallm_nw<1, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+    if (M <= 32) return launch_smallm_nw<2, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+    return launch_smallm_nw<4, OUT>(q, sa, qw, sw, M, N, K, y, stream);
 }
 
 template <int OUT>
 hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                         int M, int N, int K, void *y, hipStream_t stream) {
-    // smallm addresses a 64-row weight slice and the whole activation matrix
-    // with 32-bit buffer offsets
-    if (M <= 64 && (int64_t)64 * K < ((int64_t)1 << 31))
+    // smallm addresses a weight slice (at most 128 rows) and the whole
+    // activation matrix (at most 64 rows) with 32-bit buffer offsets
+    if (M <= 64 && (int64_t)128 * K < ((int64_t)1 << 31))
         return launch_smallm<OUT>(q, sa, qw, sw, M, N, K, y, stream);
     TileArgs a{q, sa, qw, sw, nullptr, y, M, N, K, 0};
     return launch_tile<OUT, false>(a, (M + TBM - 1) / TBM, stream);
