@@ -14,8 +14,9 @@ traffic between reuses) so that the 256 MB last-level cache cannot serve them.
 Reported (one JSON line on stdout):
   value          algorithmic HBM bytes of the step / step time, GB/s
   roofline       the GEMM kernel's algorithmic bytes per launch / its mean
-                 duration (HIP events around every launch in the timed
-                 region, on the launch stream), against 8 TB/s; `traffic`
+                 duration (a timed region of back-to-back GEMM launches
+                 between HIP events on the launch stream), against 8 TB/s;
+                 `traffic`
                  = measured HBM bytes per launch from rocprofv3 counters
                  (profiles/traffic.json), null when the kernel sources have
                  changed since they were taken
@@ -99,44 +100,36 @@ class Linear:
         del x, qw, sw
 
 
-def run_steps(torch, L, lin, stream, n, t_events=None, with_quant=True):
-    """Enqueue n steps; optionally record per-kernel events (start/end pairs)."""
+def enqueue(L, lin, stream, n, what=("quant", "gemm")):
+    """Enqueue n passes over the rotating copies: the quantisation and/or the GEMM."""
     M, K, N = lin.M, lin.K, lin.N
     for i in range(n):
         p = lin.bufs[i % len(lin.bufs)]["ptr"]
-        if with_quant:
-            if t_events is not None:
-                t_events["q0"][i].record()
+        if "quant" in what:
             s = L.bsb_quantize_act(p["x"], M, K, p["q"], p["sa"], stream)
             if s:
                 raise RuntimeError(L.bsb_status_string(s).decode())
-            if t_events is not None:
-                t_events["q1"][i].record()
-        if t_events is not None:
-            t_events["g0"][i].record()
-        s = L.bsb_gemm_w8a8_g128(p["q"], p["sa"], p["qw"], p["sw"], M, N, K, p["y"], 0, stream)
-        if s:
-            raise RuntimeError(L.bsb_status_string(s).decode())
-        if t_events is not None:
-            t_events["g1"][i].record()
+        if "gemm" in what:
+            s = L.bsb_gemm_w8a8_g128(p["q"], p["sa"], p["qw"], p["sw"], M, N, K, p["y"], 0,
+                                     stream)
+            if s:
+                raise RuntimeError(L.bsb_status_string(s).decode())
 
 
-def timed(torch, L, lin, stream, steps, warmup, with_quant=True):
-    run_steps(torch, L, lin, stream, warmup, with_quant=with_quant)
-    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-          for k in ("q0", "q1", "g0", "g1")}
+def timed(torch, L, lin, stream, steps, warmup, what=("quant", "gemm")):
+    """Warm up, then time `steps` back-to-back passes between two HIP events
+    recorded on the launch stream (torch's current stream). Returns
+    (ms per pass from the events, wall-clock s per pass)."""
+    enqueue(L, lin, stream, warmup, what)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    run_steps(torch, L, lin, stream, steps, ev, with_quant=with_quant)
+    enqueue(L, lin, stream, steps, what)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    g_ms = [ev["g0"][i].elapsed_time(ev["g1"][i]) for i in range(steps)]
-    q_ms = [ev["q0"][i].elapsed_time(ev["q1"][i]) for i in range(steps)] if with_quant else []
-    return total_ms, wall, g_ms, q_ms
+    return start.elapsed_time(end) / steps, wall / steps
 
 
 def cpu_baseline(budget_s=10.0):
@@ -207,14 +200,14 @@ def main():
     # ---- decode-shaped linear: the step ----
     M, K, N = 32, 8192, 28672
     lin = Linear(torch, M, K, N, 0.005, 30.0, args.copies, dev)
-    total_ms, wall, g_ms, q_ms = timed(torch, L, lin, stream, args.steps, args.warmup)
-    ms_step = total_ms / args.steps
+    ms_step, wall = timed(torch, L, lin, stream, args.steps, args.warmup)
+    # per-kernel mean durations: each kernel alone, back to back, same buffers
+    g_avg, _ = timed(torch, L, lin, stream, args.steps, args.warmup, ("gemm",))
+    q_avg, _ = timed(torch, L, lin, stream, args.steps, args.warmup, ("quant",))
     step_bytes = quant_bytes(M, K) + gemm_bytes(M, N, K)
-    g_avg = sum(g_ms) / len(g_ms)
-    q_avg = sum(q_ms) / len(q_ms)
     g_bytes = gemm_bytes(M, N, K)
     achieved = g_bytes / (g_avg * 1e-3) / 1e9
-    log(f"decode step {ms_step * 1e3:.1f} us (wall {wall / args.steps * 1e6:.1f} us/step); "
+    log(f"decode step {ms_step * 1e3:.1f} us (wall {wall * 1e6:.1f} us/step); "
         f"gemm {g_avg * 1e3:.1f} us = {achieved:.0f} GB/s; quant {q_avg * 1e3:.1f} us")
     del lin
     torch.cuda.empty_cache()
@@ -240,6 +233,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gemm_decode"),
                      "kernel": "gemm_smallm_kernel (M<=32)",
+                     "timing": "mean of back-to-back launches between HIP events on the launch stream",
                      "bytes_per_launch": g_bytes, "avg_us": round(g_avg * 1e3, 2),
                      "quant_avg_us": round(q_avg * 1e3, 2)},
     }
@@ -252,9 +246,7 @@ def main():
         for b in pre.bufs:
             L.bsb_quantize_act(b["ptr"]["x"], Mp, Kp, b["ptr"]["q"], b["ptr"]["sa"], stream)
         psteps = max(5, min(50, args.steps // 4))
-        _, _, pg_ms, _ = timed(torch, L, pre, stream, psteps, max(2, args.warmup // 4),
-                               with_quant=False)
-        pg = sum(pg_ms) / len(pg_ms)
+        pg, _ = timed(torch, L, pre, stream, psteps, max(2, args.warmup // 4), ("gemm",))
         tops = 2.0 * Mp * Np * Kp / (pg * 1e-3) / 1e12
         log(f"prefill gemm {pg * 1e3:.1f} us = {tops:.0f} TOPS")
         out["prefill"] = {"M": Mp, "K": Kp, "N": Np, "avg_us": round(pg * 1e3, 2),

@@ -473,17 +473,28 @@ hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, 
     return hipGetLastError();
 }
 
-// Workgroup width: the widest (fewest activation re-reads) that still gives
-// about one workgroup per CU; never narrower than the activation tile needs.
+// Workgroup width NW waves (16 weight rows each): spread the 16-row column
+// blocks over whole rounds of one workgroup per CU, as wide as possible (the
+// wider the workgroup, the fewer times the activation tile is re-read), at
+// most 8 waves, and at least what the activation tile needs (register ring).
+constexpr int kCUs = 256;
+
 template <int MB, int OUT>
 hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                             int M, int N, int K, void *y, hipStream_t stream) {
-    constexpr int kMinGrid = 224;
-    if (N >= 16 * 8 * kMinGrid)
-        return launch_smallm_mb<MB, 8, OUT>(q, sa, qw, sw, M, N, K, y, stream);
-    if (MB >= 4 || N >= 16 * 4 * kMinGrid)
-        return launch_smallm_mb<MB, 4, OUT>(q, sa, qw, sw, M, N, K, y, stream);
-    return launch_smallm_mb<MB, 2, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+    const int blocks16 = (N + 15) / 16;
+    const int rounds = (blocks16 + 8 * kCUs - 1) / (8 * kCUs);
+    int nw = (blocks16 + kCUs * rounds - 1) / (kCUs * rounds);
+    nw = nw < (MB >= 4 ? 4 : 2) ? (MB >= 4 ? 4 : 2) : nw;
+    switch (nw) {
+        case 2: return launch_smallm_mb<MB, 2, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+        case 3: return launch_smallm_mb<MB, 3, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+        case 4: return launch_smallm_mb<MB, 4, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+        case 5: return launch_smallm_mb<MB, 5, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+        case 6: return launch_smallm_mb<MB, 6, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+        case 7: return launch_smallm_mb<MB, 7, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+        default: return launch_smallm_mb<MB, 8, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+    }
 }
 
 template <int OUT>
