@@ -91,6 +91,14 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
 
 constexpr uint32_t kOOB = 0x80000000u;   // an offset past every resource used here
 
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// lds + 16*l (lds must be wave-uniform).
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff,
+                                               uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+
 // Cache-policy bits of a buffer load: non-temporal (streamed once, do not
 // keep in the caches).
 constexpr int kNonTemporal = 2;
