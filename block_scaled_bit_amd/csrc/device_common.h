@@ -91,13 +91,34 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
 
 constexpr uint32_t kOOB = 0x80000000u;   // an offset past every resource used here
 
-// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
-// lds + 16*l (lds must be wave-uniform).
-__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff,
-                                               uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)lds, 16, (int)voff, (int)soff, 0, 0);
+// Buffer descriptor as four words for inline assembly (same fields as
+// make_rsrc: base, stride 0, size in bytes, raw-buffer flags).
+__device__ __forceinline__ v4i make_rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
 }
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// LDS address lds + 16*l (lds wave-uniform, passed in M0). Out-of-range
+// offsets write zeros. Issued through inline assembly so that the compiler
+// does not treat it as a write of unknown LDS and hold every later LDS read
+// until it lands: the caller calls wait_vmem() and then a barrier before any
+// wave reads the destination. The s_nop is the one wait state the hardware
+// needs between the M0 write and the load that reads M0.
+__device__ __forceinline__ void buf_load16_lds(v4i rsrc, uint32_t lds, uint32_t voff,
+                                               uint32_t soff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "{m0}"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// Wait until every vector memory load of this wave, including the LDS-bound
+// ones above, has completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Cache-policy bits of a buffer load: non-temporal (streamed once, do not
 // keep in the caches).

@@ -457,9 +457,12 @@ gemm_tile_kernel(TileArgs p, int n_tiles) {
 // (128 KB) with an XOR swizzle (16-byte chunk j of row r at j ^ ((r>>1)&7)).
 // The next group's tiles are loaded straight into the other LDS buffer (buffer
 // loads with the LDS-destination bit, 8 lanes per 128-byte row line) while the
-// current group is multiplied, so the staging needs no registers. The group's
-// 256 weight scales are staged in LDS beside the tiles. One barrier per K
-// group. Workgroup ids are remapped so that each XCD works
+// current group is multiplied, so the staging needs no registers; those loads
+// are waited for only at the end of the group (issued through inline assembly,
+// the compiler would otherwise wait for them before the group's first LDS
+// read and expose their whole latency every group). The group's 256 weight
+// scales are staged in LDS beside the tiles. One barrier per K group.
+// Workgroup ids are remapped so that each XCD works
 // on a contiguous run of tiles, ordered in groups of 4 tile rows, which keeps
 // the operand panels its workgroups share in that XCD's L2.
 constexpr int BBM = 256, BBN = 256;
@@ -499,8 +502,8 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     const int m0 = bm * BBM, n0 = bn * BBN;
     const int mrows = min(BBM, M - m0), ncols = min(BBN, N - n0);
 
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(q + (int64_t)m0 * K, (uint32_t)(mrows * K));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(qw + (int64_t)n0 * K, (uint32_t)(ncols * K));
+    const v4i ra = make_rsrc_words(q + (int64_t)m0 * K, (uint32_t)(mrows * K));
+    const v4i rb = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(ncols * K));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(sw + (int64_t)n0 * G, (uint32_t)(ncols * G * 4));
 
     // Staging goes straight from global memory to LDS (buffer loads with the
@@ -528,7 +531,8 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         const uint32_t so = sgo(g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            int8_t *blk = smem[buf] + (wave * 4 + i) * 1024;
+            const uint32_t blk = __builtin_amdgcn_readfirstlane(
+                (uint32_t)(uintptr_t)(smem[buf] + (wave * 4 + i) * 1024));
             const uint32_t s2 = g < G ? so + (uint32_t)((i >> 1) * 16 * K) : kOOB;
             buf_load16_lds(ra, blk, dvoff[i & 1], s2);
             buf_load16_lds(rb, blk + BBM * kGroup, dvoff[i & 1], s2);
@@ -627,15 +631,17 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     dma_group(0, 0);
     load_scale(0);
     store_scale(0);
+    wait_vmem();
     __syncthreads();
 
     for (int g = 0; g < G; ++g) {
         const int buf = g & 1;
-        dma_group(buf ^ 1, g + 1);     // zeros past the end
+        dma_group(buf ^ 1, g + 1);     // zeros past the end; lands while group g is multiplied
         load_scale(g + 1);
         group(buf, g, g > 0);
         store_scale(buf ^ 1);
-        __syncthreads();               // waits for the next group's loads, then swaps buffers
+        wait_vmem();                   // the next group's tiles are in LDS ...
+        __syncthreads();               // ... for every wave: swap buffers
     }
     epilogue(acc[1], 1, 3, sc_last, g_last);
 
