@@ -23,6 +23,13 @@ Reported (one JSON line on stdout):
   cpu_baseline   the CPU oracle on the same workload, timed on this host
   prefill        the prefill-shaped GEMM M=4096, K=8192, N=8192 timed the same
                  way, against the 5.0 POPS dense INT8 MFMA peak
+  rows           every other workload, each kernel timed alone the same way
+                 with its own rotating input sets: the tiny linear (16x1024x1024),
+                 the prefill quantisation, the routed MoE layer (4096 tokens,
+                 top-8 of 64 Zipf-routed experts, K=4096, N=2048: quantisation
+                 and grouped GEMM), the block-format decoders (FP8 [128,128]
+                 4096x7168 in both dialects, MXFP4 8x2048x4096) and the dense and
+                 grouped GEMMs on the decoded weights at 32 and 1024 tokens
 """
 from __future__ import annotations
 
@@ -163,6 +170,230 @@ def cpu_baseline(budget_s=10.0):
                        f"algorithmic bytes / time")}
 
 
+class Row:
+    """One measured workload: device-resident inputs in `copies` rotating sets
+    and a raw C-ABI call that enqueues one pass over set i."""
+
+    def __init__(self, name, sets, call):
+        self.name, self.sets, self.call = name, sets, call
+
+    def time(self, torch, stream, steps, warmup):
+        """Mean ms per pass over `steps` back-to-back passes between HIP events
+        recorded on the launch stream."""
+        n = len(self.sets)
+        for i in range(warmup):
+            self.call(self.sets[i % n], stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(steps):
+            self.call(self.sets[i % n], stream)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+
+def _ok(L, status):
+    if status:
+        raise RuntimeError(L.bsb_status_string(status).decode())
+
+
+def _copies(bytes_per_set, floor=1 << 30, cap=64):
+    """Rotating sets so that a set is reused only after >= 1 GiB of other traffic."""
+    return max(1, min(cap, -(-floor // max(1, bytes_per_set)) + 1))
+
+
+def _rate(us, ops=None, byts=None, bound="hbm"):
+    """avg_us plus achieved TOPS / GB/s against the published peaks."""
+    r = {"avg_us": round(us, 2), "bound": bound}
+    t = us * 1e-6
+    if byts is not None:
+        r["bytes"] = int(byts)
+        r["gbs"] = round(byts / t / 1e9, 1)
+        r["hbm_frac"] = round(byts / t / 1e9 / HBM_PEAK_GBS, 4)
+    if ops is not None:
+        r["ops"] = int(ops)
+        r["tops"] = round(ops / t / 1e12, 1)
+        r["mfma_frac"] = round(ops / t / 1e12 / INT8_PEAK_TOPS, 4)
+    if ops is not None and byts is not None:
+        # a kernel bound by both: the slower roofline over the measured time
+        r["frac"] = round(max(ops / (INT8_PEAK_TOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9)) / t, 4)
+    else:
+        r["frac"] = r.get("mfma_frac" if bound == "mfma" else "hbm_frac")
+    return r
+
+
+def extra_rows(torch, L, stream, dev, steps):
+    """Every other workload of the path, each kernel timed on its own:
+    the tiny linear, the prefill quantisation, the routed MoE layer and the
+    block-format weights (decoders, then the dense and grouped GEMMs on the
+    decoded weights)."""
+    import numpy as np
+    from block_scaled_bit_amd import synth
+    rows = {}
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    def linear_rows(tag, M, K, N, p, f):
+        d = synth.linear_inputs(M, K, N, outlier_p=p, outlier_f=f, seed=0)
+        gb = gemm_bytes(M, N, K)
+        n = _copies(gb)
+        x, qw, sw = t(d["x"].view(np.int16)), t(d["qw"]), t(d["sw"])
+        sets = []
+        for _ in range(n):
+            b = dict(x=x.clone(), qw=qw.clone(), sw=sw.clone(),
+                     q=torch.empty((M, K), dtype=torch.int8, device=dev),
+                     sa=torch.empty((M,), dtype=torch.float32, device=dev),
+                     y=torch.empty((M, N), dtype=torch.int16, device=dev))
+            sets.append({k: v.data_ptr() for k, v in b.items()} | {"_keep": b})
+        quant = Row(f"{tag} quantize_act", sets, lambda p, st: _ok(
+            L, L.bsb_quantize_act(p["x"], M, K, p["q"], p["sa"], st)))
+        gemm = Row(f"{tag} gemm", sets, lambda p, st: _ok(
+            L, L.bsb_gemm_w8a8_g128(p["q"], p["sa"], p["qw"], p["sw"], M, N, K, p["y"], 0, st)))
+        tq = quant.time(torch, stream, steps, 3)
+        tg = gemm.time(torch, stream, steps, 3)
+        return tq, tg
+
+    # tiny linear: latency-bound, reported in microseconds
+    tq, tg = linear_rows("tiny", 16, 1024, 1024, 0.01, 20.0)
+    rows["tiny_16x1024x1024_quant"] = _rate(tq * 1e3, byts=quant_bytes(16, 1024),
+                                            bound="latency")
+    rows["tiny_16x1024x1024_gemm"] = _rate(tg * 1e3, ops=2 * 16 * 1024 * 1024,
+                                           byts=gemm_bytes(16, 1024, 1024), bound="latency")
+    log(f"tiny: quant {tq * 1e3:.1f} us, gemm {tg * 1e3:.1f} us")
+    torch.cuda.empty_cache()
+
+    # prefill-shaped quantisation (the GEMM is timed separately)
+    M, K = 4096, 8192
+    d = synth.linear_inputs(M, K, 128, outlier_p=0.005, outlier_f=30.0, seed=0)
+    x = t(d["x"].view(np.int16))
+    sets = []
+    for _ in range(_copies(quant_bytes(M, K))):
+        b = dict(x=x.clone(), q=torch.empty((M, K), dtype=torch.int8, device=dev),
+                 sa=torch.empty((M,), dtype=torch.float32, device=dev))
+        sets.append({k: v.data_ptr() for k, v in b.items()} | {"_keep": b})
+    tq = Row("prefill quant", sets, lambda p, st: _ok(
+        L, L.bsb_quantize_act(p["x"], M, K, p["q"], p["sa"], st))).time(torch, stream, steps, 3)
+    rows["prefill_4096x8192_quant"] = _rate(tq * 1e3, byts=quant_bytes(M, K))
+    log(f"prefill quant {tq * 1e3:.1f} us")
+    del sets, x
+    torch.cuda.empty_cache()
+
+    # routed MoE layer: 4096 tokens, top-8 of 64 experts (Zipf, 4 empty), K=4096, N=2048
+    m = synth.moe_inputs()
+    R, E, K, N = m["R"], m["E"], m["K"], m["N"]
+    G = K // 128
+    off_h = m["offsets"]
+    nonempty = int((np.diff(off_h) > 0).sum())
+    xs, qw, sw, off = t(m["x_sorted"].view(np.int16)), t(m["qw"]), t(m["sw"]), t(off_h)
+    q = torch.empty((R, K), dtype=torch.int8, device=dev)
+    sa = torch.empty((R,), dtype=torch.float32, device=dev)
+    y = torch.empty((R, N), dtype=torch.int16, device=dev)
+    p = {"x": xs.data_ptr(), "q": q.data_ptr(), "sa": sa.data_ptr(), "qw": qw.data_ptr(),
+         "sw": sw.data_ptr(), "off": off.data_ptr(), "y": y.data_ptr()}
+    # 768 MB of weights and activations per pass: larger than the last-level cache
+    tq = Row("moe quant", [p], lambda p, st: _ok(
+        L, L.bsb_quantize_act(p["x"], R, K, p["q"], p["sa"], st))).time(torch, stream, 20, 3)
+    tg = Row("moe grouped", [p], lambda p, st: _ok(
+        L, L.bsb_grouped_gemm_w8a8_g128(p["q"], p["sa"], p["qw"], p["sw"], p["off"], E, R, N, K,
+                                        p["y"], 0, st))).time(torch, stream, 20, 3)
+    gbytes = R * K + 4 * R + nonempty * (N * K + 4 * N * G) + 2 * R * N + 4 * (E + 1)
+    rows["moe_4096tok_top8_64e_quant"] = _rate(tq * 1e3, byts=quant_bytes(R, K))
+    rows["moe_4096tok_top8_64e_grouped"] = _rate(tg * 1e3, ops=2 * R * N * K, byts=gbytes,
+                                                 bound="mfma+hbm")
+    rows["moe_4096tok_top8_64e_grouped"].update(rows=R, experts_nonempty=nonempty)
+    log(f"moe: quant {tq * 1e3:.1f} us, grouped {tg * 1e3:.1f} us")
+    del m, xs, qw, sw, off, q, sa, y, p
+    torch.cuda.empty_cache()
+
+    # block formats: FP8 [128,128] dense 4096x7168 and MXFP4 experts 8x2048x4096
+    b = synth.blockfmt_inputs(M=32)
+    Nd, Kd, Ee, Ne, Ke = b["N_d"], b["K_d"], b["E"], b["N_e"], b["K_e"]
+    Gd, Ge = Kd // 128, Ke // 128
+    fp8_bytes = Nd * Kd + (Nd // 128) * (Kd // 128) + Nd * Kd + 4 * Nd * Gd
+    w, bs = t(b["w_fp8"]), t(b["bs"])
+    dsets = []
+    for _ in range(_copies(fp8_bytes)):
+        o = dict(w=w.clone(), bs=bs.clone(),
+                 qw=torch.empty((Nd, Kd), dtype=torch.int8, device=dev),
+                 sw=torch.empty((Nd, Gd), dtype=torch.float32, device=dev))
+        dsets.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
+    for dialect, dname in ((0, "ocp"), (1, "fnuz")):
+        td = Row("decode fp8", dsets, lambda p, st, dl=dialect: _ok(
+            L, L.bsb_decode_fp8_block(p["w"], p["bs"], Nd, Kd, dl, p["qw"], p["sw"], st))).time(
+            torch, stream, steps, 3)
+        rows[f"blockfmt_decode_fp8_{dname}_4096x7168"] = _rate(td * 1e3, byts=fp8_bytes)
+        log(f"decode fp8 {dname} {td * 1e3:.1f} us")
+    qwd = torch.empty((Nd, Kd), dtype=torch.int8, device=dev)
+    swd = torch.empty((Nd, Gd), dtype=torch.float32, device=dev)
+    _ok(L, L.bsb_decode_fp8_block(w.data_ptr(), bs.data_ptr(), Nd, Kd, 0, qwd.data_ptr(),
+                                  swd.data_ptr(), stream))
+    del dsets, w, bs
+    torch.cuda.empty_cache()
+
+    mx_bytes = Ee * Ne * Ke // 2 + Ee * Ne * Ke // 32 + Ee * Ne * Ke + 4 * Ee * Ne * Ge
+    pk, sc = t(b["packed"]), t(b["scale"])
+    msets = []
+    for _ in range(_copies(mx_bytes)):
+        o = dict(pk=pk.clone(), sc=sc.clone(),
+                 qw=torch.empty((Ee, Ne, Ke), dtype=torch.int8, device=dev),
+                 sw=torch.empty((Ee, Ne, Ge), dtype=torch.float32, device=dev))
+        msets.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
+    tm = Row("decode mxfp4", msets, lambda p, st: _ok(
+        L, L.bsb_decode_mxfp4(p["pk"], p["sc"], Ee, Ne, Ke, p["qw"], p["sw"], st))).time(
+        torch, stream, steps, 3)
+    rows["blockfmt_decode_mxfp4_8x2048x4096"] = _rate(tm * 1e3, byts=mx_bytes)
+    log(f"decode mxfp4 {tm * 1e3:.1f} us")
+    qwe = torch.empty((Ee, Ne, Ke), dtype=torch.int8, device=dev)
+    swe = torch.empty((Ee, Ne, Ge), dtype=torch.float32, device=dev)
+    _ok(L, L.bsb_decode_mxfp4(pk.data_ptr(), sc.data_ptr(), Ee, Ne, Ke, qwe.data_ptr(),
+                              swe.data_ptr(), stream))
+    del msets, pk, sc
+    torch.cuda.empty_cache()
+
+    # GEMMs on the decoded weights, M = 32 and 1024 tokens (per expert for the grouped one)
+    for Mt in (32, 1024):
+        bb = b if Mt == 32 else synth.blockfmt_inputs(M=Mt)
+        xd, xe = t(bb["x_d"].view(np.int16)), t(bb["x_e"].view(np.int16))
+        offe = t(bb["offsets"])
+        Re = Ee * Mt
+        db = gemm_bytes(Mt, Nd, Kd)
+        eb = Re * Ke + 4 * Re + Ee * (Ne * Ke + 4 * Ne * Ge) + 2 * Re * Ne + 4 * (Ee + 1)
+        gs, es = [], []
+        for _ in range(_copies(db)):
+            o = dict(qw=qwd.clone(), sw=swd.clone(),
+                     q=torch.empty((Mt, Kd), dtype=torch.int8, device=dev),
+                     sa=torch.empty((Mt,), dtype=torch.float32, device=dev),
+                     y=torch.empty((Mt, Nd), dtype=torch.int16, device=dev))
+            _ok(L, L.bsb_quantize_act(xd.data_ptr(), Mt, Kd, o["q"].data_ptr(),
+                                      o["sa"].data_ptr(), stream))
+            gs.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
+        for _ in range(_copies(eb)):
+            o = dict(qw=qwe.clone(), sw=swe.clone(), off=offe.clone(),
+                     q=torch.empty((Re, Ke), dtype=torch.int8, device=dev),
+                     sa=torch.empty((Re,), dtype=torch.float32, device=dev),
+                     y=torch.empty((Re, Ne), dtype=torch.int16, device=dev))
+            _ok(L, L.bsb_quantize_act(xe.data_ptr(), Re, Ke, o["q"].data_ptr(),
+                                      o["sa"].data_ptr(), stream))
+            es.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
+        tg = Row("blockfmt gemm", gs, lambda p, st: _ok(
+            L, L.bsb_gemm_w8a8_g128(p["q"], p["sa"], p["qw"], p["sw"], Mt, Nd, Kd, p["y"], 0,
+                                    st))).time(torch, stream, steps, 3)
+        te = Row("blockfmt grouped", es, lambda p, st: _ok(
+            L, L.bsb_grouped_gemm_w8a8_g128(p["q"], p["sa"], p["qw"], p["sw"], p["off"], Ee, Re,
+                                            Ne, Ke, p["y"], 0, st))).time(torch, stream, steps, 3)
+        bound = "hbm" if Mt == 32 else "mfma"
+        rows[f"blockfmt_gemm_m{Mt}_4096x7168"] = _rate(tg * 1e3, ops=2 * Mt * Nd * Kd,
+                                                       byts=db, bound=bound)
+        rows[f"blockfmt_grouped_m{Mt}_8x2048x4096"] = _rate(te * 1e3, ops=2 * Re * Ne * Ke,
+                                                            byts=eb, bound=bound)
+        log(f"blockfmt M={Mt}: gemm {tg * 1e3:.1f} us, grouped {te * 1e3:.1f} us")
+        del gs, es, xd, xe, offe
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +402,8 @@ def main():
     ap.add_argument("--copies", type=int, default=5, help="rotating weight copies (decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other workloads (tiny, MoE, block formats)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -252,10 +485,13 @@ def main():
         out["prefill"] = {"M": Mp, "K": Kp, "N": Np, "avg_us": round(pg * 1e3, 2),
                           "tops": round(tops, 1), "peak_tops": INT8_PEAK_TOPS,
                           "frac": round(tops / INT8_PEAK_TOPS, 4), "bound": "mfma",
-                          "kernel": "gemm_tile_kernel 128x128",
+                          "kernel": "gemm_big_kernel 256x256",
                           "traffic": measured_traffic("gemm_prefill")}
         del pre
         torch.cuda.empty_cache()
+
+    if not args.no_rows:
+        out["rows"] = extra_rows(torch, L, stream, dev, max(10, min(50, args.steps // 4)))
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

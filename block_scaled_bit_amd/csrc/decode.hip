@@ -9,9 +9,13 @@
 // element). A thread owns one 16-byte input chunk; the lanes that cover one
 // 128-wide K group are consecutive, so the group maximum is a shuffle
 // reduction inside the wave, and the quantised bytes leave as one 16-byte
-// store per 16 elements. Values are decoded from the bit fields (exact in
-// float32) rather than with the hardware FP8 converts, which implement only
-// the OCP dialect.
+// store per 16 elements. Elements are decoded by the hardware converts (two
+// per instruction), which are exact: FP8 values and E2M1 values are float32
+// values with few significant bits, and the block scales are powers of two
+// applied by an exact multiply. The converts read FP8 as OCP e4m3; the fnuz
+// reading of the same byte is exactly half of it except for 0x7F / 0xFF,
+// NaN in OCP and +-240 in fnuz, which are patched. Quantisation uses one
+// reciprocal per group and fused corrections instead of a division per element.
 #include "device_common.h"
 #include "launch.h"
 
@@ -19,27 +23,28 @@ namespace bsb {
 
 namespace {
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+
 // UE8M0 exponent byte -> 2^(E-127). E = 0 is the subnormal 2^-127.
 __device__ __forceinline__ float ue8m0_to_f32(uint32_t E) {
     return E ? __uint_as_float(E << 23) : __uint_as_float(0x00400000u);
 }
 
-// e4m3 byte -> float32. fnuz: bias 8, else OCP bias 7.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b, int fnuz) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    const float sub = (float)m * (fnuz ? 0x1p-10f : 0x1p-9f);
-    const float nrm = __uint_as_float(((e + (fnuz ? 119u : 120u)) << 23) | (m << 20));
-    const float mag = e ? nrm : sub;
-    return (b & 0x80u) ? -mag : mag;
-}
-
-// E2M1 nibble -> float32: {0, .5, 1, 1.5, 2, 3, 4, 6} with a sign bit.
-__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
-    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-    const float sub = m ? 0.5f : 0.0f;
-    const float nrm = __uint_as_float(((e + 126u) << 23) | (m << 22));
-    const float mag = e ? nrm : sub;
-    return (c & 8u) ? -mag : mag;
+// Sixteen elements (four dwords of four INT8 codes) against the group scale.
+__device__ __forceinline__ void quant16(const float *f, float s, float amax, uint32_t *o) {
+    if (s >= kFastScaleMin) {
+        const float y = 1.0f / s;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = quant4_refined(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], s, y);
+    } else if (amax == 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = 0u;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = quant4_divide(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], s);
+    }
 }
 
 __global__ void __launch_bounds__(256)
@@ -58,26 +63,41 @@ decode_fp8_block_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict
         v = reinterpret_cast<const uint4 *>(w)[chunk];
         scale = ue8m0_to_f32(bs[(n >> 7) * gpr + (kc >> 3)]);
     }
+    // fnuz = OCP / 2: fold the half into the (power-of-two) block scale
+    if (fnuz) scale *= 0.5f;
     const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
     float f[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], false);   // bytes 0, 1
+        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], true);    // bytes 2, 3
+        f[4 * i] = lo.x;
+        f[4 * i + 1] = lo.y;
+        f[4 * i + 2] = hi.x;
+        f[4 * i + 3] = hi.y;
+        if (fnuz) {
+            // a byte with all of e and m set: 0x7F / 0xFF read as fnuz is +-240,
+            // i.e. +-480 before the folded half
+            const uint32_t t = (wd[i] & 0x7F7F7F7Fu) ^ 0x7F7F7F7Fu;
+            if ((t - 0x01010101u) & ~t & 0x80808080u) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t byte = (wd[i] >> (8 * b)) & 0xFFu;
+                    if ((byte & 0x7Fu) == 0x7Fu) f[4 * i + b] = (byte & 0x80u) ? -480.0f : 480.0f;
+                }
+            }
+        }
+    }
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        f[i] = e4m3_to_f32((wd[i >> 2] >> (8 * (i & 3))) & 0xFFu, fnuz) * scale;
+        f[i] *= scale;
         amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
     }
     amax = group_max(amax, 8);
     const float s = absmax_scale(amax);
     uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (amax == 0.0f) {
-            o[i] = 0u;
-        } else {
-            o[i] = pack4_i8(quant_elem(f[4 * i], s), quant_elem(f[4 * i + 1], s),
-                            quant_elem(f[4 * i + 2], s), quant_elem(f[4 * i + 3], s));
-        }
-    }
+    quant16(f, s, amax, o);
     if (valid) {
         reinterpret_cast<uint4 *>(qw)[chunk] = make_uint4(o[0], o[1], o[2], o[3]);
         if ((kc & 7u) == 0u) sw[n * gpr + (kc >> 3)] = s;
@@ -99,27 +119,33 @@ decode_mxfp4_kernel(const uint8_t *__restrict__ packed, const uint8_t *__restric
     }
     const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
     float f[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // byte b of dword i holds elements 2(4i+b) (low nibble) and 2(4i+b)+1
+        const v2f p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 1.0f, 0);
+        const v2f p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 1.0f, 1);
+        const v2f p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 1.0f, 2);
+        const v2f p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 1.0f, 3);
+        f[8 * i] = p0.x;
+        f[8 * i + 1] = p0.y;
+        f[8 * i + 2] = p1.x;
+        f[8 * i + 3] = p1.y;
+        f[8 * i + 4] = p2.x;
+        f[8 * i + 5] = p2.y;
+        f[8 * i + 6] = p3.x;
+        f[8 * i + 7] = p3.y;
+    }
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const uint32_t byte = (wd[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-        f[2 * j] = e2m1_to_f32(byte & 0xFu) * sc;       // element 2j: low nibble
-        f[2 * j + 1] = e2m1_to_f32(byte >> 4) * sc;     // element 2j+1: high nibble
-        amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(f[2 * j]),
-                                                     __builtin_fabsf(f[2 * j + 1])));
+    for (int i = 0; i < 32; ++i) {
+        f[i] *= sc;
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
     }
     amax = group_max(amax, 4);
     const float s = absmax_scale(amax);
     uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (amax == 0.0f) {
-            o[i] = 0u;
-        } else {
-            o[i] = pack4_i8(quant_elem(f[4 * i], s), quant_elem(f[4 * i + 1], s),
-                            quant_elem(f[4 * i + 2], s), quant_elem(f[4 * i + 3], s));
-        }
-    }
+    quant16(f, s, amax, o);
+    quant16(f + 16, s, amax, o + 4);
     if (valid) {
         uint4 *dst = reinterpret_cast<uint4 *>(qw) + 2 * (size_t)chunk;
         dst[0] = make_uint4(o[0], o[1], o[2], o[3]);

@@ -40,6 +40,46 @@ __device__ __forceinline__ float absmax_scale(float amax) {
     return amax / 127.0f;
 }
 
+// Quantising a group of elements against its scale s = RN(amax / 127) > 0
+// without one division per element. For s >= 2^-100:
+//   y  = RN(1 / s)                          (one IEEE division per group)
+//   q0 = RN(x * y)                          (within 1.5 ulp of x / s)
+//   q1 = RN(q0 + y * (x - s * q0))          (fused; faithful)
+//   q2 = RN(q1 + y * (x - s * q1))          (fused; = RN(x / s))
+// The first correction brings q within an ulp of x / s (its residual is
+// rounded once, a relative error of 2^-24 on a correction that is itself
+// within 1.5 ulp); the residual of such a faithful quotient is exact in one
+// fused multiply-add, and with y the correctly rounded reciprocal the second
+// correction returns the correctly rounded quotient (Markstein's theorem; the
+// range condition keeps every step clear of overflow, and an element small
+// enough to underflow quantises to 0 either way). Since |x| <= amax, |x / s| <= 127*(1 + 2^-23)
+// and no clamp is needed. Adding 1.5 * 2^23 rounds the quotient to an integer,
+// half to even, and leaves that integer in the low byte of the sum.
+// Smaller s (subnormal scales, where rounding s loses precision and the clamp
+// matters) take the per-element division of quant_elem.
+constexpr float kFastScaleMin = 0x1p-100f;
+
+__device__ __forceinline__ float div_refined(float x, float s, float y) {
+    float q = x * y;
+    q = __builtin_fmaf(__builtin_fmaf(-s, q, x), y, q);
+    return __builtin_fmaf(__builtin_fmaf(-s, q, x), y, q);
+}
+
+// Four elements -> four INT8 codes packed little-endian into one dword.
+__device__ __forceinline__ uint32_t quant4_refined(float a, float b, float c, float d, float s,
+                                                   float y) {
+    constexpr float kRound = 12582912.0f;   // 1.5 * 2^23
+    const uint32_t ua = __float_as_uint(div_refined(a, s, y) + kRound);
+    const uint32_t ub = __float_as_uint(div_refined(b, s, y) + kRound);
+    const uint32_t uc = __float_as_uint(div_refined(c, s, y) + kRound);
+    const uint32_t ud = __float_as_uint(div_refined(d, s, y) + kRound);
+    // low bytes of a, b into bytes 0, 1 and of c, d into bytes 2, 3
+    return __builtin_amdgcn_perm(ub, ua, 0x0c0c0400u) | __builtin_amdgcn_perm(ud, uc, 0x04000c0cu);
+}
+
+// The same four codes by the per-element rule (any s > 0).
+__device__ __forceinline__ uint32_t quant4_divide(float a, float b, float c, float d, float s);
+
 // Max over the `width` consecutive lanes that share an aligned lane group.
 __device__ __forceinline__ float group_max(float v, int width) {
     for (int off = width >> 1; off > 0; off >>= 1)
@@ -59,6 +99,10 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v, int width) {
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
     return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) |
            ((uint32_t)(c & 0xFF) << 16) | ((uint32_t)(d & 0xFF) << 24);
+}
+
+__device__ __forceinline__ uint32_t quant4_divide(float a, float b, float c, float d, float s) {
+    return pack4_i8(quant_elem(a, s), quant_elem(b, s), quant_elem(c, s), quant_elem(d, s));
 }
 
 }  // namespace bsb

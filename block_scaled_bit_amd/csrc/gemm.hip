@@ -485,11 +485,15 @@ __device__ __forceinline__ void big_tile_of(int b, BigTiles t, int &bm, int &bn)
     bn = in / gsz;
 }
 
-template <int OUT>
+// GROUPED: q holds R = M rows sorted by expert, rows [offsets[e], offsets[e+1])
+// multiply expert e's weights qw[e] / sw[e]; tile rows are laid out expert
+// after expert (a tile never spans two experts) and the host sizes the grid
+// for the most tiles any split of R rows over E experts can need.
+template <int OUT, bool GROUPED>
 __global__ void __launch_bounds__(512, 1)
 gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                 const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N, int K,
-                void *__restrict__ y, BigTiles tiles) {
+                void *__restrict__ y, BigTiles tiles, const int32_t *__restrict__ offsets, int E) {
     __shared__ __align__(16) int8_t smem[2][(BBM + BBN) * kGroup];   // 2 x 64 KB
     __shared__ __align__(16) float sws[2][2 * BBN];   // second half: unused slots
 
@@ -497,10 +501,60 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, half = lane >> 5;
     const int G = K >> 7;
+    auto seg = [&](int e, int &lo, int &hi) {   // expert e's rows, clamped to [0, R]
+        lo = offsets[e];
+        hi = offsets[e + 1];
+        lo = lo < 0 ? 0 : (lo > M ? M : lo);
+        hi = hi < lo ? lo : (hi > M ? M : hi);
+    };
+    if (GROUPED) {
+        // The tiles that exist are known only here: count them and let the
+        // first mt*nt workgroups take them (the dispatcher deals workgroups
+        // round-robin to the XCDs, so the idle surplus spreads evenly).
+        // (Offsets that overlap, which the contract excludes, could count more
+        // than the host bound; the count is capped at it, so every tile stays
+        // inside [0, R).)
+        int64_t mt = 0;
+        for (int e = 0; e < E; ++e) {
+            int lo, hi;
+            seg(e, lo, hi);
+            mt += (hi - lo + BBM - 1) / BBM;
+        }
+        mt = mt < tiles.mt ? mt : tiles.mt;
+        if ((int64_t)blockIdx.x >= mt * tiles.nt) return;   // whole workgroup
+        tiles.mt = (int)mt;
+    }
     int bm, bn;
     big_tile_of(blockIdx.x, tiles, bm, bn);
-    const int m0 = bm * BBM, n0 = bn * BBN;
-    const int mrows = min(BBM, M - m0), ncols = min(BBN, N - n0);
+    const int n0 = bn * BBN;
+    int m0, row_end;
+    if (GROUPED) {
+        // tile row bm -> (expert, 256-row block)
+        int t = bm, e = 0;
+        m0 = -1;
+        row_end = 0;
+        for (; e < E; ++e) {
+            int lo, hi;
+            seg(e, lo, hi);
+            const int nt = (hi - lo + BBM - 1) / BBM;
+            if (t < nt) {
+                m0 = lo + t * BBM;
+                row_end = hi;
+                break;
+            }
+            t -= nt;
+        }
+        if (m0 < 0) return;   // unreachable: bm < mt
+        qw += (int64_t)e * N * K;
+        sw += (int64_t)e * N * G;
+    } else {
+        m0 = bm * BBM;
+        row_end = M;
+    }
+    const int mrows = min(BBM, row_end - m0), ncols = min(BBN, N - n0);
+    // a wave whose 64 rows all lie past the tile's last row has nothing to
+    // multiply (short expert segments); it still stages tiles and meets the barriers
+    const bool active = wm * 64 < mrows;
 
     const v4i ra = make_rsrc_words(q + (int64_t)m0 * K, (uint32_t)(mrows * K));
     const v4i rb = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(ncols * K));
@@ -638,12 +692,12 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         const int buf = g & 1;
         dma_group(buf ^ 1, g + 1);     // zeros past the end; lands while group g is multiplied
         load_scale(g + 1);
-        group(buf, g, g > 0);
+        if (!GROUPED || active) group(buf, g, g > 0);
         store_scale(buf ^ 1);
         wait_vmem();                   // the next group's tiles are in LDS ...
         __syncthreads();               // ... for every wave: swap buffers
     }
-    epilogue(acc[1], 1, 3, sc_last, g_last);
+    if (!GROUPED || active) epilogue(acc[1], 1, 3, sc_last, g_last);
 
     if (OUT != OUT_PARTIALS) {
 #pragma unroll
@@ -651,7 +705,7 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (m >= M) continue;
+                if (m >= row_end) continue;
                 const float s = sa[m];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -662,13 +716,16 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     }
 }
 
-template <int OUT>
+// Grouped: sum over experts of ceil(rows_e / 256) <= ceil(R / 256) + E tile rows.
+template <int OUT, bool GROUPED>
 hipError_t launch_big(const int8_t *q, const float *sa, const int8_t *qw, const float *sw, int M,
-                      int N, int K, void *y, hipStream_t stream) {
-    const BigTiles t{(M + BBM - 1) / BBM, (N + BBN - 1) / BBN};
-    const int64_t total = (int64_t)t.mt * t.nt;
+                      int N, int K, void *y, const int32_t *offsets, int E, hipStream_t stream) {
+    const int64_t mt = (M + BBM - 1) / BBM + (GROUPED ? E : 0), nt = (N + BBN - 1) / BBN;
+    const int64_t total = mt * nt;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    gemm_big_kernel<OUT><<<dim3((unsigned)total), 512, 0, stream>>>(q, sa, qw, sw, M, N, K, y, t);
+    const BigTiles t{(int)mt, (int)nt};
+    gemm_big_kernel<OUT, GROUPED>
+        <<<dim3((unsigned)total), 512, 0, stream>>>(q, sa, qw, sw, M, N, K, y, t, offsets, E);
     return hipGetLastError();
 }
 
@@ -745,7 +802,7 @@ hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, cons
         return launch_smallm<OUT>(q, sa, qw, sw, M, N, K, y, stream);
     // the 256x256 kernel addresses its operand panels with 32-bit buffer offsets
     if (M >= kBigMinM && (int64_t)256 * K < ((int64_t)1 << 31))
-        return launch_big<OUT>(q, sa, qw, sw, M, N, K, y, stream);
+        return launch_big<OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 0, stream);
     TileArgs a{q, sa, qw, sw, nullptr, y, M, N, K, 0};
     return launch_tile<OUT, false>(a, (M + TBM - 1) / TBM, stream);
 }
@@ -764,6 +821,15 @@ hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw, const
 hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *qw,
                                const float *sw, const int32_t *offsets, int64_t E, int64_t R,
                                int64_t N, int64_t K, void *y, int out, hipStream_t stream) {
+    // Rows per expert are known only on the device; the mean decides. With
+    // at least 128 rows per expert on average the 256x256 kernel is used.
+    if (R >= 128 * E && (int64_t)256 * K < ((int64_t)1 << 31)) {
+        if (out == OUT_BF16)
+            return launch_big<OUT_BF16, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y, offsets,
+                                              (int)E, stream);
+        return launch_big<OUT_FP32, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y, offsets,
+                                          (int)E, stream);
+    }
     TileArgs a{q, sa, qw, sw, offsets, y, (int)R, (int)N, (int)K, (int)E};
     // Upper bound on the row tiles over all segments, from host values only.
     const int64_t row_tiles = (R + TBM - 1) / TBM + E;

@@ -5,7 +5,9 @@
 //
 // HBM-bound: 2 bytes in, 1 byte out per element. One workgroup per token row;
 // the row is read once with 16-byte coalesced loads and kept in registers
-// while the workgroup reduces the row maximum, then quantised from registers.
+// while the workgroup reduces the row maximum, then quantised from registers
+// (one reciprocal per row and fused corrections instead of a division per
+// element; the result is the same correctly rounded quotient).
 #include "device_common.h"
 #include "launch.h"
 
@@ -32,16 +34,22 @@ __device__ __forceinline__ uint32_t row_reduce_max(uint32_t v, uint32_t *red) {
     return r;
 }
 
-__device__ __forceinline__ uint2 quant8(uint4 v, float s, bool zero) {
-    if (zero) return make_uint2(0u, 0u);
+// Eight BF16 elements -> eight INT8 codes. y = RN(1/s) when s takes the
+// division-free path (s >= kFastScaleMin), unused otherwise.
+__device__ __forceinline__ uint2 quant8(uint4 v, float s, float y, bool fast, bool zero) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    int o[8];
+    float f[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        o[2 * i] = quant_elem(bf16_to_f32(w[i] & 0xFFFFu), s);
-        o[2 * i + 1] = quant_elem(bf16_to_f32(w[i] >> 16), s);
+        f[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
     }
-    return make_uint2(pack4_i8(o[0], o[1], o[2], o[3]), pack4_i8(o[4], o[5], o[6], o[7]));
+    if (fast)
+        return make_uint2(quant4_refined(f[0], f[1], f[2], f[3], s, y),
+                          quant4_refined(f[4], f[5], f[6], f[7], s, y));
+    if (zero) return make_uint2(0u, 0u);
+    return make_uint2(quant4_divide(f[0], f[1], f[2], f[3], s),
+                      quant4_divide(f[4], f[5], f[6], f[7], s));
 }
 
 // CH 16-byte chunks per thread live in registers (K <= 8 * CH * blockDim).
@@ -67,11 +75,13 @@ quantize_act_kernel(const uint16_t *__restrict__ x, int64_t K, int8_t *__restric
     }
     amax = row_reduce_max(amax, red);
     const float s = absmax_scale(bf16_to_f32(amax));
+    const bool fast = s >= kFastScaleMin;
+    const float y = fast ? 1.0f / s : 0.0f;
     if (threadIdx.x == 0) sa[m] = s;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int idx = threadIdx.x + c * blockDim.x;
-        if (idx < nchunk) qr[idx] = quant8(v[c], s, amax == 0);
+        if (idx < nchunk) qr[idx] = quant8(v[c], s, y, fast, amax == 0);
     }
 }
 
@@ -95,9 +105,11 @@ quantize_act_stream_kernel(const uint16_t *__restrict__ x, int64_t K, int8_t *__
     }
     amax = row_reduce_max(amax, red);
     const float s = absmax_scale(bf16_to_f32(amax));
+    const bool fast = s >= kFastScaleMin;
+    const float y = fast ? 1.0f / s : 0.0f;
     if (threadIdx.x == 0) sa[m] = s;
     for (int64_t idx = threadIdx.x; idx < nchunk; idx += blockDim.x)
-        qr[idx] = quant8(xr[idx], s, amax == 0);
+        qr[idx] = quant8(xr[idx], s, y, fast, amax == 0);
 }
 
 }  // namespace

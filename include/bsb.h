@@ -116,7 +116,9 @@ bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa,
  *           to [0, R], so a violated precondition gives unspecified values in
  *           y but never an out-of-bounds access.
  *   y       [R, N] BF16 bits or float32
- * The launch grid is sized from host values only: ceil(R/BM) + E row tiles.
+ * The launch grid is sized from host values only (the row tiles any split of
+ * R rows over E experts can need); with R >= 128*E the kernel uses 256-row
+ * tiles, otherwise 128-row tiles. Neither choice changes a result bit.
  */
 bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa,
                                       const int8_t *qw, const float *sw,

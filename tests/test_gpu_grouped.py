@@ -35,10 +35,16 @@ def _gpu_grouped(q, sa, qw, sw, off, dtype, d):
 
 
 @pytest.mark.parametrize("lengths,N,K", [
+    # fewer than 128 rows per expert on average: 128x128 tiles
     ([0, 1, 127, 128, 129, 0, 5], 96, 256),     # segment ends at 0, 1, BM-1, BM, BM+1
     ([300, 0, 0, 2], 130, 384),
     ([0, 0, 0, 64], 64, 128),
     ([17] * 9, 257, 512),
+    # at least 128 rows per expert on average: 256x256 tiles; segments ending at
+    # 1, 63/64/65 (one wave's rows), 255/256/257 (one tile)
+    ([0, 1, 255, 256, 257, 0, 64, 65, 300], 96, 256),
+    ([700, 0, 129, 513, 63], 300, 384),
+    ([1, 1100], 520, 128),
 ])
 def test_segments_and_tails(lengths, N, K):
     d = require_gpu()
