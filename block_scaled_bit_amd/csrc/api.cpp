@@ -36,6 +36,15 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxElems = (int64_t)1 << 36;
 
+// a * b * c <= limit for positive extents, without overflowing int64.
+inline bool prod_le(int64_t a, int64_t b, int64_t c, int64_t limit) {
+    return a >= 1 && b >= 1 && c >= 1 && a <= limit && b <= limit / a && c <= limit / (a * b);
+}
+
+// The decoders index 16-byte chunks with 32-bit arithmetic: N*K/16 plus one
+// workgroup of slack must stay below 2^32.
+constexpr int64_t kMaxDecodeElems = (int64_t)1 << 35;
+
 inline bool dims_ok(int64_t rows, int64_t N, int64_t K) {
     return rows >= 0 && N >= 1 && K >= 128 && (K % 128) == 0 && rows < kMaxDim && N < kMaxDim &&
            K < kMaxDim;
@@ -89,7 +98,8 @@ bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa, const int8_t *qw
 
 bsb_status bsb_gemm_w8a8_g128_partials(const int8_t *q, const int8_t *qw, int64_t M, int64_t N,
                                        int64_t K, int32_t *P, void *stream) {
-    if (!dims_ok(M, N, K) || N * K > kMaxElems || M * N * (K / 128) > kMaxElems)
+    if (!dims_ok(M, N, K) || N * K > kMaxElems ||
+        (M > 0 && !prod_le(M, N, K / 128, kMaxElems)))
         return BSB_ERR_INVALID_ARG;
     if (M == 0) return BSB_OK;
     if (!q || !qw || !P) return BSB_ERR_INVALID_ARG;
@@ -103,7 +113,7 @@ bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa, const in
                                       const float *sw, const int32_t *offsets, int64_t E,
                                       int64_t R, int64_t N, int64_t K, void *y,
                                       bsb_out_dtype out, void *stream) {
-    if (!dims_ok(R, N, K) || E < 1 || E >= (1 << 20) || E * N * K > kMaxElems)
+    if (!dims_ok(R, N, K) || E < 1 || E >= (1 << 20) || !prod_le(E, N, K, kMaxElems))
         return BSB_ERR_INVALID_ARG;
     if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
     if (R == 0) return BSB_OK;
@@ -120,7 +130,7 @@ bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa, const in
 bsb_status bsb_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t N, int64_t K,
                                 bsb_fp8_dialect dialect, int8_t *qw, float *sw, void *stream) {
     if (N < 128 || N % 128 || K < 128 || K % 128 || N >= kMaxDim || K >= kMaxDim ||
-        N * K >= kMaxElems)
+        N * K > kMaxDecodeElems)
         return BSB_ERR_INVALID_ARG;
     if (dialect != BSB_FP8_OCP && dialect != BSB_FP8_FNUZ) return BSB_ERR_INVALID_ARG;
     if (!w || !bs || !qw || !sw) return BSB_ERR_INVALID_ARG;
@@ -135,7 +145,7 @@ bsb_status bsb_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t N, 
 bsb_status bsb_decode_mxfp4(const uint8_t *packed, const uint8_t *scale, int64_t E, int64_t N,
                             int64_t K, int8_t *qw, float *sw, void *stream) {
     if (E < 1 || N < 1 || K < 128 || K % 128 || E >= kMaxDim || N >= kMaxDim || K >= kMaxDim ||
-        E * N * K >= kMaxElems)
+        !prod_le(E, N, K, kMaxDecodeElems))
         return BSB_ERR_INVALID_ARG;
     if (!packed || !scale || !qw || !sw) return BSB_ERR_INVALID_ARG;
     if (!aligned16(packed) || !aligned16(scale) || !aligned16(qw) || !aligned16(sw))

@@ -800,8 +800,11 @@ hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, cons
     // activation matrix (at most 64 rows) with 32-bit buffer offsets
     if (M <= 64 && (int64_t)128 * K < ((int64_t)1 << 31))
         return launch_smallm<OUT>(q, sa, qw, sw, M, N, K, y, stream);
-    // the 256x256 kernel addresses its operand panels with 32-bit buffer offsets
-    if (M >= kBigMinM && (int64_t)256 * K < ((int64_t)1 << 31))
+    // The 256x256 kernel (which addresses its operand panels with 32-bit
+    // buffer offsets) when it has at least one tile per CU; below that the
+    // 128x128 kernel's four times as many tiles finish sooner.
+    const int64_t big_tiles = (int64_t)((M + BBM - 1) / BBM) * ((N + BBN - 1) / BBN);
+    if (M >= kBigMinM && (int64_t)256 * K < ((int64_t)1 << 31) && big_tiles >= kCUs)
         return launch_big<OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 0, stream);
     TileArgs a{q, sa, qw, sw, nullptr, y, M, N, K, 0};
     return launch_tile<OUT, false>(a, (M + TBM - 1) / TBM, stream);
@@ -822,8 +825,10 @@ hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *q
                                const float *sw, const int32_t *offsets, int64_t E, int64_t R,
                                int64_t N, int64_t K, void *y, int out, hipStream_t stream) {
     // Rows per expert are known only on the device; the mean decides. With
-    // at least 128 rows per expert on average the 256x256 kernel is used.
-    if (R >= 128 * E && (int64_t)256 * K < ((int64_t)1 << 31)) {
+    // at least 128 rows per expert on average, and enough rows for a tile per
+    // CU, the 256x256 kernel is used.
+    const int64_t big_tiles = ((R + BBM - 1) / BBM) * ((N + BBN - 1) / BBN);
+    if (R >= 128 * E && big_tiles >= kCUs && (int64_t)256 * K < ((int64_t)1 << 31)) {
         if (out == OUT_BF16)
             return launch_big<OUT_BF16, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y, offsets,
                                               (int)E, stream);

@@ -26,7 +26,10 @@
  *    and is contiguous in both operands; G = K / 128 is the number of
  *    128-wide K groups.
  *  - Sizes: K % 128 == 0 and K > 0; N >= 1; M, R >= 0 (0 rows is a
- *    successful no-op that launches nothing).
+ *    successful no-op that launches nothing). Every extent is below 2^30;
+ *    a weight matrix (all experts together) holds at most 2^36 elements,
+ *    2^35 for the decoders' inputs, and the partials at most 2^36 values.
+ *    Larger sizes return BSB_ERR_INVALID_ARG.
  *  - Every pointer must be 16-byte aligned (BSB_ERR_MISALIGNED otherwise).
  *  - Arguments are validated before anything is launched: a NULL pointer
  *    with a non-empty size, a negative or inconsistent size, or a bad enum

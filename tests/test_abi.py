@@ -55,6 +55,12 @@ def test_invalid_sizes_return_invalid_arg(L):
     assert L.bsb_grouped_gemm_w8a8_g128(A, A, A, A, A, 0, 4, 8, 128, A, 0, None) == INVALID
     assert L.bsb_decode_fp8_block(A, A, 100, 128, 0, A, A, None) == INVALID   # N % 128
     assert L.bsb_decode_mxfp4(A, A, 1, 8, 96, A, A, None) == INVALID
+    # products of in-range extents that overflow int64 or the index limits
+    big = 1 << 29
+    assert L.bsb_grouped_gemm_w8a8_g128(A, A, A, A, A, 1 << 19, 4, big, big, A, 0, None) == INVALID
+    assert L.bsb_decode_mxfp4(A, A, big, big, big, A, A, None) == INVALID
+    assert L.bsb_gemm_w8a8_g128_partials(A, A, big, big, 1 << 20, A, None) == INVALID
+    assert L.bsb_decode_fp8_block(A, A, 1 << 23, 1 << 13, 0, A, A, None) == INVALID   # 2^36
 
 
 def test_bad_enums_return_invalid_arg(L):

@@ -68,9 +68,12 @@ def test_tiny_config():
     (1, 1, 128), (3, 65, 256), (16, 64, 384), (17, 100, 128), (32, 257, 512),
     (33, 64, 256), (64, 130, 640), (65, 129, 256), (100, 300, 384), (128, 128, 128),
     (130, 257, 512), (257, 1, 256), (300, 96, 1024),
-    (512, 256, 256), (600, 300, 384), (777, 1000, 256), (1024, 520, 128), (513, 7, 1152)])
+    (512, 256, 256), (600, 300, 384), (777, 1000, 256), (1024, 520, 128), (513, 7, 1152),
+    (2049, 7425, 256), (2305, 7000, 384)])
 def test_ragged_shapes(M, N, K):
-    """Every kernel (M <= 64, up to 511, from 512), partial tiles in M and N, several groups."""
+    """Every kernel (M <= 64; 128x128 tiles; 256x256 tiles from 512 rows when there is at
+    least one such tile per CU, the last two shapes), partial tiles in M and N, several
+    groups."""
     d = require_gpu()
     say(f"gemm ragged M={M} N={N} K={K}")
     cfg, q, sa = _inputs(M, K, N, M * 1000 + N + K)
