@@ -77,11 +77,15 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // Out-of-range rows, columns and groups read zero through the buffer
 // descriptors, so no load sits behind a branch. Requires 16*NW*K < 2^31
 // (checked by the launcher).
-template <int MB, int NW, int OUT, int S, int D>
+//
+// GROUPED (MoE with few rows per expert): blockIdx.y is the expert; the
+// workgroup walks that expert's rows [offsets[e], offsets[e+1]) in passes of
+// 16*MB rows against its slice of the expert's weights.
+template <int MB, int NW, int OUT, int S, int D, bool GROUPED>
 __global__ void __launch_bounds__(64 * NW)
 gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                    const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N,
-                   int K, void *__restrict__ y) {
+                   int K, void *__restrict__ y, const int32_t *__restrict__ offsets) {
     constexpr int ROWS = 16 * MB;              // activation rows
     constexpr int WR = 16 * NW;                // weight rows per workgroup
     constexpr int NT = 64 * NW;                // threads
@@ -99,9 +103,22 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     const int nl = wave * 16 + col;     // this lane's weight row within the slice
     const int n = n0 + nl;
 
+    int lo = 0, hi = M;                 // rows of this workgroup
+    if (GROUPED) {
+        const int e = blockIdx.y;       // segment clamped to [0, R]
+        lo = offsets[e];
+        hi = offsets[e + 1];
+        lo = lo < 0 ? 0 : (lo > M ? M : lo);
+        hi = hi < lo ? lo : (hi > M ? M : hi);
+        if (hi == lo) return;           // whole workgroup: empty expert
+        qw += (int64_t)e * N * K;
+        sw += (int64_t)e * N * G;
+    }
+
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw + (int64_t)n0 * K, (uint32_t)(nrows * K));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(sw + (int64_t)n0 * G, (uint32_t)(nrows * G * 4));
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(q, (uint32_t)(M * K));
+    __amdgpu_buffer_rsrc_t ra;          // the current pass's activation rows
+    int rows = 0, r0 = 0;
 
     constexpr int BPT = S * BT / (NT * 16);           // weight chunks per thread per set
     constexpr int ACH = S * AT / 16;                  // activation chunks per set
@@ -166,10 +183,6 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     };
 
     float facc[MB][4];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
 
     auto compute = [&](const float *scale, int buf, int s0) {
 #pragma unroll
@@ -202,9 +215,9 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int m = i * 16 + slot * 4 + r;
-                            if (m < M)
-                                reinterpret_cast<int32_t *>(y)[((int64_t)m * N + n) * G + g] =
-                                    acc[i][r];
+                            if (m < rows)
+                                reinterpret_cast<int32_t *>(
+                                    y)[((int64_t)(r0 + m) * N + n) * G + g] = acc[i][r];
                         }
                 }
             } else {
@@ -236,25 +249,44 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         compute(scale, buf, ss);
     };
 
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d) {
-        issue(d, d * S);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int s0 = 0; s0 < G; s0 += D * S) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) step(d, s0 + d * S);   // may run past G: zeros
-    }
-
-    if (OUT != OUT_PARTIALS && nl < nrows) {
+    // One pass: rows r0 .. r0+rows-1 (rows <= 16*MB) against the whole K walk.
+    auto pass = [&]() {
+        ra = make_rsrc(q + (int64_t)r0 * K, (uint32_t)(rows * K));
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = i * 16 + slot * 4 + r;
-                if (m < M) store_out<OUT>(y, (int64_t)m * N + n, facc[i][r] * sa[m]);
-            }
+            for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d) {
+            issue(d, d * S);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int s0 = 0; s0 < G; s0 += D * S) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) step(d, s0 + d * S);   // may run past G: zeros
+        }
+        if (OUT != OUT_PARTIALS && nl < nrows) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = i * 16 + slot * 4 + r;
+                    if (m < rows)
+                        store_out<OUT>(y, (int64_t)(r0 + m) * N + n, facc[i][r] * sa[r0 + m]);
+                }
+        }
+    };
+
+    if (!GROUPED) {
+        rows = M;
+        pass();
+    } else {
+        for (r0 = lo; r0 < hi; r0 += ROWS) {
+            rows = min(ROWS, hi - r0);
+            pass();
+            __syncthreads();            // the next pass restages both LDS buffers
+        }
     }
 }
 
@@ -747,12 +779,13 @@ hipError_t launch_tile(const TileArgs &a, int64_t row_tiles, hipStream_t stream)
 constexpr int kSmallS = BSB_SMALLM_S;     // K groups per super-stage
 constexpr int kSmallD = BSB_SMALLM_D;     // super-stages in flight (register ring depth)
 
-template <int MB, int NW, int OUT>
+template <int MB, int NW, int OUT, bool GROUPED>
 hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
-                            int M, int N, int K, void *y, hipStream_t stream) {
-    const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW)));
-    gemm_smallm_kernel<MB, NW, OUT, kSmallS, kSmallD>
-        <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y);
+                            int M, int N, int K, void *y, const int32_t *offsets, int E,
+                            hipStream_t stream) {
+    const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW)), GROUPED ? (unsigned)E : 1u);
+    gemm_smallm_kernel<MB, NW, OUT, kSmallS, kSmallD, GROUPED>
+        <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets);
     return hipGetLastError();
 }
 
@@ -762,30 +795,36 @@ hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, 
 // most 8 waves, and at least what the activation tile needs (register ring).
 constexpr int kCUs = 256;
 
-template <int MB, int OUT>
+template <int MB, int OUT, bool GROUPED>
 hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
-                            int M, int N, int K, void *y, hipStream_t stream) {
-    const int blocks16 = (N + 15) / 16;
-    const int rounds = (blocks16 + 8 * kCUs - 1) / (8 * kCUs);
-    int nw = (blocks16 + kCUs * rounds - 1) / (kCUs * rounds);
+                            int M, int N, int K, void *y, const int32_t *offsets, int E,
+                            hipStream_t stream) {
+    const int64_t blocks16 = (int64_t)((N + 15) / 16) * (GROUPED ? E : 1);
+    const int64_t rounds = (blocks16 + 8 * kCUs - 1) / (8 * kCUs);
+    int nw = (int)((blocks16 + kCUs * rounds - 1) / (kCUs * rounds));
     nw = nw < (MB >= 4 ? 4 : 2) ? (MB >= 4 ? 4 : 2) : nw;
+#define BSB_SMALLM_CASE(W)                                                                       \
+    case W:                                                                                      \
+        return launch_smallm_mb<MB, W, OUT, GROUPED>(q, sa, qw, sw, M, N, K, y, offsets, E, stream);
     switch (nw) {
-        case 2: return launch_smallm_mb<MB, 2, OUT>(q, sa, qw, sw, M, N, K, y, stream);
-        case 3: return launch_smallm_mb<MB, 3, OUT>(q, sa, qw, sw, M, N, K, y, stream);
-        case 4: return launch_smallm_mb<MB, 4, OUT>(q, sa, qw, sw, M, N, K, y, stream);
-        case 5: return launch_smallm_mb<MB, 5, OUT>(q, sa, qw, sw, M, N, K, y, stream);
-        case 6: return launch_smallm_mb<MB, 6, OUT>(q, sa, qw, sw, M, N, K, y, stream);
-        case 7: return launch_smallm_mb<MB, 7, OUT>(q, sa, qw, sw, M, N, K, y, stream);
-        default: return launch_smallm_mb<MB, 8, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+        BSB_SMALLM_CASE(2)
+        BSB_SMALLM_CASE(3)
+        BSB_SMALLM_CASE(4)
+        BSB_SMALLM_CASE(5)
+        BSB_SMALLM_CASE(6)
+        BSB_SMALLM_CASE(7)
+        default: return launch_smallm_mb<MB, 8, OUT, GROUPED>(q, sa, qw, sw, M, N, K, y, offsets,
+                                                               E, stream);
     }
+#undef BSB_SMALLM_CASE
 }
 
 template <int OUT>
 hipError_t launch_smallm(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                          int M, int N, int K, void *y, hipStream_t stream) {
-    if (M <= 16) return launch_smallm_nw<1, OUT>(q, sa, qw, sw, M, N, K, y, stream);
-    if (M <= 32) return launch_smallm_nw<2, OUT>(q, sa, qw, sw, M, N, K, y, stream);
-    return launch_smallm_nw<4, OUT>(q, sa, qw, sw, M, N, K, y, stream);
+    if (M <= 16) return launch_smallm_nw<1, OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 1, stream);
+    if (M <= 32) return launch_smallm_nw<2, OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 1, stream);
+    return launch_smallm_nw<4, OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 1, stream);
 }
 
 #ifndef BSB_BIG_MIN_M
@@ -834,6 +873,15 @@ hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *q
                                               (int)E, stream);
         return launch_big<OUT_FP32, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y, offsets,
                                           (int)E, stream);
+    }
+    // At most 32 rows per expert on average (decode-shaped MoE): stream each
+    // expert's weights once per 32 of its rows.
+    if (R <= 32 * E && E <= 65535 && (int64_t)128 * K < ((int64_t)1 << 31)) {
+        if (out == OUT_BF16)
+            return launch_smallm_nw<2, OUT_BF16, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y,
+                                                       offsets, (int)E, stream);
+        return launch_smallm_nw<2, OUT_FP32, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y,
+                                                   offsets, (int)E, stream);
     }
     TileArgs a{q, sa, qw, sw, offsets, y, (int)R, (int)N, (int)K, (int)E};
     // Upper bound on the row tiles over all segments, from host values only.

@@ -35,11 +35,14 @@ def _gpu_grouped(q, sa, qw, sw, off, dtype, d):
 
 
 @pytest.mark.parametrize("lengths,N,K", [
-    # fewer than 128 rows per expert on average: 128x128 tiles
-    ([0, 1, 127, 128, 129, 0, 5], 96, 256),     # segment ends at 0, 1, BM-1, BM, BM+1
-    ([300, 0, 0, 2], 130, 384),
+    # at most 32 rows per expert on average: weights streamed per expert, rows
+    # in passes of 32 (segments of 1, 2, 31, 33, 64, 70 rows)
     ([0, 0, 0, 64], 64, 128),
     ([17] * 9, 257, 512),
+    ([0, 70, 1, 33, 0, 31, 2], 200, 384),
+    # up to 128 rows per expert on average: 128x128 tiles
+    ([0, 1, 127, 128, 129, 0, 5], 96, 256),     # segment ends at 0, 1, BM-1, BM, BM+1
+    ([300, 0, 0, 2], 130, 384),
     # at least 128 rows per expert on average: 256x256 tiles; segments ending at
     # 1, 63/64/65 (one wave's rows), 255/256/257 (one tile)
     ([0, 1, 255, 256, 257, 0, 64, 65, 300], 96, 256),
