@@ -154,7 +154,7 @@ def cpu_baseline(budget_s=10.0):
     Ns = 7168                                # a quarter of the output columns
     d = synth.linear_inputs(M, K, Ns, outlier_p=0.005, outlier_f=30.0, seed=0)
     runs, t_tot = 0, 0.0
-    while t_tot < budget_s and runs < 20:
+    while t_tot < budget_s and runs < 1000:
         t0 = time.perf_counter()
         q, sa = oracle.quantize_act_ref(d["x"])
         oracle.gemm_fp32_ordered_ref(q, sa, d["qw"], d["sw"])
