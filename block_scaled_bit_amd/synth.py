@@ -117,14 +117,33 @@ def sort_by_expert(topk_ids: np.ndarray, E: int):
     return token_of_row, offsets
 
 
+def row_of_pair(topk_ids: np.ndarray) -> np.ndarray:
+    """int32 [T, topk]: the sorted row that holds token t's k-th expert slot
+    (the inverse of the stable sort of sort_by_expert)."""
+    flat = topk_ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    inv = np.empty(flat.size, np.int64)
+    inv[order] = np.arange(flat.size)
+    return inv.reshape(topk_ids.shape).astype(np.int32)
+
+
+def gate_weights(rng: np.random.Generator, T: int, topk: int) -> np.ndarray:
+    """float32 [T, topk] router weights of the selected experts: positive,
+    each token's weights normalised to sum to 1."""
+    g = rng.random((T, topk)) + 0.05
+    return (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
 def moe_inputs(T: int = 4096, K: int = 4096, N: int = 2048, E: int = 64,
                topk: int = 8, zipf_s: float = 1.1, n_empty: int = 4,
                outlier_p: float = 0.0, outlier_f: float = 1.0, seed: int = 0) -> dict:
     """Routed MoE expert layer.
 
-    x_sorted BF16 bits [R,K] holds the token rows gathered in expert order,
-    offsets int32 [E+1] the per-expert row ranges, qw int8 [E,N,K],
-    sw float32 [E,N,K/128].
+    x_tokens BF16 bits [T,K] are the tokens; x_sorted [R,K] holds their rows
+    gathered in expert order (token_of_row int32 [R]), offsets int32 [E+1]
+    the per-expert row ranges, qw int8 [E,N,K], sw float32 [E,N,K/128];
+    row_of_pair int32 [T,topk] is the inverse map and gate float32 [T,topk]
+    the router weights of the combine.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     X = activations(rng, T, K, outlier_p, outlier_f)
@@ -132,9 +151,11 @@ def moe_inputs(T: int = 4096, K: int = 4096, N: int = 2048, E: int = 64,
     token_of_row, offsets = sort_by_expert(topk_ids, E)
     qw = int8_weights(rng, (E, N, K))
     sw = group_scales(rng, (E, N, K // GROUP))
-    return dict(x_tokens=X, topk_ids=topk_ids, token_of_row=token_of_row,
+    gate = gate_weights(rng, T, topk)          # drawn last: earlier tensors unchanged
+    return dict(x_tokens=X, topk_ids=topk_ids, token_of_row=token_of_row.astype(np.int32),
+                row_of_pair=row_of_pair(topk_ids), gate=gate,
                 x_sorted=X[token_of_row], offsets=offsets, qw=qw, sw=sw,
-                T=T, K=K, N=N, E=E, R=int(offsets[-1]))
+                T=T, K=K, N=N, E=E, R=int(offsets[-1]), topk=topk)
 
 
 def fp8_block_weights(rng: np.random.Generator, N: int, K: int, exp_lo: int = -8,
