@@ -26,8 +26,8 @@ Reported (one JSON line on stdout):
   rows           every other workload, each kernel timed alone the same way
                  with its own rotating input sets: the tiny linear (16x1024x1024),
                  the prefill quantisation, the routed MoE layer (4096 tokens,
-                 top-8 of 64 Zipf-routed experts, K=4096, N=2048: quantisation
-                 and grouped GEMM), the block-format decoders (FP8 [128,128]
+                 top-8 of 64 Zipf-routed experts, K=4096, N=2048: quantisation,
+                 gather into expert order, grouped GEMM, top-k combine), the block-format decoders (FP8 [128,128]
                  4096x7168 in both dialects, MXFP4 8x2048x4096) and the dense and
                  grouped GEMMs on the decoded weights at 32 and 1024 tokens
 """
@@ -304,7 +304,38 @@ def extra_rows(torch, L, stream, dev, steps):
                                                  bound="mfma+hbm")
     rows["moe_4096tok_top8_64e_grouped"].update(rows=R, experts_nonempty=nonempty)
     log(f"moe: quant {tq * 1e3:.1f} us, grouped {tg * 1e3:.1f} us")
-    del m, xs, qw, sw, off, q, sa, y, p
+    # the glue either side: quantise the T tokens, gather into expert order,
+    # (grouped GEMM), combine the top-k outputs per token
+    T, topk = m["T"], m["topk"]
+    xt = t(m["x_tokens"].view(np.int16))
+    qt = torch.empty((T, K), dtype=torch.int8, device=dev)
+    st = torch.empty((T,), dtype=torch.float32, device=dev)
+    tor, rp, gate = t(m["token_of_row"]), t(m["row_of_pair"]), t(m["gate"])
+    out = torch.empty((T, N), dtype=torch.int16, device=dev)
+    p.update(xt=xt.data_ptr(), qt=qt.data_ptr(), st=st.data_ptr(), tor=tor.data_ptr(),
+             rp=rp.data_ptr(), gate=gate.data_ptr(), out=out.data_ptr())
+    tqt = Row("moe quant tokens", [p], lambda p, st_: _ok(
+        L, L.bsb_quantize_act(p["xt"], T, K, p["qt"], p["st"], st_))).time(torch, stream, 20, 3)
+    tga = Row("moe gather", [p], lambda p, st_: _ok(
+        L, L.bsb_gather_rows(p["qt"], p["st"], p["tor"], R, T, K, p["q"], p["sa"], st_))).time(
+        torch, stream, 20, 3)
+    tco = Row("moe combine", [p], lambda p, st_: _ok(
+        L, L.bsb_moe_combine(p["y"], p["rp"], p["gate"], T, topk, R, N, p["out"], st_))).time(
+        torch, stream, 20, 3)
+    rows["moe_4096tok_top8_64e_quant_tokens"] = _rate(tqt * 1e3, byts=quant_bytes(T, K))
+    # gather: the token rows (which the last-level cache holds) are read once
+    # per slot, the sorted rows written once; counted: T*K + R*K + scales + index
+    rows["moe_4096tok_top8_64e_gather"] = _rate(tga * 1e3, byts=T * K + R * K + 4 * T + 8 * R)
+    rows["moe_4096tok_top8_64e_combine"] = _rate(
+        tco * 1e3, byts=2 * R * N + 2 * T * N + 8 * T * topk)
+    rows["moe_4096tok_top8_64e_layer"] = {
+        "avg_us": round((tqt + tga + tg + tco) * 1e3, 2),
+        "parts": "quantize_act(tokens) + gather_rows + grouped GEMM + moe_combine",
+        "quantise_after_gather_us": round((tq + tg) * 1e3, 2),
+        "note": "quantise_after_gather_us = quantize_act(gathered rows) + grouped GEMM, no combine"}
+    log(f"moe glue: quant tokens {tqt * 1e3:.1f} us, gather {tga * 1e3:.1f} us, "
+        f"combine {tco * 1e3:.1f} us")
+    del m, xs, qw, sw, off, q, sa, y, p, xt, qt, st, tor, rp, gate, out
     torch.cuda.empty_cache()
 
     # block formats: FP8 [128,128] dense 4096x7168 and MXFP4 experts 8x2048x4096

@@ -33,6 +33,8 @@ _SIGNATURES = {
     "bsb_decode_fp8_block": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_p],
     "bsb_decode_mxfp4": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "bsb_gemm_w8a8_g128_partials": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+    "bsb_gather_rows": [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
+    "bsb_moe_combine": [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
 }
 EXPORTED = tuple(_SIGNATURES) + ("bsb_status_string", "bsb_abi_version")
 
@@ -227,3 +229,48 @@ def decode_mxfp4(packed: torch.Tensor, scale: torch.Tensor,
         _check(lib().bsb_decode_mxfp4(_ptr(packed), _ptr(scale), E, N, K, _ptr(qw), _ptr(sw),
                                       _stream(dev)), "bsb_decode_mxfp4")
     return qw, sw
+
+
+def gather_rows(q: torch.Tensor, sa: torch.Tensor, index: torch.Tensor,
+                q_out: Optional[torch.Tensor] = None,
+                sa_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Quantised tokens q [T,K] / sa [T] -> rows in expert order q[index], sa[index] ([R,K], [R])."""
+    _need(q, "q", (torch.int8,))
+    if q.dim() != 2:
+        raise ValueError("q must be [T, K]")
+    T, K = q.shape
+    dev = q.device
+    _need(sa, "sa", (torch.float32,), (T,), dev)
+    _need(index, "index", (torch.int32,), None, dev)
+    if index.dim() != 1:
+        raise ValueError("index must be [R]")
+    R = index.shape[0]
+    q_out = torch.empty((R, K), dtype=torch.int8, device=dev) if q_out is None else q_out
+    sa_out = torch.empty((R,), dtype=torch.float32, device=dev) if sa_out is None else sa_out
+    _need(q_out, "q_out", (torch.int8,), (R, K), dev)
+    _need(sa_out, "sa_out", (torch.float32,), (R,), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_gather_rows(_ptr(q), _ptr(sa), _ptr(index), R, T, K, _ptr(q_out),
+                                     _ptr(sa_out), _stream(dev)), "bsb_gather_rows")
+    return q_out, sa_out
+
+
+def moe_combine(y: torch.Tensor, row_of_pair: torch.Tensor, gate: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Expert outputs y [R,N] (BF16) -> per-token sum_k gate[t,k] * y[row_of_pair[t,k]] [T,N] BF16."""
+    _need(y, "y", _BF16_BITS)
+    if y.dim() != 2:
+        raise ValueError("y must be [R, N]")
+    R, N = y.shape
+    dev = y.device
+    _need(row_of_pair, "row_of_pair", (torch.int32,), None, dev)
+    if row_of_pair.dim() != 2:
+        raise ValueError("row_of_pair must be [T, topk]")
+    T, topk = row_of_pair.shape
+    _need(gate, "gate", (torch.float32,), (T, topk), dev)
+    out = torch.empty((T, N), dtype=y.dtype, device=dev) if out is None else out
+    _need(out, "out", _BF16_BITS, (T, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_moe_combine(_ptr(y), _ptr(row_of_pair), _ptr(gate), T, topk, R, N,
+                                     _ptr(out), _stream(dev)), "bsb_moe_combine")
+    return out

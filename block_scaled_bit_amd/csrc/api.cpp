@@ -45,6 +45,9 @@ inline bool prod_le(int64_t a, int64_t b, int64_t c, int64_t limit) {
 // workgroup of slack must stay below 2^32.
 constexpr int64_t kMaxDecodeElems = (int64_t)1 << 35;
 
+// Experts per token accepted by the combine.
+constexpr int64_t kMaxTopk = 256;
+
 inline bool dims_ok(int64_t rows, int64_t N, int64_t K) {
     return rows >= 0 && N >= 1 && K >= 128 && (K % 128) == 0 && rows < kMaxDim && N < kMaxDim &&
            K < kMaxDim;
@@ -153,6 +156,38 @@ bsb_status bsb_decode_mxfp4(const uint8_t *packed, const uint8_t *scale, int64_t
     if (bsb_status s = check_device()) return s;
     (void)hipGetLastError();
     return finish(bsb::launch_decode_mxfp4(packed, scale, E, N, K, qw, sw, as_stream(stream)));
+}
+
+bsb_status bsb_gather_rows(const int8_t *q, const float *sa, const int32_t *index, int64_t R,
+                           int64_t T, int64_t K, int8_t *q_out, float *sa_out, void *stream) {
+    if (R < 0 || R >= kMaxDim || T < 1 || T >= kMaxDim || K < 128 || K % 128 || K >= kMaxDim ||
+        (R > 0 && !prod_le(R, K, 1, kMaxElems)) || !prod_le(T, K, 1, kMaxElems))
+        return BSB_ERR_INVALID_ARG;
+    if (R == 0) return BSB_OK;
+    if (!q || !sa || !index || !q_out || !sa_out) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(sa) || !aligned16(index) || !aligned16(q_out) ||
+        !aligned16(sa_out))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_gather_rows(q, sa, index, R, T, K, q_out, sa_out, as_stream(stream)));
+}
+
+bsb_status bsb_moe_combine(const uint16_t *y, const int32_t *row_of_pair, const float *gate,
+                           int64_t T, int64_t topk, int64_t R, int64_t N, uint16_t *out,
+                           void *stream) {
+    if (T < 0 || T >= kMaxDim || topk < 1 || topk > kMaxTopk || R < 1 || R >= kMaxDim ||
+        N < 8 || N % 8 || N >= kMaxDim || !prod_le(R, N, 1, kMaxElems) ||
+        (T > 0 && !prod_le(T, N, 1, kMaxElems)) || (T > 0 && !prod_le(T, topk, 1, kMaxElems)))
+        return BSB_ERR_INVALID_ARG;
+    if (T == 0) return BSB_OK;
+    if (!y || !row_of_pair || !gate || !out) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(y) || !aligned16(row_of_pair) || !aligned16(gate) || !aligned16(out))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_moe_combine(y, row_of_pair, gate, T, topk, R, N, out,
+                                          as_stream(stream)));
 }
 
 }  // extern "C"

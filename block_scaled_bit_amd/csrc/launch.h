@@ -28,4 +28,12 @@ hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *q
                                int64_t R, int64_t N, int64_t K, void *y, int out,
                                hipStream_t stream);
 
+hipError_t launch_gather_rows(const int8_t *q, const float *sa, const int32_t *index, int64_t R,
+                              int64_t T, int64_t K, int8_t *q_out, float *sa_out,
+                              hipStream_t stream);
+
+hipError_t launch_moe_combine(const uint16_t *y, const int32_t *row_of_pair, const float *gate,
+                              int64_t T, int64_t topk, int64_t R, int64_t N, uint16_t *out,
+                              hipStream_t stream);
+
 }  // namespace bsb

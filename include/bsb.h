@@ -9,7 +9,8 @@
  *        retrospective" (aimsg.uk), sections "FP8 dialect clash",
  *        "HIP Graphs limits" and "Loose ends".
  *   [P3] "Hunyuan 770B in INT8 on domestic accelerators"
- *        (pwwt.cn/news/4495474), sec. 3.1 and sec. 1.3 / 4.4.
+ *        (pwwt.cn/news/4495474), sec. 3.1 and sec. 1.3 / 4.4 (MoE dispatch
+ *        and combine).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -168,6 +169,36 @@ bsb_status bsb_decode_mxfp4(const uint8_t *packed, const uint8_t *scale,
 bsb_status bsb_gemm_w8a8_g128_partials(const int8_t *q, const int8_t *qw,
                                        int64_t M, int64_t N, int64_t K,
                                        int32_t *P, void *stream);
+
+/*
+ * MoE dispatch on one GPU ([P3] sec. 1.3 / 4.4: tokens are sent to the
+ * experts they selected): gather quantised token rows into expert order.
+ *     q_out[r, :] = q[index[r], :],  sa_out[r] = sa[index[r]]
+ * Quantising T tokens with bsb_quantize_act and gathering gives the same
+ * bits as quantising the R gathered BF16 rows (the rule works per row).
+ *   q      [T, K] int8, sa [T] float32 (bsb_quantize_act's outputs)
+ *   index  [R] int32 token of each sorted row (values outside [0, T) are
+ *          outside the domain: that row is written as zeros with scale 0)
+ *   q_out  [R, K] int8, sa_out [R] float32 (written)
+ */
+bsb_status bsb_gather_rows(const int8_t *q, const float *sa, const int32_t *index,
+                           int64_t R, int64_t T, int64_t K,
+                           int8_t *q_out, float *sa_out, void *stream);
+
+/*
+ * MoE combine ([P3] sec. 4.4: the experts' outputs come back to their token):
+ *     out[t, :] = sum_{k = 0 .. topk-1} gate[t, k] * y[row_of_pair[t, k], :]
+ * in float32, one fused multiply-add per slot with k ascending from 0, then
+ * BF16 round to nearest even.
+ *   y            [R, N] BF16 bits: the grouped GEMM's output rows
+ *   row_of_pair  [T, topk] int32: the sorted row of token t's k-th expert
+ *                (values outside [0, R) are outside the domain and add nothing)
+ *   gate         [T, topk] float32 router weights
+ *   out          [T, N] BF16 bits (written); N % 8 == 0, 1 <= topk <= 256
+ */
+bsb_status bsb_moe_combine(const uint16_t *y, const int32_t *row_of_pair,
+                           const float *gate, int64_t T, int64_t topk,
+                           int64_t R, int64_t N, uint16_t *out, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *bsb_status_string(bsb_status s);

@@ -61,6 +61,11 @@ def test_invalid_sizes_return_invalid_arg(L):
     assert L.bsb_decode_mxfp4(A, A, big, big, big, A, A, None) == INVALID
     assert L.bsb_gemm_w8a8_g128_partials(A, A, big, big, 1 << 20, A, None) == INVALID
     assert L.bsb_decode_fp8_block(A, A, 1 << 23, 1 << 13, 0, A, A, None) == INVALID   # 2^36
+    assert L.bsb_gather_rows(A, A, A, 4, 0, 128, A, A, None) == INVALID          # no tokens
+    assert L.bsb_gather_rows(A, A, A, 4, 8, 100, A, A, None) == INVALID          # K % 128
+    assert L.bsb_moe_combine(A, A, A, 4, 0, 16, 64, A, None) == INVALID          # topk 0
+    assert L.bsb_moe_combine(A, A, A, 4, 257, 16, 64, A, None) == INVALID        # topk > 256
+    assert L.bsb_moe_combine(A, A, A, 4, 2, 16, 60, A, None) == INVALID          # N % 8
 
 
 def test_bad_enums_return_invalid_arg(L):
@@ -76,6 +81,8 @@ def test_null_pointers_return_invalid_arg(L):
     assert L.bsb_decode_fp8_block(A, A, 128, 128, 0, None, A, None) == INVALID
     assert L.bsb_decode_mxfp4(A, None, 1, 8, 128, A, A, None) == INVALID
     assert L.bsb_gemm_w8a8_g128_partials(A, A, 4, 8, 128, None, None) == INVALID
+    assert L.bsb_gather_rows(A, A, None, 4, 8, 128, A, A, None) == INVALID
+    assert L.bsb_moe_combine(A, None, A, 4, 2, 16, 64, A, None) == INVALID
 
 
 def test_misaligned_pointers(L):
@@ -83,6 +90,8 @@ def test_misaligned_pointers(L):
     assert L.bsb_gemm_w8a8_g128(A, A, A, U, 4, 8, 128, A, 1, None) == MISALIGNED
     assert L.bsb_grouped_gemm_w8a8_g128(A, A, A, A, U, 2, 4, 8, 128, A, 0, None) == MISALIGNED
     assert L.bsb_decode_mxfp4(A, A, 1, 8, 128, U, A, None) == MISALIGNED
+    assert L.bsb_gather_rows(A, A, U, 4, 8, 128, A, A, None) == MISALIGNED
+    assert L.bsb_moe_combine(A, A, U, 4, 2, 16, 64, A, None) == MISALIGNED
 
 
 def test_empty_rows_are_a_successful_no_op(L):
@@ -91,6 +100,8 @@ def test_empty_rows_are_a_successful_no_op(L):
     assert L.bsb_gemm_w8a8_g128(None, None, None, None, 0, 8, 128, None, 0, None) == OK
     assert L.bsb_grouped_gemm_w8a8_g128(None, None, None, None, None, 3, 0, 8, 128, None, 0,
                                         None) == OK
+    assert L.bsb_gather_rows(None, None, None, 0, 8, 128, None, None, None) == OK
+    assert L.bsb_moe_combine(None, None, None, 0, 2, 16, 64, None, None) == OK
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
@@ -98,6 +109,8 @@ def test_no_gpu_is_unsupported_device(L):
     # valid arguments, but no gfx950 device is present: fail fast, launch nothing
     assert L.bsb_quantize_act(A, 4, 128, A, A, None) == UNSUPPORTED
     assert L.bsb_gemm_w8a8_g128(A, A, A, A, 4, 8, 128, A, 0, None) == UNSUPPORTED
+    assert L.bsb_gather_rows(A, A, A, 4, 8, 128, A, A, None) == UNSUPPORTED
+    assert L.bsb_moe_combine(A, A, A, 4, 2, 16, 64, A, None) == UNSUPPORTED
 
 
 def test_python_binding_validates_before_calling():
