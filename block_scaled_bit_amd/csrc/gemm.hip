@@ -498,16 +498,28 @@ gemm_tile_kernel(TileArgs p, int n_tiles) {
 // on a contiguous run of tiles, ordered in groups of 4 tile rows, which keeps
 // the operand panels its workgroups share in that XCD's L2.
 constexpr int BBM = 256, BBN = 256;
+#ifndef BSB_GROUPED_COLUMN_MAJOR
+#define BSB_GROUPED_COLUMN_MAJOR 1
+#endif
+constexpr bool kGroupedColumnMajor = BSB_GROUPED_COLUMN_MAJOR;
 
 struct BigTiles {
     int mt, nt;   // tile rows / columns
 };
 
+template <bool COLUMN_MAJOR>
 __device__ __forceinline__ void big_tile_of(int b, BigTiles t, int &bm, int &bn) {
     const int num = t.mt * t.nt;
     const int x = b & 7, per = num >> 3, rem = num & 7;
     const int start = x * per + (x < rem ? x : rem);
     const int tid = start + (b >> 3);                       // bijection onto [0, num)
+    if (COLUMN_MAJOR) {
+        // each XCD walks whole tile columns: consecutive row tiles share the
+        // weight panel of the column (per expert, in the grouped form)
+        bm = tid % t.mt;
+        bn = tid / t.mt;
+        return;
+    }
     constexpr int GM = 4;
     const int grp = tid / (GM * t.nt);
     const int first = grp * GM;
@@ -557,7 +569,7 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         tiles.mt = (int)mt;
     }
     int bm, bn;
-    big_tile_of(blockIdx.x, tiles, bm, bn);
+    big_tile_of<GROUPED && kGroupedColumnMajor>(blockIdx.x, tiles, bm, bn);
     const int n0 = bn * BBN;
     int m0, row_end;
     if (GROUPED) {
@@ -806,7 +818,11 @@ hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, 
     const int64_t blocks16 = (int64_t)((N + 15) / 16) * (GROUPED ? E : 1);
     const int64_t rounds = (blocks16 + 8 * kCUs - 1) / (8 * kCUs);
     int nw = (int)((blocks16 + kCUs * rounds - 1) / (kCUs * rounds));
-    nw = nw < (MB >= 4 ? 4 : 2) ? (MB >= 4 ? 4 : 2) : nw;
+    // at least what the activation ring needs per thread: 4 waves for 64 rows,
+    // 2 for up to 32 rows (one-wave workgroups, tried for small N so that more
+    // CUs stream weights, were slower: one wave keeps too few bytes in flight)
+    const int min_nw = MB >= 4 ? 4 : 2;
+    nw = nw < min_nw ? min_nw : nw;
 #ifdef BSB_SMALLM_NW
     nw = BSB_SMALLM_NW;
 #endif
