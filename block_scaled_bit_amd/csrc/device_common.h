@@ -152,11 +152,30 @@ __device__ __forceinline__ v4i make_rsrc_words(const void *base, uint32_t bytes)
 // offsets write zeros. Issued through inline assembly so that the compiler
 // does not treat it as a write of unknown LDS and hold every later LDS read
 // until it lands: the caller calls wait_vmem() and then a barrier before any
-// wave reads the destination. The s_nop is the one wait state the hardware
-// needs between the M0 write and the load that reads M0.
+// wave reads the destination.
+// The compiler cannot see that the assembly is a vector memory instruction,
+// so it inserts none of the wait states the hardware needs before one; the
+// s_nop supplies them. A VALU write of an SGPR the load reads needs five
+// (the compiler writes soffset or the descriptor with v_readfirstlane, or
+// restores a spilled SGPR from a VGPR lane with v_readlane, right before the
+// assembly), which also covers the one wait state after an SALU write of M0.
 __device__ __forceinline__ void buf_load16_lds(v4i rsrc, uint32_t lds, uint32_t voff,
                                                uint32_t soff) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "{m0}"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// The same with the non-temporal hint (data streamed once).
+__device__ __forceinline__ void buf_load16_lds_nt(v4i rsrc, uint32_t lds, uint32_t voff,
+                                                  uint32_t soff) {
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :: "{m0}"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// 4 bytes per lane straight into LDS: lane l's bytes land at lds + 4*l.
+__device__ __forceinline__ void buf_load4_lds(v4i rsrc, uint32_t lds, uint32_t voff,
+                                              uint32_t soff) {
+    asm volatile("s_nop 4\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  :: "{m0}"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 

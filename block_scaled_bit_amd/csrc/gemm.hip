@@ -59,40 +59,56 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // Workgroup = NW waves = 16*NW weight rows (output columns) n0 .. n0+16*NW-1;
 // each wave owns 16 of them (v_mfma_i32_16x16x64_i8, MB 16-token blocks).
 //
-// K is walked in super-stages of S groups. A super-stage's weight tile
-// (16*NW rows x S*128 B) and activation tile (16*MB rows x S*128 B) are read
-// with fully coalesced 16-byte buffer loads (8 lanes per 128-byte row line,
-// the pattern HBM streams fastest, with the non-temporal hint on the
-// weights, which are touched once) into a ring of D register sets, then
-// written to a double-buffered LDS tile from which every wave reads its MFMA
-// fragments. One barrier per super-stage. The memory counter completes loads
-// in issue order; a set is waited for only after the D-1 younger sets have
-// been issued, so (D-1)*S groups stay in flight without any drain.
+// K is walked in stages of S groups through a ring of D LDS buffers. A
+// stage's weight tile (16*NW rows x S*128 B), activation tile (16*MB rows x
+// S*128 B) and weight scales go from global memory straight into LDS: buffer
+// loads with the LDS-destination bit, each wave instruction filling one 1 KB
+// block of 8 rows x 128 B (8 lanes per row line, the pattern HBM streams
+// fastest; lane l lands at byte 16*l and fetches the chunk the swizzle puts
+// there), with the non-temporal hint on weight streams large enough to gain
+// from it. Nothing is staged through registers, so D-1 stages stay in flight.
+// Every wave issues the same number of loads per stage (spare ones read zero
+// into a sink), so a single wait with a constant count finds the oldest stage
+// landed; one barrier per stage then publishes it to all waves and frees the
+// buffer that the next stage is loaded into. The loads are issued through
+// inline assembly and waited for by hand: the compiler would otherwise wait
+// for all of them before any LDS read.
 //
 // LDS tile layout: [group][row][8 x 16-byte chunks], chunk j of row r stored
-// at position j ^ ((r >> 1) & 7). Fragment reads (16 rows, one chunk index)
-// and the row-line writes (2 rows x 8 chunks per 16 lanes) both hit 16
-// distinct 16-byte bank groups.
+// at position j ^ ((r >> 1) & 7): fragment reads (16 rows, one chunk index)
+// hit 16 distinct 16-byte bank groups.
 //
 // Out-of-range rows, columns and groups read zero through the buffer
-// descriptors, so no load sits behind a branch. Requires 16*NW*K < 2^31
-// (checked by the launcher).
+// descriptors (a group past the end adds fmaf(0, 0, acc) = acc, bit for bit),
+// so no load sits behind a branch. Requires 16*NW*K < 2^31 (checked by the
+// launcher).
 //
 // GROUPED (MoE with few rows per expert): blockIdx.y is the expert; the
 // workgroup walks that expert's rows [offsets[e], offsets[e+1]) in passes of
 // 16*MB rows against its slice of the expert's weights.
-template <int MB, int NW, int OUT, int S, int D, bool GROUPED>
+template <int MB, int NW, int S>
+constexpr int smallm_stage_bytes() {
+    return S * 16 * NW * kGroup + S * 16 * MB * kGroup + 4 * S * 16 * NW;
+}
+
+template <int MB, int NW, int OUT, int S, int D, bool GROUPED, bool NT>
 __global__ void __launch_bounds__(64 * NW)
 gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                    const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N,
                    int K, void *__restrict__ y, const int32_t *__restrict__ offsets) {
     constexpr int ROWS = 16 * MB;              // activation rows
     constexpr int WR = 16 * NW;                // weight rows per workgroup
-    constexpr int NT = 64 * NW;                // threads
     constexpr int BT = WR * kGroup;            // one group of the weight tile (bytes)
     constexpr int AT = ROWS * kGroup;          // one group of the activation tile
-    __shared__ __align__(16) int8_t Bs[2][S * BT];
-    __shared__ __align__(16) int8_t As[2][S * AT];
+    constexpr int SPAD = ((S * WR + 63) / 64) * 64;
+    constexpr int WBLK = 2 * S;                // 1 KB weight blocks per wave per stage
+    constexpr int ABLK = (S * AT / 1024 + NW - 1) / NW;   // activation blocks per wave
+    constexpr int NLD = WBLK + ABLK + 1;       // loads per wave per stage (+1: scales)
+    static_assert(D >= 2 && (D - 2) * NLD <= 63, "ring depth or wait count out of range");
+    __shared__ __align__(16) int8_t Bs[D][S * BT];
+    __shared__ __align__(16) int8_t As[D][S * AT];
+    __shared__ __align__(16) float Ss[D][SPAD];
+    __shared__ __align__(16) int8_t sink[1024];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = K >> 7;
@@ -102,6 +118,7 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     const int nrows = min(WR, N - n0);
     const int nl = wave * 16 + col;     // this lane's weight row within the slice
     const int n = n0 + nl;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
 
     int lo = 0, hi = M;                 // rows of this workgroup
     if (GROUPED) {
@@ -115,98 +132,107 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         sw += (int64_t)e * N * G;
     }
 
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw + (int64_t)n0 * K, (uint32_t)(nrows * K));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sw + (int64_t)n0 * G, (uint32_t)(nrows * G * 4));
-    __amdgpu_buffer_rsrc_t ra;          // the current pass's activation rows
+    const v4i rw = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(nrows * K));
+    // The partials form has no scales (sw may be null): an empty descriptor
+    // makes its scale loads read zero without touching memory.
+    const v4i rsc = make_rsrc_words(OUT == OUT_PARTIALS ? nullptr : sw + (int64_t)n0 * G,
+                                    OUT == OUT_PARTIALS ? 0u : (uint32_t)(nrows * G * 4));
+    v4i ra;                             // the current pass's activation rows
     int rows = 0, r0 = 0;
 
-    constexpr int BPT = S * BT / (NT * 16);           // weight chunks per thread per set
-    constexpr int ACH = S * AT / 16;                  // activation chunks per set
-    constexpr int APT = (ACH + NT - 1) / NT;
-    static_assert(BPT * NT * 16 == S * BT, "weight tile must split evenly");
-
-    v4i breg[D][BPT];
-    v4i areg[D][APT];
-    float sreg[D][S];
-
-    // Per-lane parts of the load offsets are fixed for the whole K walk; the
-    // group offset of a step is wave-uniform and travels in the scalar offset.
-    // Offsets past a resource's end read zero; a group past G is pushed there
-    // through the scalar part (weights, scales) or a select (activations,
-    // whose group within a super-stage can differ across lanes).
-    uint32_t bvo[BPT], avo[APT];
-    int agl[APT];
+    // Per-lane parts of the staging offsets and LDS destinations. A block's
+    // group (stage start + its group within the stage) travels in the scalar
+    // offset, pushed past the end of the descriptor for groups past the last,
+    // so those read zero.
+    uint32_t wvo[WBLK], avo[ABLK];
+    uint32_t wdst[WBLK], adst[ABLK];
+    int wgl[WBLK], agl[ABLK];
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-        const int c = tid + NT * i;
-        bvo[i] = (uint32_t)(((c >> 3) % WR) * K + (c & 7) * 16);   // group within stage: i*NT/(WR*8)
+    for (int i = 0; i < WBLK; ++i) {
+        const int blk = wv * WBLK + i;                 // 0 .. 2*NW*S-1
+        const int gl = blk / (2 * NW), rb = blk % (2 * NW);
+        const int row = rb * 8 + (lane >> 3), pos = lane & 7;
+        wvo[i] = (uint32_t)(row * K + ((pos ^ ((row >> 1) & 7)) << 4));
+        wdst[i] = (uint32_t)(gl * BT + rb * 1024);
+        wgl[i] = gl;
     }
 #pragma unroll
-    for (int i = 0; i < APT; ++i) {
-        const int c = tid + NT * i;
-        agl[i] = c / (ROWS * 8);
-        avo[i] = (c < ACH) ? (uint32_t)(((c >> 3) % ROWS) * K + agl[i] * kGroup + (c & 7) * 16)
-                           : kOOB;
+    for (int i = 0; i < ABLK; ++i) {
+        const int blk = wv * ABLK + i;
+        const bool ok = blk < S * AT / 1024;
+        const int gl = blk / (ROWS / 8), rb = blk % (ROWS / 8);
+        const int row = rb * 8 + (lane >> 3), pos = lane & 7;
+        avo[i] = ok ? (uint32_t)(row * K + ((pos ^ ((row >> 1) & 7)) << 4)) : kOOB;
+        adst[i] = ok ? (uint32_t)(gl * AT + rb * 1024) : 0xFFFFFFFFu;
+        agl[i] = ok ? gl : 0;
     }
-    const uint32_t svo = (uint32_t)(nl * G * 4);
+    // scales: lane l of wave w stages entry 64w + l = (group within stage,
+    // weight row) of the stage, in that order; its group is per lane
+    const int sidx = wv * 64 + lane;
+    const int sgl = sidx / WR;
+    const uint32_t svo =
+        (sidx < S * WR && OUT != OUT_PARTIALS) ? (uint32_t)((sidx % WR) * G * 4 + sgl * 4) : kOOB;
+    const bool s_wave = wv * 64 < SPAD;
+    auto goff = [&](int g) { return g < G ? (uint32_t)g * kGroup : kOOB; };
 
-    auto issue = [&](int d, int s0) {   // loads of the super-stage starting at group s0
+    auto lds_addr = [](const void *p) {
+        return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+    };
+    auto issue = [&](int d, int s0) {   // stage of groups s0 .. s0+S-1 into buffer d
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            const int g = s0 + (i * NT) / (WR * 8);          // uniform per i
-            breg[d][i] = buf_load16s<kNonTemporal>(rw, bvo[i], g < G ? (uint32_t)g * kGroup : kOOB);
+        for (int i = 0; i < WBLK; ++i) {
+            if (NT)
+                buf_load16_lds_nt(rw, lds_addr(&Bs[d][wdst[i]]), wvo[i], goff(s0 + wgl[i]));
+            else
+                buf_load16_lds(rw, lds_addr(&Bs[d][wdst[i]]), wvo[i], goff(s0 + wgl[i]));
         }
 #pragma unroll
-        for (int i = 0; i < APT; ++i)
-            areg[d][i] = buf_load16s(ra, (s0 + agl[i] < G) ? avo[i] : kOOB, (uint32_t)s0 * kGroup);
-#pragma unroll
-        for (int j = 0; j < S; ++j)
-            sreg[d][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                rs, (int)svo, (int)(s0 + j < G ? (uint32_t)(s0 + j) * 4 : kOOB), 0));
+        for (int i = 0; i < ABLK; ++i)
+            buf_load16_lds(ra, lds_addr(adst[i] != 0xFFFFFFFFu ? &As[d][adst[i]] : sink), avo[i],
+                           adst[i] != 0xFFFFFFFFu ? goff(s0 + agl[i]) : 0u);   // spare: reads zero
+        buf_load4_lds(rsc, lds_addr(s_wave ? &Ss[d][wv * 64] : reinterpret_cast<float *>(sink)),
+                      s0 + sgl < G ? svo : kOOB, (uint32_t)s0 * 4);
     };
     auto swz = [](int row, int j) { return (j ^ ((row >> 1) & 7)) * 16; };
-    auto stage = [&](int d, int buf) {
-#pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            const int c = tid + NT * i;
-            const int gl = c / (WR * 8), row = (c >> 3) % WR, j = c & 7;
-            *reinterpret_cast<v4i *>(&Bs[buf][gl * BT + row * kGroup + swz(row, j)]) = breg[d][i];
-        }
-#pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int c = tid + NT * i;
-            const int gl = c / (ROWS * 8), row = (c >> 3) % ROWS, j = c & 7;
-            if (ACH % NT == 0 || c < ACH)
-                *reinterpret_cast<v4i *>(&As[buf][gl * AT + row * kGroup + swz(row, j)]) =
-                    areg[d][i];
-        }
-    };
 
     float facc[MB][4];
-
-    auto compute = [&](const float *scale, int buf, int s0) {
+    // One stage: every LDS fragment first, then all matrix instructions, then
+    // the per-group epilogues in group order, so that the stage pays one LDS
+    // round trip and one matrix-pipeline drain rather than one per instruction.
+    auto compute = [&](int d, int s0) {
+        v4i bf[S][2], af[S][2][MB];
 #pragma unroll
-        for (int gl = 0; gl < S; ++gl) {
-            // Groups past the end hold zero weights and a zero scale, so they
-            // leave the accumulators unchanged bit for bit (fmaf(+0, 0, acc) ==
-            // acc); running them keeps the step free of branches.
-            const int g = s0 + gl;
-            v4i acc[MB];
-#pragma unroll
-            for (int i = 0; i < MB; ++i) acc[i] = v4i{0, 0, 0, 0};
+        for (int gl = 0; gl < S; ++gl)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int j = slot * 2 + t;
-                const v4i b = *reinterpret_cast<const v4i *>(
-                    &Bs[buf][gl * BT + nl * kGroup + swz(nl, j)]);
+                bf[gl][t] =
+                    *reinterpret_cast<const v4i *>(&Bs[d][gl * BT + nl * kGroup + swz(nl, j)]);
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
                     const int ar = i * 16 + col;
-                    const v4i a = *reinterpret_cast<const v4i *>(
-                        &As[buf][gl * AT + ar * kGroup + swz(ar, j)]);
-                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[i], 0, 0, 0);
+                    af[gl][t][i] =
+                        *reinterpret_cast<const v4i *>(&As[d][gl * AT + ar * kGroup + swz(ar, j)]);
                 }
             }
+        float sc[S];
+        if (OUT != OUT_PARTIALS) {
+#pragma unroll
+            for (int gl = 0; gl < S; ++gl) sc[gl] = Ss[d][gl * WR + nl];
+        }
+        v4i acc[S][MB];
+#pragma unroll
+        for (int gl = 0; gl < S; ++gl)
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                acc[gl][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[gl][0][i], bf[gl][0],
+                                                                   v4i{0, 0, 0, 0}, 0, 0, 0);
+                acc[gl][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[gl][1][i], bf[gl][1],
+                                                                   acc[gl][i], 0, 0, 0);
+            }
+#pragma unroll
+        for (int gl = 0; gl < S; ++gl) {
+            const int g = s0 + gl;
             if (OUT == OUT_PARTIALS) {
                 // C layout of 16x16: lane holds column `col`, rows 4*slot + r.
                 if (nl < nrows && g < G) {
@@ -217,55 +243,40 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                             const int m = i * 16 + slot * 4 + r;
                             if (m < rows)
                                 reinterpret_cast<int32_t *>(
-                                    y)[((int64_t)(r0 + m) * N + n) * G + g] = acc[i][r];
+                                    y)[((int64_t)(r0 + m) * N + n) * G + g] = acc[gl][i][r];
                         }
                 }
             } else {
-                const float s = scale[gl];
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        facc[i][r] = __builtin_fmaf((float)acc[i][r], s, facc[i][r]);
+                        facc[i][r] = __builtin_fmaf((float)acc[gl][i][r], sc[gl], facc[i][r]);
             }
         }
     };
 
-    // One step: refill the slot freed by the previous step, wait for the
-    // oldest slot (D-1 younger sets outstanding), stage it, multiply. The
-    // scheduling fences keep the loads in ring order, which the exact wait
-    // counts rely on.
-    auto step = [&](int d, int ss) {
-        const int buf = (ss / S) & 1;
-        __builtin_amdgcn_sched_barrier(0);
-        issue((d + D - 1) % D, ss + (D - 1) * S);
-        asm volatile("" ::: "memory");   // no IR-level motion of the loads either
-        __builtin_amdgcn_sched_barrier(0);
-        stage(d, buf);
-        float scale[S];                  // take the scales out before the slot is reused
-#pragma unroll
-        for (int j = 0; j < S; ++j) scale[j] = sreg[d][j];
-        __syncthreads();
-        compute(scale, buf, ss);
-    };
-
     // One pass: rows r0 .. r0+rows-1 (rows <= 16*MB) against the whole K walk.
     auto pass = [&]() {
-        ra = make_rsrc(q + (int64_t)r0 * K, (uint32_t)(rows * K));
+        ra = make_rsrc_words(q + (int64_t)r0 * K, (uint32_t)(rows * K));
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
+        const int nst = (G + S - 1) / S;
 #pragma unroll
-        for (int d = 0; d < D - 1; ++d) {
-            issue(d, d * S);
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        for (int s0 = 0; s0 < G; s0 += D * S) {
+        for (int d = 0; d < D - 1; ++d) issue(d, d * S);
+        for (int st0 = 0; st0 < nst; st0 += D) {
 #pragma unroll
-            for (int d = 0; d < D; ++d) step(d, s0 + d * S);   // may run past G: zeros
+            for (int d = 0; d < D; ++d) {   // may run past the last stage: zeros
+                // the oldest stage has landed (the D-2 younger ones may not) ...
+                asm volatile("s_waitcnt vmcnt(%0)" :: "n"((D - 2) * NLD) : "memory");
+                __syncthreads();            // ... for every wave; buffer d-1 is free
+                issue((d + D - 1) % D, (st0 + d + D - 1) * S);
+                compute(d, (st0 + d) * S);
+            }
         }
+        wait_vmem();                        // nothing may still write LDS past this pass
         if (OUT != OUT_PARTIALS && nl < nrows) {
 #pragma unroll
             for (int i = 0; i < MB; ++i)
@@ -285,7 +296,7 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         for (r0 = lo; r0 < hi; r0 += ROWS) {
             rows = min(ROWS, hi - r0);
             pass();
-            __syncthreads();            // the next pass restages both LDS buffers
+            __syncthreads();            // the next pass restages every LDS buffer
         }
     }
 }
@@ -405,9 +416,11 @@ gemm_tile_kernel(TileArgs p, int n_tiles) {
 
     for (int g = 0; g < G; ++g) {
         if (g + 1 < G) load_stage(g + 1);
-        float swv[2];
+        float swv[2] = {0.0f, 0.0f};   // the partials form has no scales (sw may be null)
+        if (OUT != OUT_PARTIALS) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) swv[j] = nok[j] ? sw[(int64_t)ncol[j] * G + g] : 0.0f;
+            for (int j = 0; j < 2; ++j) swv[j] = nok[j] ? sw[(int64_t)ncol[j] * G + g] : 0.0f;
+        }
 
         const int8_t *As = smem + (g & 1) * (TBM + TBN) * TLD;
         const int8_t *Bs = As + TBM * TLD;
@@ -602,7 +615,10 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 
     const v4i ra = make_rsrc_words(q + (int64_t)m0 * K, (uint32_t)(mrows * K));
     const v4i rb = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(ncols * K));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sw + (int64_t)n0 * G, (uint32_t)(ncols * G * 4));
+    // no scales in the partials form (sw may be null): an empty descriptor
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(OUT == OUT_PARTIALS ? nullptr : sw + (int64_t)n0 * G,
+                  OUT == OUT_PARTIALS ? 0u : (uint32_t)(ncols * G * 4));
 
     // Staging goes straight from global memory to LDS (buffer loads with the
     // LDS-destination bit): each wave instruction fills one 1 KB block of the
@@ -788,20 +804,30 @@ hipError_t launch_tile(const TileArgs &a, int64_t row_tiles, hipStream_t stream)
 #ifndef BSB_SMALLM_D
 #define BSB_SMALLM_D 4
 #endif
-constexpr int kSmallS = BSB_SMALLM_S;     // K groups per super-stage
-constexpr int kSmallD = BSB_SMALLM_D;     // super-stages in flight (register ring depth)
-// 64 activation rows need twice the activation registers per set: one set
-// fewer keeps them out of spills (measured 77 -> 59 us at 64x8192x28672)
-template <int MB>
-constexpr int small_depth() { return MB >= 4 ? kSmallD - 1 : kSmallD; }
+constexpr int kSmallS = BSB_SMALLM_S;     // K groups per stage
+constexpr int kSmallD = BSB_SMALLM_D;     // LDS stage buffers (D-1 stages in flight)
+
+// Ring depth: as many stage buffers as fit in 158 KB of LDS, at most kSmallD.
+template <int MB, int NW>
+constexpr int small_depth() {
+    constexpr int st = smallm_stage_bytes<MB, NW, kSmallS>();
+    return (kSmallD * st <= 158 * 1024) ? kSmallD : (158 * 1024) / st;
+}
 
 template <int MB, int NW, int OUT, bool GROUPED>
 hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                             int M, int N, int K, void *y, const int32_t *offsets, int E,
                             hipStream_t stream) {
     const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW)), GROUPED ? (unsigned)E : 1u);
-    gemm_smallm_kernel<MB, NW, OUT, kSmallS, small_depth<MB>(), GROUPED>
-        <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets);
+    // the non-temporal hint pays on weight streams far larger than the caches
+    // (measured: faster at 235 MB, slower at 29 MB)
+    const bool nt = (int64_t)N * K * (GROUPED ? E : 1) >= ((int64_t)1 << 27);
+    if (nt)
+        gemm_smallm_kernel<MB, NW, OUT, kSmallS, small_depth<MB, NW>(), GROUPED, true>
+            <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets);
+    else
+        gemm_smallm_kernel<MB, NW, OUT, kSmallS, small_depth<MB, NW>(), GROUPED, false>
+            <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets);
     return hipGetLastError();
 }
 
@@ -830,6 +856,9 @@ hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, 
     case W:                                                                                      \
         return launch_smallm_mb<MB, W, OUT, GROUPED>(q, sa, qw, sw, M, N, K, y, offsets, E, stream);
     switch (nw) {
+#ifdef BSB_SMALLM_NW
+        BSB_SMALLM_CASE(1)
+#endif
         BSB_SMALLM_CASE(2)
         BSB_SMALLM_CASE(3)
         BSB_SMALLM_CASE(4)
