@@ -60,8 +60,8 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // each wave owns 16 of them (v_mfma_i32_16x16x64_i8, MB 16-token blocks).
 //
 // K is walked in stages of S groups through a ring of D LDS buffers. A
-// stage's weight tile (16*NW rows x S*128 B), activation tile (16*MB rows x
-// S*128 B) and weight scales go from global memory straight into LDS: buffer
+// stage's weight tile (16*NW rows x S*128 B) and activation tile (16*MB rows
+// x S*128 B) go from global memory straight into LDS: buffer
 // loads with the LDS-destination bit, each wave instruction filling one 1 KB
 // block of 8 rows x 128 B (8 lanes per row line, the pattern HBM streams
 // fastest; lane l lands at byte 16*l and fetches the chunk the swizzle puts
@@ -73,6 +73,17 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // buffer that the next stage is loaded into. The loads are issued through
 // inline assembly and waited for by hand: the compiler would otherwise wait
 // for all of them before any LDS read.
+//
+// Workgroups of 4 or more waves stage the weight scales in chunks of 16
+// groups (double-buffered): a chunk
+// is 16*NW rows x 64 contiguous bytes, loaded in pieces of 4 rows (one 4-byte
+// load per lane, 4 row segments per instruction rather than a line per lane).
+// Each wave adds one piece load to every stage (a spare one reads zero into
+// the sink), so the per-stage count stays constant; the pieces of chunk c+1
+// ride on stages of chunk c that are issued after the barrier that retires
+// chunk c-1, whose buffer they reuse, and land before chunk c+1's first stage.
+// Narrower workgroups (where that measured slower) load each stage's own S
+// groups of scales with it instead, one entry per lane.
 //
 // LDS tile layout: [group][row][8 x 16-byte chunks], chunk j of row r stored
 // at position j ^ ((r >> 1) & 7): fragment reads (16 rows, one chunk index)
@@ -86,9 +97,27 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // GROUPED (MoE with few rows per expert): blockIdx.y is the expert; the
 // workgroup walks that expert's rows [offsets[e], offsets[e+1]) in passes of
 // 16*MB rows against its slice of the expert's weights.
+constexpr int kScaleChunk = 16;   // groups per staged chunk of weight scales
+
+template <int NW>
+constexpr bool smallm_chunked_scales() {
+    return NW >= 4;
+}
+
+template <int NW, int S>
+constexpr int smallm_stage_scale_floats() {   // per-stage scales, padded to whole waves
+    return ((S * 16 * NW + 63) / 64) * 64;
+}
+
 template <int MB, int NW, int S>
 constexpr int smallm_stage_bytes() {
-    return S * 16 * NW * kGroup + S * 16 * MB * kGroup + 4 * S * 16 * NW;
+    return S * 16 * NW * kGroup + S * 16 * MB * kGroup +
+           (smallm_chunked_scales<NW>() ? 0 : 4 * smallm_stage_scale_floats<NW, S>());
+}
+
+template <int NW>
+constexpr int smallm_fixed_bytes() {   // scale chunks + sink
+    return (smallm_chunked_scales<NW>() ? 2 * 16 * NW * kScaleChunk * 4 : 0) + 1024;
 }
 
 template <int MB, int NW, int OUT, int S, int D, bool GROUPED, bool NT>
@@ -100,14 +129,21 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     constexpr int WR = 16 * NW;                // weight rows per workgroup
     constexpr int BT = WR * kGroup;            // one group of the weight tile (bytes)
     constexpr int AT = ROWS * kGroup;          // one group of the activation tile
-    constexpr int SPAD = ((S * WR + 63) / 64) * 64;
     constexpr int WBLK = 2 * S;                // 1 KB weight blocks per wave per stage
     constexpr int ABLK = (S * AT / 1024 + NW - 1) / NW;   // activation blocks per wave
     constexpr int NLD = WBLK + ABLK + 1;       // loads per wave per stage (+1: scales)
+    constexpr int SCH = kScaleChunk;
+    constexpr int SPC = SCH / S;               // stages per scale chunk
+    constexpr int NP = WR * SCH / 64;          // 4-row pieces per scale chunk (= 4*NW)
+    constexpr bool CHUNKED = smallm_chunked_scales<NW>();
+    constexpr int SPAD = smallm_stage_scale_floats<NW, S>();
     static_assert(D >= 2 && (D - 2) * NLD <= 63, "ring depth or wait count out of range");
+    static_assert(!CHUNKED || (SCH % S == 0 && NP == 4 * NW && SPC >= D + 3),
+                  "scale pieces must fit the stages issued after a chunk's buffer is free");
     __shared__ __align__(16) int8_t Bs[D][S * BT];
     __shared__ __align__(16) int8_t As[D][S * AT];
-    __shared__ __align__(16) float Ss[D][SPAD];
+    // scales: [2][WR][SCH] in chunks, or [D][SPAD] per stage (entry gl*WR + row)
+    __shared__ __align__(16) float Sc[CHUNKED ? 2 * WR * SCH : D * SPAD];
     __shared__ __align__(16) int8_t sink[1024];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -166,18 +202,30 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         adst[i] = ok ? (uint32_t)(gl * AT + rb * 1024) : 0xFFFFFFFFu;
         agl[i] = ok ? gl : 0;
     }
-    // scales: lane l of wave w stages entry 64w + l = (group within stage,
-    // weight row) of the stage, in that order; its group is per lane
-    const int sidx = wv * 64 + lane;
-    const int sgl = sidx / WR;
-    const uint32_t svo =
-        (sidx < S * WR && OUT != OUT_PARTIALS) ? (uint32_t)((sidx % WR) * G * 4 + sgl * 4) : kOOB;
-    const bool s_wave = wv * 64 < SPAD;
     auto goff = [&](int g) { return g < G ? (uint32_t)g * kGroup : kOOB; };
 
     auto lds_addr = [](const void *p) {
         return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
     };
+    // piece p (wave-uniform) of scale chunk c: rows 4p .. 4p+3, lane l -> row
+    // 4p + (l >> 4), group c*SCH + (l & 15); p outside [0, NP) is a spare
+    auto piece = [&](int c, int p) {
+        const bool ok = p >= 0 && p < NP;
+        const int row = 4 * p + (lane >> 4), g = c * SCH + (lane & 15);
+        const uint32_t vo = (OUT != OUT_PARTIALS && ok && g < G) ? (uint32_t)(row * G * 4 + g * 4)
+                                                                  : kOOB;
+        buf_load4_lds(rsc,
+                      lds_addr(ok ? &Sc[(c & 1) * WR * SCH + p * 64]
+                                  : reinterpret_cast<float *>(sink)),
+                      vo, 0u);
+    };
+    // per-stage form: lane l of wave w stages entry 64w + l = (group within
+    // stage, weight row) of the stage, in that order; its group is per lane
+    const int sidx = wv * 64 + lane;
+    const int sgl = sidx / WR;
+    const uint32_t svo =
+        (sidx < S * WR && OUT != OUT_PARTIALS) ? (uint32_t)((sidx % WR) * G * 4 + sgl * 4) : kOOB;
+    const bool s_wave = wv * 64 < SPAD;
     auto issue = [&](int d, int s0) {   // stage of groups s0 .. s0+S-1 into buffer d
 #pragma unroll
         for (int i = 0; i < WBLK; ++i) {
@@ -190,8 +238,16 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         for (int i = 0; i < ABLK; ++i)
             buf_load16_lds(ra, lds_addr(adst[i] != 0xFFFFFFFFu ? &As[d][adst[i]] : sink), avo[i],
                            adst[i] != 0xFFFFFFFFu ? goff(s0 + agl[i]) : 0u);   // spare: reads zero
-        buf_load4_lds(rsc, lds_addr(s_wave ? &Ss[d][wv * 64] : reinterpret_cast<float *>(sink)),
-                      s0 + sgl < G ? svo : kOOB, (uint32_t)s0 * 4);
+        if (CHUNKED) {
+            // the stage's scale piece: stage X = s0 / S, position sg in its chunk
+            const int X = s0 / S, sg = X % SPC;
+            piece(X / SPC + 1, sg >= D - 1 ? (sg - (D - 1)) * NW + wv : -1);
+        } else {
+            buf_load4_lds(rsc,
+                          lds_addr(s_wave ? &Sc[d * SPAD + wv * 64]
+                                          : reinterpret_cast<float *>(sink)),
+                          s0 + sgl < G ? svo : kOOB, (uint32_t)s0 * 4);
+        }
     };
     auto swz = [](int row, int j) { return (j ^ ((row >> 1) & 7)) * 16; };
 
@@ -218,7 +274,9 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         float sc[S];
         if (OUT != OUT_PARTIALS) {
 #pragma unroll
-            for (int gl = 0; gl < S; ++gl) sc[gl] = Ss[d][gl * WR + nl];
+            for (int gl = 0; gl < S; ++gl)
+                sc[gl] = CHUNKED ? Sc[(((s0 + gl) / SCH) & 1) * WR * SCH + nl * SCH + (s0 + gl) % SCH]
+                                 : Sc[d * SPAD + gl * WR + nl];
         }
         v4i acc[S][MB];
 #pragma unroll
@@ -264,6 +322,10 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 #pragma unroll
             for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
         const int nst = (G + S - 1) / S;
+        if (CHUNKED) {
+#pragma unroll
+            for (int j = 0; j < NP / NW; ++j) piece(0, j * NW + wv);   // scale chunk 0
+        }
 #pragma unroll
         for (int d = 0; d < D - 1; ++d) issue(d, d * S);
         for (int st0 = 0; st0 < nst; st0 += D) {
@@ -807,11 +869,13 @@ hipError_t launch_tile(const TileArgs &a, int64_t row_tiles, hipStream_t stream)
 constexpr int kSmallS = BSB_SMALLM_S;     // K groups per stage
 constexpr int kSmallD = BSB_SMALLM_D;     // LDS stage buffers (D-1 stages in flight)
 
-// Ring depth: as many stage buffers as fit in 158 KB of LDS, at most kSmallD.
+// Ring depth: as many stage buffers as fit in the 160 KB of LDS beside the
+// scale chunks, at most kSmallD.
 template <int MB, int NW>
 constexpr int small_depth() {
     constexpr int st = smallm_stage_bytes<MB, NW, kSmallS>();
-    return (kSmallD * st <= 158 * 1024) ? kSmallD : (158 * 1024) / st;
+    constexpr int room = 160 * 1024 - smallm_fixed_bytes<NW>();
+    return (kSmallD * st <= room) ? kSmallD : room / st;
 }
 
 template <int MB, int NW, int OUT, bool GROUPED>
@@ -821,7 +885,10 @@ hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, 
     const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW)), GROUPED ? (unsigned)E : 1u);
     // the non-temporal hint pays on weight streams far larger than the caches
     // (measured: faster at 235 MB, slower at 29 MB)
-    const bool nt = (int64_t)N * K * (GROUPED ? E : 1) >= ((int64_t)1 << 27);
+#ifndef BSB_NT_MIN
+#define BSB_NT_MIN (1LL << 27)
+#endif
+    const bool nt = (int64_t)N * K * (GROUPED ? E : 1) >= (int64_t)BSB_NT_MIN;
     if (nt)
         gemm_smallm_kernel<MB, NW, OUT, kSmallS, small_depth<MB, NW>(), GROUPED, true>
             <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets);
@@ -849,6 +916,8 @@ hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, 
     // CUs stream weights, were slower: one wave keeps too few bytes in flight)
     const int min_nw = MB >= 4 ? 4 : 2;
     nw = nw < min_nw ? min_nw : nw;
+    // 64 rows across 8 waves would leave room for only two stage buffers
+    if (MB >= 4 && nw > 7) nw = 7;
 #ifdef BSB_SMALLM_NW
     nw = BSB_SMALLM_NW;
 #endif
