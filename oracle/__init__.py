@@ -16,7 +16,8 @@ Sources ("pages"):
        expert-mask layout; padding lanes masked by the logical block size).
   [P3] "Hunyuan 770B in INT8 on domestic accelerators" (pwwt.cn/news/4495474),
        sec. 3.1 (per-group-128 weights, per-token dynamic activations, INT8
-       multiply-accumulate into INT32, FP32 scales applied last), sec. 1.3
+       multiply-accumulate into INT32, FP32 scales applied last; per-tensor and
+       per-channel weight scales as the coarser alternatives), sec. 1.3
        (MoE: few experts active per token) and sec. 4.4 (tokens dispatched to
        their experts and combined back).
 
@@ -37,6 +38,7 @@ from .grouped import grouped_gemm_ref, grouped_gemm_fp32_ordered_ref
 from .decode import (fp8_e4m3_table, ue8m0_value, e2m1_table, decode_fp8_block_ref,
                      dequant_fp8_block_ref, decode_mxfp4_ref, dequant_mxfp4_ref)
 from .moe import gather_rows_ref, moe_combine_ref, moe_combine_fp32_ordered_ref
+from .channel import gemm_channel_ref, gemm_channel_fp32_ordered_ref, channel_total_ref
 
 __all__ = [
     "bf16_bits_to_f32", "quantize_rows_ref", "quantize_act_ref",
@@ -46,4 +48,5 @@ __all__ = [
     "fp8_e4m3_table", "ue8m0_value", "e2m1_table", "decode_fp8_block_ref",
     "dequant_fp8_block_ref", "decode_mxfp4_ref", "dequant_mxfp4_ref",
     "gather_rows_ref", "moe_combine_ref", "moe_combine_fp32_ordered_ref",
+    "gemm_channel_ref", "gemm_channel_fp32_ordered_ref", "channel_total_ref",
 ]
