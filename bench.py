@@ -225,7 +225,8 @@ def _rate(us, ops=None, byts=None, bound="hbm"):
 
 def extra_rows(torch, L, stream, dev, steps):
     """Every other workload of the path, each kernel timed on its own:
-    the tiny linear, the prefill quantisation, the routed MoE layer and the
+    the tiny linear, the prefill quantisation, the per-channel and per-tensor
+    GEMMs at the decode and prefill shapes, the routed MoE layer and the
     block-format weights (decoders, then the dense and grouped GEMMs on the
     decoded weights)."""
     import numpy as np
@@ -279,6 +280,36 @@ def extra_rows(torch, L, stream, dev, steps):
     log(f"prefill quant {tq * 1e3:.1f} us")
     del sets, x
     torch.cuda.empty_cache()
+
+    # the coarser weight-scale granularities on the same shapes: one scale per output
+    # row (per-channel) or one for the whole weight (per-tensor), INT32 totals over
+    # all of K rescaled once ([P3] sec. 3.1's taxonomy)
+    for shape, (M, K, N) in (("decode_32x8192x28672", (32, 8192, 28672)),
+                             ("prefill_4096x8192x8192", (4096, 8192, 8192))):
+        d = synth.linear_inputs(M, K, N, outlier_p=0.005, outlier_f=30.0, seed=0)
+        x, qw = t(d["x"].view(np.int16)), t(d["qw"])
+        for form, ns in (("channel", N), ("tensor", 1)):
+            sw = t(synth.channel_scales(ns))
+            byts = M * K + 4 * M + N * K + 4 * ns + 2 * M * N
+            sets = []
+            for _ in range(_copies(byts)):
+                b = dict(qw=qw.clone(), sw=sw.clone(),
+                         q=torch.empty((M, K), dtype=torch.int8, device=dev),
+                         sa=torch.empty((M,), dtype=torch.float32, device=dev),
+                         y=torch.empty((M, N), dtype=torch.int16, device=dev))
+                _ok(L, L.bsb_quantize_act(x.data_ptr(), M, K, b["q"].data_ptr(),
+                                          b["sa"].data_ptr(), stream))
+                sets.append({k: v.data_ptr() for k, v in b.items()} | {"_keep": b})
+            stride = 1 if ns == N else 0
+            tg = Row(f"{form} {shape}", sets, lambda p, st: _ok(
+                L, L.bsb_gemm_w8a8_channel(p["q"], p["sa"], p["qw"], p["sw"], stride, M, N, K,
+                                           p["y"], 0, st))).time(torch, stream, steps, 3)
+            rows[f"granularity_{form}_{shape}"] = _rate(
+                tg * 1e3, ops=2 * M * N * K, byts=byts, bound="hbm" if M <= 64 else "mfma")
+            log(f"per-{form} {shape}: gemm {tg * 1e3:.1f} us")
+            del sets
+        del x, qw
+        torch.cuda.empty_cache()
 
     # routed MoE layer: 4096 tokens, top-8 of 64 experts (Zipf, 4 empty), K=4096, N=2048
     m = synth.moe_inputs()

@@ -28,6 +28,8 @@ _c_int = ctypes.c_int
 _SIGNATURES = {
     "bsb_quantize_act": [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "bsb_gemm_w8a8_g128": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
+    "bsb_gemm_w8a8_channel": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_int,
+                              _c_p],
     "bsb_grouped_gemm_w8a8_g128": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
                                    _c_p, _c_int, _c_p],
     "bsb_decode_fp8_block": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_p],
@@ -141,6 +143,31 @@ def gemm_w8a8_g128(q: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torc
     with torch.cuda.device(dev):
         _check(lib().bsb_gemm_w8a8_g128(_ptr(q), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K,
                                         _ptr(out), code, _stream(dev)), "bsb_gemm_w8a8_g128")
+    return out
+
+
+def gemm_w8a8_channel(q: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                      out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [M,N] = W8A8 GEMM of q [M,K] (scales sa [M]) with qw [N,K] and one weight scale per
+    row (sw [N], per-channel) or one for all rows (sw [1], per-tensor)."""
+    _need(q, "q", (torch.int8,))
+    if q.dim() != 2 or qw.dim() != 2:
+        raise ValueError("q [M,K] and qw [N,K] required")
+    M, K = q.shape
+    N = qw.shape[0]
+    dev = q.device
+    _need(qw, "qw", (torch.int8,), (N, K), dev)
+    _need(sa, "sa", (torch.float32,), (M,), dev)
+    _need(sw, "sw", (torch.float32,), None, dev)
+    if sw.dim() != 1 or sw.shape[0] not in (1, N):
+        raise ValueError("sw must be [N] (per-channel) or [1] (per-tensor)")
+    stride = 1 if sw.shape[0] == N and N > 1 else 0
+    code = _out_code(out_dtype)
+    out = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", (out_dtype,), (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_gemm_w8a8_channel(_ptr(q), _ptr(sa), _ptr(qw), _ptr(sw), stride, M, N, K,
+                                           _ptr(out), code, _stream(dev)), "bsb_gemm_w8a8_channel")
     return out
 
 

@@ -45,6 +45,10 @@ inline bool prod_le(int64_t a, int64_t b, int64_t c, int64_t limit) {
 // workgroup of slack must stay below 2^32.
 constexpr int64_t kMaxDecodeElems = (int64_t)1 << 35;
 
+// K accepted by the per-channel / per-tensor GEMM: its INT32 total over the
+// whole of K stays in range (127 * 127 * 131072 < 2^31).
+constexpr int64_t kMaxChannelK = 131072;
+
 // Experts per token accepted by the combine.
 constexpr int64_t kMaxTopk = 256;
 
@@ -97,6 +101,23 @@ bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa, const int8_t *qw
     if (bsb_status s = check_device()) return s;
     (void)hipGetLastError();
     return finish(bsb::launch_gemm(q, sa, qw, sw, M, N, K, y, (int)out, as_stream(stream)));
+}
+
+bsb_status bsb_gemm_w8a8_channel(const int8_t *q, const float *sa, const int8_t *qw,
+                                 const float *sw, int64_t sw_stride, int64_t M, int64_t N,
+                                 int64_t K, void *y, bsb_out_dtype out, void *stream) {
+    if (!dims_ok(M, N, K) || N * K > kMaxElems || K > kMaxChannelK) return BSB_ERR_INVALID_ARG;
+    if (sw_stride != 0 && sw_stride != 1) return BSB_ERR_INVALID_ARG;
+    if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
+    if (M == 0) return BSB_OK;
+    if (!q || !sa || !qw || !sw || !y) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(sa) || !aligned16(qw) || !aligned16(y) ||
+        (reinterpret_cast<uintptr_t>(sw) & 3))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_gemm_channel(q, sa, qw, sw, sw_stride, M, N, K, y, (int)out,
+                                           as_stream(stream)));
 }
 
 bsb_status bsb_gemm_w8a8_g128_partials(const int8_t *q, const int8_t *qw, int64_t M, int64_t N,

@@ -37,7 +37,22 @@ namespace bsb {
 
 namespace {
 
-enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_PARTIALS = 2 };
+// Output forms. The *_CH forms take one weight scale per row n of the weight
+// (or one for all rows: scale index n * sw_stride with stride 0): the INT32
+// total over the whole of K is formed and rescaled once at the end.
+enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_PARTIALS = 2, OUT_BF16_CH = 3, OUT_FP32_CH = 4 };
+
+template <int OUT>
+constexpr bool per_channel() {
+    return OUT == OUT_BF16_CH || OUT == OUT_FP32_CH;
+}
+
+// (float)P, times the weight scale, then the activation scale, each rounded
+// to float32 (the build does not contract multiplies into FMAs)
+__device__ __forceinline__ float channel_value(int32_t p, float swn, float sa) {
+    const float t = (float)p * swn;
+    return t * sa;
+}
 
 __device__ __forceinline__ v4i as_v4i(uint4 u) {
     v4i r;
@@ -47,7 +62,7 @@ __device__ __forceinline__ v4i as_v4i(uint4 u) {
 
 template <int OUT>
 __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
-    if (OUT == OUT_BF16)
+    if (OUT == OUT_BF16 || OUT == OUT_BF16_CH)
         reinterpret_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
     else
         reinterpret_cast<float *>(y)[idx] = v;
@@ -124,18 +139,20 @@ template <int MB, int NW, int OUT, int S, int D, bool GROUPED, bool NT>
 __global__ void __launch_bounds__(64 * NW)
 gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                    const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N,
-                   int K, void *__restrict__ y, const int32_t *__restrict__ offsets) {
+                   int K, void *__restrict__ y, const int32_t *__restrict__ offsets,
+                   int sw_stride) {
     constexpr int ROWS = 16 * MB;              // activation rows
     constexpr int WR = 16 * NW;                // weight rows per workgroup
     constexpr int BT = WR * kGroup;            // one group of the weight tile (bytes)
     constexpr int AT = ROWS * kGroup;          // one group of the activation tile
     constexpr int WBLK = 2 * S;                // 1 KB weight blocks per wave per stage
     constexpr int ABLK = (S * AT / 1024 + NW - 1) / NW;   // activation blocks per wave
-    constexpr int NLD = WBLK + ABLK + 1;       // loads per wave per stage (+1: scales)
+    constexpr bool CHN = per_channel<OUT>();   // one scale per row, applied at the end
+    constexpr int NLD = WBLK + ABLK + (CHN ? 0 : 1);   // loads per wave per stage (+1: scales)
     constexpr int SCH = kScaleChunk;
     constexpr int SPC = SCH / S;               // stages per scale chunk
     constexpr int NP = WR * SCH / 64;          // 4-row pieces per scale chunk (= 4*NW)
-    constexpr bool CHUNKED = smallm_chunked_scales<NW>();
+    constexpr bool CHUNKED = smallm_chunked_scales<NW>() && !CHN;
     constexpr int SPAD = smallm_stage_scale_floats<NW, S>();
     static_assert(D >= 2 && (D - 2) * NLD <= 63, "ring depth or wait count out of range");
     static_assert(!CHUNKED || (SCH % S == 0 && NP == 4 * NW && SPC >= D + 3),
@@ -143,7 +160,7 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     __shared__ __align__(16) int8_t Bs[D][S * BT];
     __shared__ __align__(16) int8_t As[D][S * AT];
     // scales: [2][WR][SCH] in chunks, or [D][SPAD] per stage (entry gl*WR + row)
-    __shared__ __align__(16) float Sc[CHUNKED ? 2 * WR * SCH : D * SPAD];
+    __shared__ __align__(16) float Sc[CHN ? 64 : CHUNKED ? 2 * WR * SCH : D * SPAD];
     __shared__ __align__(16) int8_t sink[1024];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -171,8 +188,8 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     const v4i rw = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(nrows * K));
     // The partials form has no scales (sw may be null): an empty descriptor
     // makes its scale loads read zero without touching memory.
-    const v4i rsc = make_rsrc_words(OUT == OUT_PARTIALS ? nullptr : sw + (int64_t)n0 * G,
-                                    OUT == OUT_PARTIALS ? 0u : (uint32_t)(nrows * G * 4));
+    const v4i rsc = make_rsrc_words(OUT == OUT_PARTIALS || CHN ? nullptr : sw + (int64_t)n0 * G,
+                                    OUT == OUT_PARTIALS || CHN ? 0u : (uint32_t)(nrows * G * 4));
     v4i ra;                             // the current pass's activation rows
     int rows = 0, r0 = 0;
 
@@ -238,7 +255,9 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         for (int i = 0; i < ABLK; ++i)
             buf_load16_lds(ra, lds_addr(adst[i] != 0xFFFFFFFFu ? &As[d][adst[i]] : sink), avo[i],
                            adst[i] != 0xFFFFFFFFu ? goff(s0 + agl[i]) : 0u);   // spare: reads zero
-        if (CHUNKED) {
+        if (CHN) {
+            // no per-group scales
+        } else if (CHUNKED) {
             // the stage's scale piece: stage X = s0 / S, position sg in its chunk
             const int X = s0 / S, sg = X % SPC;
             piece(X / SPC + 1, sg >= D - 1 ? (sg - (D - 1)) * NW + wv : -1);
@@ -252,6 +271,7 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     auto swz = [](int row, int j) { return (j ^ ((row >> 1) & 7)) * 16; };
 
     float facc[MB][4];
+    v4i iacc[MB];   // per-channel form: the INT32 total so far
     // One stage: every LDS fragment first, then all matrix instructions, then
     // the per-group epilogues in group order, so that the stage pays one LDS
     // round trip and one matrix-pipeline drain rather than one per instruction.
@@ -271,6 +291,19 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                         *reinterpret_cast<const v4i *>(&As[d][gl * AT + ar * kGroup + swz(ar, j)]);
                 }
             }
+        if (CHN) {
+            // groups past the end hold zero weights and add nothing
+#pragma unroll
+            for (int gl = 0; gl < S; ++gl)
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[gl][0][i], bf[gl][0],
+                                                                        iacc[i], 0, 0, 0);
+                    iacc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[gl][1][i], bf[gl][1], c,
+                                                                    0, 0, 0);
+                }
+            return;
+        }
         float sc[S];
         if (OUT != OUT_PARTIALS) {
 #pragma unroll
@@ -318,9 +351,11 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     auto pass = [&]() {
         ra = make_rsrc_words(q + (int64_t)r0 * K, (uint32_t)(rows * K));
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MB; ++i) {
+            iacc[i] = v4i{0, 0, 0, 0};
 #pragma unroll
             for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
+        }
         const int nst = (G + S - 1) / S;
         if (CHUNKED) {
 #pragma unroll
@@ -339,7 +374,18 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
             }
         }
         wait_vmem();                        // nothing may still write LDS past this pass
-        if (OUT != OUT_PARTIALS && nl < nrows) {
+        if (CHN && nl < nrows) {
+            const float swn = sw[(int64_t)n * sw_stride];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = i * 16 + slot * 4 + r;
+                    if (m < rows)
+                        store_out<OUT>(y, (int64_t)(r0 + m) * N + n,
+                                       channel_value(iacc[i][r], swn, sa[r0 + m]));
+                }
+        } else if (OUT != OUT_PARTIALS && nl < nrows) {
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -375,6 +421,7 @@ struct TileArgs {
     void *y;
     int M;                    // dense rows, or R for grouped
     int N, K, E;
+    int sw_stride;            // per-channel forms: scale index n * sw_stride
 };
 
 constexpr int TBM = 128, TBN = 128, TLD = kGroup + 16;
@@ -386,6 +433,7 @@ constexpr int kTileSmem = 2 * (TBM + TBN) * TLD;   // 73728 bytes (gfx950 allows
 template <int OUT, bool GROUPED>
 __global__ void __launch_bounds__(256, 2)
 gemm_tile_kernel(TileArgs p, int n_tiles) {
+    constexpr bool CHN = per_channel<OUT>();   // one scale per row, applied at the end
     __shared__ __align__(16) int8_t smem[kTileSmem];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -465,12 +513,16 @@ gemm_tile_kernel(TileArgs p, int n_tiles) {
     }
 
     v16f facc[2][2];
+    v16i pacc[2][2];   // per-channel form: the INT32 totals so far
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) facc[i][j][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) {
+                facc[i][j][r] = 0.0f;
+                pacc[i][j][r] = 0;
+            }
 
     load_stage(0);
     store_stage(0);
@@ -479,7 +531,7 @@ gemm_tile_kernel(TileArgs p, int n_tiles) {
     for (int g = 0; g < G; ++g) {
         if (g + 1 < G) load_stage(g + 1);
         float swv[2] = {0.0f, 0.0f};   // the partials form has no scales (sw may be null)
-        if (OUT != OUT_PARTIALS) {
+        if (OUT != OUT_PARTIALS && !CHN) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) swv[j] = nok[j] ? sw[(int64_t)ncol[j] * G + g] : 0.0f;
         }
@@ -492,7 +544,7 @@ gemm_tile_kernel(TileArgs p, int n_tiles) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = CHN ? pacc[i][j][r] : 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             v4i a[2], b[2];
@@ -511,7 +563,12 @@ gemm_tile_kernel(TileArgs p, int n_tiles) {
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
         }
 
-        if (OUT == OUT_PARTIALS) {
+        if (CHN) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) pacc[i][j] = acc[i][j];
+        } else if (OUT == OUT_PARTIALS) {
             // C layout of 32x32: lane holds column l32, rows 8*(r/4) + 4*half + r%4.
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -538,7 +595,24 @@ gemm_tile_kernel(TileArgs p, int n_tiles) {
         __syncthreads();
     }
 
-    if (OUT != OUT_PARTIALS) {
+    if (CHN) {
+        float swn[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) swn[j] = nok[j] ? p.sw[(int64_t)ncol[j] * p.sw_stride] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (m >= row_end) continue;
+                const float s = p.sa[m];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    if (nok[j])
+                        store_out<OUT>(p.y, (int64_t)m * N + ncol[j],
+                                       channel_value(pacc[i][j][r], swn[j], s));
+            }
+    } else if (OUT != OUT_PARTIALS) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -612,7 +686,9 @@ template <int OUT, bool GROUPED>
 __global__ void __launch_bounds__(512, 1)
 gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                 const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N, int K,
-                void *__restrict__ y, BigTiles tiles, const int32_t *__restrict__ offsets, int E) {
+                void *__restrict__ y, BigTiles tiles, const int32_t *__restrict__ offsets, int E,
+                int sw_stride) {
+    constexpr bool CHN = per_channel<OUT>();   // one scale per row, applied at the end
     __shared__ __align__(16) int8_t smem[2][(BBM + BBN) * kGroup];   // 2 x 64 KB
     __shared__ __align__(16) float sws[2][2 * BBN];   // second half: unused slots
 
@@ -679,8 +755,8 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     const v4i rb = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(ncols * K));
     // no scales in the partials form (sw may be null): an empty descriptor
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(OUT == OUT_PARTIALS ? nullptr : sw + (int64_t)n0 * G,
-                  OUT == OUT_PARTIALS ? 0u : (uint32_t)(ncols * G * 4));
+        make_rsrc(OUT == OUT_PARTIALS || CHN ? nullptr : sw + (int64_t)n0 * G,
+                  OUT == OUT_PARTIALS || CHN ? 0u : (uint32_t)(ncols * G * 4));
 
     // Staging goes straight from global memory to LDS (buffer loads with the
     // LDS-destination bit): each wave instruction fills one 1 KB block of the
@@ -725,12 +801,16 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     };
 
     v16f facc[2][4];
+    v16i pacc[2][4];   // per-channel form: the INT32 totals so far
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) facc[i][j][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) {
+                facc[i][j][r] = 0.0f;
+                pacc[i][j][r] = 0;
+            }
 
     auto frag = [&](const int8_t *tile, int row, int c) {
         return *reinterpret_cast<const v4i *>(tile + row * kGroup + ((c ^ ((row >> 1) & 7)) << 4));
@@ -775,7 +855,7 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         for (int t = 0; t < 4; ++t) b[0][t] = frag(Bs, wn * 128 + l32, half * 4 + t);
         const float *scl = &sws[buf][wn * 128 + l32 * 4];   // [j] = scale of column block j
         float sc_prev = 0.0f, sc_cur = scl[0];
-        if (has_prev) epilogue(acc[1], 1, 3, sc_last, g_last);   // unit 7 of the previous group
+        if (!CHN && has_prev) epilogue(acc[1], 1, 3, sc_last, g_last);   // unit 7 of the previous group
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int j = u >> 1, i = u & 1, cur = j & 1;
@@ -788,11 +868,13 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                 sc_prev = sc_cur;
                 sc_cur = scl[j];
             }
-            v16i c = {};
+            v16i c = CHN ? pacc[i][j] : v16i{};
 #pragma unroll
             for (int t = 0; t < 4; ++t)
                 c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][t], b[cur][t], c, 0, 0, 0);
-            if (u > 0) {
+            if (CHN) {
+                pacc[i][j] = c;
+            } else if (u > 0) {
                 const int pj = (u - 1) >> 1, pi = (u - 1) & 1;
                 epilogue(acc[(u - 1) & 1], pi, pj, pj == j ? sc_cur : sc_prev, g);
             }
@@ -805,23 +887,46 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 
     // prologue: group 0 into buffer 0
     dma_group(0, 0);
-    load_scale(0);
-    store_scale(0);
+    if (!CHN) {
+        load_scale(0);
+        store_scale(0);
+    }
     wait_vmem();
     __syncthreads();
 
     for (int g = 0; g < G; ++g) {
         const int buf = g & 1;
         dma_group(buf ^ 1, g + 1);     // zeros past the end; lands while group g is multiplied
-        load_scale(g + 1);
+        if (!CHN) load_scale(g + 1);
         if (!GROUPED || active) group(buf, g, g > 0);
-        store_scale(buf ^ 1);
+        if (!CHN) store_scale(buf ^ 1);
         wait_vmem();                   // the next group's tiles are in LDS ...
         __syncthreads();               // ... for every wave: swap buffers
     }
-    if (!GROUPED || active) epilogue(acc[1], 1, 3, sc_last, g_last);
+    if (!CHN && (!GROUPED || active)) epilogue(acc[1], 1, 3, sc_last, g_last);
 
-    if (OUT != OUT_PARTIALS) {
+    if (CHN) {
+        float swn[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wn * 128 + j * 32 + l32;
+            swn[j] = n < N ? sw[(int64_t)n * sw_stride] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (m >= row_end) continue;
+                const float s = sa[m];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = n0 + wn * 128 + j * 32 + l32;
+                    if (n < N)
+                        store_out<OUT>(y, (int64_t)m * N + n, channel_value(pacc[i][j][r], swn[j], s));
+                }
+            }
+    } else if (OUT != OUT_PARTIALS) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -841,13 +946,15 @@ gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 // Grouped: sum over experts of ceil(rows_e / 256) <= ceil(R / 256) + E tile rows.
 template <int OUT, bool GROUPED>
 hipError_t launch_big(const int8_t *q, const float *sa, const int8_t *qw, const float *sw, int M,
-                      int N, int K, void *y, const int32_t *offsets, int E, hipStream_t stream) {
+                      int N, int K, void *y, const int32_t *offsets, int E, hipStream_t stream,
+                      int sw_stride = 1) {
     const int64_t mt = (M + BBM - 1) / BBM + (GROUPED ? E : 0), nt = (N + BBN - 1) / BBN;
     const int64_t total = mt * nt;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const BigTiles t{(int)mt, (int)nt};
     gemm_big_kernel<OUT, GROUPED>
-        <<<dim3((unsigned)total), 512, 0, stream>>>(q, sa, qw, sw, M, N, K, y, t, offsets, E);
+        <<<dim3((unsigned)total), 512, 0, stream>>>(q, sa, qw, sw, M, N, K, y, t, offsets, E,
+                                                          sw_stride);
     return hipGetLastError();
 }
 
@@ -881,7 +988,7 @@ constexpr int small_depth() {
 template <int MB, int NW, int OUT, bool GROUPED>
 hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                             int M, int N, int K, void *y, const int32_t *offsets, int E,
-                            hipStream_t stream) {
+                            hipStream_t stream, int sw_stride) {
     const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW)), GROUPED ? (unsigned)E : 1u);
     // the non-temporal hint pays on weight streams far larger than the caches
     // (measured: faster at 235 MB, slower at 29 MB)
@@ -891,10 +998,10 @@ hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, 
     const bool nt = (int64_t)N * K * (GROUPED ? E : 1) >= (int64_t)BSB_NT_MIN;
     if (nt)
         gemm_smallm_kernel<MB, NW, OUT, kSmallS, small_depth<MB, NW>(), GROUPED, true>
-            <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets);
+            <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets, sw_stride);
     else
         gemm_smallm_kernel<MB, NW, OUT, kSmallS, small_depth<MB, NW>(), GROUPED, false>
-            <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets);
+            <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets, sw_stride);
     return hipGetLastError();
 }
 
@@ -907,7 +1014,7 @@ constexpr int kCUs = 256;
 template <int MB, int OUT, bool GROUPED>
 hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                             int M, int N, int K, void *y, const int32_t *offsets, int E,
-                            hipStream_t stream) {
+                            hipStream_t stream, int sw_stride = 1) {
     const int64_t blocks16 = (int64_t)((N + 15) / 16) * (GROUPED ? E : 1);
     const int64_t rounds = (blocks16 + 8 * kCUs - 1) / (8 * kCUs);
     int nw = (int)((blocks16 + kCUs * rounds - 1) / (kCUs * rounds));
@@ -923,7 +1030,8 @@ hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, 
 #endif
 #define BSB_SMALLM_CASE(W)                                                                       \
     case W:                                                                                      \
-        return launch_smallm_mb<MB, W, OUT, GROUPED>(q, sa, qw, sw, M, N, K, y, offsets, E, stream);
+        return launch_smallm_mb<MB, W, OUT, GROUPED>(q, sa, qw, sw, M, N, K, y, offsets, E, stream, \
+                                                     sw_stride);
     switch (nw) {
 #ifdef BSB_SMALLM_NW
         BSB_SMALLM_CASE(1)
@@ -935,17 +1043,22 @@ hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, 
         BSB_SMALLM_CASE(6)
         BSB_SMALLM_CASE(7)
         default: return launch_smallm_mb<MB, 8, OUT, GROUPED>(q, sa, qw, sw, M, N, K, y, offsets,
-                                                               E, stream);
+                                                               E, stream, sw_stride);
     }
 #undef BSB_SMALLM_CASE
 }
 
 template <int OUT>
 hipError_t launch_smallm(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
-                         int M, int N, int K, void *y, hipStream_t stream) {
-    if (M <= 16) return launch_smallm_nw<1, OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 1, stream);
-    if (M <= 32) return launch_smallm_nw<2, OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 1, stream);
-    return launch_smallm_nw<4, OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 1, stream);
+                         int M, int N, int K, void *y, hipStream_t stream, int sw_stride) {
+    if (M <= 16)
+        return launch_smallm_nw<1, OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 1, stream,
+                                               sw_stride);
+    if (M <= 32)
+        return launch_smallm_nw<2, OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 1, stream,
+                                               sw_stride);
+    return launch_smallm_nw<4, OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 1, stream,
+                                           sw_stride);
 }
 
 #ifndef BSB_BIG_MIN_M
@@ -955,18 +1068,18 @@ constexpr int kBigMinM = BSB_BIG_MIN_M;   // rows from which the 256x256 kernel 
 
 template <int OUT>
 hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
-                        int M, int N, int K, void *y, hipStream_t stream) {
+                        int M, int N, int K, void *y, hipStream_t stream, int sw_stride = 1) {
     // smallm addresses a weight slice (at most 128 rows) and the whole
     // activation matrix (at most 64 rows) with 32-bit buffer offsets
     if (M <= 64 && (int64_t)128 * K < ((int64_t)1 << 31))
-        return launch_smallm<OUT>(q, sa, qw, sw, M, N, K, y, stream);
+        return launch_smallm<OUT>(q, sa, qw, sw, M, N, K, y, stream, sw_stride);
     // The 256x256 kernel (which addresses its operand panels with 32-bit
     // buffer offsets) when it has at least one tile per CU; below that the
     // 128x128 kernel's four times as many tiles finish sooner.
     const int64_t big_tiles = (int64_t)((M + BBM - 1) / BBM) * ((N + BBN - 1) / BBN);
     if (M >= kBigMinM && (int64_t)256 * K < ((int64_t)1 << 31) && big_tiles >= kCUs)
-        return launch_big<OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 0, stream);
-    TileArgs a{q, sa, qw, sw, nullptr, y, M, N, K, 0};
+        return launch_big<OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 0, stream, sw_stride);
+    TileArgs a{q, sa, qw, sw, nullptr, y, M, N, K, 0, sw_stride};
     return launch_tile<OUT, false>(a, (M + TBM - 1) / TBM, stream);
 }
 
@@ -979,6 +1092,16 @@ hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw, const
         case OUT_FP32: return launch_dense<OUT_FP32>(q, sa, qw, sw, (int)M, (int)N, (int)K, y, stream);
         default: return launch_dense<OUT_PARTIALS>(q, nullptr, qw, nullptr, (int)M, (int)N, (int)K, y, stream);
     }
+}
+
+hipError_t launch_gemm_channel(const int8_t *q, const float *sa, const int8_t *qw,
+                               const float *sw, int64_t sw_stride, int64_t M, int64_t N,
+                               int64_t K, void *y, int out, hipStream_t stream) {
+    if (out == OUT_BF16)
+        return launch_dense<OUT_BF16_CH>(q, sa, qw, sw, (int)M, (int)N, (int)K, y, stream,
+                                         (int)sw_stride);
+    return launch_dense<OUT_FP32_CH>(q, sa, qw, sw, (int)M, (int)N, (int)K, y, stream,
+                                     (int)sw_stride);
 }
 
 hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *qw,
@@ -1004,7 +1127,7 @@ hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *q
         return launch_smallm_nw<2, OUT_FP32, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y,
                                                    offsets, (int)E, stream);
     }
-    TileArgs a{q, sa, qw, sw, offsets, y, (int)R, (int)N, (int)K, (int)E};
+    TileArgs a{q, sa, qw, sw, offsets, y, (int)R, (int)N, (int)K, (int)E, 1};
     // Upper bound on the row tiles over all segments, from host values only.
     const int64_t row_tiles = (R + TBM - 1) / TBM + E;
     if (out == OUT_BF16) return launch_tile<OUT_BF16, true>(a, row_tiles, stream);

@@ -23,6 +23,12 @@ hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw,
                        const float *sw, int64_t M, int64_t N, int64_t K, void *y,
                        int out, hipStream_t stream);
 
+// Per-channel (sw_stride 1, sw[N]) or per-tensor (sw_stride 0, sw[1]) weight
+// scales: out 0 = BF16, 1 = FP32.
+hipError_t launch_gemm_channel(const int8_t *q, const float *sa, const int8_t *qw,
+                               const float *sw, int64_t sw_stride, int64_t M, int64_t N,
+                               int64_t K, void *y, int out, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *qw,
                                const float *sw, const int32_t *offsets, int64_t E,
                                int64_t R, int64_t N, int64_t K, void *y, int out,

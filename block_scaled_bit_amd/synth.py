@@ -68,6 +68,14 @@ def group_scales(rng: np.random.Generator, shape) -> np.ndarray:
     return np.exp(rng.normal(-6.0, 0.5, size=shape)).astype(np.float32)
 
 
+def channel_scales(n: int, seed: int = 0) -> np.ndarray:
+    """float32 lognormal(mu=-6, sigma=0.5) weight scales, one per output row (n = N)
+    or one for the whole weight (n = 1): the group-scale distribution, drawn from a
+    stream of its own so that the other inputs of a seed do not change."""
+    rng = np.random.Generator(np.random.PCG64([seed, 0xC4A]))
+    return group_scales(rng, (n,))
+
+
 def linear_inputs(M: int, K: int, N: int, outlier_p: float = 0.005,
                   outlier_f: float = 30.0, seed: int = 0) -> dict:
     """One dense linear layer: x BF16 bits [M,K], qw int8 [N,K], sw float32 [N,K/128]."""

@@ -107,6 +107,27 @@ bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa,
                               void *y, bsb_out_dtype out, void *stream);
 
 /*
+ * W8A8 GEMM with one weight scale per output row (per-channel) or one for the
+ * whole weight (per-tensor): the coarser granularities of [P3] sec. 3.1's
+ * taxonomy, whose deployment checklist (sec. 6) runs per-tensor before moving
+ * to per-group 128. Same operands as bsb_gemm_w8a8_g128 except the scales:
+ *     P[m,n]  = sum_k q[m,k] * qw[n,k]              (exact INT32, all of K)
+ *     y[m,n]  = ((float)P[m,n] * sw[n * sw_stride]) * sa[m]
+ * (float)P rounds to nearest even, each product is rounded to float32, then
+ * the store rounds to BF16 (RNE) or keeps FP32.
+ *   sw         [N] float32 (sw_stride = 1, per-channel) or [1] (sw_stride = 0,
+ *              per-tensor); 4-byte aligned
+ *   sw_stride  0 or 1
+ *   K          a multiple of 128, at most 131072, so that the INT32 total
+ *              cannot overflow (127 * 127 * 131072 < 2^31)
+ * Other arguments, limits and errors as bsb_gemm_w8a8_g128.
+ */
+bsb_status bsb_gemm_w8a8_channel(const int8_t *q, const float *sa,
+                                 const int8_t *qw, const float *sw, int64_t sw_stride,
+                                 int64_t M, int64_t N, int64_t K,
+                                 void *y, bsb_out_dtype out, void *stream);
+
+/*
  * Grouped (MoE) form: rows are sorted by expert and expert e owns rows
  * [offsets[e], offsets[e+1]) ([P3] sec. 1.3: experts resident, each token
  * runs through a few of them). Each segment is multiplied with its expert's

@@ -119,3 +119,21 @@ def test_python_binding_validates_before_calling():
         bsb.quantize_act(cpu)                      # not on a GPU
     with pytest.raises(ValueError):
         bsb.gemm_w8a8_g128(torch.zeros(4, 128, dtype=torch.int8), None, None, None)
+
+
+def test_channel_gemm_argument_checks(L):
+    """Per-channel / per-tensor GEMM: stride 0 or 1 only, K within the INT32 total's
+    bound, sw 4-byte aligned (one float for per-tensor), the usual null, enum and
+    empty-input rules; with valid arguments and no gfx950 device it fails fast."""
+    f = L.bsb_gemm_w8a8_channel
+    assert f(A, A, A, A, 2, 4, 8, 128, A, 0, None) == INVALID          # stride
+    assert f(A, A, A, A, -1, 4, 8, 128, A, 0, None) == INVALID
+    assert f(A, A, A, A, 1, 4, 8, 131072 + 128, A, 0, None) == INVALID  # INT32 total bound
+    assert f(A, A, A, A, 1, 4, 8, 130, A, 0, None) == INVALID
+    assert f(A, A, A, A, 1, 4, 8, 128, A, 5, None) == INVALID          # out enum
+    assert f(A, None, A, A, 1, 4, 8, 128, A, 0, None) == INVALID
+    assert f(A, A, A, A + 2, 1, 4, 8, 128, A, 0, None) == MISALIGNED
+    assert f(A, A, U, A, 0, 4, 8, 128, A, 0, None) == MISALIGNED
+    assert f(None, None, None, None, 1, 0, 8, 128, None, 0, None) == OK
+    if not torch.cuda.is_available():
+        assert f(A, A, A, A + 4, 0, 4, 8, 131072, A, 1, None) == UNSUPPORTED
