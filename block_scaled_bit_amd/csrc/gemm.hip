@@ -82,10 +82,13 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // fastest; lane l lands at byte 16*l and fetches the chunk the swizzle puts
 // there), with the non-temporal hint on weight streams large enough to gain
 // from it. Nothing is staged through registers, so D-1 stages stay in flight.
-// Every wave issues the same number of loads per stage (spare ones read zero
-// into a sink), so a single wait with a constant count finds the oldest stage
-// landed; one barrier per stage then publishes it to all waves and frees the
-// buffer that the next stage is loaded into. The loads are issued through
+// A single wait with a constant count finds the oldest stage landed: in
+// narrow workgroups every wave issues the same number of loads per stage
+// (spare ones read zero into a sink); wider ones skip the spares and each wave
+// waits with the smallest count any wave issues every stage, which the
+// in-order completion of loads makes sufficient. One barrier per stage then
+// publishes the stage to all waves and frees the buffer that the next stage
+// is loaded into. The loads are issued through
 // inline assembly and waited for by hand: the compiler would otherwise wait
 // for all of them before any LDS read.
 //
@@ -113,6 +116,10 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
 // workgroup walks that expert's rows [offsets[e], offsets[e+1]) in passes of
 // 16*MB rows against its slice of the expert's weights.
 constexpr int kScaleChunk = 16;   // groups per staged chunk of weight scales
+#ifndef BSB_SMALLM_NOSPARE
+#define BSB_SMALLM_NOSPARE 1
+#endif
+constexpr bool kSmallNoSpare = BSB_SMALLM_NOSPARE;
 
 template <int NW>
 constexpr bool smallm_chunked_scales() {
@@ -148,13 +155,26 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     constexpr int WBLK = 2 * S;                // 1 KB weight blocks per wave per stage
     constexpr int ABLK = (S * AT / 1024 + NW - 1) / NW;   // activation blocks per wave
     constexpr bool CHN = per_channel<OUT>();   // one scale per row, applied at the end
-    constexpr int NLD = WBLK + ABLK + (CHN ? 0 : 1);   // loads per wave per stage (+1: scales)
+    constexpr int NLD = WBLK + ABLK + (CHN ? 0 : 1);   // load slots per wave per stage (+1: scales)
+    constexpr int TBLK = S * AT / 1024;        // activation blocks per stage
+    // Spare slots issue nothing (a load past the end still costs an
+    // instruction on the LDS-destination path), so waves issue different
+    // numbers of loads per stage; each waits with the smallest number any wave
+    // issues every stage: weights plus the activation blocks of the last wave.
+    // With loads completing in issue order, at most (D-2)*NLD_MIN outstanding
+    // means the oldest stage has landed whatever this wave issued after it.
+    // (workgroups of 4 or more waves; narrower ones, with at most one spare,
+    // measured faster keeping it)
+    constexpr bool NOSPARE = kSmallNoSpare && NW >= 4;
+    constexpr int A_MIN = TBLK - (NW - 1) * ABLK > 0 ? TBLK - (NW - 1) * ABLK : 0;
+    constexpr int NLD_MIN = NOSPARE ? WBLK + A_MIN : NLD;
     constexpr int SCH = kScaleChunk;
     constexpr int SPC = SCH / S;               // stages per scale chunk
     constexpr int NP = WR * SCH / 64;          // 4-row pieces per scale chunk (= 4*NW)
     constexpr bool CHUNKED = smallm_chunked_scales<NW>() && !CHN;
     constexpr int SPAD = smallm_stage_scale_floats<NW, S>();
-    static_assert(D >= 2 && (D - 2) * NLD <= 63, "ring depth or wait count out of range");
+    static_assert(D >= 2 && (D - 2) * NLD <= 63 && NLD_MIN >= 1,
+                  "ring depth or wait count out of range");
     static_assert(!CHUNKED || (SCH % S == 0 && NP == 4 * NW && SPC >= D + 3),
                   "scale pieces must fit the stages issued after a chunk's buffer is free");
     __shared__ __align__(16) int8_t Bs[D][S * BT];
@@ -252,16 +272,19 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                 buf_load16_lds(rw, lds_addr(&Bs[d][wdst[i]]), wvo[i], goff(s0 + wgl[i]));
         }
 #pragma unroll
-        for (int i = 0; i < ABLK; ++i)
+        for (int i = 0; i < ABLK; ++i) {
+            if (NOSPARE && wv * ABLK + i >= TBLK) continue;   // wave-uniform
             buf_load16_lds(ra, lds_addr(adst[i] != 0xFFFFFFFFu ? &As[d][adst[i]] : sink), avo[i],
                            adst[i] != 0xFFFFFFFFu ? goff(s0 + agl[i]) : 0u);   // spare: reads zero
+        }
         if (CHN) {
             // no per-group scales
         } else if (CHUNKED) {
             // the stage's scale piece: stage X = s0 / S, position sg in its chunk
             const int X = s0 / S, sg = X % SPC;
-            piece(X / SPC + 1, sg >= D - 1 ? (sg - (D - 1)) * NW + wv : -1);
-        } else {
+            const int pc = sg >= D - 1 ? (sg - (D - 1)) * NW + wv : -1;
+            if (!NOSPARE || (pc >= 0 && pc < NP)) piece(X / SPC + 1, pc);
+        } else if (!NOSPARE || s_wave) {
             buf_load4_lds(rsc,
                           lds_addr(s_wave ? &Sc[d * SPAD + wv * 64]
                                           : reinterpret_cast<float *>(sink)),
@@ -367,7 +390,7 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 #pragma unroll
             for (int d = 0; d < D; ++d) {   // may run past the last stage: zeros
                 // the oldest stage has landed (the D-2 younger ones may not) ...
-                asm volatile("s_waitcnt vmcnt(%0)" :: "n"((D - 2) * NLD) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" :: "n"((D - 2) * NLD_MIN) : "memory");
                 __syncthreads();            // ... for every wave; buffer d-1 is free
                 issue((d + D - 1) % D, (st0 + d + D - 1) * S);
                 compute(d, (st0 + d) * S);
