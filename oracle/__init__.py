@@ -9,7 +9,8 @@ Sources ("pages"):
   [P1] "Running DeepSeek-V4-Flash-Vision on 4x A800: adaptation"
        (yfxerp.com/news/113390), sec. 1 (the constraints table: FP8 e4m3
        [128,128] UE8M0 block-scaled linears, dynamic activations, MXFP4 E2M1
-       UE8M0 routed experts) and sec. 2 (dequantise / repack to the INT8 route).
+       UE8M0 routed experts) and sec. 2 (dequantise / repack to the INT8 route;
+       the BF16 dense route and the weight-only INT8 expert route).
   [P2] "Deploying DeepSeek-V4-Flash on AMD MI300X: a hard-core retrospective"
        (aimsg.uk), section "FP8 dialect clash" (OCP vs fnuz: same bits, bias
        off by one, values exactly 2x apart) and "Loose ends" items 1-2 (MoE
@@ -39,6 +40,7 @@ from .decode import (fp8_e4m3_table, ue8m0_value, e2m1_table, decode_fp8_block_r
                      dequant_fp8_block_ref, decode_mxfp4_ref, dequant_mxfp4_ref)
 from .moe import gather_rows_ref, moe_combine_ref, moe_combine_fp32_ordered_ref
 from .channel import gemm_channel_ref, gemm_channel_fp32_ordered_ref, channel_total_ref
+from .a16 import gemm_w8a16_ref, gemm_bf16_ref, a16_tolerance, dequant_fp8_block_bf16_ref
 
 __all__ = [
     "bf16_bits_to_f32", "quantize_rows_ref", "quantize_act_ref",
@@ -49,4 +51,5 @@ __all__ = [
     "dequant_fp8_block_ref", "decode_mxfp4_ref", "dequant_mxfp4_ref",
     "gather_rows_ref", "moe_combine_ref", "moe_combine_fp32_ordered_ref",
     "gemm_channel_ref", "gemm_channel_fp32_ordered_ref", "channel_total_ref",
+    "gemm_w8a16_ref", "gemm_bf16_ref", "a16_tolerance", "dequant_fp8_block_bf16_ref",
 ]
