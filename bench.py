@@ -311,6 +311,38 @@ def extra_rows(torch, L, stream, dev, steps):
         del x, qw
         torch.cuda.empty_cache()
 
+    # the BF16-activation routes at the decode shape: weight-only INT8 (W8A16, no
+    # activation quantisation) and BF16 weights (twice the weight bytes)
+    M, K, N = 32, 8192, 28672
+    d = synth.linear_inputs(M, K, N, outlier_p=0.005, outlier_f=30.0, seed=0)
+    x, qw, sw = t(d["x"].view(np.int16)), t(d["qw"]), t(d["sw"])
+    byts = 2 * M * K + N * K + 4 * N * K // 128 + 2 * M * N
+    sets = []
+    for _ in range(_copies(byts)):
+        b = dict(x=x.clone(), qw=qw.clone(), sw=sw.clone(),
+                 y=torch.empty((M, N), dtype=torch.int16, device=dev))
+        sets.append({k: v.data_ptr() for k, v in b.items()} | {"_keep": b})
+    tg = Row("w8a16 decode", sets, lambda p, st: _ok(
+        L, L.bsb_gemm_w8a16_g128(p["x"], p["qw"], p["sw"], M, N, K, p["y"], 0, st))).time(
+        torch, stream, steps, 3)
+    rows["w8a16_decode_32x8192x28672"] = _rate(tg * 1e3, ops=2 * M * N * K, byts=byts)
+    log(f"w8a16 decode: gemm {tg * 1e3:.1f} us")
+    del sets, qw, sw
+    torch.cuda.empty_cache()
+    wb = t((np.random.default_rng(0).standard_normal((N, K)).astype(np.float32) * 0.02)
+           ).to(torch.bfloat16).view(torch.int16)
+    byts = 2 * M * K + 2 * N * K + 2 * M * N
+    sets = []
+    for _ in range(_copies(byts, cap=6)):
+        b = dict(x=x.clone(), w=wb.clone(), y=torch.empty((M, N), dtype=torch.int16, device=dev))
+        sets.append({k: v.data_ptr() for k, v in b.items()} | {"_keep": b})
+    tg = Row("bf16 decode", sets, lambda p, st: _ok(
+        L, L.bsb_gemm_bf16(p["x"], p["w"], M, N, K, p["y"], 0, st))).time(torch, stream, steps, 3)
+    rows["bf16_decode_32x8192x28672"] = _rate(tg * 1e3, ops=2 * M * N * K, byts=byts)
+    log(f"bf16 decode: gemm {tg * 1e3:.1f} us")
+    del sets, wb, x
+    torch.cuda.empty_cache()
+
     # routed MoE layer: 4096 tokens, top-8 of 64 experts (Zipf, 4 empty), K=4096, N=2048
     m = synth.moe_inputs()
     R, E, K, N = m["R"], m["E"], m["K"], m["N"]
@@ -387,6 +419,19 @@ def extra_rows(torch, L, stream, dev, steps):
             torch, stream, steps, 3)
         rows[f"blockfmt_decode_fp8_{dname}_4096x7168"] = _rate(td * 1e3, byts=fp8_bytes)
         log(f"decode fp8 {dname} {td * 1e3:.1f} us")
+    # the BF16 route's load-time dequantisation of the same FP8 blocks
+    bf_bytes = Nd * Kd + (Nd // 128) * (Kd // 128) + 2 * Nd * Kd
+    bsets = []
+    for i in range(_copies(bf_bytes)):
+        o = dict(w=w.clone(), bs=bs.clone(),
+                 wb=torch.empty((Nd, Kd), dtype=torch.int16, device=dev))
+        bsets.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
+    tb = Row("dequant fp8 bf16", bsets, lambda p, st: _ok(
+        L, L.bsb_dequant_fp8_block_bf16(p["w"], p["bs"], Nd, Kd, 0, p["wb"], st))).time(
+        torch, stream, steps, 3)
+    rows["blockfmt_dequant_fp8_bf16_4096x7168"] = _rate(tb * 1e3, byts=bf_bytes)
+    log(f"dequant fp8 -> bf16 {tb * 1e3:.1f} us")
+    del bsets
     qwd = torch.empty((Nd, Kd), dtype=torch.int8, device=dev)
     swd = torch.empty((Nd, Gd), dtype=torch.float32, device=dev)
     _ok(L, L.bsb_decode_fp8_block(w.data_ptr(), bs.data_ptr(), Nd, Kd, 0, qwd.data_ptr(),

@@ -6,7 +6,7 @@ Importing the package does not load the library; the first call does, and
 raises if it has not been built.
 """
 from ._lib import (quantize_act, gemm_w8a8_g128, gemm_w8a8_g128_partials,  # noqa: F401
-                   gemm_w8a8_channel,
+                   gemm_w8a8_channel, gemm_w8a16_g128, gemm_bf16, dequant_fp8_block_bf16,
                    grouped_gemm_w8a8_g128, decode_fp8_block, decode_mxfp4, gather_rows,
                    moe_combine, BsbError,
                    BSB_OUT_BF16, BSB_OUT_FP32, BSB_FP8_OCP, BSB_FP8_FNUZ, lib, LIB_PATH)

@@ -33,6 +33,9 @@ _SIGNATURES = {
     "bsb_grouped_gemm_w8a8_g128": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
                                    _c_p, _c_int, _c_p],
     "bsb_decode_fp8_block": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_p],
+    "bsb_dequant_fp8_block_bf16": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p],
+    "bsb_gemm_w8a16_g128": [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
+    "bsb_gemm_bf16": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
     "bsb_decode_mxfp4": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "bsb_gemm_w8a8_g128_partials": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "bsb_gather_rows": [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
@@ -235,6 +238,65 @@ def decode_fp8_block(w: torch.Tensor, bs: torch.Tensor, dialect: int,
         _check(lib().bsb_decode_fp8_block(_ptr(w), _ptr(bs), N, K, dialect, _ptr(qw), _ptr(sw),
                                           _stream(dev)), "bsb_decode_fp8_block")
     return qw, sw
+
+
+def dequant_fp8_block_bf16(w: torch.Tensor, bs: torch.Tensor, dialect: int,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """FP8 e4m3 bytes [N,K] + UE8M0 block exponents [N/128,K/128] -> BF16 weights [N,K]."""
+    _need(w, "w", (torch.uint8,))
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    N, K = w.shape
+    dev = w.device
+    _need(bs, "bs", (torch.uint8,), (N // 128, K // 128), dev)
+    if dialect not in (BSB_FP8_OCP, BSB_FP8_FNUZ):
+        raise ValueError("dialect must be BSB_FP8_OCP or BSB_FP8_FNUZ")
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(out, "out", _BF16_BITS, (N, K), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_dequant_fp8_block_bf16(_ptr(w), _ptr(bs), N, K, dialect, _ptr(out),
+                                                _stream(dev)), "bsb_dequant_fp8_block_bf16")
+    return out
+
+
+def gemm_w8a16_g128(x: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                    out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [M,N] = weight-only INT8 GEMM of BF16 activations x [M,K] (M <= 64) with qw [N,K]
+    and per-group scales sw [N,K/128]."""
+    _need(x, "x", _BF16_BITS)
+    if x.dim() != 2 or qw.dim() != 2:
+        raise ValueError("x [M,K] and qw [N,K] required")
+    M, K = x.shape
+    N = qw.shape[0]
+    dev = x.device
+    _need(qw, "qw", (torch.int8,), (N, K), dev)
+    _need(sw, "sw", (torch.float32,), (N, K // 128), dev)
+    code = _out_code(out_dtype)
+    out = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", (out_dtype,), (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_gemm_w8a16_g128(_ptr(x), _ptr(qw), _ptr(sw), M, N, K, _ptr(out), code,
+                                         _stream(dev)), "bsb_gemm_w8a16_g128")
+    return out
+
+
+def gemm_bf16(x: torch.Tensor, w: torch.Tensor, out_dtype=torch.bfloat16,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [M,N] = BF16 GEMM of x [M,K] (M <= 64) with w [N,K] (BF16)."""
+    _need(x, "x", _BF16_BITS)
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x [M,K] and w [N,K] required")
+    M, K = x.shape
+    N = w.shape[0]
+    dev = x.device
+    _need(w, "w", _BF16_BITS, (N, K), dev)
+    code = _out_code(out_dtype)
+    out = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", (out_dtype,), (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_gemm_bf16(_ptr(x), _ptr(w), M, N, K, _ptr(out), code, _stream(dev)),
+               "bsb_gemm_bf16")
+    return out
 
 
 def decode_mxfp4(packed: torch.Tensor, scale: torch.Tensor,

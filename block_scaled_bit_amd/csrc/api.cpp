@@ -49,6 +49,9 @@ constexpr int64_t kMaxDecodeElems = (int64_t)1 << 35;
 // whole of K stays in range (127 * 127 * 131072 < 2^31).
 constexpr int64_t kMaxChannelK = 131072;
 
+// Rows of the BF16-activation GEMMs (the decode-shaped kernel).
+constexpr int64_t kMaxA16Rows = 64;
+
 // Experts per token accepted by the combine.
 constexpr int64_t kMaxTopk = 256;
 
@@ -164,6 +167,59 @@ bsb_status bsb_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t N, 
     (void)hipGetLastError();
     return finish(bsb::launch_decode_fp8_block(w, bs, N, K, dialect == BSB_FP8_FNUZ ? 1 : 0, qw,
                                                sw, as_stream(stream)));
+}
+
+bsb_status bsb_dequant_fp8_block_bf16(const uint8_t *w, const uint8_t *bs, int64_t N, int64_t K,
+                                      bsb_fp8_dialect dialect, uint16_t *w_bf16, void *stream) {
+    if (N < 128 || N % 128 || K < 128 || K % 128 || N >= kMaxDim || K >= kMaxDim ||
+        N * K > kMaxDecodeElems)
+        return BSB_ERR_INVALID_ARG;
+    if (dialect != BSB_FP8_OCP && dialect != BSB_FP8_FNUZ) return BSB_ERR_INVALID_ARG;
+    if (!w || !bs || !w_bf16) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(bs) || !aligned16(w_bf16)) return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_dequant_fp8_block_bf16(w, bs, N, K, dialect == BSB_FP8_FNUZ ? 1 : 0,
+                                                     w_bf16, as_stream(stream)));
+}
+
+namespace {
+
+// The BF16-activation GEMMs run the decode-shaped kernel: at most 64 rows, and
+// 128 weight rows of 2K bytes addressed with 32-bit offsets.
+bsb_status a16_checks(int64_t M, int64_t N, int64_t K, bsb_out_dtype out) {
+    if (!dims_ok(M, N, K) || M > kMaxA16Rows || N * K > kMaxElems ||
+        (int64_t)256 * K >= ((int64_t)1 << 31))
+        return BSB_ERR_INVALID_ARG;
+    if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
+    return BSB_OK;
+}
+
+}  // namespace
+
+bsb_status bsb_gemm_w8a16_g128(const uint16_t *x_bf16, const int8_t *qw, const float *sw,
+                               int64_t M, int64_t N, int64_t K, void *y, bsb_out_dtype out,
+                               void *stream) {
+    if (bsb_status s = a16_checks(M, N, K, out)) return s;
+    if (M == 0) return BSB_OK;
+    if (!x_bf16 || !qw || !sw || !y) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(x_bf16) || !aligned16(qw) || !aligned16(sw) || !aligned16(y))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_gemm_a16(x_bf16, qw, sw, M, N, K, y, (int)out, 1, as_stream(stream)));
+}
+
+bsb_status bsb_gemm_bf16(const uint16_t *x_bf16, const uint16_t *w_bf16, int64_t M, int64_t N,
+                         int64_t K, void *y, bsb_out_dtype out, void *stream) {
+    if (bsb_status s = a16_checks(M, N, K, out)) return s;
+    if (M == 0) return BSB_OK;
+    if (!x_bf16 || !w_bf16 || !y) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(x_bf16) || !aligned16(w_bf16) || !aligned16(y)) return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_gemm_a16(x_bf16, w_bf16, nullptr, M, N, K, y, (int)out, 2,
+                                       as_stream(stream)));
 }
 
 bsb_status bsb_decode_mxfp4(const uint8_t *packed, const uint8_t *scale, int64_t E, int64_t N,

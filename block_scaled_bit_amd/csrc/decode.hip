@@ -5,6 +5,9 @@
 // re-routes both onto the INT8 path by dequantise-and-repack. [P2] "FP8
 // dialect clash": OCP and fnuz share the bit layout, biases 7 vs 8.
 //
+// The BF16 route's dequantisation (the same FP8 blocks to BF16, [P1] sec. 2's
+// load-time path for the dense linears) shares the element decode.
+//
 // Both decoders are HBM streams (1 or 0.5 byte in, 1 byte + 4/128 out per
 // element). A thread owns one 16-byte input chunk; the lanes that cover one
 // 128-wide K group are consecutive, so the group maximum is a shuffle
@@ -47,6 +50,33 @@ __device__ __forceinline__ void quant16(const float *f, float s, float amax, uin
     }
 }
 
+// Sixteen FP8 bytes -> float32 as the OCP reading; with fnuz the caller folds
+// the factor 1/2 into its block scale, and 0x7F / 0xFF (NaN in OCP, +-240 in
+// fnuz) come out as +-480 so that the half gives +-240.
+__device__ __forceinline__ void fp8x16_to_f32(uint4 v, int fnuz, float *f) {
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], false);   // bytes 0, 1
+        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], true);    // bytes 2, 3
+        f[4 * i] = lo.x;
+        f[4 * i + 1] = lo.y;
+        f[4 * i + 2] = hi.x;
+        f[4 * i + 3] = hi.y;
+        if (fnuz) {
+            // a byte with all of e and m set
+            const uint32_t t = (wd[i] & 0x7F7F7F7Fu) ^ 0x7F7F7F7Fu;
+            if ((t - 0x01010101u) & ~t & 0x80808080u) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t byte = (wd[i] >> (8 * b)) & 0xFFu;
+                    if ((byte & 0x7Fu) == 0x7Fu) f[4 * i + b] = (byte & 0x80u) ? -480.0f : 480.0f;
+                }
+            }
+        }
+    }
+}
+
 __global__ void __launch_bounds__(256)
 decode_fp8_block_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ bs,
                         uint32_t nchunks, uint32_t cpr, uint32_t gpr, int fnuz,
@@ -65,29 +95,8 @@ decode_fp8_block_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict
     }
     // fnuz = OCP / 2: fold the half into the (power-of-two) block scale
     if (fnuz) scale *= 0.5f;
-    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
     float f[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], false);   // bytes 0, 1
-        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], true);    // bytes 2, 3
-        f[4 * i] = lo.x;
-        f[4 * i + 1] = lo.y;
-        f[4 * i + 2] = hi.x;
-        f[4 * i + 3] = hi.y;
-        if (fnuz) {
-            // a byte with all of e and m set: 0x7F / 0xFF read as fnuz is +-240,
-            // i.e. +-480 before the folded half
-            const uint32_t t = (wd[i] & 0x7F7F7F7Fu) ^ 0x7F7F7F7Fu;
-            if ((t - 0x01010101u) & ~t & 0x80808080u) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const uint32_t byte = (wd[i] >> (8 * b)) & 0xFFu;
-                    if ((byte & 0x7Fu) == 0x7Fu) f[4 * i + b] = (byte & 0x80u) ? -480.0f : 480.0f;
-                }
-            }
-        }
-    }
+    fp8x16_to_f32(v, fnuz, f);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -154,7 +163,44 @@ decode_mxfp4_kernel(const uint8_t *__restrict__ packed, const uint8_t *__restric
     }
 }
 
+// FP8 block -> BF16 (the load-time dequantisation of the BF16 route): each
+// element is e4m3(w) * 2^(E-127), exact in float32, then rounded to BF16 to
+// nearest even (exact unless it is a BF16 subnormal). One thread per 16 input
+// bytes, two 16-byte stores.
+__global__ void __launch_bounds__(256)
+dequant_fp8_block_bf16_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ bs,
+                              uint32_t nchunks, uint32_t cpr, uint32_t gpr, int fnuz,
+                              uint16_t *__restrict__ out) {
+    const uint32_t chunk = blockIdx.x * 256u + threadIdx.x;
+    if (chunk >= nchunks) return;
+    const uint32_t n = chunk / cpr, kc = chunk - n * cpr;
+    const uint4 v = reinterpret_cast<const uint4 *>(w)[chunk];
+    float scale = ue8m0_to_f32(bs[(n >> 7) * gpr + (kc >> 3)]);
+    if (fnuz) scale *= 0.5f;
+    float f[16];
+    fp8x16_to_f32(v, fnuz, f);
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const __bf16 a = (__bf16)(f[2 * i] * scale), b = (__bf16)(f[2 * i + 1] * scale);
+        o[i] = (uint32_t)__builtin_bit_cast(uint16_t, a) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(out) + 2 * (size_t)chunk;
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 }  // namespace
+
+hipError_t launch_dequant_fp8_block_bf16(const uint8_t *w, const uint8_t *bs, int64_t N,
+                                         int64_t K, int fnuz, uint16_t *out, hipStream_t stream) {
+    const uint32_t nchunks = (uint32_t)(N * K / 16);
+    const uint32_t blocks = (nchunks + 255u) / 256u;
+    dequant_fp8_block_bf16_kernel<<<blocks, 256, 0, stream>>>(
+        w, bs, nchunks, (uint32_t)(K / 16), (uint32_t)(K / 128), fnuz, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t N, int64_t K,
                                    int fnuz, int8_t *qw, float *sw, hipStream_t stream) {

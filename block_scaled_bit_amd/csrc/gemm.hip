@@ -68,6 +68,14 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
         reinterpret_cast<float *>(y)[idx] = v;
 }
 
+// LDS position of 16-byte chunk j of row r is j ^ chunk_swizzle(r): rows of
+// 128 B (8 chunks) share a pattern in pairs, rows of 256 B (16 chunks) each
+// have their own, so 16 rows read at one chunk index hit 16 distinct bank groups.
+template <int ROW_BYTES>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+    return ROW_BYTES == 256 ? (r & 15) : ((r >> 1) & 7);
+}
+
 // --------------------------------------------------------------------------
 // smallm: M <= 16*MB tokens, weight-streaming.
 // --------------------------------------------------------------------------
@@ -131,18 +139,25 @@ constexpr int smallm_stage_scale_floats() {   // per-stage scales, padded to who
     return ((S * 16 * NW + 63) / 64) * 64;
 }
 
-template <int MB, int NW, int S>
+// Activation modes of the small-M kernel: INT8 activations with their
+// per-token scales (W8A8), BF16 activations with INT8 weights and per-group
+// scales (W8A16), BF16 activations with BF16 weights (no scales).
+enum { AM_W8A8 = 0, AM_W8A16 = 1, AM_BF16 = 2 };
+
+template <int MB, int NW, int S, int AM = AM_W8A8>
 constexpr int smallm_stage_bytes() {
-    return S * 16 * NW * kGroup + S * 16 * MB * kGroup +
-           (smallm_chunked_scales<NW>() ? 0 : 4 * smallm_stage_scale_floats<NW, S>());
+    return S * 16 * NW * kGroup * (AM == AM_BF16 ? 2 : 1) + S * 16 * MB * kGroup * (AM ? 2 : 1) +
+           (smallm_chunked_scales<NW>() || AM == AM_BF16 ? 0
+                                                         : 4 * smallm_stage_scale_floats<NW, S>());
 }
 
-template <int NW>
+template <int NW, int AM = AM_W8A8>
 constexpr int smallm_fixed_bytes() {   // scale chunks + sink
-    return (smallm_chunked_scales<NW>() ? 2 * 16 * NW * kScaleChunk * 4 : 0) + 1024;
+    return (smallm_chunked_scales<NW>() && AM != AM_BF16 ? 2 * 16 * NW * kScaleChunk * 4 : 0) +
+           1024;
 }
 
-template <int MB, int NW, int OUT, int S, int D, bool GROUPED, bool NT>
+template <int MB, int NW, int OUT, int S, int D, bool GROUPED, bool NT, int AM = AM_W8A8>
 __global__ void __launch_bounds__(64 * NW)
 gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                    const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N,
@@ -150,12 +165,15 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                    int sw_stride) {
     constexpr int ROWS = 16 * MB;              // activation rows
     constexpr int WR = 16 * NW;                // weight rows per workgroup
-    constexpr int BT = WR * kGroup;            // one group of the weight tile (bytes)
-    constexpr int AT = ROWS * kGroup;          // one group of the activation tile
-    constexpr int WBLK = 2 * S;                // 1 KB weight blocks per wave per stage
+    constexpr int RW = kGroup * (AM == AM_BF16 ? 2 : 1);   // bytes of a weight row per group
+    constexpr int RA = kGroup * (AM ? 2 : 1);             // bytes of an activation row per group
+    constexpr int BT = WR * RW;                // one group of the weight tile (bytes)
+    constexpr int AT = ROWS * RA;              // one group of the activation tile
+    constexpr int WBLK = S * BT / 1024 / NW;   // 1 KB weight blocks per wave per stage
     constexpr int ABLK = (S * AT / 1024 + NW - 1) / NW;   // activation blocks per wave
     constexpr bool CHN = per_channel<OUT>();   // one scale per row, applied at the end
-    constexpr int NLD = WBLK + ABLK + (CHN ? 0 : 1);   // load slots per wave per stage (+1: scales)
+    constexpr bool NOSCALE = CHN || AM == AM_BF16;   // no per-group scales to stage
+    constexpr int NLD = WBLK + ABLK + (NOSCALE ? 0 : 1);   // load slots per wave per stage (+1: scales)
     constexpr int TBLK = S * AT / 1024;        // activation blocks per stage
     // Spare slots issue nothing (a load past the end still costs an
     // instruction on the LDS-destination path), so waves issue different
@@ -171,7 +189,7 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     constexpr int SCH = kScaleChunk;
     constexpr int SPC = SCH / S;               // stages per scale chunk
     constexpr int NP = WR * SCH / 64;          // 4-row pieces per scale chunk (= 4*NW)
-    constexpr bool CHUNKED = smallm_chunked_scales<NW>() && !CHN;
+    constexpr bool CHUNKED = smallm_chunked_scales<NW>() && !NOSCALE;
     constexpr int SPAD = smallm_stage_scale_floats<NW, S>();
     static_assert(D >= 2 && (D - 2) * NLD <= 63 && NLD_MIN >= 1,
                   "ring depth or wait count out of range");
@@ -180,7 +198,7 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     __shared__ __align__(16) int8_t Bs[D][S * BT];
     __shared__ __align__(16) int8_t As[D][S * AT];
     // scales: [2][WR][SCH] in chunks, or [D][SPAD] per stage (entry gl*WR + row)
-    __shared__ __align__(16) float Sc[CHN ? 64 : CHUNKED ? 2 * WR * SCH : D * SPAD];
+    __shared__ __align__(16) float Sc[NOSCALE ? 64 : CHUNKED ? 2 * WR * SCH : D * SPAD];
     __shared__ __align__(16) int8_t sink[1024];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -205,11 +223,12 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         sw += (int64_t)e * N * G;
     }
 
-    const v4i rw = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(nrows * K));
+    const v4i rw = make_rsrc_words(qw + (int64_t)n0 * K * (RW / kGroup),
+                                   (uint32_t)(nrows * K * (RW / kGroup)));
     // The partials form has no scales (sw may be null): an empty descriptor
     // makes its scale loads read zero without touching memory.
-    const v4i rsc = make_rsrc_words(OUT == OUT_PARTIALS || CHN ? nullptr : sw + (int64_t)n0 * G,
-                                    OUT == OUT_PARTIALS || CHN ? 0u : (uint32_t)(nrows * G * 4));
+    const v4i rsc = make_rsrc_words(OUT == OUT_PARTIALS || NOSCALE ? nullptr : sw + (int64_t)n0 * G,
+                                    OUT == OUT_PARTIALS || NOSCALE ? 0u : (uint32_t)(nrows * G * 4));
     v4i ra;                             // the current pass's activation rows
     int rows = 0, r0 = 0;
 
@@ -220,26 +239,32 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     uint32_t wvo[WBLK], avo[ABLK];
     uint32_t wdst[WBLK], adst[ABLK];
     int wgl[WBLK], agl[ABLK];
+    // A 1 KB block holds 1024 / R rows of R bytes (R = 128 or 256 per group),
+    // R / 16 lanes per row; chunk j of row r sits at position j ^ swz(r).
 #pragma unroll
     for (int i = 0; i < WBLK; ++i) {
-        const int blk = wv * WBLK + i;                 // 0 .. 2*NW*S-1
-        const int gl = blk / (2 * NW), rb = blk % (2 * NW);
-        const int row = rb * 8 + (lane >> 3), pos = lane & 7;
-        wvo[i] = (uint32_t)(row * K + ((pos ^ ((row >> 1) & 7)) << 4));
+        constexpr int LPR = RW / 16, RPB = 1024 / RW;
+        const int blk = wv * WBLK + i;
+        const int gl = blk / (BT / 1024), rb = blk % (BT / 1024);
+        const int row = rb * RPB + lane / LPR, pos = lane % LPR;
+        wvo[i] = (uint32_t)(row * K * (RW / kGroup) + ((pos ^ chunk_swizzle<RW>(row)) << 4));
         wdst[i] = (uint32_t)(gl * BT + rb * 1024);
         wgl[i] = gl;
     }
 #pragma unroll
     for (int i = 0; i < ABLK; ++i) {
+        constexpr int LPR = RA / 16, RPB = 1024 / RA;
         const int blk = wv * ABLK + i;
         const bool ok = blk < S * AT / 1024;
-        const int gl = blk / (ROWS / 8), rb = blk % (ROWS / 8);
-        const int row = rb * 8 + (lane >> 3), pos = lane & 7;
-        avo[i] = ok ? (uint32_t)(row * K + ((pos ^ ((row >> 1) & 7)) << 4)) : kOOB;
+        const int gl = blk / (AT / 1024), rb = blk % (AT / 1024);
+        const int row = rb * RPB + lane / LPR, pos = lane % LPR;
+        avo[i] = ok ? (uint32_t)(row * K * (RA / kGroup) + ((pos ^ chunk_swizzle<RA>(row)) << 4))
+                    : kOOB;
         adst[i] = ok ? (uint32_t)(gl * AT + rb * 1024) : 0xFFFFFFFFu;
         agl[i] = ok ? gl : 0;
     }
-    auto goff = [&](int g) { return g < G ? (uint32_t)g * kGroup : kOOB; };
+    auto goffw = [&](int g) { return g < G ? (uint32_t)g * RW : kOOB; };
+    auto goffa = [&](int g) { return g < G ? (uint32_t)g * RA : kOOB; };
 
     auto lds_addr = [](const void *p) {
         return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
@@ -267,17 +292,17 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 #pragma unroll
         for (int i = 0; i < WBLK; ++i) {
             if (NT)
-                buf_load16_lds_nt(rw, lds_addr(&Bs[d][wdst[i]]), wvo[i], goff(s0 + wgl[i]));
+                buf_load16_lds_nt(rw, lds_addr(&Bs[d][wdst[i]]), wvo[i], goffw(s0 + wgl[i]));
             else
-                buf_load16_lds(rw, lds_addr(&Bs[d][wdst[i]]), wvo[i], goff(s0 + wgl[i]));
+                buf_load16_lds(rw, lds_addr(&Bs[d][wdst[i]]), wvo[i], goffw(s0 + wgl[i]));
         }
 #pragma unroll
         for (int i = 0; i < ABLK; ++i) {
             if (NOSPARE && wv * ABLK + i >= TBLK) continue;   // wave-uniform
             buf_load16_lds(ra, lds_addr(adst[i] != 0xFFFFFFFFu ? &As[d][adst[i]] : sink), avo[i],
-                           adst[i] != 0xFFFFFFFFu ? goff(s0 + agl[i]) : 0u);   // spare: reads zero
+                           adst[i] != 0xFFFFFFFFu ? goffa(s0 + agl[i]) : 0u);   // spare: reads zero
         }
-        if (CHN) {
+        if (NOSCALE) {
             // no per-group scales
         } else if (CHUNKED) {
             // the stage's scale piece: stage X = s0 / S, position sg in its chunk
@@ -298,7 +323,71 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     // One stage: every LDS fragment first, then all matrix instructions, then
     // the per-group epilogues in group order, so that the stage pays one LDS
     // round trip and one matrix-pipeline drain rather than one per instruction.
+    // BF16 activations: per group four v_mfma_f32_16x16x32_bf16; lane (col,
+    // slot) of instruction kk holds K elements 8*(4kk + slot) .. +7 of its row
+    // (A: activation row i*16 + col, B: weight row nl), the same for both
+    // operands. INT8 weights are read 8 bytes at a time and converted to BF16
+    // (exact: |w| <= 127 has at most 7 significant bits).
+    auto compute_a16 = [&](int d, int s0) {
+#pragma unroll
+        for (int gl = 0; gl < S; ++gl) {
+            const int8_t *at = &As[d][gl * AT];
+            const int8_t *bt = &Bs[d][gl * BT];
+            bf16x8 a[4][MB], b[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int c = 4 * kk + slot;
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const int ar = i * 16 + col;
+                    a[kk][i] = *reinterpret_cast<const bf16x8 *>(
+                        at + ar * RA + ((c ^ chunk_swizzle<RA>(ar)) << 4));
+                }
+                if (AM == AM_BF16) {
+                    b[kk] = *reinterpret_cast<const bf16x8 *>(
+                        bt + nl * RW + ((c ^ chunk_swizzle<RW>(nl)) << 4));
+                } else {
+                    const uint2 w8 = *reinterpret_cast<const uint2 *>(
+                        bt + nl * RW + (((c >> 1) ^ chunk_swizzle<RW>(nl)) << 4) + (c & 1) * 8);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        b[kk][e] = (__bf16)(float)(int8_t)(w8.x >> (8 * e));
+                        b[kk][4 + e] = (__bf16)(float)(int8_t)(w8.y >> (8 * e));
+                    }
+                }
+            }
+            v4f acc[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk][i], b[kk], acc[i], 0, 0,
+                                                                     0);
+            }
+            if (AM == AM_BF16) {
+                // groups past the end add zeros (+0 leaves the sum unchanged)
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) facc[i][r] = facc[i][r] + acc[i][r];
+            } else {
+                const int g = s0 + gl;
+                const float sc = CHUNKED ? Sc[((g / SCH) & 1) * WR * SCH + nl * SCH + g % SCH]
+                                         : Sc[d * SPAD + gl * WR + nl];
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        facc[i][r] = __builtin_fmaf(acc[i][r], sc, facc[i][r]);
+            }
+        }
+    };
     auto compute = [&](int d, int s0) {
+        if (AM != AM_W8A8) {
+            compute_a16(d, s0);
+            return;
+        }
         v4i bf[S][2], af[S][2][MB];
 #pragma unroll
         for (int gl = 0; gl < S; ++gl)
@@ -372,7 +461,8 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
 
     // One pass: rows r0 .. r0+rows-1 (rows <= 16*MB) against the whole K walk.
     auto pass = [&]() {
-        ra = make_rsrc_words(q + (int64_t)r0 * K, (uint32_t)(rows * K));
+        ra = make_rsrc_words(q + (int64_t)r0 * K * (RA / kGroup),
+                             (uint32_t)(rows * K * (RA / kGroup)));
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
             iacc[i] = v4i{0, 0, 0, 0};
@@ -407,6 +497,14 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                     if (m < rows)
                         store_out<OUT>(y, (int64_t)(r0 + m) * N + n,
                                        channel_value(iacc[i][r], swn, sa[r0 + m]));
+                }
+        } else if (AM != AM_W8A8 && nl < nrows) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = i * 16 + slot * 4 + r;
+                    if (m < rows) store_out<OUT>(y, (int64_t)(r0 + m) * N + n, facc[i][r]);
                 }
         } else if (OUT != OUT_PARTIALS && nl < nrows) {
 #pragma unroll
@@ -1001,29 +1099,40 @@ constexpr int kSmallD = BSB_SMALLM_D;     // LDS stage buffers (D-1 stages in fl
 
 // Ring depth: as many stage buffers as fit in the 160 KB of LDS beside the
 // scale chunks, at most kSmallD.
-template <int MB, int NW>
+template <int MB, int NW, int S = kSmallS, int AM = AM_W8A8>
 constexpr int small_depth() {
-    constexpr int st = smallm_stage_bytes<MB, NW, kSmallS>();
-    constexpr int room = 160 * 1024 - smallm_fixed_bytes<NW>();
+    constexpr int st = smallm_stage_bytes<MB, NW, S, AM>();
+    constexpr int room = 160 * 1024 - smallm_fixed_bytes<NW, AM>();
     return (kSmallD * st <= room) ? kSmallD : room / st;
 }
 
-template <int MB, int NW, int OUT, bool GROUPED>
+// Groups per stage: BF16 tiles are twice as large, so one group per stage
+// where two would leave fewer than three stage buffers.
+template <int MB, int NW, int AM>
+constexpr int small_stage() {
+    return AM == AM_BF16 || (AM == AM_W8A16 && small_depth<MB, NW, kSmallS, AM>() < 3) ? 1
+                                                                                     : kSmallS;
+}
+
+template <int MB, int NW, int OUT, bool GROUPED, int AM = AM_W8A8>
 hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                             int M, int N, int K, void *y, const int32_t *offsets, int E,
                             hipStream_t stream, int sw_stride) {
+    constexpr int S = small_stage<MB, NW, AM>();
+    constexpr int D = small_depth<MB, NW, S, AM>();
     const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW)), GROUPED ? (unsigned)E : 1u);
     // the non-temporal hint pays on weight streams far larger than the caches
     // (measured: faster at 235 MB, slower at 29 MB)
 #ifndef BSB_NT_MIN
 #define BSB_NT_MIN (1LL << 27)
 #endif
-    const bool nt = (int64_t)N * K * (GROUPED ? E : 1) >= (int64_t)BSB_NT_MIN;
+    const bool nt = (int64_t)N * K * (GROUPED ? E : 1) * (AM == AM_BF16 ? 2 : 1) >=
+                    (int64_t)BSB_NT_MIN;
     if (nt)
-        gemm_smallm_kernel<MB, NW, OUT, kSmallS, small_depth<MB, NW>(), GROUPED, true>
+        gemm_smallm_kernel<MB, NW, OUT, S, D, GROUPED, true, AM>
             <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets, sw_stride);
     else
-        gemm_smallm_kernel<MB, NW, OUT, kSmallS, small_depth<MB, NW>(), GROUPED, false>
+        gemm_smallm_kernel<MB, NW, OUT, S, D, GROUPED, false, AM>
             <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets, sw_stride);
     return hipGetLastError();
 }
@@ -1034,7 +1143,7 @@ hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, 
 // most 8 waves, and at least what the activation tile needs (register ring).
 constexpr int kCUs = 256;
 
-template <int MB, int OUT, bool GROUPED>
+template <int MB, int OUT, bool GROUPED, int AM = AM_W8A8>
 hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                             int M, int N, int K, void *y, const int32_t *offsets, int E,
                             hipStream_t stream, int sw_stride = 1) {
@@ -1053,8 +1162,8 @@ hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, 
 #endif
 #define BSB_SMALLM_CASE(W)                                                                       \
     case W:                                                                                      \
-        return launch_smallm_mb<MB, W, OUT, GROUPED>(q, sa, qw, sw, M, N, K, y, offsets, E, stream, \
-                                                     sw_stride);
+        return launch_smallm_mb<MB, W, OUT, GROUPED, AM>(q, sa, qw, sw, M, N, K, y, offsets, E,   \
+                                                         stream, sw_stride);
     switch (nw) {
 #ifdef BSB_SMALLM_NW
         BSB_SMALLM_CASE(1)
@@ -1065,8 +1174,8 @@ hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, 
         BSB_SMALLM_CASE(5)
         BSB_SMALLM_CASE(6)
         BSB_SMALLM_CASE(7)
-        default: return launch_smallm_mb<MB, 8, OUT, GROUPED>(q, sa, qw, sw, M, N, K, y, offsets,
-                                                               E, stream, sw_stride);
+        default: return launch_smallm_mb<MB, 8, OUT, GROUPED, AM>(q, sa, qw, sw, M, N, K, y,
+                                                                   offsets, E, stream, sw_stride);
     }
 #undef BSB_SMALLM_CASE
 }
@@ -1115,6 +1224,38 @@ hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw, const
         case OUT_FP32: return launch_dense<OUT_FP32>(q, sa, qw, sw, (int)M, (int)N, (int)K, y, stream);
         default: return launch_dense<OUT_PARTIALS>(q, nullptr, qw, nullptr, (int)M, (int)N, (int)K, y, stream);
     }
+}
+
+namespace {
+
+// BF16 activations (M <= 64): W8A16 (am 1: qw INT8 + sw) or BF16 weights (am 2).
+template <int OUT, int AM>
+hipError_t launch_a16_rows(const uint16_t *x, const void *w, const float *sw, int M, int N, int K,
+                           void *y, hipStream_t stream) {
+    const int8_t *xq = reinterpret_cast<const int8_t *>(x);
+    const int8_t *wq = reinterpret_cast<const int8_t *>(w);
+    if (M <= 16)
+        return launch_smallm_nw<1, OUT, false, AM>(xq, nullptr, wq, sw, M, N, K, y, nullptr, 1,
+                                                   stream);
+    if (M <= 32)
+        return launch_smallm_nw<2, OUT, false, AM>(xq, nullptr, wq, sw, M, N, K, y, nullptr, 1,
+                                                   stream);
+    return launch_smallm_nw<4, OUT, false, AM>(xq, nullptr, wq, sw, M, N, K, y, nullptr, 1,
+                                               stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_a16(const uint16_t *x, const void *w, const float *sw, int64_t M,
+                           int64_t N, int64_t K, void *y, int out, int am, hipStream_t stream) {
+    if (am == 1) {
+        if (out == OUT_BF16)
+            return launch_a16_rows<OUT_BF16, AM_W8A16>(x, w, sw, (int)M, (int)N, (int)K, y, stream);
+        return launch_a16_rows<OUT_FP32, AM_W8A16>(x, w, sw, (int)M, (int)N, (int)K, y, stream);
+    }
+    if (out == OUT_BF16)
+        return launch_a16_rows<OUT_BF16, AM_BF16>(x, w, nullptr, (int)M, (int)N, (int)K, y, stream);
+    return launch_a16_rows<OUT_FP32, AM_BF16>(x, w, nullptr, (int)M, (int)N, (int)K, y, stream);
 }
 
 hipError_t launch_gemm_channel(const int8_t *q, const float *sa, const int8_t *qw,

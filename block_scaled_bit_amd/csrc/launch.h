@@ -14,6 +14,10 @@ hipError_t launch_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t 
                                    int64_t K, int fnuz, int8_t *qw, float *sw,
                                    hipStream_t stream);
 
+// FP8 e4m3 [N,K] with [N/128, K/128] UE8M0 block scales -> BF16 bits [N,K].
+hipError_t launch_dequant_fp8_block_bf16(const uint8_t *w, const uint8_t *bs, int64_t N,
+                                         int64_t K, int fnuz, uint16_t *out, hipStream_t stream);
+
 hipError_t launch_decode_mxfp4(const uint8_t *packed, const uint8_t *scale, int64_t E,
                                int64_t N, int64_t K, int8_t *qw, float *sw,
                                hipStream_t stream);
@@ -28,6 +32,11 @@ hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw,
 hipError_t launch_gemm_channel(const int8_t *q, const float *sa, const int8_t *qw,
                                const float *sw, int64_t sw_stride, int64_t M, int64_t N,
                                int64_t K, void *y, int out, hipStream_t stream);
+
+// BF16 activations x [M,K], M <= 64: am 1 = W8A16 (w INT8 [N,K], sw [N,K/128]),
+// am 2 = BF16 weights (w BF16 bits [N,K], no scales); out 0 = BF16, 1 = FP32.
+hipError_t launch_gemm_a16(const uint16_t *x, const void *w, const float *sw, int64_t M,
+                           int64_t N, int64_t K, void *y, int out, int am, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *qw,
                                const float *sw, const int32_t *offsets, int64_t E,

@@ -152,6 +152,45 @@ bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa,
                                       void *y, bsb_out_dtype out, void *stream);
 
 /*
+ * The routes the pages run beside W8A8 ([P1] sec. 1-2): weight-only INT8
+ * ("WNA16": INT8 weights with the per-group scales above, BF16 activations)
+ * and BF16 weights dequantised from FP8 at load time. Both take BF16
+ * activations as they are (no activation quantisation) and are built for
+ * decode-shaped M:
+ *     W8A16: y[m,n] = sum_g sw[n,g] * sum_{k in g} x[m,k] * qw[n,k]
+ *     BF16:  y[m,n] = sum_k x[m,k] * w[n,k]
+ * Products are exact in float32; the matrix core sums each group's 128
+ * products in float32 in its own order, and group sums are combined in group
+ * order (a fused multiply-add with sw[n,g], or a float32 add), so results are
+ * within (127 + G) * 2^-24 * sum |terms| of the exact value and do not depend
+ * on the launch shape.
+ *   x_bf16  [M, K] BF16 bits, 0 <= M <= 64
+ *   qw      [N, K] int8, sw [N, G] float32   (W8A16)
+ *   w_bf16  [N, K] BF16 bits                 (BF16)
+ *   y       [M, N] BF16 bits or float32 per `out`
+ * K a multiple of 128 and below 2^23; other limits and errors as
+ * bsb_gemm_w8a8_g128; M > 64 -> BSB_ERR_INVALID_ARG.
+ */
+bsb_status bsb_gemm_w8a16_g128(const uint16_t *x_bf16, const int8_t *qw, const float *sw,
+                               int64_t M, int64_t N, int64_t K,
+                               void *y, bsb_out_dtype out, void *stream);
+
+bsb_status bsb_gemm_bf16(const uint16_t *x_bf16, const uint16_t *w_bf16,
+                         int64_t M, int64_t N, int64_t K,
+                         void *y, bsb_out_dtype out, void *stream);
+
+/*
+ * FP8 e4m3 weights with [128,128] UE8M0 block scales -> BF16, the load-time
+ * dequantisation of the BF16 route ([P1] sec. 2):
+ *     w_bf16[n,k] = RNE_bf16(e4m3_dialect(w[n,k]) * 2^(bs[n/128, k/128] - 127))
+ * exact unless the value is a BF16 subnormal. Arguments and limits as
+ * bsb_decode_fp8_block; w_bf16 [N, K] BF16 bits (written).
+ */
+bsb_status bsb_dequant_fp8_block_bf16(const uint8_t *w, const uint8_t *bs,
+                                      int64_t N, int64_t K, bsb_fp8_dialect dialect,
+                                      uint16_t *w_bf16, void *stream);
+
+/*
  * FP8 e4m3 weights with [128,128] UE8M0 block scales ([P1] sec. 1) ->
  * INT8 per-group-128 ([P1] sec. 2 repack onto the INT8 path). The dialect is
  * explicit: the same bytes read as OCP are exactly twice their fnuz reading

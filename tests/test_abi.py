@@ -137,3 +137,27 @@ def test_channel_gemm_argument_checks(L):
     assert f(None, None, None, None, 1, 0, 8, 128, None, 0, None) == OK
     if not torch.cuda.is_available():
         assert f(A, A, A, A + 4, 0, 4, 8, 131072, A, 1, None) == UNSUPPORTED
+
+
+def test_bf16_activation_routes_argument_checks(L):
+    """W8A16 / BF16 GEMMs: at most 64 rows, K a multiple of 128 below 2^23; the FP8 -> BF16
+    dequantisation: the decoder's size and dialect rules."""
+    w16, b16, dq = L.bsb_gemm_w8a16_g128, L.bsb_gemm_bf16, L.bsb_dequant_fp8_block_bf16
+    assert w16(A, A, A, 65, 8, 128, A, 0, None) == INVALID          # M > 64
+    assert b16(A, A, 65, 8, 128, A, 0, None) == INVALID
+    assert w16(A, A, A, 4, 8, 1 << 23, A, 0, None) == INVALID       # 256*K >= 2^31
+    assert b16(A, A, 4, 8, 130, A, 0, None) == INVALID
+    assert w16(A, A, A, 4, 8, 128, A, 3, None) == INVALID           # out enum
+    assert w16(A, None, A, 4, 8, 128, A, 0, None) == INVALID
+    assert b16(A, A, 4, 8, 128, None, 0, None) == INVALID
+    assert w16(A, A, U, 4, 8, 128, A, 0, None) == MISALIGNED
+    assert b16(U, A, 4, 8, 128, A, 0, None) == MISALIGNED
+    assert w16(None, None, None, 0, 8, 128, None, 0, None) == OK
+    assert b16(None, None, 0, 8, 128, None, 0, None) == OK
+    assert dq(A, A, 100, 128, 0, A, None) == INVALID                # N % 128
+    assert dq(A, A, 128, 128, 2, A, None) == INVALID                # dialect
+    assert dq(A, A, 128, 128, 0, U, None) == MISALIGNED
+    if not torch.cuda.is_available():
+        assert w16(A, A, A, 64, 8, 128, A, 1, None) == UNSUPPORTED
+        assert b16(A, A, 1, 8, 128, A, 0, None) == UNSUPPORTED
+        assert dq(A, A, 128, 128, 1, A, None) == UNSUPPORTED
