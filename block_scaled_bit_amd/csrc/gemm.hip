@@ -281,6 +281,16 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                                   : reinterpret_cast<float *>(sink)),
                       vo, 0u);
     };
+    // With G a multiple of 4 a piece can be 16 rows x 64 B, one 16-byte load
+    // per lane (lane l -> row 16p + l/4, groups c*SCH + 4*(l%4) .. +3, all
+    // inside or all past G): a chunk is then NW pieces, one per wave, all on
+    // the first stage issued after the chunk's buffer is free.
+    const bool g4 = (G & 3) == 0;
+    auto piece4 = [&](int c, int p) {
+        const int row = 16 * p + (lane >> 2), g = c * SCH + 4 * (lane & 3);
+        const uint32_t vo = (OUT != OUT_PARTIALS && g < G) ? (uint32_t)(row * G * 4 + g * 4) : kOOB;
+        buf_load16_lds(rsc, lds_addr(&Sc[(c & 1) * WR * SCH + p * 256]), vo, 0u);
+    };
     // per-stage form: lane l of wave w stages entry 64w + l = (group within
     // stage, weight row) of the stage, in that order; its group is per lane
     const int sidx = wv * 64 + lane;
@@ -307,8 +317,12 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         } else if (CHUNKED) {
             // the stage's scale piece: stage X = s0 / S, position sg in its chunk
             const int X = s0 / S, sg = X % SPC;
-            const int pc = sg >= D - 1 ? (sg - (D - 1)) * NW + wv : -1;
-            if (!NOSPARE || (pc >= 0 && pc < NP)) piece(X / SPC + 1, pc);
+            if (g4) {
+                if (sg == D - 1) piece4(X / SPC + 1, wv);
+            } else {
+                const int pc = sg >= D - 1 ? (sg - (D - 1)) * NW + wv : -1;
+                if (!NOSPARE || (pc >= 0 && pc < NP)) piece(X / SPC + 1, pc);
+            }
         } else if (!NOSPARE || s_wave) {
             buf_load4_lds(rsc,
                           lds_addr(s_wave ? &Sc[d * SPAD + wv * 64]
@@ -470,9 +484,13 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
             for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
         }
         const int nst = (G + S - 1) / S;
-        if (CHUNKED) {
+        if (CHUNKED) {   // scale chunk 0
+            if (g4) {
+                piece4(0, wv);
+            } else {
 #pragma unroll
-            for (int j = 0; j < NP / NW; ++j) piece(0, j * NW + wv);   // scale chunk 0
+                for (int j = 0; j < NP / NW; ++j) piece(0, j * NW + wv);
+            }
         }
 #pragma unroll
         for (int d = 0; d < D - 1; ++d) issue(d, d * S);

@@ -72,7 +72,8 @@ def test_tiny_config():
     (2049, 7425, 256), (2305, 7000, 384),
     # M <= 64 with at least 4 waves per workgroup (scales staged in 16-group
     # chunks): a ragged last chunk, less than one chunk, odd N
-    (33, 12400, 2176), (1, 20000, 1152), (64, 13001, 4224)])
+    (33, 12400, 2176), (1, 20000, 1152), (64, 13001, 4224),
+    (17, 12900, 2560)])     # G a multiple of 4: 16-row scale pieces, partial last chunk
 def test_ragged_shapes(M, N, K):
     """Every kernel (M <= 64; 128x128 tiles; 256x256 tiles from 512 rows when there is at
     least one such tile per CU, the last two shapes), partial tiles in M and N, several

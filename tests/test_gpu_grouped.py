@@ -41,6 +41,7 @@ def _gpu_grouped(q, sa, qw, sw, off, dtype, d):
     ([17] * 9, 257, 512),
     ([0, 70, 1, 33, 0, 31, 2], 200, 384),
     ([31, 0, 33, 1, 32, 5, 64, 2], 2048, 4224),    # >= 4 waves per workgroup, 33 groups
+    ([5, 40, 0, 64, 3, 20, 31, 1], 2048, 2560),     # 20 groups: 16-row scale pieces
     # up to 128 rows per expert on average: 128x128 tiles
     ([0, 1, 127, 128, 129, 0, 5], 96, 256),     # segment ends at 0, 1, BM-1, BM, BM+1
     ([300, 0, 0, 2], 130, 384),
