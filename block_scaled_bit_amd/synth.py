@@ -19,6 +19,9 @@ stand in for them):
               N=2048 per expert
 * ``blockfmt`` dense FP8-e4m3 [4096, 7168] with [128,128] UE8M0 block scales,
               plus 8 MXFP4 experts [2048, 4096] with 1x32 UE8M0 scales.
+* ``kv``      decode attention over a KV cache: 32 sequences of 4096 cached
+              tokens, 64 query heads over 8 KV heads of dimension 128; queries,
+              keys and values N(0,1) with 0.5 % outliers x30.
 
 Weights are INT8 uniform over [-127, 127]; weight group scales are
 lognormal(mu=-6, sigma=0.5) in float32, one per (output row, 128-wide K group).
@@ -201,3 +204,25 @@ def blockfmt_inputs(M: int = 32, N_d: int = 4096, K_d: int = 7168, E: int = 8,
     offsets = (np.arange(E + 1) * M).astype(np.int32)
     return dict(w_fp8=w, bs=bs, packed=packed, scale=sc, x_d=x_d, x_e=x_e,
                 offsets=offsets, M=M, N_d=N_d, K_d=K_d, E=E, N_e=N_e, K_e=K_e)
+
+
+KV_CONFIG = dict(B=32, Hq=64, Hkv=8, T=4096, D=128)
+
+
+def kv_inputs(B: int, Hq: int, Hkv: int, T: int, lens=None, q_gain: float = 1.0,
+              outlier_p: float = 0.005, outlier_f: float = 30.0, seed: int = 0) -> dict:
+    """One decode step of attention over a cache of T token slots per sequence.
+
+    q BF16 bits [B,Hq,128] (N(0,1) times q_gain, which sharpens the softmax),
+    k and v BF16 bits [B,Hkv,T,128] (N(0,1) with outliers), lens int32 [B]
+    (given, or uniform over 1..T when None): the cached tokens of each sequence.
+    """
+    D = 128
+    rng = np.random.Generator(np.random.PCG64([seed, 0x4B56]))
+    q = rng.standard_normal((B, Hq, D), dtype=np.float32) * np.float32(q_gain)
+    k = activations(rng, B * Hkv * T, D, outlier_p, outlier_f).reshape(B, Hkv, T, D)
+    v = activations(rng, B * Hkv * T, D, outlier_p, outlier_f).reshape(B, Hkv, T, D)
+    if lens is None:
+        lens = rng.integers(1, T + 1, size=B)
+    return dict(q=to_bf16_bits(q), k=k, v=v, lens=np.asarray(lens, np.int32),
+                B=B, Hq=Hq, Hkv=Hkv, T=T, D=D)

@@ -20,7 +20,9 @@ Sources ("pages"):
        multiply-accumulate into INT32, FP32 scales applied last; per-tensor and
        per-channel weight scales as the coarser alternatives), sec. 1.3
        (MoE: few experts active per token) and sec. 4.4 (tokens dispatched to
-       their experts and combined back).
+       their experts and combined back); sec. 2.2, 3.4 and 4.1 (the INT8 KV
+       cache: one dynamic scale per key / value vector, dequantised inside the
+       attention kernel).
 
 The pages state the method in prose only. The constants of the quantisation
 rule (scale = amax/127 in float32, round-half-to-even, clamp to [-127, 127])
@@ -41,6 +43,8 @@ from .decode import (fp8_e4m3_table, ue8m0_value, e2m1_table, decode_fp8_block_r
 from .moe import gather_rows_ref, moe_combine_ref, moe_combine_fp32_ordered_ref
 from .channel import gemm_channel_ref, gemm_channel_fp32_ordered_ref, channel_total_ref
 from .a16 import gemm_w8a16_ref, gemm_bf16_ref, a16_tolerance, dequant_fp8_block_bf16_ref
+from .kvcache import (kv_quantize_ref, dequant_kv_ref, attention_int8kv_ref,
+                      attention_tolerance)
 
 __all__ = [
     "bf16_bits_to_f32", "quantize_rows_ref", "quantize_act_ref",
@@ -52,4 +56,5 @@ __all__ = [
     "gather_rows_ref", "moe_combine_ref", "moe_combine_fp32_ordered_ref",
     "gemm_channel_ref", "gemm_channel_fp32_ordered_ref", "channel_total_ref",
     "gemm_w8a16_ref", "gemm_bf16_ref", "a16_tolerance", "dequant_fp8_block_bf16_ref",
+    "kv_quantize_ref", "dequant_kv_ref", "attention_int8kv_ref", "attention_tolerance",
 ]

@@ -1,0 +1,208 @@
+"""Pins of the INT8 KV-cache oracle: quantisation on write and decode attention.
+
+The write is pinned to exact rational arithmetic (each (token, head) vector by
+itself), the attention to closed forms (one token, equal scores, two tokens),
+to torch's scaled-dot-product attention in float64 on the dequantised cache
+(grouped heads by repeat_interleave), to invariances, and the tolerance to an
+emulation of float32 / BF16 kernel arithmetic (which it must cover) and to
+plausible mistakes (which it must not).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_bit_amd import synth
+from oracle import (kv_quantize_ref, dequant_kv_ref, attention_int8kv_ref, attention_tolerance,
+                    bf16_bits_to_f32_ref, f32_to_bf16_bits_ref)
+from tests.exact import F, quant_rule_exact, f32_bits
+
+
+def _cache(rng_seed, B, Hq, Hkv, T, lens=None, q_gain=1.0):
+    d = synth.kv_inputs(B, Hq, Hkv, T, lens=lens, q_gain=q_gain, seed=rng_seed)
+    kc, ks = kv_quantize_ref(d["k"])
+    vc, vs = kv_quantize_ref(d["v"])
+    return d, kc, ks, vc, vs
+
+
+def test_write_quantises_each_vector_alone_exactly():
+    d = synth.kv_inputs(2, 2, 2, 6, seed=1)
+    k = d["k"].copy()
+    k[1, 0, 3, 17] = synth.to_bf16_bits(np.array([900.0], np.float32))[0]   # one outlier
+    kc, ks = kv_quantize_ref(k)
+    x = bf16_bits_to_f32_ref(k)
+    for b, h, t in [(0, 0, 0), (1, 0, 3), (1, 0, 2), (1, 1, 3), (0, 1, 5)]:
+        q, s = quant_rule_exact(x[b, h, t])
+        assert f32_bits(ks[b, h, t]) == f32_bits(s)
+        assert list(kc[b, h, t].astype(int)) == q
+    # the outlier sets only its own vector's scale
+    assert ks[1, 0, 3] == np.float32(900.0) / np.float32(127.0)
+    assert ks[1, 0, 2] < 1.0 and ks[1, 1, 3] < 1.0
+
+
+def test_single_token_returns_its_value():
+    d, kc, ks, vc, vs = _cache(2, 1, 4, 2, 8, lens=[1])
+    o, mag = attention_int8kv_ref(d["q"], kc, ks, vc, vs, d["lens"])
+    V0 = dequant_kv_ref(vc[0, :, 0], vs[0, :, 0])           # [Hkv, D]
+    for h in range(4):
+        assert np.array_equal(o[0, h], V0[h // 2])
+        assert np.array_equal(mag[0, h], np.abs(V0[h // 2]))
+
+
+def test_zero_query_averages_the_values():
+    d, kc, ks, vc, vs = _cache(3, 2, 2, 1, 40, lens=[40, 13])
+    q0 = np.zeros_like(d["q"])
+    o, _ = attention_int8kv_ref(q0, kc, ks, vc, vs, d["lens"])
+    for b, L in enumerate([40, 13]):
+        V = dequant_kv_ref(vc[b, 0, :L], vs[b, 0, :L])
+        assert np.allclose(o[b, 0], V.mean(axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_two_tokens_closed_form():
+    """Integer codes and power-of-two scales make the scores exact: z1 - z0 =
+    (2 - 1) * 8 / sqrt(128) * ... chosen so that w0 = 1 / (1 + e^(z1 - z0))."""
+    D = 128
+    q = np.zeros((1, 1, D), np.float32)
+    q[0, 0, :4] = 1.0
+    kc = np.zeros((1, 1, 2, D), np.int8)
+    kc[0, 0, 0, :4] = 1
+    kc[0, 0, 1, :4] = 3
+    ks = np.array([[[0.5, 0.5]]], np.float32)
+    vc = np.zeros((1, 1, 2, D), np.int8)
+    vc[0, 0, 0, :] = 10
+    vc[0, 0, 1, :] = -20
+    vs = np.array([[[0.25, 0.125]]], np.float32)
+    o, mag = attention_int8kv_ref(synth.to_bf16_bits(q), kc, ks, vc, vs, np.array([2]))
+    z0, z1 = 4 * 0.5 / np.sqrt(D), 12 * 0.5 / np.sqrt(D)
+    w0 = 1.0 / (1.0 + np.exp(z1 - z0))
+    expect = w0 * 2.5 + (1 - w0) * -2.5
+    assert np.allclose(o[0, 0], expect, rtol=1e-14)
+    assert np.allclose(mag[0, 0], 2.5, rtol=1e-14)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 1), (16, 2), (6, 3)])
+def test_matches_torch_sdpa_in_float64(Hq, Hkv):
+    B, T = 3, 70
+    d, kc, ks, vc, vs = _cache(10 + Hq, B, Hq, Hkv, T, lens=[70, 1, 33], q_gain=2.0)
+    o, _ = attention_int8kv_ref(d["q"], kc, ks, vc, vs, d["lens"])
+    q = torch.from_numpy(bf16_bits_to_f32_ref(d["q"]).astype(np.float64))
+    K = torch.from_numpy(dequant_kv_ref(kc, ks))
+    V = torch.from_numpy(dequant_kv_ref(vc, vs))
+    G = Hq // Hkv
+    for b, L in enumerate(d["lens"]):
+        Kb = K[b, :, :L].repeat_interleave(G, dim=0)[None]      # [1, Hq, L, D]
+        Vb = V[b, :, :L].repeat_interleave(G, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q[b][None, :, None, :], Kb, Vb)
+        assert np.allclose(o[b], ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_grouped_heads_read_their_own_kv_head():
+    """Query head h reads KV head h // G (not h % Hkv): distinct constant values
+    per KV head come back per group of G query heads."""
+    B, Hq, Hkv, T, D = 1, 6, 3, 5, 128
+    d, kc, ks, vc, _ = _cache(4, B, Hq, Hkv, T, lens=[5])
+    vc = np.ones_like(vc)
+    vs = np.zeros((B, Hkv, T), np.float32)
+    for h in range(Hkv):
+        vs[0, h, :] = 2.0 ** h
+    o, _ = attention_int8kv_ref(d["q"], kc, ks, vc, vs, d["lens"])
+    for h in range(Hq):
+        assert np.allclose(o[0, h], 2.0 ** (h // 2), rtol=1e-14)
+
+
+def test_empty_sequence_gives_zero_and_permutation_invariance():
+    d, kc, ks, vc, vs = _cache(5, 2, 2, 2, 24, lens=[0, 24])
+    o, mag = attention_int8kv_ref(d["q"], kc, ks, vc, vs, d["lens"])
+    assert not o[0].any() and not mag[0].any()
+    perm = np.random.default_rng(0).permutation(24)
+    o2, _ = attention_int8kv_ref(d["q"], kc[:, :, perm], ks[:, :, perm], vc[:, :, perm],
+                                 vs[:, :, perm], d["lens"])
+    assert np.allclose(o, o2, rtol=1e-12, atol=1e-15)
+    o3, _ = attention_int8kv_ref(d["q"], kc, ks, vc, vs * np.float32(8.0), d["lens"])
+    assert np.array_equal(o3, 8.0 * o)
+
+
+# ---- the tolerance against an emulation of the kernel's arithmetic ----------
+
+def _bf16_round(x32):
+    return bf16_bits_to_f32_ref(f32_to_bf16_bits_ref(x32.astype(np.float32)))
+
+
+def _emulate(qv, kc, ks, vc, vs, out_bf16, chunk=64, scale=None, drop_sv=False):
+    """Float32 steps of a split-softmax kernel for one query head: sequential
+    float32 dot products, scores times the key scale and log2(e)/sqrt(D), a
+    float32 exp2 against each chunk's own maximum, the weights times the value
+    scales rounded to BF16, float32 accumulation, then the chunks merged and
+    divided by the total weight."""
+    D = qv.shape[0]
+    L = kc.shape[0]
+    C = np.float32(np.log2(np.e) / (np.sqrt(D) if scale is None else scale))
+    prods = qv[None, :].astype(np.float32) * kc.astype(np.float32)       # exact
+    a = np.zeros(L, np.float32)
+    for dd in range(D):
+        a = (a + prods[:, dd]).astype(np.float32)
+    x = ((a * ks).astype(np.float32) * C).astype(np.float32)
+    Ms, Ls, Os = [], [], []
+    for c0 in range(0, L, chunk):
+        xs = x[c0:c0 + chunk]
+        m = xs.max()
+        p = np.exp2((xs - m).astype(np.float32)).astype(np.float32)
+        l = np.float32(0)
+        for pi in p:
+            l = np.float32(l + pi)
+        pw = _bf16_round(p if drop_sv else (p * vs[c0:c0 + chunk]).astype(np.float32))
+        o = np.zeros(D, np.float32)
+        for t in range(len(p)):
+            o = (o + pw[t] * vc[c0 + t].astype(np.float32)).astype(np.float32)
+        Ms.append(m), Ls.append(l), Os.append(o)
+    M = max(Ms)
+    f = [np.exp2(np.float32(m - M)).astype(np.float32) for m in Ms]
+    Lt = np.float32(sum(np.float32(l * fi) for l, fi in zip(Ls, f)))
+    Ot = np.zeros(D, np.float32)
+    for o, fi in zip(Os, f):
+        Ot = (Ot + o * fi).astype(np.float32)
+    out = (Ot / Lt).astype(np.float32)
+    return _bf16_round(out) if out_bf16 else out
+
+
+@pytest.mark.parametrize("q_gain,T", [(1.0, 4096), (4.0, 1000), (12.0, 300), (0.05, 2000)])
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_tolerance_covers_float32_and_bf16_kernel_arithmetic(q_gain, T, out_bf16):
+    d, kc, ks, vc, vs = _cache(20, 1, 2, 1, T, lens=[T], q_gain=q_gain)
+    o, mag = attention_int8kv_ref(d["q"], kc, ks, vc, vs, d["lens"])
+    qf = bf16_bits_to_f32_ref(d["q"])
+    tol = attention_tolerance(out_bf16)
+    for h in range(2):
+        e = _emulate(qf[0, h], kc[0, 0], ks[0, 0], vc[0, 0], vs[0, 0], out_bf16)
+        err = np.abs(e.astype(np.float64) - o[0, h])
+        assert np.all(err <= tol * mag[0, h]), float((err / mag[0, h]).max())
+
+
+def test_tolerance_rejects_plausible_mistakes():
+    """Leaving out the value scales or using 1/D for 1/sqrt(D) lands far outside
+    the bound; so does reading the wrong KV head."""
+    T = 512
+    d, kc, ks, vc, vs = _cache(21, 1, 2, 2, T, lens=[T], q_gain=2.0)
+    o, mag = attention_int8kv_ref(d["q"], kc, ks, vc, vs, d["lens"])
+    qf = bf16_bits_to_f32_ref(d["q"])
+    tol = attention_tolerance(False)
+
+    def worst(e, h=0):
+        return float(np.max(np.abs(e - o[0, h]) / (tol * mag[0, h])))
+
+    assert worst(_emulate(qf[0, 0], kc[0, 0], ks[0, 0], vc[0, 0], vs[0, 0], False)) <= 1.0
+    assert worst(_emulate(qf[0, 0], kc[0, 0], ks[0, 0], vc[0, 0], vs[0, 0], False,
+                          drop_sv=True)) > 100.0
+    assert worst(_emulate(qf[0, 0], kc[0, 0], ks[0, 0], vc[0, 0], vs[0, 0], False,
+                          scale=128.0)) > 10.0
+    assert worst(_emulate(qf[0, 0], kc[0, 1], ks[0, 1], vc[0, 1], vs[0, 1], False)) > 10.0
+
+
+def test_dequant_is_exact():
+    codes = np.array([[-127, -1, 0, 1, 127]], np.int8)
+    s = np.array([np.float32(0.1)], np.float32)
+    V = dequant_kv_ref(codes, s)
+    for j, c in enumerate(codes[0]):
+        assert F(V[0, j]) == F(s[0]) * int(c)
+    assert Fraction(V[0, 4]) == F(np.float32(0.1)) * 127
