@@ -40,8 +40,13 @@ _SIGNATURES = {
     "bsb_gemm_w8a8_g128_partials": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "bsb_gather_rows": [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "bsb_moe_combine": [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
+    "bsb_kv_cache_write": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p,
+                           _c_p, _c_p, _c_p, _c_p],
+    "bsb_attention_decode_int8kv": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                    _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_int, _c_p],
 }
-EXPORTED = tuple(_SIGNATURES) + ("bsb_status_string", "bsb_abi_version")
+EXPORTED = tuple(_SIGNATURES) + ("bsb_status_string", "bsb_abi_version",
+                                 "bsb_attention_workspace_bytes")
 
 _lib = None
 
@@ -61,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.bsb_status_string.restype = ctypes.c_char_p
         L.bsb_abi_version.argtypes = []
         L.bsb_abi_version.restype = _c_int
+        L.bsb_attention_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64]
+        L.bsb_attention_workspace_bytes.restype = _c_i64
         _lib = L
     return _lib
 
@@ -362,4 +369,86 @@ def moe_combine(y: torch.Tensor, row_of_pair: torch.Tensor, gate: torch.Tensor,
     with torch.cuda.device(dev):
         _check(lib().bsb_moe_combine(_ptr(y), _ptr(row_of_pair), _ptr(gate), T, topk, R, N,
                                      _ptr(out), _stream(dev)), "bsb_moe_combine")
+    return out
+
+
+KV_HEAD_DIM = 128
+KV_VBLOCK = 32
+
+
+def kv_cache_empty(B: int, Hkv: int, T: int, device) -> Tuple[torch.Tensor, ...]:
+    """Allocate (k_cache, k_scale, v_cache, v_scale) for B sequences of T token
+    slots (T a multiple of 64) over Hkv heads of dimension 128, in the layout of
+    bsb_kv_cache_write (contents undefined until written)."""
+    dev = torch.device(device)
+    return (torch.empty((B, Hkv, T, KV_HEAD_DIM), dtype=torch.int8, device=dev),
+            torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
+            torch.empty((B, Hkv, T // KV_VBLOCK, KV_VBLOCK * KV_HEAD_DIM), dtype=torch.int8,
+                        device=dev),
+            torch.empty((B, Hkv, T), dtype=torch.float32, device=dev))
+
+
+def _kv_shapes(k_cache, k_scale, v_cache, v_scale):
+    _need(k_cache, "k_cache", (torch.int8,))
+    if k_cache.dim() != 4 or k_cache.shape[3] != KV_HEAD_DIM:
+        raise ValueError("k_cache must be [B, Hkv, T, 128]")
+    B, Hkv, T, _ = k_cache.shape
+    dev = k_cache.device
+    _need(k_scale, "k_scale", (torch.float32,), (B, Hkv, T), dev)
+    _need(v_cache, "v_cache", (torch.int8,), (B, Hkv, T // KV_VBLOCK, KV_VBLOCK * KV_HEAD_DIM), dev)
+    _need(v_scale, "v_scale", (torch.float32,), (B, Hkv, T), dev)
+    return B, Hkv, T, dev
+
+
+def kv_cache_write(k: torch.Tensor, v: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor,
+                   k_cache: torch.Tensor, k_scale: torch.Tensor, v_cache: torch.Tensor,
+                   v_scale: torch.Tensor) -> None:
+    """Quantise n new tokens' keys and values k, v [n, Hkv, 128] (BF16) per vector and
+    write them to slot pos[i] of sequence seq[i] (int32 [n])."""
+    B, Hkv, T, dev = _kv_shapes(k_cache, k_scale, v_cache, v_scale)
+    _need(k, "k", _BF16_BITS, None, dev)
+    if k.dim() != 3 or k.shape[1:] != (Hkv, KV_HEAD_DIM):
+        raise ValueError("k must be [n, Hkv, 128]")
+    n = k.shape[0]
+    _need(v, "v", _BF16_BITS, (n, Hkv, KV_HEAD_DIM), dev)
+    _need(seq, "seq", (torch.int32,), (n,), dev)
+    _need(pos, "pos", (torch.int32,), (n,), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_kv_cache_write(_ptr(k), _ptr(v), _ptr(seq), _ptr(pos), n, B, Hkv, T,
+                                        KV_HEAD_DIM, _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+                                        _ptr(v_scale), _stream(dev)), "bsb_kv_cache_write")
+
+
+def attention_workspace_bytes(B: int, Hq: int, max_len: int) -> int:
+    n = lib().bsb_attention_workspace_bytes(B, Hq, max_len)
+    if n < 0:
+        raise ValueError("invalid attention sizes")
+    return n
+
+
+def attention_decode_int8kv(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor,
+                            v_cache: torch.Tensor, v_scale: torch.Tensor, lens: torch.Tensor,
+                            max_len: int, out_dtype=torch.bfloat16,
+                            out: Optional[torch.Tensor] = None,
+                            work: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention of q [B, Hq, 128] (BF16) over the INT8 cache, lens int32 [B]
+    cached tokens per sequence (<= max_len); returns out [B, Hq, 128]."""
+    B, Hkv, T, dev = _kv_shapes(k_cache, k_scale, v_cache, v_scale)
+    _need(q, "q", _BF16_BITS, None, dev)
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != KV_HEAD_DIM:
+        raise ValueError("q must be [B, Hq, 128]")
+    Hq = q.shape[1]
+    _need(lens, "lens", (torch.int32,), (B,), dev)
+    code = _out_code(out_dtype)
+    out = torch.empty((B, Hq, KV_HEAD_DIM), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", (out_dtype,), (B, Hq, KV_HEAD_DIM), dev)
+    nbytes = attention_workspace_bytes(B, Hq, max_len)
+    if work is None:
+        work = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=dev)
+    _need(work, "work", (torch.float32,), None, dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_attention_decode_int8kv(
+            _ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(lens),
+            B, Hq, Hkv, T, KV_HEAD_DIM, max_len, _ptr(work), work.numel() * 4, _ptr(out), code,
+            _stream(dev)), "bsb_attention_decode_int8kv")
     return out

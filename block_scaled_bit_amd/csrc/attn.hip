@@ -1,0 +1,332 @@
+// INT8 KV cache on gfx950: quantisation on write, and decode attention with
+// the dequantisation fused into the attention kernel.
+//
+// [P3] sec. 3.4: one dynamic scale per key vector and per value vector, taken
+// when the vector is written; attention multiplies the INT8 keys and values by
+// their scales while reading them, inside the attention kernel (sec. 4.1: a
+// blockwise attention that dequantises the INT8 cache itself), so the cache is
+// read once and never expanded in memory.
+//
+// Cache layout (head dimension 128; T = token slots per sequence, a multiple of 64):
+//   k_cache [B, Hkv, T, 128] INT8, token-major (one 128-byte row per token)
+//   v_cache [B, Hkv, T/32, 4096] INT8: 32-token blocks; token tau of a block,
+//           dimension d at byte (((tau%16)/4)*16 + d%16)*64 + (d/16)*8 + (tau/16)*4 + tau%4
+//   k_scale, v_scale [B, Hkv, T] float32
+// The V block order is the matrix cores' operand order for the P.V product
+// (lane l of a wave reads the block's bytes 64l .. 64l+63), so a block streams
+// in with one coalesced 4 KB read and no transpose.
+//
+// Decode attention (one query token per sequence, grouped-query heads, up to
+// 16 query heads per KV head): a workgroup of 8 waves takes 512 cached tokens
+// of one (sequence, KV head); each wave takes 64 tokens. Per wave, all of its
+// operands are loaded at once (keys, values, their scales, the queries), then
+//   scores  S^T[token, head] = K . Q^T   on v_mfma_f32_16x16x32_bf16, the INT8
+//           codes converted to BF16 in registers (exact), the query in BF16;
+//   x = S * k_scale * log2(e)/sqrt(128) (float32), masked past the sequence;
+//   p = exp2(x - max) per head (float32), l = sum p;
+//   o^T[d, head] += V^T . (p * v_scale)^T on the same MFMA, the weights times
+//           the value scales rounded to BF16, the value codes converted exactly.
+// The 8 wave results are merged in LDS (max, rescaled sums) into one partial
+// (m, l, o[128]) per head and split; a second kernel merges the splits and
+// divides by the total weight.
+#include "device_common.h"
+#include "launch.h"
+
+namespace bsb {
+
+namespace {
+
+constexpr int kHD = 128;                       // head dimension
+constexpr int kVBlk = 32;                      // tokens per V block
+constexpr int kAttnWaves = 8;                  // waves per attention workgroup
+constexpr int kWaveTok = 64;                   // tokens per wave
+constexpr int kSplitTok = kAttnWaves * kWaveTok;
+constexpr int kPart = kHD + 2;                 // floats per (head, split) partial: o, m, l
+constexpr int kORow = kHD + 4;                 // LDS row stride of the wave partials
+constexpr float kNegInf = -__builtin_huge_valf();
+// log2(e) / sqrt(128), rounded to float32
+constexpr float kScoreScale = (float)(1.4426950408889634 / 11.313708498984761);
+
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int vblk_off(int tau, int d) {
+    return ((((tau & 15) >> 2) * 16 + (d & 15)) * 64) + (d >> 4) * 8 + (tau >> 4) * 4 + (tau & 3);
+}
+
+// eight INT8 codes (little-endian in two dwords) -> eight BF16 values (exact)
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = (__bf16)(float)(int8_t)(lo >> (8 * e));
+        r[4 + e] = (__bf16)(float)(int8_t)(hi >> (8 * e));
+    }
+    return r;
+}
+
+__device__ __forceinline__ uint32_t word(const uint4 &v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// One wave per (token, KV head, K or V) vector of 128 BF16 values: two per lane.
+__global__ void __launch_bounds__(256)
+kv_write_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, int64_t n,
+                int B, int Hkv, int T, int8_t *__restrict__ kc, float *__restrict__ ks,
+                int8_t *__restrict__ vc, float *__restrict__ vs) {
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (item >= n * Hkv * 2) return;                     // whole wave
+    const int which = (int)(item & 1);
+    const int64_t th = item >> 1;                        // token * Hkv + head
+    const int64_t tok = th / Hkv;
+    const int h = (int)(th - tok * Hkv);
+    const int b = seq[tok], t = pos[tok];
+    if (b < 0 || b >= B || t < 0 || t >= T) return;     // whole wave: nothing written
+    const uint32_t w = reinterpret_cast<const uint32_t *>((which ? v : k) + th * kHD)[lane];
+    uint32_t amax = w & 0x7FFFu;
+    amax = amax > ((w >> 16) & 0x7FFFu) ? amax : ((w >> 16) & 0x7FFFu);
+    amax = group_max_u32(amax, kWave);
+    const float s = absmax_scale(bf16_to_f32(amax));
+    int c0 = 0, c1 = 0;
+    if (amax != 0) {
+        c0 = quant_elem(bf16_to_f32(w & 0xFFFFu), s);
+        c1 = quant_elem(bf16_to_f32(w >> 16), s);
+    }
+    const int64_t vec = ((int64_t)b * Hkv + h) * T + t;
+    if (which == 0) {
+        reinterpret_cast<uint16_t *>(kc + vec * kHD)[lane] =
+            (uint16_t)((uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8));
+        if (lane == 0) ks[vec] = s;
+    } else {
+        int8_t *blk = vc + (((int64_t)b * Hkv + h) * (T / kVBlk) + t / kVBlk) * (kVBlk * kHD);
+        const int tau = t % kVBlk;
+        blk[vblk_off(tau, 2 * lane)] = (int8_t)c0;
+        blk[vblk_off(tau, 2 * lane + 1)] = (int8_t)c1;
+        if (lane == 0) vs[vec] = s;
+    }
+}
+
+// grid (splits, B * Hkv); 512 threads. part: [B*Hkv, splits, G, kPart] float32.
+__global__ void __launch_bounds__(512)
+attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
+                  const float *__restrict__ ks, const int8_t *__restrict__ vc,
+                  const float *__restrict__ vs, const int32_t *__restrict__ lens, int Hq, int Hkv,
+                  int T, int max_len, float *__restrict__ part) {
+    __shared__ __align__(16) float s_o[kAttnWaves][16][kORow];
+    __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
+
+    const int split = blockIdx.x, nsplit = gridDim.x;
+    const int bh = blockIdx.y;
+    const int b = bh / Hkv, hk = bh - b * Hkv;
+    const int G = Hq / Hkv;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, grp = lane >> 4;
+    int L = lens[b];
+    const int lim = max_len < T ? max_len : T;
+    L = L < 0 ? 0 : (L > lim ? lim : L);
+    const int t0 = split * kSplitTok + wave * kWaveTok;
+
+    float m = kNegInf, l = 0.0f;
+    v4f_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (t0 < L) {   // whole wave; then t0 + 64 <= T, so every load below is in range
+        const int8_t *kb = kc + ((int64_t)bh * T + t0) * kHD;
+        const int8_t *vb = vc + ((int64_t)bh * (T / kVBlk) + t0 / kVBlk) * (kVBlk * kHD);
+        const float *ksb = ks + (int64_t)bh * T + t0;
+        const float *vsb = vs + (int64_t)bh * T + t0;
+        uint4 kd[4][2], vd[2][4], qd[4];
+        float4 skv[4], svv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                kd[c][j] = *reinterpret_cast<const uint4 *>(kb + (16 * c + col) * kHD + 32 * grp +
+                                                            16 * j);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                vd[s][j] = *reinterpret_cast<const uint4 *>(vb + s * (kVBlk * kHD) + lane * 64 +
+                                                            16 * j);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            skv[c] = *reinterpret_cast<const float4 *>(ksb + 16 * c + 4 * grp);
+            svv[c] = *reinterpret_cast<const float4 *>(vsb + 16 * c + 4 * grp);
+        }
+        const bool hv = col < G;
+        const uint16_t *qr = q + ((int64_t)b * Hq + hk * G + (hv ? col : 0)) * kHD + 32 * grp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qd[j] = hv ? *reinterpret_cast<const uint4 *>(qr + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
+
+        // scores: tile c holds tokens t0 + 16c + 4grp + r (rows) for head col
+        float x[4][4];
+        float mloc = kNegInf;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            v4f_t acc = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint4 &kk = kd[c][s >> 1];
+                const bf16x8 a = i8x8_to_bf16(word(kk, 2 * (s & 1)), word(kk, 2 * (s & 1) + 1));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qd[s]),
+                                                              acc, 0, 0, 0);
+            }
+            const float skr[4] = {skv[c].x, skv[c].y, skv[c].z, skv[c].w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float sv = (acc[r] * skr[r]) * kScoreScale;
+                x[c][r] = (t0 + 16 * c + 4 * grp + r < L) ? sv : kNegInf;
+                mloc = __builtin_fmaxf(mloc, x[c][r]);
+            }
+        }
+        mloc = __builtin_fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+        mloc = __builtin_fmaxf(mloc, __shfl_xor(mloc, 32, kWave));   // finite: token t0 is valid
+        float p[4][4];
+        float lsum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[c][r] = __builtin_amdgcn_exp2f(x[c][r] - mloc);
+                lsum += p[c][r];
+            }
+        lsum += __shfl_xor(lsum, 16, kWave);
+        lsum += __shfl_xor(lsum, 32, kWave);
+        m = mloc;
+        l = lsum;
+
+        // P.V over two 32-token blocks; slot j < 4 is token 32s + 4grp + j,
+        // slot 4 + j is token 32s + 16 + 4grp + j (the V block order above)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const float sva[4] = {svv[2 * s].x, svv[2 * s].y, svv[2 * s].z, svv[2 * s].w};
+            const float svb[4] = {svv[2 * s + 1].x, svv[2 * s + 1].y, svv[2 * s + 1].z,
+                                  svv[2 * s + 1].w};
+            const int ta = t0 + 32 * s + 4 * grp, tb = ta + 16;
+            bf16x8 pw;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pw[j] = (__bf16)(ta + j < L ? p[2 * s][j] * sva[j] : 0.0f);
+                pw[4 + j] = (__bf16)(tb + j < L ? p[2 * s + 1][j] * svb[j] : 0.0f);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint4 &vv = vd[s][i >> 1];
+                const bf16x8 a = i8x8_to_bf16(word(vv, 2 * (i & 1)), word(vv, 2 * (i & 1) + 1));
+                o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pw, o[i], 0, 0, 0);
+            }
+        }
+    }
+
+    // merge the 8 waves: lane (col, grp) holds o[head col][16i + 4grp + r]
+    if (grp == 0) {
+        s_m[wave][col] = m;
+        s_l[wave][col] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<float4 *>(&s_o[wave][col][16 * i + 4 * grp]) =
+            make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
+    __syncthreads();
+    float *pb = part + ((int64_t)bh * nsplit + split) * G * kPart;
+    for (int idx = threadIdx.x; idx < G * kHD; idx += kAttnWaves * kWave) {
+        const int h = idx / kHD, d = idx - h * kHD;
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) M = __builtin_fmaxf(M, s_m[w][h]);
+        float O = 0.0f, Ls = 0.0f;
+        if (M != kNegInf) {
+#pragma unroll
+            for (int w = 0; w < kAttnWaves; ++w) {
+                const float f = __builtin_amdgcn_exp2f(s_m[w][h] - M);   // 0 for an empty wave
+                O += s_o[w][h][d] * f;
+                Ls += s_l[w][h] * f;
+            }
+        }
+        pb[h * kPart + d] = O;
+        if (d == 0) {
+            pb[h * kPart + kHD] = M;
+            pb[h * kPart + kHD + 1] = Ls;
+        }
+    }
+}
+
+// one wave per (sequence, query head); lane holds dimensions 2 lane, 2 lane + 1
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(64)
+attn_combine_kernel(const float *__restrict__ part, int Hq, int Hkv, int nsplit,
+                    void *__restrict__ out) {
+    const int bq = blockIdx.x;
+    const int Hq_ = Hq, G = Hq / Hkv;
+    const int b = bq / Hq_, hq = bq - b * Hq_;
+    const int hk = hq / G, h = hq - hk * G;
+    const int lane = threadIdx.x;
+    const int64_t stride = (int64_t)G * kPart;
+    const float *pp = part + ((int64_t)(b * Hkv + hk) * nsplit) * stride + h * kPart;
+    float M = kNegInf;
+    for (int s = 0; s < nsplit; ++s) M = __builtin_fmaxf(M, pp[s * stride + kHD]);
+    float o0 = 0.0f, o1 = 0.0f;
+    if (M != kNegInf) {
+        float Lt = 0.0f;
+        for (int s = 0; s < nsplit; ++s) {
+            const float f = __builtin_amdgcn_exp2f(pp[s * stride + kHD] - M);
+            Lt += pp[s * stride + kHD + 1] * f;
+            const float2 v = *reinterpret_cast<const float2 *>(pp + s * stride + 2 * lane);
+            o0 += v.x * f;
+            o1 += v.y * f;
+        }
+        o0 = o0 / Lt;
+        o1 = o1 / Lt;
+    }
+    const int64_t oi = (int64_t)bq * kHD + 2 * lane;
+    if (OUT_BF16) {
+        reinterpret_cast<uint32_t *>(out)[oi >> 1] = f32_to_bf16_rne(o0) | (f32_to_bf16_rne(o1) << 16);
+    } else {
+        *reinterpret_cast<float2 *>(reinterpret_cast<float *>(out) + oi) = make_float2(o0, o1);
+    }
+}
+
+}  // namespace
+
+int64_t attention_splits(int64_t max_len) { return (max_len + kSplitTok - 1) / kSplitTok; }
+
+int64_t attention_workspace_floats(int64_t B, int64_t Hq, int64_t max_len) {
+    return B * Hq * attention_splits(max_len) * kPart;
+}
+
+hipError_t launch_kv_cache_write(const uint16_t *k, const uint16_t *v, const int32_t *seq,
+                                 const int32_t *pos, int64_t n, int B, int Hkv, int T, int8_t *kc,
+                                 float *ks, int8_t *vc, float *vs, hipStream_t stream) {
+    const int64_t items = n * Hkv * 2;
+    const int64_t blocks = (items + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    kv_write_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(k, v, seq, pos, n, B, Hkv, T, kc,
+                                                                ks, vc, vs);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_decode(const uint16_t *q, const int8_t *kc, const float *ks,
+                                   const int8_t *vc, const float *vs, const int32_t *lens, int B,
+                                   int Hq, int Hkv, int T, int max_len, float *work, void *out,
+                                   int out_bf16, hipStream_t stream) {
+    const int64_t ns = attention_splits(max_len);
+    if (ns > 0) {   // max_len == 0: no split to run, the combine writes zeros
+        attn_split_kernel<<<dim3((unsigned)ns, (unsigned)(B * Hkv)), kAttnWaves * kWave, 0,
+                            stream>>>(q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (out_bf16)
+        attn_combine_kernel<true><<<dim3((unsigned)(B * Hq)), 64, 0, stream>>>(work, Hq, Hkv,
+                                                                               (int)ns, out);
+    else
+        attn_combine_kernel<false><<<dim3((unsigned)(B * Hq)), 64, 0, stream>>>(work, Hq, Hkv,
+                                                                                (int)ns, out);
+    return hipGetLastError();
+}
+
+}  // namespace bsb

@@ -51,4 +51,17 @@ hipError_t launch_moe_combine(const uint16_t *y, const int32_t *row_of_pair, con
                               int64_t T, int64_t topk, int64_t R, int64_t N, uint16_t *out,
                               hipStream_t stream);
 
+// INT8 KV cache (head dimension 128): quantise-on-write and decode attention.
+int64_t attention_splits(int64_t max_len);
+int64_t attention_workspace_floats(int64_t B, int64_t Hq, int64_t max_len);
+
+hipError_t launch_kv_cache_write(const uint16_t *k, const uint16_t *v, const int32_t *seq,
+                                 const int32_t *pos, int64_t n, int B, int Hkv, int T, int8_t *kc,
+                                 float *ks, int8_t *vc, float *vs, hipStream_t stream);
+
+hipError_t launch_attention_decode(const uint16_t *q, const int8_t *kc, const float *ks,
+                                   const int8_t *vc, const float *vs, const int32_t *lens, int B,
+                                   int Hq, int Hkv, int T, int max_len, float *work, void *out,
+                                   int out_bf16, hipStream_t stream);
+
 }  // namespace bsb

@@ -260,6 +260,70 @@ bsb_status bsb_moe_combine(const uint16_t *y, const int32_t *row_of_pair,
                            const float *gate, int64_t T, int64_t topk,
                            int64_t R, int64_t N, uint16_t *out, void *stream);
 
+/*
+ * INT8 KV cache ([P3] sec. 2.2 / 3.4): one dynamic scale per key vector and
+ * per value vector (one token of one KV head, D = 128 values), taken on write
+ * by the rule of bsb_quantize_act over those 128 values.
+ * Cache layout (T = token slots per sequence, a multiple of 64, 64 <= T < 2^24):
+ *   k_cache [B, Hkv, T, 128] int8, token-major
+ *   v_cache [B, Hkv, T/32, 4096] int8: blocks of 32 tokens; token tau of a
+ *           block and dimension d sit at byte
+ *           (((tau%16)/4)*16 + d%16)*64 + (d/16)*8 + (tau/16)*4 + tau%4
+ *   k_scale, v_scale [B, Hkv, T] float32
+ * The caller allocates and owns every buffer; nothing is written outside the
+ * slots named by (seq, pos).
+ */
+
+/*
+ * Write n new tokens' keys and values into the cache, quantised.
+ *   k_bf16, v_bf16 [n, Hkv, 128] BF16 bits
+ *   seq, pos [n] int32 (device): token i goes to sequence seq[i], slot pos[i];
+ *            entries outside [0, B) x [0, T) are skipped (nothing written);
+ *            two entries naming the same slot race.
+ * n == 0 is a no-op. D must be 128, else BSB_ERR_INVALID_ARG.
+ */
+bsb_status bsb_kv_cache_write(const uint16_t *k_bf16, const uint16_t *v_bf16,
+                              const int32_t *seq, const int32_t *pos, int64_t n,
+                              int64_t B, int64_t Hkv, int64_t T, int64_t D,
+                              int8_t *k_cache, float *k_scale,
+                              int8_t *v_cache, float *v_scale, void *stream);
+
+/*
+ * Bytes of float32 workspace bsb_attention_decode_int8kv needs:
+ * B * Hq * ceil(max_len / 512) * 130 * 4.
+ */
+int64_t bsb_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t max_len);
+
+/*
+ * Decode attention of one query token per sequence over the INT8 cache, the
+ * dequantisation fused into the kernel ([P3] sec. 3.4, sec. 4.1):
+ *     K[t,d] = k_scale[t] * k_cache[t,d],  V[t,d] = v_scale[t] * v_cache[t,d]
+ *     z[t] = q . K[t] / sqrt(128),  w = softmax(z over t < lens[b]),
+ *     out[b, h, :] = sum_t w[t] * V[t, :]
+ * query head h reads KV head h / (Hq / Hkv); lens[b] == 0 gives zeros. The
+ * matrix cores take the BF16 query and the INT8 codes converted exactly to
+ * BF16, with float32 accumulation; scores, exponentials and sums are float32;
+ * the weights times the value scales enter the P.V product rounded to BF16.
+ * Results are within 2^-7 * sum_t w[t] |V[t,d]| of the exact value (plus
+ * 2^-8 of that for a BF16 output) for score terms sum_d |q[d] K[t,d]| / sqrt(128)
+ * up to ~100.
+ *   q_bf16   [B, Hq, 128] BF16 bits; 1 <= Hq / Hkv <= 16, Hq % Hkv == 0
+ *   lens     [B] int32 (device): cached tokens per sequence; values are
+ *            clamped to [0, min(max_len, T)] (tokens past max_len are not read)
+ *   max_len  host bound on lens that sizes the launch, 0 <= max_len <= T
+ *   work     float32 scratch of bsb_attention_workspace_bytes(B, Hq, max_len)
+ *            bytes (contents on entry ignored); work_bytes its size
+ *   out      [B, Hq, 128] BF16 bits or float32 per `out_dtype` (written)
+ * B * Hkv <= 65535, B * Hq < 2^31; other errors as bsb_gemm_w8a8_g128.
+ */
+bsb_status bsb_attention_decode_int8kv(const uint16_t *q_bf16,
+                                       const int8_t *k_cache, const float *k_scale,
+                                       const int8_t *v_cache, const float *v_scale,
+                                       const int32_t *lens, int64_t B, int64_t Hq,
+                                       int64_t Hkv, int64_t T, int64_t D, int64_t max_len,
+                                       float *work, int64_t work_bytes,
+                                       void *out, bsb_out_dtype out_dtype, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *bsb_status_string(bsb_status s);
 

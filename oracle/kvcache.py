@@ -75,8 +75,6 @@ def attention_int8kv_ref(q_bits, k_codes, k_scales, v_codes, v_scales, lens):
     if Dk != D or v_codes.shape != k_codes.shape or Hq % Hkv:
         raise ValueError("q [B,Hq,D], k/v [B,Hkv,T,D] with Hq a multiple of Hkv required")
     G = Hq // Hkv
-    K = dequant_kv_ref(k_codes, k_scales)
-    V = dequant_kv_ref(v_codes, v_scales)
     o = np.zeros((B, Hq, D))
     mag = np.zeros((B, Hq, D))
     for b in range(B):
@@ -85,13 +83,15 @@ def attention_int8kv_ref(q_bits, k_codes, k_scales, v_codes, v_scales, lens):
             raise ValueError("lens out of range")
         if L == 0:
             continue
-        for h in range(Hq):
-            kv = h // G
-            z = K[b, kv, :L] @ q[b, h] / np.sqrt(D)
-            e = np.exp(z - z.max())
-            w = e / e.sum()
-            o[b, h] = w @ V[b, kv, :L]
-            mag[b, h] = w @ np.abs(V[b, kv, :L])
+        for kv in range(Hkv):       # only the attended slots are read
+            K = dequant_kv_ref(k_codes[b, kv, :L], k_scales[b, kv, :L])
+            V = dequant_kv_ref(v_codes[b, kv, :L], v_scales[b, kv, :L])
+            for h in range(kv * G, (kv + 1) * G):
+                z = K @ q[b, h] / np.sqrt(D)
+                e = np.exp(z - z.max())
+                w = e / e.sum()
+                o[b, h] = w @ V
+                mag[b, h] = w @ np.abs(V)
     return o, mag
 
 

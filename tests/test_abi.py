@@ -161,3 +161,42 @@ def test_bf16_activation_routes_argument_checks(L):
         assert w16(A, A, A, 64, 8, 128, A, 1, None) == UNSUPPORTED
         assert b16(A, A, 1, 8, 128, A, 0, None) == UNSUPPORTED
         assert dq(A, A, 128, 128, 1, A, None) == UNSUPPORTED
+
+
+def test_kv_cache_argument_checks(L):
+    """KV cache write and decode attention: head dimension 128, T a multiple of 64,
+    at most 16 query heads per KV head, max_len <= T, a large enough workspace;
+    nothing to write is a no-op; with valid arguments and no gfx950 device they
+    fail fast."""
+    wr, at, wb = L.bsb_kv_cache_write, L.bsb_attention_decode_int8kv, L.bsb_attention_workspace_bytes
+    assert wb(2, 16, 1000) == 2 * 16 * 2 * 130 * 4                    # two 512-token splits
+    assert wb(2, 16, 0) == 0 and wb(0, 16, 10) == -1 and wb(2, 16, -1) == -1
+    assert wr(A, A, A, A, 3, 2, 4, 128, 64, A, A, A, A, None) == INVALID     # D != 128
+    assert wr(A, A, A, A, 3, 2, 4, 96, 128, A, A, A, A, None) == INVALID     # T % 64
+    assert wr(A, A, A, None, 3, 2, 4, 128, 128, A, A, A, A, None) == INVALID
+    assert wr(A, A, A, A, 3, 2, 4, 128, 128, A, A, U, A, None) == MISALIGNED
+    assert wr(None, None, None, None, 0, 2, 4, 128, 128, None, None, None, None, None) == OK
+    need = wb(2, 16, 128)
+    ok = (A, A, A, A, A, A, 2, 16, 4, 128, 128, 128, A, need, A, 0, None)
+
+    def call(**kw):
+        names = ["q", "kc", "ks", "vc", "vs", "lens", "B", "Hq", "Hkv", "T", "D", "max_len",
+                 "work", "work_bytes", "out", "dtype", "stream"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return at(*[args[n] for n in names])
+
+    assert call(Hq=15) == INVALID                                   # Hq % Hkv
+    assert call(Hq=68, Hkv=4) == INVALID                            # 17 heads per KV head
+    assert call(D=64) == INVALID
+    assert call(T=100) == INVALID
+    assert call(max_len=129) == INVALID                             # above T
+    assert call(work_bytes=need - 4) == INVALID
+    assert call(dtype=2) == INVALID
+    assert call(lens=None) == INVALID
+    assert call(B=65536 // 4 + 1) == INVALID                        # B * Hkv > 65535
+    assert call(vs=U) == MISALIGNED
+    if not torch.cuda.is_available():
+        assert call() == UNSUPPORTED
+        assert call(max_len=0, work=None, work_bytes=0) == UNSUPPORTED
+        assert wr(A, A, A, A, 3, 2, 4, 128, 128, A, A, A, A, None) == UNSUPPORTED

@@ -1,0 +1,225 @@
+"""GPU parity: the INT8 KV cache (quantisation on write) and decode attention over it.
+
+The write is integer work: codes and scales are compared bit for bit with the
+oracle's per-vector rule, and slots the call does not name must keep their
+contents. The attention is compared with the oracle's float64 definition on the
+same cache within the bound derived for the kernel's float32 / BF16 arithmetic,
+|o - o64| <= t * sum_t w[t] |V[t,d]|. The cache layout is the one documented in
+include/bsb.h; these tests encode and decode it on the host.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_bit_amd as bsb
+from block_scaled_bit_amd import synth
+from oracle import (kv_quantize_ref, attention_int8kv_ref, attention_tolerance,
+                    bf16_bits_to_f32_ref)
+from tests.gpu_util import require_gpu, dev, dev_bf16, host, say
+
+pytestmark = pytest.mark.gpu
+
+D, VB = 128, 32
+_tau = np.arange(VB)[:, None]
+_d = np.arange(D)[None, :]
+V_OFF = (((_tau % 16) // 4) * 16 + _d % 16) * 64 + (_d // 16) * 8 + (_tau // 16) * 4 + _tau % 4
+
+
+def v_encode(vc):
+    """[B, H, T, 128] int8 -> the V block layout [B, H, T/32, 4096]."""
+    B, H, T, _ = vc.shape
+    out = np.empty((B, H, T // VB, VB * D), np.int8)
+    out[..., V_OFF] = vc.reshape(B, H, T // VB, VB, D)
+    return out
+
+
+def v_decode(vb):
+    B, H, NB, _ = vb.shape
+    return vb[..., V_OFF].reshape(B, H, NB * VB, D)
+
+
+def test_v_layout_is_a_permutation():
+    assert np.array_equal(np.sort(V_OFF.ravel()), np.arange(VB * D))
+    x = np.random.default_rng(0).integers(-127, 128, size=(2, 3, 64, D)).astype(np.int8)
+    assert np.array_equal(v_decode(v_encode(x)), x)
+
+
+def _poisoned_cache(B, H, T, d):
+    kc, ks, vc, vs = bsb.kv_cache_empty(B, H, T, d)
+    kc.fill_(0x55)
+    vc.fill_(0x55)
+    ks.fill_(-1.0)
+    vs.fill_(-2.0)
+    return kc, ks, vc, vs
+
+
+@pytest.mark.parametrize("B,H,T,frac", [(3, 2, 128, 1.0), (2, 8, 192, 0.4), (1, 1, 64, 0.1)])
+def test_write_is_bit_exact_and_touches_only_named_slots(B, H, T, frac):
+    d = require_gpu()
+    rng = np.random.default_rng(B * 100 + H)
+    inp = synth.kv_inputs(B, H, H, T, seed=B + H)
+    k, v = inp["k"], inp["v"]
+    # special vectors: all zero, tiny (subnormal scale), one huge outlier
+    k[0, 0, 1] = 0
+    v[0, 0, 2] = synth.to_bf16_bits(np.full(D, 1e-37, np.float32))
+    k[-1, -1, 3, 5] = synth.to_bf16_bits(np.array([3e4], np.float32))[0]
+    slots = [(b, t) for b in range(B) for t in range(T) if rng.random() < frac]
+    seq = np.array([s[0] for s in slots] + [B, -1, 0], np.int32)      # last three: out of range
+    pos = np.array([s[1] for s in slots] + [0, 0, T], np.int32)
+    kn = np.stack([k[b, :, t] for b, t in slots] + [k[0, :, 0]] * 3)   # [n, H, D]
+    vn = np.stack([v[b, :, t] for b, t in slots] + [v[0, :, 0]] * 3)
+    kc, ks, vc, vs = _poisoned_cache(B, H, T, d)
+    say(f"kv write B={B} H={H} T={T} n={len(seq)}")
+    bsb.kv_cache_write(dev_bf16(kn, d), dev_bf16(vn, d), dev(seq, d), dev(pos, d), kc, ks, vc, vs)
+    torch.cuda.synchronize()
+    qk, sk = kv_quantize_ref(k)
+    qv, sv = kv_quantize_ref(v)
+    gk, gks, gv, gvs = host(kc), host(ks), v_decode(host(vc)), host(vs)
+    written = np.zeros((B, T), bool)
+    for b, t in slots:
+        written[b, t] = True
+    for b in range(B):
+        for t in range(T):
+            if written[b, t]:
+                assert np.array_equal(gk[b, :, t], qk[b, :, t]), (b, t)
+                assert np.array_equal(gv[b, :, t], qv[b, :, t]), (b, t)
+                assert np.array_equal(gks[b, :, t].view(np.uint32), sk[b, :, t].view(np.uint32))
+                assert np.array_equal(gvs[b, :, t].view(np.uint32), sv[b, :, t].view(np.uint32))
+            else:
+                assert (gk[b, :, t] == 0x55).all() and (gv[b, :, t] == 0x55).all(), (b, t)
+                assert (gks[b, :, t] == -1.0).all() and (gvs[b, :, t] == -2.0).all()
+
+
+def test_decode_step_appends_one_token_per_sequence():
+    d = require_gpu()
+    B, H, T = 4, 2, 128
+    lens = np.array([5, 0, 127, 64], np.int32)
+    inp = synth.kv_inputs(B, H, H, T, seed=7)
+    kc, ks, vc, vs = _poisoned_cache(B, H, T, d)
+    seq = np.arange(B, dtype=np.int32)
+    kn = inp["k"][np.arange(B), :, lens]
+    vn = inp["v"][np.arange(B), :, lens]
+    bsb.kv_cache_write(dev_bf16(kn, d), dev_bf16(vn, d), dev(seq, d), dev(lens, d), kc, ks, vc, vs)
+    torch.cuda.synchronize()
+    qk, sk = kv_quantize_ref(kn)
+    qv, sv = kv_quantize_ref(vn)
+    gk, gv, gks = host(kc), v_decode(host(vc)), host(ks)
+    for b in range(B):
+        assert np.array_equal(gk[b, :, lens[b]], qk[b])
+        assert np.array_equal(gv[b, :, lens[b]], qv[b])
+        assert np.array_equal(gks[b, :, lens[b]], sk[b])
+
+
+def _upload_cache(kc, ks, vc, vs, d):
+    return dev(kc, d), dev(ks, d), dev(v_encode(vc), d), dev(vs, d)
+
+
+def _attn_case(B, Hq, Hkv, T, lens, max_len, seed, q_gain=1.0):
+    lens = np.asarray(lens, np.int32)
+    inp = synth.kv_inputs(B, Hq, Hkv, T, lens=lens, q_gain=q_gain, seed=seed)
+    kc, ks = kv_quantize_ref(inp["k"])
+    vc, vs = kv_quantize_ref(inp["v"])
+    rng = np.random.default_rng(seed + 1)
+    for b in range(B):           # slots past each sequence hold garbage, NaN / inf scales
+        L = lens[b]
+        kc[b, :, L:] = rng.integers(-128, 128, size=kc[b, :, L:].shape)
+        vc[b, :, L:] = rng.integers(-128, 128, size=vc[b, :, L:].shape)
+        ks[b, :, L:] = np.nan
+        vs[b, :, L:] = np.inf
+    eff = np.minimum(lens, max_len)
+    o64, mag = attention_int8kv_ref(inp["q"], kc, ks, vc, vs, eff)
+    return inp["q"], kc, ks, vc, vs, lens, o64, mag
+
+
+def _run_attn(qb, kc, ks, vc, vs, lens, max_len, dtype, d):
+    out = bsb.attention_decode_int8kv(dev_bf16(qb, d), *_upload_cache(kc, ks, vc, vs, d),
+                                      dev(lens, d), max_len, out_dtype=dtype)
+    torch.cuda.synchronize()
+    y = host(out)
+    if dtype == torch.bfloat16:
+        return bf16_bits_to_f32_ref(y).astype(np.float64)
+    return y.astype(np.float64)
+
+
+def _check(y, o64, mag, bf16):
+    t = attention_tolerance(bf16)
+    err = np.abs(y - o64)
+    bad = err > t * mag
+    assert not bad.any(), f"{bad.sum()} outputs beyond the bound (max err/mag {(err / np.maximum(mag, 1e-300)).max():.3g})"
+    assert np.all(y[mag == 0] == 0)
+
+
+CASES = [
+    # B, Hq, Hkv, T, lens, max_len
+    (2, 8, 1, 128, [128, 77], 128),
+    (3, 16, 2, 576, [576, 1, 300], 576),          # two splits, one-token sequence
+    (2, 32, 2, 1088, [1088, 513], 1088),         # G = 16, three splits
+    (2, 4, 4, 256, [200, 64], 256),              # G = 1
+    (2, 6, 2, 192, [191, 65], 192),              # G = 3
+    (3, 8, 2, 1024, [700, 0, 599], 600),         # max_len below T and below lens[0]; an empty sequence
+    (2, 8, 8, 640, [640, 640], 640),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_attention_matches_oracle(case, dtype):
+    d = require_gpu()
+    B, Hq, Hkv, T, lens, max_len = case
+    say(f"attention B={B} Hq={Hq} Hkv={Hkv} T={T} lens={lens} max_len={max_len} {dtype}")
+    qb, kc, ks, vc, vs, lens, o64, mag = _attn_case(B, Hq, Hkv, T, lens, max_len, seed=B + Hq + T)
+    y = _run_attn(qb, kc, ks, vc, vs, lens, max_len, dtype, d)
+    _check(y, o64, mag, dtype == torch.bfloat16)
+
+
+@pytest.mark.parametrize("q_gain", [0.05, 6.0])
+def test_attention_flat_and_peaked_softmax(q_gain):
+    d = require_gpu()
+    say(f"attention q_gain={q_gain}")
+    qb, kc, ks, vc, vs, lens, o64, mag = _attn_case(2, 16, 2, 1024, [1024, 700], 1024, seed=31,
+                                                    q_gain=q_gain)
+    y = _run_attn(qb, kc, ks, vc, vs, lens, 1024, torch.float32, d)
+    _check(y, o64, mag, False)
+
+
+def test_attention_no_tokens_gives_zeros_and_is_deterministic():
+    d = require_gpu()
+    qb, kc, ks, vc, vs, lens, o64, mag = _attn_case(2, 8, 1, 128, [0, 0], 128, seed=5)
+    y = _run_attn(qb, kc, ks, vc, vs, lens, 128, torch.float32, d)
+    assert not y.any()
+    y0 = _run_attn(qb, kc, ks, vc, vs, lens, 0, torch.bfloat16, d)     # max_len 0: no split runs
+    assert not y0.any()
+    qb, kc, ks, vc, vs, lens, o64, mag = _attn_case(2, 8, 1, 256, [256, 100], 256, seed=6)
+    a = _run_attn(qb, kc, ks, vc, vs, lens, 256, torch.float32, d)
+    b = _run_attn(qb, kc, ks, vc, vs, lens, 256, torch.float32, d)
+    assert np.array_equal(a, b)
+
+
+def test_full_size_decode_attention_sampled():
+    """The benchmark's workload: 32 sequences x 4096 cached tokens, 64 query heads over
+    8 KV heads, written through the GPU write kernel and attended in the launch the
+    benchmark times; three sequences are checked against the oracle (cache bytes bit
+    for bit, outputs within the bound)."""
+    d = require_gpu()
+    c = synth.KV_CONFIG
+    B, Hq, Hkv, T = c["B"], c["Hq"], c["Hkv"], c["T"]
+    inp = synth.kv_inputs(B, Hq, Hkv, T, lens=np.full(B, T), seed=0)
+    say("full-size kv write + attention")
+    kc, ks, vc, vs = bsb.kv_cache_empty(B, Hkv, T, d)
+    kt = dev_bf16(inp["k"], d).permute(0, 2, 1, 3).reshape(B * T, Hkv, D).contiguous()
+    vt = dev_bf16(inp["v"], d).permute(0, 2, 1, 3).reshape(B * T, Hkv, D).contiguous()
+    seq = torch.arange(B, dtype=torch.int32, device=d).repeat_interleave(T)
+    pos = torch.arange(T, dtype=torch.int32, device=d).repeat(B)
+    bsb.kv_cache_write(kt, vt, seq, pos, kc, ks, vc, vs)
+    lens = dev(inp["lens"], d)
+    out = bsb.attention_decode_int8kv(dev_bf16(inp["q"], d), kc, ks, vc, vs, lens, T)
+    torch.cuda.synchronize()
+    y = bf16_bits_to_f32_ref(host(out)).astype(np.float64)
+    for b in (0, 17, 31):
+        qk, sk = kv_quantize_ref(inp["k"][b:b + 1])
+        qv, sv = kv_quantize_ref(inp["v"][b:b + 1])
+        assert np.array_equal(host(kc[b:b + 1]), qk)
+        assert np.array_equal(v_decode(host(vc[b:b + 1])), qv)
+        assert np.array_equal(host(ks[b:b + 1]), sk) and np.array_equal(host(vs[b:b + 1]), sv)
+        o64, mag = attention_int8kv_ref(inp["q"][b:b + 1], qk, sk, qv, sv, inp["lens"][b:b + 1])
+        _check(y[b:b + 1], o64, mag, True)
