@@ -226,9 +226,9 @@ def _rate(us, ops=None, byts=None, bound="hbm"):
 def extra_rows(torch, L, stream, dev, steps):
     """Every other workload of the path, each kernel timed on its own:
     the tiny linear, the prefill quantisation, the per-channel and per-tensor
-    GEMMs at the decode and prefill shapes, the routed MoE layer and the
+    GEMMs at the decode and prefill shapes, the routed MoE layer, the
     block-format weights (decoders, then the dense and grouped GEMMs on the
-    decoded weights)."""
+    decoded weights) and the INT8 KV cache (write, decode attention)."""
     import numpy as np
     from block_scaled_bit_amd import synth
     rows = {}
@@ -498,6 +498,72 @@ def extra_rows(torch, L, stream, dev, steps):
         log(f"blockfmt M={Mt}: gemm {tg * 1e3:.1f} us, grouped {te * 1e3:.1f} us")
         del gs, es, xd, xe, offe
         torch.cuda.empty_cache()
+    del qwd, swd, qwe, swe
+    torch.cuda.empty_cache()
+    rows.update(kv_rows(torch, L, stream, dev, steps))
+    return rows
+
+
+def kv_rows(torch, L, stream, dev, steps):
+    """The INT8 KV cache at 32 sequences x 4096 cached tokens, 64 query heads over
+    8 KV heads of 128: one decode step's write of the new keys and values, and the
+    decode attention over the whole cache (dequantisation fused in). Algorithmic
+    bytes of the attention: the INT8 codes and float32 scales of every cached key
+    and value, the BF16 queries and the BF16 output."""
+    import numpy as np
+    from block_scaled_bit_amd import synth
+    rows = {}
+    c = synth.KV_CONFIG
+    B, Hq, Hkv, T, D = c["B"], c["Hq"], c["Hkv"], c["T"], c["D"]
+    inp = synth.kv_inputs(B, Hq, Hkv, T, lens=np.full(B, T), seed=0)
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    kt = t(inp["k"].view(np.int16)).permute(0, 2, 1, 3).reshape(B * T, Hkv, D).contiguous()
+    vt = t(inp["v"].view(np.int16)).permute(0, 2, 1, 3).reshape(B * T, Hkv, D).contiguous()
+    seq = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(T)
+    pos = torch.arange(T, dtype=torch.int32, device=dev).repeat(B)
+    kc = torch.empty((B, Hkv, T // 16, 16 * D), dtype=torch.int8, device=dev)
+    ks = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+    vc = torch.empty((B, Hkv, T // 32, 32 * D), dtype=torch.int8, device=dev)
+    vs = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+    _ok(L, L.bsb_kv_cache_write(kt.data_ptr(), vt.data_ptr(), seq.data_ptr(), pos.data_ptr(),
+                                B * T, B, Hkv, T, D, kc.data_ptr(), ks.data_ptr(), vc.data_ptr(),
+                                vs.data_ptr(), stream))
+    # one decode step: the last slot of every sequence rewritten with its own key / value
+    step = dict(k=kt.view(B, T, Hkv, D)[:, T - 1].contiguous(),
+                v=vt.view(B, T, Hkv, D)[:, T - 1].contiguous(),
+                seq=torch.arange(B, dtype=torch.int32, device=dev),
+                pos=torch.full((B,), T - 1, dtype=torch.int32, device=dev))
+    del kt, vt, seq, pos
+    torch.cuda.empty_cache()
+    wsets = [{k: v.data_ptr() for k, v in step.items()} | {"_keep": step}]
+    tw = Row("kv write", wsets, lambda p, st: _ok(L, L.bsb_kv_cache_write(
+        p["k"], p["v"], p["seq"], p["pos"], B, B, Hkv, T, D, kc.data_ptr(), ks.data_ptr(),
+        vc.data_ptr(), vs.data_ptr(), st))).time(torch, stream, steps, 3)
+    w_bytes = 2 * (B * Hkv * D * 2 + B * Hkv * D + 4 * B * Hkv) + 8 * B
+    rows["kv_int8_write_decode_step_b32"] = _rate(tw * 1e3, byts=w_bytes)
+    log(f"kv write (decode step) {tw * 1e3:.1f} us")
+
+    a_bytes = 2 * B * Hkv * T * D + 8 * B * Hkv * T + 2 * B * Hq * D + 2 * B * Hq * D
+    lens = t(inp["lens"])
+    q = t(inp["q"].view(np.int16))
+    wbytes = L.bsb_attention_workspace_bytes(B, Hq, T)
+    asets = []
+    for i in range(_copies(a_bytes)):
+        o = dict(kc=kc if i == 0 else kc.clone(), ks=ks if i == 0 else ks.clone(),
+                 vc=vc if i == 0 else vc.clone(), vs=vs if i == 0 else vs.clone(), q=q.clone(),
+                 lens=lens, out=torch.empty((B, Hq, D), dtype=torch.int16, device=dev),
+                 work=torch.empty((wbytes // 4,), dtype=torch.float32, device=dev))
+        asets.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
+    ta = Row("kv attention", asets, lambda p, st: _ok(L, L.bsb_attention_decode_int8kv(
+        p["q"], p["kc"], p["ks"], p["vc"], p["vs"], p["lens"], B, Hq, Hkv, T, D, T, p["work"],
+        wbytes, p["out"], 0, st))).time(torch, stream, steps, 3)
+    rows["kv_int8_attention_decode_b32_t4096"] = _rate(ta * 1e3, byts=a_bytes)
+    log(f"kv attention (decode, 32 x 4096 tokens) {ta * 1e3:.1f} us")
+    del asets, kc, ks, vc, vs, step, wsets
+    torch.cuda.empty_cache()
     return rows
 
 

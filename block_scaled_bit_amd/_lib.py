@@ -373,6 +373,7 @@ def moe_combine(y: torch.Tensor, row_of_pair: torch.Tensor, gate: torch.Tensor,
 
 
 KV_HEAD_DIM = 128
+KV_KBLOCK = 16
 KV_VBLOCK = 32
 
 
@@ -381,7 +382,8 @@ def kv_cache_empty(B: int, Hkv: int, T: int, device) -> Tuple[torch.Tensor, ...]
     slots (T a multiple of 64) over Hkv heads of dimension 128, in the layout of
     bsb_kv_cache_write (contents undefined until written)."""
     dev = torch.device(device)
-    return (torch.empty((B, Hkv, T, KV_HEAD_DIM), dtype=torch.int8, device=dev),
+    return (torch.empty((B, Hkv, T // KV_KBLOCK, KV_KBLOCK * KV_HEAD_DIM), dtype=torch.int8,
+                        device=dev),
             torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
             torch.empty((B, Hkv, T // KV_VBLOCK, KV_VBLOCK * KV_HEAD_DIM), dtype=torch.int8,
                         device=dev),
@@ -390,9 +392,10 @@ def kv_cache_empty(B: int, Hkv: int, T: int, device) -> Tuple[torch.Tensor, ...]
 
 def _kv_shapes(k_cache, k_scale, v_cache, v_scale):
     _need(k_cache, "k_cache", (torch.int8,))
-    if k_cache.dim() != 4 or k_cache.shape[3] != KV_HEAD_DIM:
-        raise ValueError("k_cache must be [B, Hkv, T, 128]")
-    B, Hkv, T, _ = k_cache.shape
+    if k_cache.dim() != 4 or k_cache.shape[3] != KV_KBLOCK * KV_HEAD_DIM:
+        raise ValueError("k_cache must be [B, Hkv, T/16, 2048]")
+    B, Hkv, nb, _ = k_cache.shape
+    T = nb * KV_KBLOCK
     dev = k_cache.device
     _need(k_scale, "k_scale", (torch.float32,), (B, Hkv, T), dev)
     _need(v_cache, "v_cache", (torch.int8,), (B, Hkv, T // KV_VBLOCK, KV_VBLOCK * KV_HEAD_DIM), dev)

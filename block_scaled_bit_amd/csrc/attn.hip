@@ -8,22 +8,24 @@
 // read once and never expanded in memory.
 //
 // Cache layout (head dimension 128; T = token slots per sequence, a multiple of 64):
-//   k_cache [B, Hkv, T, 128] INT8, token-major (one 128-byte row per token)
+//   k_cache [B, Hkv, T/16, 2048] INT8: 16-token blocks; token tau of a block,
+//           dimension d at byte ((d/16)%2)*1024 + ((d/32)*16 + tau)*16 + d%16
 //   v_cache [B, Hkv, T/32, 4096] INT8: 32-token blocks; token tau of a block,
 //           dimension d at byte (((tau%16)/4)*16 + d%16)*64 + (d/16)*8 + (tau/16)*4 + tau%4
 //   k_scale, v_scale [B, Hkv, T] float32
-// The V block order is the matrix cores' operand order for the P.V product
-// (lane l of a wave reads the block's bytes 64l .. 64l+63), so a block streams
-// in with one coalesced 4 KB read and no transpose.
+// Both block orders are the matrix cores' operand orders (lane l of a wave
+// reads bytes 16l .. 16l+15 of each 1 KB half of a K block and bytes 64l ..
+// 64l+63 of a V block), so every load instruction reads 1 KB contiguous and
+// nothing is transposed.
 //
 // Decode attention (one query token per sequence, grouped-query heads, up to
-// 16 query heads per KV head): a workgroup of 8 waves takes 512 cached tokens
-// of one (sequence, KV head); each wave takes 64 tokens. Per wave, all of its
-// operands are loaded at once (keys, values, their scales, the queries), then
+// 16 query heads per KV head): a workgroup of 8 waves takes a split of the
+// cached tokens of one (sequence, KV head), each wave chunks of 64 tokens.
+// Per chunk:
 //   scores  S^T[token, head] = K . Q^T   on v_mfma_f32_16x16x32_bf16, the INT8
 //           codes converted to BF16 in registers (exact), the query in BF16;
 //   x = S * k_scale * log2(e)/sqrt(128) (float32), masked past the sequence;
-//   p = exp2(x - max) per head (float32), l = sum p;
+//   p = exp2(x - m) against the running maximum m per head (float32);
 //   o^T[d, head] += V^T . (p * v_scale)^T on the same MFMA, the weights times
 //           the value scales rounded to BF16, the value codes converted exactly.
 // The 8 wave results are merged in LDS (max, rescaled sums) into one partial
@@ -40,7 +42,9 @@ constexpr int kHD = 128;                       // head dimension
 constexpr int kVBlk = 32;                      // tokens per V block
 constexpr int kAttnWaves = 8;                  // waves per attention workgroup
 constexpr int kWaveTok = 64;                   // tokens per wave
-constexpr int kSplitTok = kAttnWaves * kWaveTok;
+constexpr int kSplitTok = kAttnWaves * kWaveTok;   // tokens per split per chunk step
+constexpr int64_t kMinWorkgroups = 256;   // grid size the chunk count aims for (one per CU)
+constexpr int kMaxChunks = 8;              // chunks per wave at most
 constexpr int kPart = kHD + 2;                 // floats per (head, split) partial: o, m, l
 constexpr int kORow = kHD + 4;                 // LDS row stride of the wave partials
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -48,6 +52,13 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kScoreScale = (float)(1.4426950408889634 / 11.313708498984761);
 
 typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+// byte of (token tau in a 16-token block, dim d) in a 2 KB K block: one wave
+// instruction j reads bytes 1024j .. 1024j+1023, lane 16g + tau getting dims
+// 32g + 16j .. 32g + 16j + 15 of token tau
+__device__ __forceinline__ int kblk_off(int tau, int d) {
+    return ((d >> 4) & 1) * 1024 + ((d >> 5) * 16 + tau) * 16 + (d & 15);
+}
 
 __device__ __forceinline__ int vblk_off(int tau, int d) {
     return ((((tau & 15) >> 2) * 16 + (d & 15)) * 64) + (d >> 4) * 8 + (tau >> 4) * 4 + (tau & 3);
@@ -62,10 +73,6 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
         r[4 + e] = (__bf16)(float)(int8_t)(hi >> (8 * e));
     }
     return r;
-}
-
-__device__ __forceinline__ uint32_t word(const uint4 &v, int i) {
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
 // One wave per (token, KV head, K or V) vector of 128 BF16 values: two per lane.
@@ -95,8 +102,9 @@ kv_write_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     }
     const int64_t vec = ((int64_t)b * Hkv + h) * T + t;
     if (which == 0) {
-        reinterpret_cast<uint16_t *>(kc + vec * kHD)[lane] =
-            (uint16_t)((uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8));
+        const uint16_t pair = (uint16_t)((uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8));
+        int8_t *blk = kc + (((int64_t)b * Hkv + h) * T + (t & ~15)) * kHD;
+        *reinterpret_cast<uint16_t *>(blk + kblk_off(t & 15, 2 * lane)) = pair;
         if (lane == 0) ks[vec] = s;
     } else {
         int8_t *blk = vc + (((int64_t)b * Hkv + h) * (T / kVBlk) + t / kVBlk) * (kVBlk * kHD);
@@ -107,7 +115,20 @@ kv_write_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     }
 }
 
-// grid (splits, B * Hkv); 512 threads. part: [B*Hkv, splits, G, kPart] float32.
+// The cached tokens of one (sequence, KV head) this wave owns: chunks of 64.
+struct KvChunk {
+    v4i kd[4][2];   // keys: 16-token tile c, half j
+    v4i vd[2][4];   // values: 32-token block s, quarter j
+    float skl, svl; // scales of token t0 + lane
+};
+
+// grid (splits, B * Hkv); 512 threads; a split is 8 * 64 * R tokens. Wave w
+// takes chunks r * 8 + w (r < R) of its split, so at each step the 8 waves
+// read adjacent 8 KB regions of the keys and of the values; a wave issues a
+// chunk's 18 loads together and keeps a running maximum, weight sum and
+// output across its chunks (online softmax).
+// part: [B*Hkv, splits, G, kPart] float32.
+template <int R>
 __global__ void __launch_bounds__(512)
 attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
                   const float *__restrict__ ks, const int8_t *__restrict__ vc,
@@ -120,107 +141,136 @@ attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
     const int bh = blockIdx.y;
     const int b = bh / Hkv, hk = bh - b * Hkv;
     const int G = Hq / Hkv;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave index as a uniform value, so the offsets derived from it stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 15, grp = lane >> 4;
     int L = lens[b];
     const int lim = max_len < T ? max_len : T;
     L = L < 0 ? 0 : (L > lim ? lim : L);
-    const int t0 = split * kSplitTok + wave * kWaveTok;
+    const int base = split * kSplitTok * R + wave * kWaveTok;
+    auto t0_of = [&](int r) { return base + r * kSplitTok; };
 
-    float m = kNegInf, l = 0.0f;
-    v4f_t o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // this (sequence, KV head)'s slice of the cache, range-checked by the buffer
+    // descriptors; the lane's part of an offset is in a VGPR, the rest scalar
+    const uint32_t tb = (uint32_t)T * kHD;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + (int64_t)bh * tb, tb);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + (int64_t)bh * tb, tb);
+    const __amdgpu_buffer_rsrc_t rks = make_rsrc(ks + (int64_t)bh * T, (uint32_t)T * 4);
+    const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vs + (int64_t)bh * T, (uint32_t)T * 4);
+    const uint32_t kvo = (uint32_t)lane * 16;
+    const uint32_t vvo = (uint32_t)lane * 64;
 
-    if (t0 < L) {   // whole wave; then t0 + 64 <= T, so every load below is in range
-        const int8_t *kb = kc + ((int64_t)bh * T + t0) * kHD;
-        const int8_t *vb = vc + ((int64_t)bh * (T / kVBlk) + t0 / kVBlk) * (kVBlk * kHD);
-        const float *ksb = ks + (int64_t)bh * T + t0;
-        const float *vsb = vs + (int64_t)bh * T + t0;
-        uint4 kd[4][2], vd[2][4], qd[4];
-        float4 skv[4], svv[4];
+    auto load = [&](KvChunk &ch, int r) {
+        const int t0 = t0_of(r);
+        const bool ok = r < R && t0 < L;
+        const uint32_t so = ok ? (uint32_t)t0 * kHD : kOOB, ss = ok ? (uint32_t)t0 * 4 : kOOB;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                kd[c][j] = *reinterpret_cast<const uint4 *>(kb + (16 * c + col) * kHD + 32 * grp +
-                                                            16 * j);
+                ch.kd[c][j] = buf_load16s(rk, kvo, ok ? so + c * 2048 + j * 1024 : kOOB);
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                vd[s][j] = *reinterpret_cast<const uint4 *>(vb + s * (kVBlk * kHD) + lane * 64 +
-                                                            16 * j);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            skv[c] = *reinterpret_cast<const float4 *>(ksb + 16 * c + 4 * grp);
-            svv[c] = *reinterpret_cast<const float4 *>(vsb + 16 * c + 4 * grp);
-        }
+                ch.vd[s][j] = buf_load16s(rv, vvo, ok ? so + s * (kVBlk * kHD) + 16 * j : kOOB);
+        ch.skl = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rks, (int)(lane * 4), (int)ss, 0));
+        ch.svl = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rvs, (int)(lane * 4), (int)ss, 0));
+        // keep the whole chunk's loads here, ahead of the computation that follows
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // queries: head hk*G + col (zero rows for col >= G), dims 32grp .. 32grp+31
+    uint4 qd[4];
+    {
         const bool hv = col < G;
         const uint16_t *qr = q + ((int64_t)b * Hq + hk * G + (hv ? col : 0)) * kHD + 32 * grp;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             qd[j] = hv ? *reinterpret_cast<const uint4 *>(qr + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
+    }
 
+    // running maximum (log2 units), this lane's partial weight sum, unnormalised o^T
+    float m = kNegInf, lpart = 0.0f;
+    v4f_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](const KvChunk &ch, int t0) {
         // scores: tile c holds tokens t0 + 16c + 4grp + r (rows) for head col
         float x[4][4];
-        float mloc = kNegInf;
+        float mc = kNegInf;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             v4f_t acc = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const uint4 &kk = kd[c][s >> 1];
-                const bf16x8 a = i8x8_to_bf16(word(kk, 2 * (s & 1)), word(kk, 2 * (s & 1) + 1));
+                const v4i &kk = ch.kd[c][s >> 1];
+                const bf16x8 a = i8x8_to_bf16((uint32_t)kk[2 * (s & 1)], (uint32_t)kk[2 * (s & 1) + 1]);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qd[s]),
                                                               acc, 0, 0, 0);
             }
-            const float skr[4] = {skv[c].x, skv[c].y, skv[c].z, skv[c].w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float sv = (acc[r] * skr[r]) * kScoreScale;
-                x[c][r] = (t0 + 16 * c + 4 * grp + r < L) ? sv : kNegInf;
-                mloc = __builtin_fmaxf(mloc, x[c][r]);
+                const int tt = 16 * c + 4 * grp + r;
+                const float sk = __shfl(ch.skl, tt, kWave);
+                const float sv = (acc[r] * sk) * kScoreScale;
+                x[c][r] = (t0 + tt < L) ? sv : kNegInf;
+                mc = __builtin_fmaxf(mc, x[c][r]);
             }
         }
-        mloc = __builtin_fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-        mloc = __builtin_fmaxf(mloc, __shfl_xor(mloc, 32, kWave));   // finite: token t0 is valid
+        mc = __builtin_fmaxf(mc, __shfl_xor(mc, 16, kWave));
+        mc = __builtin_fmaxf(mc, __shfl_xor(mc, 32, kWave));   // finite: token t0 is valid
+        const float mn = __builtin_fmaxf(m, mc);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first chunk
+        m = mn;
+        lpart *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] *= alpha;
         float p[4][4];
-        float lsum = 0.0f;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[c][r] = __builtin_amdgcn_exp2f(x[c][r] - mloc);
-                lsum += p[c][r];
+                p[c][r] = __builtin_amdgcn_exp2f(x[c][r] - mn);
+                lpart += p[c][r];
             }
-        lsum += __shfl_xor(lsum, 16, kWave);
-        lsum += __shfl_xor(lsum, 32, kWave);
-        m = mloc;
-        l = lsum;
-
         // P.V over two 32-token blocks; slot j < 4 is token 32s + 4grp + j,
         // slot 4 + j is token 32s + 16 + 4grp + j (the V block order above)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const float sva[4] = {svv[2 * s].x, svv[2 * s].y, svv[2 * s].z, svv[2 * s].w};
-            const float svb[4] = {svv[2 * s + 1].x, svv[2 * s + 1].y, svv[2 * s + 1].z,
-                                  svv[2 * s + 1].w};
-            const int ta = t0 + 32 * s + 4 * grp, tb = ta + 16;
+            const int ta = 32 * s + 4 * grp, tbk = ta + 16;
             bf16x8 pw;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                pw[j] = (__bf16)(ta + j < L ? p[2 * s][j] * sva[j] : 0.0f);
-                pw[4 + j] = (__bf16)(tb + j < L ? p[2 * s + 1][j] * svb[j] : 0.0f);
+                const float sva = __shfl(ch.svl, ta + j, kWave);
+                const float svb = __shfl(ch.svl, tbk + j, kWave);
+                pw[j] = (__bf16)(t0 + ta + j < L ? p[2 * s][j] * sva : 0.0f);
+                pw[4 + j] = (__bf16)(t0 + tbk + j < L ? p[2 * s + 1][j] * svb : 0.0f);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint4 &vv = vd[s][i >> 1];
-                const bf16x8 a = i8x8_to_bf16(word(vv, 2 * (i & 1)), word(vv, 2 * (i & 1) + 1));
+                const v4i &vv = ch.vd[s][i >> 1];
+                const bf16x8 a = i8x8_to_bf16((uint32_t)vv[2 * (i & 1)], (uint32_t)vv[2 * (i & 1) + 1]);
                 o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pw, o[i], 0, 0, 0);
             }
         }
+    };
+
+    if (t0_of(0) < L) {   // whole wave
+        KvChunk A;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (t0_of(r) >= L) break;
+            load(A, r);
+            compute(A, t0_of(r));
+        }
     }
+    float l = lpart + __shfl_xor(lpart, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
 
     // merge the 8 waves: lane (col, grp) holds o[head col][16i + 4grp + r]
     if (grp == 0) {
@@ -255,30 +305,54 @@ attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
     }
 }
 
-// one wave per (sequence, query head); lane holds dimensions 2 lane, 2 lane + 1
+// one wave per (sequence, query head); lane holds dimensions 2 lane, 2 lane + 1.
+// Splits are read eight at a time, all loads of a batch issued together, and
+// merged with a running maximum.
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(64)
 attn_combine_kernel(const float *__restrict__ part, int Hq, int Hkv, int nsplit,
                     void *__restrict__ out) {
+    constexpr int kBatch = 8;
     const int bq = blockIdx.x;
-    const int Hq_ = Hq, G = Hq / Hkv;
-    const int b = bq / Hq_, hq = bq - b * Hq_;
+    const int G = Hq / Hkv;
+    const int b = bq / Hq, hq = bq - b * Hq;
     const int hk = hq / G, h = hq - hk * G;
     const int lane = threadIdx.x;
     const int64_t stride = (int64_t)G * kPart;
     const float *pp = part + ((int64_t)(b * Hkv + hk) * nsplit) * stride + h * kPart;
-    float M = kNegInf;
-    for (int s = 0; s < nsplit; ++s) M = __builtin_fmaxf(M, pp[s * stride + kHD]);
-    float o0 = 0.0f, o1 = 0.0f;
-    if (M != kNegInf) {
-        float Lt = 0.0f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float f = __builtin_amdgcn_exp2f(pp[s * stride + kHD] - M);
-            Lt += pp[s * stride + kHD + 1] * f;
-            const float2 v = *reinterpret_cast<const float2 *>(pp + s * stride + 2 * lane);
-            o0 += v.x * f;
-            o1 += v.y * f;
+    float M = kNegInf, Lt = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+        float ms[kBatch], ls[kBatch];
+        float2 os[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int s = s0 + j < nsplit ? s0 + j : nsplit - 1;   // in range; masked below
+            const float *ps = pp + s * stride;
+            ms[j] = ps[kHD];
+            ls[j] = ps[kHD + 1];
+            os[j] = *reinterpret_cast<const float2 *>(ps + 2 * lane);
         }
+        float Mn = M;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (s0 + j >= nsplit) ms[j] = kNegInf;
+            Mn = __builtin_fmaxf(Mn, ms[j]);
+        }
+        if (Mn == kNegInf) continue;                 // no tokens so far
+        const float a = __builtin_amdgcn_exp2f(M - Mn);   // 0 while M is -inf
+        Lt *= a;
+        o0 *= a;
+        o1 *= a;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const float f = __builtin_amdgcn_exp2f(ms[j] - Mn);   // 0 for empty splits
+            Lt += ls[j] * f;
+            o0 += os[j].x * f;
+            o1 += os[j].y * f;
+        }
+        M = Mn;
+    }
+    if (M != kNegInf) {
         o0 = o0 / Lt;
         o1 = o1 / Lt;
     }
@@ -313,10 +387,21 @@ hipError_t launch_attention_decode(const uint16_t *q, const int8_t *kc, const fl
                                    const int8_t *vc, const float *vs, const int32_t *lens, int B,
                                    int Hq, int Hkv, int T, int max_len, float *work, void *out,
                                    int out_bf16, hipStream_t stream) {
-    const int64_t ns = attention_splits(max_len);
+    // chunks per wave (1, 2, 4 or 8): the most that keep at least kMinWorkgroups
+    // workgroups in the grid (long-lived waves, fewer partials to merge)
+    const int64_t units = (int64_t)B * Hkv * attention_splits(max_len);
+    int R = 1;
+    while (R < kMaxChunks && units / (2 * R) >= kMinWorkgroups) R *= 2;
+    const int64_t ns = (max_len + kSplitTok * R - 1) / (kSplitTok * R);
     if (ns > 0) {   // max_len == 0: no split to run, the combine writes zeros
-        attn_split_kernel<<<dim3((unsigned)ns, (unsigned)(B * Hkv)), kAttnWaves * kWave, 0,
-                            stream>>>(q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work);
+        const dim3 grid((unsigned)ns, (unsigned)(B * Hkv));
+        const int nt = kAttnWaves * kWave;
+        switch (R) {
+            case 1: attn_split_kernel<1><<<grid, nt, 0, stream>>>(q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work); break;
+            case 2: attn_split_kernel<2><<<grid, nt, 0, stream>>>(q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work); break;
+            case 4: attn_split_kernel<4><<<grid, nt, 0, stream>>>(q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work); break;
+            default: attn_split_kernel<8><<<grid, nt, 0, stream>>>(q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work); break;
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -265,7 +265,9 @@ bsb_status bsb_moe_combine(const uint16_t *y, const int32_t *row_of_pair,
  * per value vector (one token of one KV head, D = 128 values), taken on write
  * by the rule of bsb_quantize_act over those 128 values.
  * Cache layout (T = token slots per sequence, a multiple of 64, 64 <= T < 2^24):
- *   k_cache [B, Hkv, T, 128] int8, token-major
+ *   k_cache [B, Hkv, T/16, 2048] int8: blocks of 16 tokens; token tau of a
+ *           block and dimension d sit at byte
+ *           ((d/16)%2)*1024 + ((d/32)*16 + tau)*16 + d%16
  *   v_cache [B, Hkv, T/32, 4096] int8: blocks of 32 tokens; token tau of a
  *           block and dimension d sit at byte
  *           (((tau%16)/4)*16 + d%16)*64 + (d/16)*8 + (tau/16)*4 + tau%4

@@ -19,10 +19,25 @@ from tests.gpu_util import require_gpu, dev, dev_bf16, host, say
 
 pytestmark = pytest.mark.gpu
 
-D, VB = 128, 32
-_tau = np.arange(VB)[:, None]
+D, KB, VB = 128, 16, 32
 _d = np.arange(D)[None, :]
+_kt = np.arange(KB)[:, None]
+K_OFF = ((_d // 16) % 2) * 1024 + ((_d // 32) * 16 + _kt) * 16 + _d % 16
+_tau = np.arange(VB)[:, None]
 V_OFF = (((_tau % 16) // 4) * 16 + _d % 16) * 64 + (_d // 16) * 8 + (_tau // 16) * 4 + _tau % 4
+
+
+def k_encode(kc):
+    """[B, H, T, 128] int8 -> the K block layout [B, H, T/16, 2048]."""
+    B, H, T, _ = kc.shape
+    out = np.empty((B, H, T // KB, KB * D), np.int8)
+    out[..., K_OFF] = kc.reshape(B, H, T // KB, KB, D)
+    return out
+
+
+def k_decode(kb):
+    B, H, NB, _ = kb.shape
+    return kb[..., K_OFF].reshape(B, H, NB * KB, D)
 
 
 def v_encode(vc):
@@ -38,9 +53,11 @@ def v_decode(vb):
     return vb[..., V_OFF].reshape(B, H, NB * VB, D)
 
 
-def test_v_layout_is_a_permutation():
+def test_kv_layouts_are_permutations():
+    assert np.array_equal(np.sort(K_OFF.ravel()), np.arange(KB * D))
     assert np.array_equal(np.sort(V_OFF.ravel()), np.arange(VB * D))
     x = np.random.default_rng(0).integers(-127, 128, size=(2, 3, 64, D)).astype(np.int8)
+    assert np.array_equal(k_decode(k_encode(x)), x)
     assert np.array_equal(v_decode(v_encode(x)), x)
 
 
@@ -74,7 +91,7 @@ def test_write_is_bit_exact_and_touches_only_named_slots(B, H, T, frac):
     torch.cuda.synchronize()
     qk, sk = kv_quantize_ref(k)
     qv, sv = kv_quantize_ref(v)
-    gk, gks, gv, gvs = host(kc), host(ks), v_decode(host(vc)), host(vs)
+    gk, gks, gv, gvs = k_decode(host(kc)), host(ks), v_decode(host(vc)), host(vs)
     written = np.zeros((B, T), bool)
     for b, t in slots:
         written[b, t] = True
@@ -103,7 +120,7 @@ def test_decode_step_appends_one_token_per_sequence():
     torch.cuda.synchronize()
     qk, sk = kv_quantize_ref(kn)
     qv, sv = kv_quantize_ref(vn)
-    gk, gv, gks = host(kc), v_decode(host(vc)), host(ks)
+    gk, gv, gks = k_decode(host(kc)), v_decode(host(vc)), host(ks)
     for b in range(B):
         assert np.array_equal(gk[b, :, lens[b]], qk[b])
         assert np.array_equal(gv[b, :, lens[b]], qv[b])
@@ -111,7 +128,7 @@ def test_decode_step_appends_one_token_per_sequence():
 
 
 def _upload_cache(kc, ks, vc, vs, d):
-    return dev(kc, d), dev(ks, d), dev(v_encode(vc), d), dev(vs, d)
+    return dev(k_encode(kc), d), dev(ks, d), dev(v_encode(vc), d), dev(vs, d)
 
 
 def _attn_case(B, Hq, Hkv, T, lens, max_len, seed, q_gain=1.0):
@@ -218,8 +235,36 @@ def test_full_size_decode_attention_sampled():
     for b in (0, 17, 31):
         qk, sk = kv_quantize_ref(inp["k"][b:b + 1])
         qv, sv = kv_quantize_ref(inp["v"][b:b + 1])
-        assert np.array_equal(host(kc[b:b + 1]), qk)
+        assert np.array_equal(k_decode(host(kc[b:b + 1])), qk)
         assert np.array_equal(v_decode(host(vc[b:b + 1])), qv)
         assert np.array_equal(host(ks[b:b + 1]), sk) and np.array_equal(host(vs[b:b + 1]), sv)
         o64, mag = attention_int8kv_ref(inp["q"][b:b + 1], qk, sk, qv, sv, inp["lens"][b:b + 1])
         _check(y[b:b + 1], o64, mag, True)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,max_len", [
+    (64, 8, 8, 512, 512),       # 512 (sequence, KV head) pairs: two chunks per wave
+    (32, 64, 8, 2048, 2000),    # 1024 split units: four chunks per wave
+])
+def test_attention_multi_chunk_waves(B, Hq, Hkv, T, max_len):
+    """Grids large enough that each wave walks several 64-token chunks (running
+    maximum and sums across chunks), ragged lengths including 0, 1, 63, 64, 65 and
+    lengths above max_len; a sample of sequences checked against the oracle."""
+    d = require_gpu()
+    rng = np.random.default_rng(B + T)
+    lens = rng.integers(1, T + 1, size=B).astype(np.int32)
+    lens[:6] = [0, 1, 63, 64, 65, T]
+    say(f"attention multi-chunk B={B} Hq={Hq} Hkv={Hkv} T={T} max_len={max_len}")
+    inp = synth.kv_inputs(B, Hq, Hkv, T, lens=lens, seed=B + Hkv)
+    kc, ks = kv_quantize_ref(inp["k"])
+    vc, vs = kv_quantize_ref(inp["v"])
+    for b in range(B):
+        ks[b, :, lens[b]:] = np.nan
+        vs[b, :, lens[b]:] = np.inf
+    for dtype in (torch.float32, torch.bfloat16):
+        y = _run_attn(inp["q"], kc, ks, vc, vs, lens, max_len, dtype, d)
+        for b in list(range(6)) + list(rng.choice(np.arange(6, B), 6, replace=False)):
+            eff = np.minimum(lens[b:b + 1], max_len)
+            o64, mag = attention_int8kv_ref(inp["q"][b:b + 1], kc[b:b + 1], ks[b:b + 1],
+                                            vc[b:b + 1], vs[b:b + 1], eff)
+            _check(y[b:b + 1], o64, mag, dtype == torch.bfloat16)
