@@ -128,12 +128,17 @@ struct KvChunk {
 // chunk's 18 loads together and keeps a running maximum, weight sum and
 // output across its chunks (online softmax).
 // part: [B*Hkv, splits, G, kPart] float32.
-template <int R>
+// OUT: kPartials writes the split's (o, m, l) for the merge kernel; with a
+// single split the kernel writes the normalised output itself (kDirectBf16,
+// kDirectF32) and no merge runs.
+enum { kPartials = 0, kDirectBf16 = 1, kDirectF32 = 2 };
+
+template <int R, int OUT>
 __global__ void __launch_bounds__(512)
 attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
                   const float *__restrict__ ks, const int8_t *__restrict__ vc,
                   const float *__restrict__ vs, const int32_t *__restrict__ lens, int Hq, int Hkv,
-                  int T, int max_len, float *__restrict__ part) {
+                  int T, int max_len, float *__restrict__ part, void *__restrict__ out) {
     __shared__ __align__(16) float s_o[kAttnWaves][16][kORow];
     __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
 
@@ -297,10 +302,20 @@ attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
                 Ls += s_l[w][h] * f;
             }
         }
-        pb[h * kPart + d] = O;
-        if (d == 0) {
-            pb[h * kPart + kHD] = M;
-            pb[h * kPart + kHD + 1] = Ls;
+        if (OUT == kPartials) {
+            pb[h * kPart + d] = O;
+            if (d == 0) {
+                pb[h * kPart + kHD] = M;
+                pb[h * kPart + kHD + 1] = Ls;
+            }
+        } else {
+            // the only split: this is the whole sequence, finish here
+            const float y = M != kNegInf ? O / Ls : 0.0f;
+            const int64_t oi = ((int64_t)b * Hq + hk * G + h) * kHD + d;
+            if (OUT == kDirectBf16)
+                reinterpret_cast<uint16_t *>(out)[oi] = (uint16_t)f32_to_bf16_rne(y);
+            else
+                reinterpret_cast<float *>(out)[oi] = y;
         }
     }
 }
@@ -364,6 +379,40 @@ attn_combine_kernel(const float *__restrict__ part, int Hq, int Hkv, int nsplit,
     }
 }
 
+template <int R, int OUT>
+hipError_t launch_split(dim3 grid, const uint16_t *q, const int8_t *kc, const float *ks,
+                        const int8_t *vc, const float *vs, const int32_t *lens, int Hq, int Hkv,
+                        int T, int max_len, float *work, void *out, hipStream_t stream) {
+    attn_split_kernel<R, OUT><<<grid, kAttnWaves * kWave, 0, stream>>>(
+        q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out);
+    return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t launch_split_o(int R, dim3 grid, const uint16_t *q, const int8_t *kc, const float *ks,
+                          const int8_t *vc, const float *vs, const int32_t *lens, int Hq, int Hkv,
+                          int T, int max_len, float *work, void *out, hipStream_t stream) {
+    switch (R) {
+        case 1: return launch_split<1, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        case 2: return launch_split<2, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        case 4: return launch_split<4, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        default: return launch_split<8, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+    }
+}
+
+// the split kernel for R chunks per wave over ceil(max_len / (512 R)) splits
+hipError_t launch_split_r(int R, int out_mode, const uint16_t *q, const int8_t *kc, const float *ks,
+                          const int8_t *vc, const float *vs, const int32_t *lens, int B, int Hq,
+                          int Hkv, int T, int max_len, float *work, void *out, hipStream_t stream) {
+    const int64_t ns = (max_len + (int64_t)kSplitTok * R - 1) / ((int64_t)kSplitTok * R);
+    const dim3 grid((unsigned)ns, (unsigned)(B * Hkv));
+    if (out_mode == kDirectBf16)
+        return launch_split_o<kDirectBf16>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+    if (out_mode == kDirectF32)
+        return launch_split_o<kDirectF32>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+    return launch_split_o<kPartials>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+}
+
 }  // namespace
 
 int64_t attention_splits(int64_t max_len) { return (max_len + kSplitTok - 1) / kSplitTok; }
@@ -393,16 +442,12 @@ hipError_t launch_attention_decode(const uint16_t *q, const int8_t *kc, const fl
     int R = 1;
     while (R < kMaxChunks && units / (2 * R) >= kMinWorkgroups) R *= 2;
     const int64_t ns = (max_len + kSplitTok * R - 1) / (kSplitTok * R);
+    if (ns == 1)   // one split holds every sequence: it writes the output, no merge
+        return launch_split_r(R, out_bf16 ? kDirectBf16 : kDirectF32, q, kc, ks, vc, vs, lens, B,
+                              Hq, Hkv, T, max_len, work, out, stream);
     if (ns > 0) {   // max_len == 0: no split to run, the combine writes zeros
-        const dim3 grid((unsigned)ns, (unsigned)(B * Hkv));
-        const int nt = kAttnWaves * kWave;
-        switch (R) {
-            case 1: attn_split_kernel<1><<<grid, nt, 0, stream>>>(q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work); break;
-            case 2: attn_split_kernel<2><<<grid, nt, 0, stream>>>(q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work); break;
-            case 4: attn_split_kernel<4><<<grid, nt, 0, stream>>>(q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work); break;
-            default: attn_split_kernel<8><<<grid, nt, 0, stream>>>(q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work); break;
-        }
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_split_r(R, kPartials, q, kc, ks, vc, vs, lens, B, Hq, Hkv, T,
+                                      max_len, work, out, stream);
         if (e != hipSuccess) return e;
     }
     if (out_bf16)

@@ -243,8 +243,9 @@ def test_full_size_decode_attention_sampled():
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,max_len", [
-    (64, 8, 8, 512, 512),       # 512 (sequence, KV head) pairs: two chunks per wave
-    (32, 64, 8, 2048, 2000),    # 1024 split units: four chunks per wave
+    (64, 8, 8, 512, 512),       # 512 (sequence, KV head) pairs: two chunks per wave, one split
+    (32, 64, 8, 2048, 2000),    # 1024 split units: four chunks per wave, one split
+    (32, 8, 8, 1280, 1280),     # two chunks per wave over two splits (merged by the second kernel)
 ])
 def test_attention_multi_chunk_waves(B, Hq, Hkv, T, max_len):
     """Grids large enough that each wave walks several 64-token chunks (running
