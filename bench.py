@@ -560,7 +560,8 @@ def kv_rows(torch, L, stream, dev, steps):
     ta = Row("kv attention", asets, lambda p, st: _ok(L, L.bsb_attention_decode_int8kv(
         p["q"], p["kc"], p["ks"], p["vc"], p["vs"], p["lens"], B, Hq, Hkv, T, D, T, p["work"],
         wbytes, p["out"], 0, st))).time(torch, stream, steps, 3)
-    rows["kv_int8_attention_decode_b32_t4096"] = _rate(ta * 1e3, byts=a_bytes)
+    rows["kv_int8_attention_decode_b32_t4096"] = _rate(ta * 1e3, byts=a_bytes) | {
+        "kernel": "attn_split_kernel<8, 1> (one launch)", "traffic": measured_traffic("kv_attention")}
     log(f"kv attention (decode, 32 x 4096 tokens) {ta * 1e3:.1f} us")
     del asets, kc, ks, vc, vs, step, wsets
     torch.cuda.empty_cache()
