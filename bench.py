@@ -531,6 +531,11 @@ def kv_rows(torch, L, stream, dev, steps):
     _ok(L, L.bsb_kv_cache_write(kt.data_ptr(), vt.data_ptr(), seq.data_ptr(), pos.data_ptr(),
                                 B * T, B, Hkv, T, D, kc.data_ptr(), ks.data_ptr(), vc.data_ptr(),
                                 vs.data_ptr(), stream))
+    # the BF16 cache the INT8 one replaces, written from the same keys and values
+    kb = torch.empty((B, Hkv, T // 16, 16 * D), dtype=torch.int16, device=dev)
+    vb = torch.empty((B, Hkv, T // 32, 32 * D), dtype=torch.int16, device=dev)
+    _ok(L, L.bsb_kv_cache_write_bf16(kt.data_ptr(), vt.data_ptr(), seq.data_ptr(), pos.data_ptr(),
+                                     B * T, B, Hkv, T, D, kb.data_ptr(), vb.data_ptr(), stream))
     # one decode step: the last slot of every sequence rewritten with its own key / value
     step = dict(k=kt.view(B, T, Hkv, D)[:, T - 1].contiguous(),
                 v=vt.view(B, T, Hkv, D)[:, T - 1].contiguous(),
@@ -564,6 +569,24 @@ def kv_rows(torch, L, stream, dev, steps):
         "kernel": "attn_split_kernel<8, 1> (one launch)", "traffic": measured_traffic("kv_attention")}
     log(f"kv attention (decode, 32 x 4096 tokens) {ta * 1e3:.1f} us")
     del asets, kc, ks, vc, vs, step, wsets
+    torch.cuda.empty_cache()
+
+    # the same attention over the BF16 cache: the comparison the pages quote for
+    # fusing the dequantisation (attention time with and without the INT8 cache)
+    b_bytes = 4 * B * Hkv * T * D + 2 * B * Hq * D + 2 * B * Hq * D
+    bsets = []
+    for i in range(_copies(b_bytes)):
+        o = dict(kc=kb if i == 0 else kb.clone(), vc=vb if i == 0 else vb.clone(), q=q.clone(),
+                 lens=lens, out=torch.empty((B, Hq, D), dtype=torch.int16, device=dev),
+                 work=torch.empty((wbytes // 4,), dtype=torch.float32, device=dev))
+        bsets.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
+    tbf = Row("kv attention bf16", bsets, lambda p, st: _ok(L, L.bsb_attention_decode_bf16kv(
+        p["q"], p["kc"], p["vc"], p["lens"], B, Hq, Hkv, T, D, T, p["work"], wbytes, p["out"], 0,
+        st))).time(torch, stream, steps, 3)
+    rows["kv_bf16_attention_decode_b32_t4096"] = _rate(tbf * 1e3, byts=b_bytes) | {
+        "int8_kv_speedup": round(tbf / ta, 3)}
+    log(f"kv attention over a BF16 cache {tbf * 1e3:.1f} us (INT8 cache {tbf / ta:.2f}x faster)")
+    del bsets, kb, vb
     torch.cuda.empty_cache()
     return rows
 

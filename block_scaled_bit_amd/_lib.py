@@ -44,6 +44,10 @@ _SIGNATURES = {
                            _c_p, _c_p, _c_p, _c_p],
     "bsb_attention_decode_int8kv": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
                                     _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_int, _c_p],
+    "bsb_kv_cache_write_bf16": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                _c_p, _c_p, _c_p],
+    "bsb_attention_decode_bf16kv": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
+                                    _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_int, _c_p],
 }
 EXPORTED = tuple(_SIGNATURES) + ("bsb_status_string", "bsb_abi_version",
                                  "bsb_attention_workspace_bytes")
@@ -454,4 +458,69 @@ def attention_decode_int8kv(q: torch.Tensor, k_cache: torch.Tensor, k_scale: tor
             _ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(lens),
             B, Hq, Hkv, T, KV_HEAD_DIM, max_len, _ptr(work), work.numel() * 4, _ptr(out), code,
             _stream(dev)), "bsb_attention_decode_int8kv")
+    return out
+
+
+def kv_cache_empty_bf16(B: int, Hkv: int, T: int, device) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Allocate the BF16 comparison cache (k_cache, v_cache) in the layout of
+    bsb_kv_cache_write_bf16 (contents undefined until written)."""
+    dev = torch.device(device)
+    return (torch.empty((B, Hkv, T // KV_KBLOCK, KV_KBLOCK * KV_HEAD_DIM), dtype=torch.bfloat16,
+                        device=dev),
+            torch.empty((B, Hkv, T // KV_VBLOCK, KV_VBLOCK * KV_HEAD_DIM), dtype=torch.bfloat16,
+                        device=dev))
+
+
+def _kv16_shapes(k_cache, v_cache):
+    _need(k_cache, "k_cache", _BF16_BITS)
+    if k_cache.dim() != 4 or k_cache.shape[3] != KV_KBLOCK * KV_HEAD_DIM:
+        raise ValueError("k_cache must be [B, Hkv, T/16, 2048]")
+    B, Hkv, nb, _ = k_cache.shape
+    T = nb * KV_KBLOCK
+    dev = k_cache.device
+    _need(v_cache, "v_cache", _BF16_BITS, (B, Hkv, T // KV_VBLOCK, KV_VBLOCK * KV_HEAD_DIM), dev)
+    return B, Hkv, T, dev
+
+
+def kv_cache_write_bf16(k: torch.Tensor, v: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Copy n new tokens' keys and values k, v [n, Hkv, 128] (BF16) into slot pos[i] of
+    sequence seq[i] of the BF16 cache."""
+    B, Hkv, T, dev = _kv16_shapes(k_cache, v_cache)
+    _need(k, "k", _BF16_BITS, None, dev)
+    if k.dim() != 3 or k.shape[1:] != (Hkv, KV_HEAD_DIM):
+        raise ValueError("k must be [n, Hkv, 128]")
+    n = k.shape[0]
+    _need(v, "v", _BF16_BITS, (n, Hkv, KV_HEAD_DIM), dev)
+    _need(seq, "seq", (torch.int32,), (n,), dev)
+    _need(pos, "pos", (torch.int32,), (n,), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_kv_cache_write_bf16(_ptr(k), _ptr(v), _ptr(seq), _ptr(pos), n, B, Hkv, T,
+                                             KV_HEAD_DIM, _ptr(k_cache), _ptr(v_cache),
+                                             _stream(dev)), "bsb_kv_cache_write_bf16")
+
+
+def attention_decode_bf16kv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            lens: torch.Tensor, max_len: int, out_dtype=torch.bfloat16,
+                            out: Optional[torch.Tensor] = None,
+                            work: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention of q [B, Hq, 128] (BF16) over the BF16 cache."""
+    B, Hkv, T, dev = _kv16_shapes(k_cache, v_cache)
+    _need(q, "q", _BF16_BITS, None, dev)
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != KV_HEAD_DIM:
+        raise ValueError("q must be [B, Hq, 128]")
+    Hq = q.shape[1]
+    _need(lens, "lens", (torch.int32,), (B,), dev)
+    code = _out_code(out_dtype)
+    out = torch.empty((B, Hq, KV_HEAD_DIM), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", (out_dtype,), (B, Hq, KV_HEAD_DIM), dev)
+    nbytes = attention_workspace_bytes(B, Hq, max_len)
+    if work is None:
+        work = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=dev)
+    _need(work, "work", (torch.float32,), None, dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_attention_decode_bf16kv(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), B, Hq, Hkv, T, KV_HEAD_DIM, max_len,
+            _ptr(work), work.numel() * 4, _ptr(out), code, _stream(dev)),
+            "bsb_attention_decode_bf16kv")
     return out

@@ -299,12 +299,14 @@ int64_t bsb_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t max_len) {
     return 4 * bsb::attention_workspace_floats(B, Hq, max_len);
 }
 
-bsb_status bsb_attention_decode_int8kv(const uint16_t *q_bf16, const int8_t *k_cache,
-                                       const float *k_scale, const int8_t *v_cache,
-                                       const float *v_scale, const int32_t *lens, int64_t B,
-                                       int64_t Hq, int64_t Hkv, int64_t T, int64_t D,
-                                       int64_t max_len, float *work, int64_t work_bytes,
-                                       void *out, bsb_out_dtype out_dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two attention entry points (caches checked by the caller).
+bsb_status attention_checks(const uint16_t *q, const int32_t *lens, int64_t B, int64_t Hq,
+                            int64_t Hkv, int64_t T, int64_t D, int64_t max_len, const float *work,
+                            int64_t work_bytes, const void *out, bsb_out_dtype out_dtype) noexcept {
     if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || Hq / Hkv > 16 || B * Hkv > 65535 ||
         B * Hq >= ((int64_t)1 << 31) || D != kKvHeadDim || T < 64 || T % 64 ||
         T >= kMaxKvSlots || max_len < 0 || max_len > T || !prod_le(B, Hkv, T, kMaxElems))
@@ -312,11 +314,27 @@ bsb_status bsb_attention_decode_int8kv(const uint16_t *q_bf16, const int8_t *k_c
     if (out_dtype != BSB_OUT_BF16 && out_dtype != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
     const int64_t need = bsb_attention_workspace_bytes(B, Hq, max_len);
     if (need < 0 || work_bytes < need) return BSB_ERR_INVALID_ARG;
-    if (!q_bf16 || !k_cache || !k_scale || !v_cache || !v_scale || !lens || !out ||
-        (need > 0 && !work))
-        return BSB_ERR_INVALID_ARG;
-    if (!aligned16(q_bf16) || !aligned16(k_cache) || !aligned16(k_scale) || !aligned16(v_cache) ||
-        !aligned16(v_scale) || !aligned16(lens) || !aligned16(out) || (work && !aligned16(work)))
+    if (!q || !lens || !out || (need > 0 && !work)) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(lens) || !aligned16(out) || (work && !aligned16(work)))
+        return BSB_ERR_MISALIGNED;
+    return BSB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bsb_status bsb_attention_decode_int8kv(const uint16_t *q_bf16, const int8_t *k_cache,
+                                       const float *k_scale, const int8_t *v_cache,
+                                       const float *v_scale, const int32_t *lens, int64_t B,
+                                       int64_t Hq, int64_t Hkv, int64_t T, int64_t D,
+                                       int64_t max_len, float *work, int64_t work_bytes,
+                                       void *out, bsb_out_dtype out_dtype, void *stream) {
+    if (bsb_status s = attention_checks(q_bf16, lens, B, Hq, Hkv, T, D, max_len, work, work_bytes,
+                                        out, out_dtype))
+        return s;
+    if (!k_cache || !k_scale || !v_cache || !v_scale) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(k_scale) || !aligned16(v_cache) || !aligned16(v_scale))
         return BSB_ERR_MISALIGNED;
     if (bsb_status s = check_device()) return s;
     (void)hipGetLastError();
@@ -324,6 +342,42 @@ bsb_status bsb_attention_decode_int8kv(const uint16_t *q_bf16, const int8_t *k_c
                                                (int)B, (int)Hq, (int)Hkv, (int)T, (int)max_len,
                                                work, out, out_dtype == BSB_OUT_BF16 ? 1 : 0,
                                                as_stream(stream)));
+}
+
+bsb_status bsb_kv_cache_write_bf16(const uint16_t *k_bf16, const uint16_t *v_bf16,
+                                   const int32_t *seq, const int32_t *pos, int64_t n, int64_t B,
+                                   int64_t Hkv, int64_t T, int64_t D, uint16_t *k_cache,
+                                   uint16_t *v_cache, void *stream) {
+    if (n < 0 || n >= kMaxDim || B < 1 || B >= kMaxDim || Hkv < 1 || Hkv >= kMaxDim ||
+        D != kKvHeadDim || T < 64 || T % 64 || T >= kMaxKvSlots ||
+        !prod_le(B, Hkv, T, kMaxElems) || (n > 0 && !prod_le(n, Hkv, 2 * D, kMaxElems)))
+        return BSB_ERR_INVALID_ARG;
+    if (n == 0) return BSB_OK;
+    if (!k_bf16 || !v_bf16 || !seq || !pos || !k_cache || !v_cache) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(seq) || !aligned16(pos) ||
+        !aligned16(k_cache) || !aligned16(v_cache))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_kv_cache_write_bf16(k_bf16, v_bf16, seq, pos, n, (int)B, (int)Hkv,
+                                                  (int)T, k_cache, v_cache, as_stream(stream)));
+}
+
+bsb_status bsb_attention_decode_bf16kv(const uint16_t *q_bf16, const uint16_t *k_cache,
+                                       const uint16_t *v_cache, const int32_t *lens, int64_t B,
+                                       int64_t Hq, int64_t Hkv, int64_t T, int64_t D,
+                                       int64_t max_len, float *work, int64_t work_bytes,
+                                       void *out, bsb_out_dtype out_dtype, void *stream) {
+    if (bsb_status s = attention_checks(q_bf16, lens, B, Hq, Hkv, T, D, max_len, work, work_bytes,
+                                        out, out_dtype))
+        return s;
+    if (!k_cache || !v_cache) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_attention_decode_bf16kv(
+        q_bf16, k_cache, v_cache, lens, (int)B, (int)Hq, (int)Hkv, (int)T, (int)max_len, work, out,
+        out_dtype == BSB_OUT_BF16 ? 1 : 0, as_stream(stream)));
 }
 
 }  // extern "C"

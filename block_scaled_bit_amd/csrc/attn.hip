@@ -64,6 +64,19 @@ __device__ __forceinline__ int vblk_off(int tau, int d) {
     return ((((tau & 15) >> 2) * 16 + (d & 15)) * 64) + (d >> 4) * 8 + (tau >> 4) * 4 + (tau & 3);
 }
 
+// The BF16 cache of the comparison route keeps the same blocks with 2-byte
+// elements: a 4 KB K block of 16 tokens (instruction s of a tile reads bytes
+// 1024s .. 1024s+1023, lane 16g + tau getting dims 32g + 8s .. 32g + 8s + 7)
+// and an 8 KB V block of 32 tokens (instruction i reads the d-tile 16i ..
+// 16i+15, lane 16g + r getting dim 16i + r of the 8 tokens of slot group g).
+__device__ __forceinline__ int kblk16_off(int tau, int d) {
+    return ((d >> 3) & 3) * 1024 + ((d >> 5) * 16 + tau) * 16 + (d & 7) * 2;
+}
+
+__device__ __forceinline__ int vblk16_off(int tau, int d) {
+    return (d >> 4) * 1024 + (((tau & 15) >> 2) * 16 + (d & 15)) * 16 + ((tau >> 4) * 4 + (tau & 3)) * 2;
+}
+
 // eight INT8 codes (little-endian in two dwords) -> eight BF16 values (exact)
 __device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
     bf16x8 r;
@@ -115,30 +128,68 @@ kv_write_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     }
 }
 
+// BF16 keys and values copied into the BF16 block layouts (no quantisation):
+// one wave per (token, KV head, K or V) vector, two values per lane.
+__global__ void __launch_bounds__(256)
+kv_write_bf16_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                     const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, int64_t n,
+                     int B, int Hkv, int T, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc) {
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (item >= n * Hkv * 2) return;                     // whole wave
+    const int which = (int)(item & 1);
+    const int64_t th = item >> 1;
+    const int64_t tok = th / Hkv;
+    const int h = (int)(th - tok * Hkv);
+    const int b = seq[tok], t = pos[tok];
+    if (b < 0 || b >= B || t < 0 || t >= T) return;     // whole wave: nothing written
+    const uint32_t w = reinterpret_cast<const uint32_t *>((which ? v : k) + th * kHD)[lane];
+    const int64_t bh = (int64_t)b * Hkv + h;
+    if (which == 0) {
+        uint8_t *blk = reinterpret_cast<uint8_t *>(kc) + (bh * T + (t & ~15)) * (2 * kHD);
+        *reinterpret_cast<uint32_t *>(blk + kblk16_off(t & 15, 2 * lane)) = w;   // d, d+1 adjacent
+    } else {
+        uint8_t *blk = reinterpret_cast<uint8_t *>(vc) + (bh * T + (t & ~31)) * (2 * kHD);
+        *reinterpret_cast<uint16_t *>(blk + vblk16_off(t & 31, 2 * lane)) = (uint16_t)(w & 0xFFFFu);
+        *reinterpret_cast<uint16_t *>(blk + vblk16_off(t & 31, 2 * lane + 1)) = (uint16_t)(w >> 16);
+    }
+}
+
 // The cached tokens of one (sequence, KV head) this wave owns: chunks of 64.
-struct KvChunk {
+// INT8: 8 KB of key codes, 8 KB of value codes and the 64 tokens' scales;
+// BF16: 16 KB of keys and 16 KB of values.
+enum { kKvInt8 = 0, kKvBf16 = 1 };
+
+template <int KVT> struct KvChunk;
+template <> struct KvChunk<kKvInt8> {
     v4i kd[4][2];   // keys: 16-token tile c, half j
     v4i vd[2][4];   // values: 32-token block s, quarter j
     float skl, svl; // scales of token t0 + lane
 };
+template <> struct KvChunk<kKvBf16> {
+    v4i kd[4][4];   // keys: 16-token tile c, k-step s
+    v4i vd[2][8];   // values: 32-token block s, d-tile i
+};
 
 // grid (splits, B * Hkv); 512 threads; a split is 8 * 64 * R tokens. Wave w
 // takes chunks r * 8 + w (r < R) of its split, so at each step the 8 waves
-// read adjacent 8 KB regions of the keys and of the values; a wave issues a
-// chunk's 18 loads together and keeps a running maximum, weight sum and
-// output across its chunks (online softmax).
+// read adjacent regions of the keys and of the values; a wave issues the loads
+// of one chunk (BF16) or of two chunks (INT8) together and keeps a running
+// maximum, weight sum and output across its chunks (online softmax).
 // part: [B*Hkv, splits, G, kPart] float32.
 // OUT: kPartials writes the split's (o, m, l) for the merge kernel; with a
 // single split the kernel writes the normalised output itself (kDirectBf16,
 // kDirectF32) and no merge runs.
 enum { kPartials = 0, kDirectBf16 = 1, kDirectF32 = 2 };
 
-template <int R, int OUT>
+template <int KVT, int R, int OUT>
 __global__ void __launch_bounds__(512)
-attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
-                  const float *__restrict__ ks, const int8_t *__restrict__ vc,
+attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
+                  const float *__restrict__ ks, const void *__restrict__ vc,
                   const float *__restrict__ vs, const int32_t *__restrict__ lens, int Hq, int Hkv,
                   int T, int max_len, float *__restrict__ part, void *__restrict__ out) {
+    constexpr bool I8 = KVT == kKvInt8;
+    constexpr int EB = I8 ? 1 : 2;                     // bytes per cached element
     __shared__ __align__(16) float s_o[kAttnWaves][16][kORow];
     __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
 
@@ -157,32 +208,48 @@ attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
 
     // this (sequence, KV head)'s slice of the cache, range-checked by the buffer
     // descriptors; the lane's part of an offset is in a VGPR, the rest scalar
-    const uint32_t tb = (uint32_t)T * kHD;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + (int64_t)bh * tb, tb);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + (int64_t)bh * tb, tb);
-    const __amdgpu_buffer_rsrc_t rks = make_rsrc(ks + (int64_t)bh * T, (uint32_t)T * 4);
-    const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vs + (int64_t)bh * T, (uint32_t)T * 4);
+    const uint32_t tb = (uint32_t)T * kHD * EB;
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc(reinterpret_cast<const uint8_t *>(kc) + (int64_t)bh * tb, tb);
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(reinterpret_cast<const uint8_t *>(vc) + (int64_t)bh * tb, tb);
     const uint32_t kvo = (uint32_t)lane * 16;
-    const uint32_t vvo = (uint32_t)lane * 64;
+    const uint32_t vvo = (uint32_t)lane * (I8 ? 64 : 16);
 
-    auto load = [&](KvChunk &ch, int r) {
+    auto load = [&](KvChunk<KVT> &ch, int r) {
         const int t0 = t0_of(r);
         const bool ok = r < R && t0 < L;
-        const uint32_t so = ok ? (uint32_t)t0 * kHD : kOOB, ss = ok ? (uint32_t)t0 * 4 : kOOB;
+        const uint32_t so = ok ? (uint32_t)t0 * kHD * EB : kOOB;
+        if constexpr (I8) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                ch.kd[c][j] = buf_load16s(rk, kvo, ok ? so + c * 2048 + j * 1024 : kOOB);
+                for (int j = 0; j < 2; ++j)
+                    ch.kd[c][j] = buf_load16s(rk, kvo, ok ? so + c * 2048 + j * 1024 : kOOB);
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                ch.vd[s][j] = buf_load16s(rv, vvo, ok ? so + s * (kVBlk * kHD) + 16 * j : kOOB);
-        ch.skl = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rks, (int)(lane * 4), (int)ss, 0));
-        ch.svl = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rvs, (int)(lane * 4), (int)ss, 0));
+                for (int j = 0; j < 4; ++j)
+                    ch.vd[s][j] = buf_load16s(rv, vvo, ok ? so + s * (kVBlk * kHD) + 16 * j : kOOB);
+            const __amdgpu_buffer_rsrc_t rks = make_rsrc(ks + (int64_t)bh * T, (uint32_t)T * 4);
+            const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vs + (int64_t)bh * T, (uint32_t)T * 4);
+            const uint32_t ss = ok ? (uint32_t)t0 * 4 : kOOB;
+            ch.skl = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rks, (int)(lane * 4), (int)ss, 0));
+            ch.svl = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rvs, (int)(lane * 4), (int)ss, 0));
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    ch.kd[c][s] = buf_load16s(rk, kvo, ok ? so + c * 4096 + s * 1024 : kOOB);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    ch.vd[s][i] = buf_load16s(rv, vvo, ok ? so + s * 8192 + i * 1024 : kOOB);
+        }
         // keep the whole chunk's loads here, ahead of the computation that follows
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
@@ -204,7 +271,7 @@ attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto compute = [&](const KvChunk &ch, int t0) {
+    auto compute = [&](const KvChunk<KVT> &ch, int t0) {
         // scores: tile c holds tokens t0 + 16c + 4grp + r (rows) for head col
         float x[4][4];
         float mc = kNegInf;
@@ -213,16 +280,22 @@ attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
             v4f_t acc = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const v4i &kk = ch.kd[c][s >> 1];
-                const bf16x8 a = i8x8_to_bf16((uint32_t)kk[2 * (s & 1)], (uint32_t)kk[2 * (s & 1) + 1]);
+                bf16x8 a;
+                if constexpr (I8) {
+                    const v4i &kk = ch.kd[c][s >> 1];
+                    a = i8x8_to_bf16((uint32_t)kk[2 * (s & 1)], (uint32_t)kk[2 * (s & 1) + 1]);
+                } else {
+                    a = __builtin_bit_cast(bf16x8, ch.kd[c][s]);
+                }
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qd[s]),
                                                               acc, 0, 0, 0);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tt = 16 * c + 4 * grp + r;
-                const float sk = __shfl(ch.skl, tt, kWave);
-                const float sv = (acc[r] * sk) * kScoreScale;
+                float sv;
+                if constexpr (I8) sv = (acc[r] * __shfl(ch.skl, tt, kWave)) * kScoreScale;
+                else sv = acc[r] * kScoreScale;
                 x[c][r] = (t0 + tt < L) ? sv : kNegInf;
                 mc = __builtin_fmaxf(mc, x[c][r]);
             }
@@ -251,27 +324,49 @@ attn_split_kernel(const uint16_t *__restrict__ q, const int8_t *__restrict__ kc,
             bf16x8 pw;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float sva = __shfl(ch.svl, ta + j, kWave);
-                const float svb = __shfl(ch.svl, tbk + j, kWave);
-                pw[j] = (__bf16)(t0 + ta + j < L ? p[2 * s][j] * sva : 0.0f);
-                pw[4 + j] = (__bf16)(t0 + tbk + j < L ? p[2 * s + 1][j] * svb : 0.0f);
+                float pa = p[2 * s][j], pb2 = p[2 * s + 1][j];
+                if constexpr (I8) {
+                    pa *= __shfl(ch.svl, ta + j, kWave);
+                    pb2 *= __shfl(ch.svl, tbk + j, kWave);
+                }
+                pw[j] = (__bf16)(t0 + ta + j < L ? pa : 0.0f);
+                pw[4 + j] = (__bf16)(t0 + tbk + j < L ? pb2 : 0.0f);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const v4i &vv = ch.vd[s][i >> 1];
-                const bf16x8 a = i8x8_to_bf16((uint32_t)vv[2 * (i & 1)], (uint32_t)vv[2 * (i & 1) + 1]);
+                bf16x8 a;
+                if constexpr (I8) {
+                    const v4i &vv = ch.vd[s][i >> 1];
+                    a = i8x8_to_bf16((uint32_t)vv[2 * (i & 1)], (uint32_t)vv[2 * (i & 1) + 1]);
+                } else {
+                    a = __builtin_bit_cast(bf16x8, ch.vd[s][i]);
+                }
                 o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pw, o[i], 0, 0, 0);
             }
         }
     };
 
     if (t0_of(0) < L) {   // whole wave
-        KvChunk A;
+        if constexpr (I8 && R >= 2) {
+            // two chunks' loads in flight together (33 KB per wave, as one BF16
+            // chunk), then both computed
+            KvChunk<KVT> A, B;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (t0_of(r) >= L) break;
-            load(A, r);
-            compute(A, t0_of(r));
+            for (int r = 0; r < R; r += 2) {
+                if (t0_of(r) >= L) break;
+                load(A, r);
+                load(B, r + 1);
+                compute(A, t0_of(r));
+                if (t0_of(r + 1) < L) compute(B, t0_of(r + 1));
+            }
+        } else {
+            KvChunk<KVT> A;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (t0_of(r) >= L) break;
+                load(A, r);
+                compute(A, t0_of(r));
+            }
         }
     }
     float l = lpart + __shfl_xor(lpart, 16, kWave);
@@ -379,38 +474,67 @@ attn_combine_kernel(const float *__restrict__ part, int Hq, int Hkv, int nsplit,
     }
 }
 
-template <int R, int OUT>
-hipError_t launch_split(dim3 grid, const uint16_t *q, const int8_t *kc, const float *ks,
-                        const int8_t *vc, const float *vs, const int32_t *lens, int Hq, int Hkv,
+template <int KVT, int R, int OUT>
+hipError_t launch_split(dim3 grid, const uint16_t *q, const void *kc, const float *ks,
+                        const void *vc, const float *vs, const int32_t *lens, int Hq, int Hkv,
                         int T, int max_len, float *work, void *out, hipStream_t stream) {
-    attn_split_kernel<R, OUT><<<grid, kAttnWaves * kWave, 0, stream>>>(
+    attn_split_kernel<KVT, R, OUT><<<grid, kAttnWaves * kWave, 0, stream>>>(
         q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out);
     return hipGetLastError();
 }
 
-template <int OUT>
-hipError_t launch_split_o(int R, dim3 grid, const uint16_t *q, const int8_t *kc, const float *ks,
-                          const int8_t *vc, const float *vs, const int32_t *lens, int Hq, int Hkv,
+template <int KVT, int OUT>
+hipError_t launch_split_o(int R, dim3 grid, const uint16_t *q, const void *kc, const float *ks,
+                          const void *vc, const float *vs, const int32_t *lens, int Hq, int Hkv,
                           int T, int max_len, float *work, void *out, hipStream_t stream) {
     switch (R) {
-        case 1: return launch_split<1, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
-        case 2: return launch_split<2, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
-        case 4: return launch_split<4, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
-        default: return launch_split<8, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        case 1: return launch_split<KVT, 1, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        case 2: return launch_split<KVT, 2, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        case 4: return launch_split<KVT, 4, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        default: return launch_split<KVT, 8, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
     }
 }
 
 // the split kernel for R chunks per wave over ceil(max_len / (512 R)) splits
-hipError_t launch_split_r(int R, int out_mode, const uint16_t *q, const int8_t *kc, const float *ks,
-                          const int8_t *vc, const float *vs, const int32_t *lens, int B, int Hq,
+template <int KVT>
+hipError_t launch_split_r(int R, int out_mode, const uint16_t *q, const void *kc, const float *ks,
+                          const void *vc, const float *vs, const int32_t *lens, int B, int Hq,
                           int Hkv, int T, int max_len, float *work, void *out, hipStream_t stream) {
     const int64_t ns = (max_len + (int64_t)kSplitTok * R - 1) / ((int64_t)kSplitTok * R);
     const dim3 grid((unsigned)ns, (unsigned)(B * Hkv));
     if (out_mode == kDirectBf16)
-        return launch_split_o<kDirectBf16>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        return launch_split_o<KVT, kDirectBf16>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
     if (out_mode == kDirectF32)
-        return launch_split_o<kDirectF32>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
-    return launch_split_o<kPartials>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        return launch_split_o<KVT, kDirectF32>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+    return launch_split_o<KVT, kPartials>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+}
+
+// Both cache types: R chunks per wave, one or several splits, then the merge.
+template <int KVT>
+hipError_t attention_decode(const uint16_t *q, const void *kc, const float *ks, const void *vc,
+                            const float *vs, const int32_t *lens, int B, int Hq, int Hkv, int T,
+                            int max_len, float *work, void *out, int out_bf16, hipStream_t stream) {
+    // chunks per wave (1, 2, 4 or 8): the most that keep at least kMinWorkgroups
+    // workgroups in the grid (long-lived waves, fewer partials to merge)
+    const int64_t units = (int64_t)B * Hkv * attention_splits(max_len);
+    int R = 1;
+    while (R < kMaxChunks && units / (2 * R) >= kMinWorkgroups) R *= 2;
+    const int64_t ns = (max_len + kSplitTok * R - 1) / (kSplitTok * R);
+    if (ns == 1)   // one split holds every sequence: it writes the output, no merge
+        return launch_split_r<KVT>(R, out_bf16 ? kDirectBf16 : kDirectF32, q, kc, ks, vc, vs, lens,
+                                   B, Hq, Hkv, T, max_len, work, out, stream);
+    if (ns > 0) {   // max_len == 0: no split to run, the combine writes zeros
+        hipError_t e = launch_split_r<KVT>(R, kPartials, q, kc, ks, vc, vs, lens, B, Hq, Hkv, T,
+                                           max_len, work, out, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (out_bf16)
+        attn_combine_kernel<true><<<dim3((unsigned)(B * Hq)), 64, 0, stream>>>(work, Hq, Hkv,
+                                                                               (int)ns, out);
+    else
+        attn_combine_kernel<false><<<dim3((unsigned)(B * Hq)), 64, 0, stream>>>(work, Hq, Hkv,
+                                                                                (int)ns, out);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -436,27 +560,27 @@ hipError_t launch_attention_decode(const uint16_t *q, const int8_t *kc, const fl
                                    const int8_t *vc, const float *vs, const int32_t *lens, int B,
                                    int Hq, int Hkv, int T, int max_len, float *work, void *out,
                                    int out_bf16, hipStream_t stream) {
-    // chunks per wave (1, 2, 4 or 8): the most that keep at least kMinWorkgroups
-    // workgroups in the grid (long-lived waves, fewer partials to merge)
-    const int64_t units = (int64_t)B * Hkv * attention_splits(max_len);
-    int R = 1;
-    while (R < kMaxChunks && units / (2 * R) >= kMinWorkgroups) R *= 2;
-    const int64_t ns = (max_len + kSplitTok * R - 1) / (kSplitTok * R);
-    if (ns == 1)   // one split holds every sequence: it writes the output, no merge
-        return launch_split_r(R, out_bf16 ? kDirectBf16 : kDirectF32, q, kc, ks, vc, vs, lens, B,
-                              Hq, Hkv, T, max_len, work, out, stream);
-    if (ns > 0) {   // max_len == 0: no split to run, the combine writes zeros
-        hipError_t e = launch_split_r(R, kPartials, q, kc, ks, vc, vs, lens, B, Hq, Hkv, T,
-                                      max_len, work, out, stream);
-        if (e != hipSuccess) return e;
-    }
-    if (out_bf16)
-        attn_combine_kernel<true><<<dim3((unsigned)(B * Hq)), 64, 0, stream>>>(work, Hq, Hkv,
-                                                                               (int)ns, out);
-    else
-        attn_combine_kernel<false><<<dim3((unsigned)(B * Hq)), 64, 0, stream>>>(work, Hq, Hkv,
-                                                                                (int)ns, out);
+    return attention_decode<kKvInt8>(q, kc, ks, vc, vs, lens, B, Hq, Hkv, T, max_len, work, out,
+                                     out_bf16, stream);
+}
+
+hipError_t launch_kv_cache_write_bf16(const uint16_t *k, const uint16_t *v, const int32_t *seq,
+                                      const int32_t *pos, int64_t n, int B, int Hkv, int T,
+                                      uint16_t *kc, uint16_t *vc, hipStream_t stream) {
+    const int64_t items = n * Hkv * 2;
+    const int64_t blocks = (items + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    kv_write_bf16_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(k, v, seq, pos, n, B, Hkv, T,
+                                                                     kc, vc);
     return hipGetLastError();
+}
+
+hipError_t launch_attention_decode_bf16kv(const uint16_t *q, const uint16_t *kc,
+                                          const uint16_t *vc, const int32_t *lens, int B, int Hq,
+                                          int Hkv, int T, int max_len, float *work, void *out,
+                                          int out_bf16, hipStream_t stream) {
+    return attention_decode<kKvBf16>(q, kc, nullptr, vc, nullptr, lens, B, Hq, Hkv, T, max_len,
+                                     work, out, out_bf16, stream);
 }
 
 }  // namespace bsb

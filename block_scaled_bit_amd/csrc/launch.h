@@ -64,4 +64,14 @@ hipError_t launch_attention_decode(const uint16_t *q, const int8_t *kc, const fl
                                    int Hq, int Hkv, int T, int max_len, float *work, void *out,
                                    int out_bf16, hipStream_t stream);
 
+// The BF16 KV cache of the comparison route (same blocks, 2-byte elements, no scales).
+hipError_t launch_kv_cache_write_bf16(const uint16_t *k, const uint16_t *v, const int32_t *seq,
+                                      const int32_t *pos, int64_t n, int B, int Hkv, int T,
+                                      uint16_t *kc, uint16_t *vc, hipStream_t stream);
+
+hipError_t launch_attention_decode_bf16kv(const uint16_t *q, const uint16_t *kc,
+                                          const uint16_t *vc, const int32_t *lens, int B, int Hq,
+                                          int Hkv, int T, int max_len, float *work, void *out,
+                                          int out_bf16, hipStream_t stream);
+
 }  // namespace bsb

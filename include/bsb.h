@@ -326,6 +326,34 @@ bsb_status bsb_attention_decode_int8kv(const uint16_t *q_bf16,
                                        float *work, int64_t work_bytes,
                                        void *out, bsb_out_dtype out_dtype, void *stream);
 
+/*
+ * The comparison route of the INT8 KV cache: the same cache and attention with
+ * BF16 keys and values (no scales, nothing quantised), the cache the INT8 one
+ * replaces ([P3] sec. 2.2 counts it at 2 bytes per element).
+ * Cache layout (T as above):
+ *   k_cache [B, Hkv, T/16, 2048] BF16 bits: blocks of 16 tokens; token tau and
+ *           dimension d at element ((d/8)%4)*512 + ((d/32)*16 + tau)*8 + d%8
+ *   v_cache [B, Hkv, T/32, 4096] BF16 bits: blocks of 32 tokens; token tau and
+ *           dimension d at element (d/16)*512 + (((tau%16)/4)*16 + d%16)*8 +
+ *           (tau/16)*4 + tau%4
+ * bsb_kv_cache_write_bf16 copies n tokens' keys and values into their slots
+ * (arguments as bsb_kv_cache_write, without scales);
+ * bsb_attention_decode_bf16kv computes the attention of
+ * bsb_attention_decode_int8kv with K and V the cached BF16 values (arguments,
+ * workspace, bound and errors as there).
+ */
+bsb_status bsb_kv_cache_write_bf16(const uint16_t *k_bf16, const uint16_t *v_bf16,
+                                   const int32_t *seq, const int32_t *pos, int64_t n,
+                                   int64_t B, int64_t Hkv, int64_t T, int64_t D,
+                                   uint16_t *k_cache, uint16_t *v_cache, void *stream);
+
+bsb_status bsb_attention_decode_bf16kv(const uint16_t *q_bf16,
+                                       const uint16_t *k_cache, const uint16_t *v_cache,
+                                       const int32_t *lens, int64_t B, int64_t Hq,
+                                       int64_t Hkv, int64_t T, int64_t D, int64_t max_len,
+                                       float *work, int64_t work_bytes,
+                                       void *out, bsb_out_dtype out_dtype, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *bsb_status_string(bsb_status s);
 

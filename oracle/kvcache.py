@@ -95,10 +95,40 @@ def attention_int8kv_ref(q_bits, k_codes, k_scales, v_codes, v_scales, lens):
     return o, mag
 
 
-def attention_tolerance(out_bf16: bool) -> float:
-    """t with |o_kernel - o| <= t * mag elementwise.
+def attention_bf16kv_ref(q_bits, k_bits, v_bits, lens):
+    """The same attention over a BF16 cache (the cache the INT8 one replaces): K and V
+    are the cached BF16 values, exact in float64. Arguments as attention_int8kv_ref
+    with k_bits, v_bits BF16 bits [B, Hkv, T, D]; returns (o, mag)."""
+    q = bf16_bits_to_f32(q_bits).astype(np.float64)
+    B, Hq, D = q.shape
+    _, Hkv, T, Dk = k_bits.shape
+    if Dk != D or v_bits.shape != k_bits.shape or Hq % Hkv:
+        raise ValueError("q [B,Hq,D], k/v [B,Hkv,T,D] with Hq a multiple of Hkv required")
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, D))
+    mag = np.zeros((B, Hq, D))
+    for b in range(B):
+        L = int(lens[b])
+        if not 0 <= L <= T:
+            raise ValueError("lens out of range")
+        if L == 0:
+            continue
+        for kv in range(Hkv):
+            K = bf16_bits_to_f32(k_bits[b, kv, :L]).astype(np.float64)
+            V = bf16_bits_to_f32(v_bits[b, kv, :L]).astype(np.float64)
+            for h in range(kv * G, (kv + 1) * G):
+                z = K @ q[b, h] / np.sqrt(D)
+                e = np.exp(z - z.max())
+                w = e / e.sum()
+                o[b, h] = w @ V
+                mag[b, h] = w @ np.abs(V)
+    return o, mag
 
-    The matrix cores take the weights w[t] * sv[t] rounded to BF16 (relative
+
+def attention_tolerance(out_bf16: bool) -> float:
+    """t with |o_kernel - o| <= t * mag elementwise (both caches).
+
+    The matrix cores take the weights w[t] * sv[t] (w[t] for BF16 values) rounded to BF16 (relative
     error <= 2^-8 each, so <= 2^-8 * mag on the sum); the float32 scores,
     exponentials and normalisation add well under another 2^-8 * mag for
     score terms sum_d |q[d] K[t,d]| / sqrt(D) up to ~100; a BF16 output adds

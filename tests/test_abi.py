@@ -200,3 +200,22 @@ def test_kv_cache_argument_checks(L):
         assert call() == UNSUPPORTED
         assert call(max_len=0, work=None, work_bytes=0) == UNSUPPORTED
         assert wr(A, A, A, A, 3, 2, 4, 128, 128, A, A, A, A, None) == UNSUPPORTED
+
+
+def test_bf16_kv_cache_argument_checks(L):
+    wr, at, wb = L.bsb_kv_cache_write_bf16, L.bsb_attention_decode_bf16kv, L.bsb_attention_workspace_bytes
+    assert wr(A, A, A, A, 3, 2, 4, 128, 64, A, A, None) == INVALID          # D != 128
+    assert wr(A, A, A, A, 3, 2, 4, 96, 128, A, A, None) == INVALID          # T % 64
+    assert wr(A, A, A, A, 3, 2, 4, 128, 128, A, None, None) == INVALID
+    assert wr(A, A, A, A, 3, 2, 4, 128, 128, U, A, None) == MISALIGNED
+    assert wr(None, None, None, None, 0, 2, 4, 128, 128, None, None, None) == OK
+    need = wb(2, 16, 128)
+    assert at(A, A, A, A, 2, 16, 4, 128, 128, 128, A, need, A, 0, None) in (OK, UNSUPPORTED)
+    assert at(A, A, A, A, 2, 15, 4, 128, 128, 128, A, need, A, 0, None) == INVALID
+    assert at(A, A, A, A, 2, 16, 4, 128, 128, 129, A, need, A, 0, None) == INVALID
+    assert at(A, A, A, A, 2, 16, 4, 128, 128, 128, A, need - 4, A, 0, None) == INVALID
+    assert at(A, None, A, A, 2, 16, 4, 128, 128, 128, A, need, A, 0, None) == INVALID
+    assert at(A, A, U, A, 2, 16, 4, 128, 128, 128, A, need, A, 0, None) == MISALIGNED
+    if not torch.cuda.is_available():
+        assert at(A, A, A, A, 2, 16, 4, 128, 128, 128, A, need, A, 1, None) == UNSUPPORTED
+        assert wr(A, A, A, A, 3, 2, 4, 128, 128, A, A, None) == UNSUPPORTED

@@ -269,3 +269,77 @@ def test_attention_multi_chunk_waves(B, Hq, Hkv, T, max_len):
             o64, mag = attention_int8kv_ref(inp["q"][b:b + 1], kc[b:b + 1], ks[b:b + 1],
                                             vc[b:b + 1], vs[b:b + 1], eff)
             _check(y[b:b + 1], o64, mag, dtype == torch.bfloat16)
+
+
+# ---- the BF16 cache of the comparison route ----------------------------------
+
+K16_OFF = ((_d // 8) % 4) * 512 + ((_d // 32) * 16 + _kt) * 8 + _d % 8
+V16_OFF = (_d // 16) * 512 + (((_tau % 16) // 4) * 16 + _d % 16) * 8 + (_tau // 16) * 4 + _tau % 4
+
+
+def k16_encode(k):
+    B, H, T, _ = k.shape
+    out = np.empty((B, H, T // KB, KB * D), np.uint16)
+    out[..., K16_OFF] = k.reshape(B, H, T // KB, KB, D)
+    return out
+
+
+def v16_encode(v):
+    B, H, T, _ = v.shape
+    out = np.empty((B, H, T // VB, VB * D), np.uint16)
+    out[..., V16_OFF] = v.reshape(B, H, T // VB, VB, D)
+    return out
+
+
+def test_bf16_layouts_are_permutations():
+    assert np.array_equal(np.sort(K16_OFF.ravel()), np.arange(KB * D))
+    assert np.array_equal(np.sort(V16_OFF.ravel()), np.arange(VB * D))
+
+
+def test_bf16_write_copies_into_the_layout():
+    d = require_gpu()
+    B, H, T = 2, 4, 128
+    inp = synth.kv_inputs(B, H, H, T, seed=50)
+    kc, vc = bsb.kv_cache_empty_bf16(B, H, T, d)
+    kc.view(torch.int16).fill_(0x5555)
+    vc.view(torch.int16).fill_(0x5555)
+    slots = [(b, t) for b in range(B) for t in range(T) if (b + t) % 3]
+    seq = np.array([s[0] for s in slots] + [B], np.int32)
+    pos = np.array([s[1] for s in slots] + [0], np.int32)
+    kn = np.stack([inp["k"][b, :, t] for b, t in slots] + [inp["k"][0, :, 0]])
+    vn = np.stack([inp["v"][b, :, t] for b, t in slots] + [inp["v"][0, :, 0]])
+    bsb.kv_cache_write_bf16(dev_bf16(kn, d), dev_bf16(vn, d), dev(seq, d), dev(pos, d), kc, vc)
+    torch.cuda.synchronize()
+    gk = host(kc)[..., K16_OFF].reshape(B, H, T, D)
+    gv = host(vc)[..., V16_OFF].reshape(B, H, T, D)
+    for b in range(B):
+        for t in range(T):
+            if (b + t) % 3:
+                assert np.array_equal(gk[b, :, t], inp["k"][b, :, t])
+                assert np.array_equal(gv[b, :, t], inp["v"][b, :, t])
+            else:
+                assert (gk[b, :, t] == 0x5555).all() and (gv[b, :, t] == 0x5555).all()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,lens,max_len", [
+    (2, 8, 1, 128, [128, 77], 128),
+    (3, 32, 2, 1088, [1088, 1, 600], 1088),     # G = 16, three splits
+    (32, 8, 8, 1280, None, 1280),               # two chunks per wave over two splits
+])
+def test_bf16_attention_matches_oracle(B, Hq, Hkv, T, lens, max_len):
+    from oracle import attention_bf16kv_ref
+    d = require_gpu()
+    say(f"bf16 attention B={B} Hq={Hq} Hkv={Hkv} T={T}")
+    inp = synth.kv_inputs(B, Hq, Hkv, T, lens=lens, seed=B + T)
+    lens = inp["lens"]
+    for dtype in (torch.float32, torch.bfloat16):
+        out = bsb.attention_decode_bf16kv(dev_bf16(inp["q"], d), dev_bf16(k16_encode(inp["k"]), d),
+                                          dev_bf16(v16_encode(inp["v"]), d), dev(lens, d),
+                                          max_len, out_dtype=dtype)
+        torch.cuda.synchronize()
+        y = host(out)
+        y = (bf16_bits_to_f32_ref(y) if dtype == torch.bfloat16 else y).astype(np.float64)
+        for b in range(min(B, 6)):
+            o64, mag = attention_bf16kv_ref(inp["q"][b:b + 1], inp["k"][b:b + 1], inp["v"][b:b + 1],
+                                            np.minimum(lens[b:b + 1], max_len))
+            _check(y[b:b + 1], o64, mag, dtype == torch.bfloat16)

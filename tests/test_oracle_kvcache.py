@@ -206,3 +206,39 @@ def test_dequant_is_exact():
     for j, c in enumerate(codes[0]):
         assert F(V[0, j]) == F(s[0]) * int(c)
     assert Fraction(V[0, 4]) == F(np.float32(0.1)) * 127
+
+
+# ---- the BF16 cache of the comparison route ----------------------------------
+
+def test_bf16_cache_matches_torch_sdpa_in_float64():
+    from oracle import attention_bf16kv_ref
+    B, Hq, Hkv, T = 2, 8, 2, 90
+    d = synth.kv_inputs(B, Hq, Hkv, T, lens=[90, 17], q_gain=2.0, seed=41)
+    o, _ = attention_bf16kv_ref(d["q"], d["k"], d["v"], d["lens"])
+    q = torch.from_numpy(bf16_bits_to_f32_ref(d["q"]).astype(np.float64))
+    K = torch.from_numpy(bf16_bits_to_f32_ref(d["k"]).astype(np.float64))
+    V = torch.from_numpy(bf16_bits_to_f32_ref(d["v"]).astype(np.float64))
+    for b, L in enumerate(d["lens"]):
+        Kb = K[b, :, :L].repeat_interleave(Hq // Hkv, dim=0)[None]
+        Vb = V[b, :, :L].repeat_interleave(Hq // Hkv, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q[b][None, :, None, :], Kb, Vb)
+        assert np.allclose(o[b], ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_bf16_cache_of_exact_int8_values_is_the_int8_attention():
+    """Codes times power-of-two scales are exact in BF16: both routes then attend
+    the same K and V, and the two definitions agree."""
+    from oracle import attention_bf16kv_ref
+    rng = np.random.default_rng(42)
+    B, Hq, Hkv, T = 2, 4, 2, 40
+    d = synth.kv_inputs(B, Hq, Hkv, T, lens=[40, 9], seed=42)
+    kc = rng.integers(-127, 128, size=(B, Hkv, T, 128)).astype(np.int8)
+    vc = rng.integers(-127, 128, size=(B, Hkv, T, 128)).astype(np.int8)
+    ks = (2.0 ** -rng.integers(4, 10, size=(B, Hkv, T))).astype(np.float32)
+    vs = (2.0 ** -rng.integers(4, 10, size=(B, Hkv, T))).astype(np.float32)
+    kb = f32_to_bf16_bits_ref(dequant_kv_ref(kc, ks).astype(np.float32))
+    vb = f32_to_bf16_bits_ref(dequant_kv_ref(vc, vs).astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f32_ref(kb), dequant_kv_ref(kc, ks).astype(np.float32))
+    o8, m8 = attention_int8kv_ref(d["q"], kc, ks, vc, vs, d["lens"])
+    o16, m16 = attention_bf16kv_ref(d["q"], kb, vb, d["lens"])
+    assert np.allclose(o8, o16, rtol=1e-13, atol=1e-15) and np.allclose(m8, m16, rtol=1e-13)
