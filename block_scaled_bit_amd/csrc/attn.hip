@@ -28,9 +28,14 @@
 //   p = exp2(x - m) against the running maximum m per head (float32);
 //   o^T[d, head] += V^T . (p * v_scale)^T on the same MFMA, the weights times
 //           the value scales rounded to BF16, the value codes converted exactly.
-// The 8 wave results are merged in LDS (max, rescaled sums) into one partial
-// (m, l, o[128]) per head and split; a second kernel merges the splits and
-// divides by the total weight.
+// The 8 wave results are merged in LDS (max, rescaled sums). With one split
+// per sequence the kernel then divides by the total weight and writes the
+// output; otherwise it writes one partial (m, l, o[128]) per head and split and
+// a second kernel merges the splits.
+//
+// The same kernel also runs over a BF16 cache (the cache the INT8 one
+// replaces, kept as the comparison route): 2-byte elements in blocks of the
+// same operand order, no conversion and no scales.
 #include "device_common.h"
 #include "launch.h"
 
