@@ -265,6 +265,14 @@ def extra_rows(torch, L, stream, dev, steps):
     log(f"tiny: quant {tq * 1e3:.1f} us, gemm {tg * 1e3:.1f} us")
     torch.cuda.empty_cache()
 
+    # one GPU's share of the decode linear under 8-way column (tensor) parallelism:
+    # N / 8 = 3584 columns, 29 MB of weights (the exchange itself is not run)
+    tq, tg = linear_rows("tp8", 32, 8192, 3584, 0.005, 30.0)
+    rows["tp8_share_decode_32x8192x3584_gemm"] = _rate(tg * 1e3, ops=2 * 32 * 3584 * 8192,
+                                                       byts=gemm_bytes(32, 3584, 8192))
+    log(f"tp8 share of the decode linear: gemm {tg * 1e3:.1f} us")
+    torch.cuda.empty_cache()
+
     # prefill-shaped quantisation (the GEMM is timed separately)
     M, K = 4096, 8192
     d = synth.linear_inputs(M, K, 128, outlier_p=0.005, outlier_f=30.0, seed=0)
@@ -367,6 +375,31 @@ def extra_rows(torch, L, stream, dev, steps):
                                                  bound="mfma+hbm")
     rows["moe_4096tok_top8_64e_grouped"].update(rows=R, experts_nonempty=nonempty)
     log(f"moe: quant {tq * 1e3:.1f} us, grouped {tg * 1e3:.1f} us")
+    # one GPU's share under 8-way expert parallelism (experts e with e % 8 == r on
+    # GPU r): the grouped GEMM over the 8 experts of the GPU with the most rows,
+    # with their real skewed row counts (the all-to-all itself is not run)
+    per = np.diff(off_h)
+    gpu = max(range(8), key=lambda r: int(per[r::8].sum()))
+    mine = list(range(gpu, E, 8))
+    idx = np.concatenate([np.arange(off_h[e], off_h[e + 1]) for e in mine]).astype(np.int64)
+    off8 = np.concatenate([[0], np.cumsum(per[mine])]).astype(np.int32)
+    R8 = int(off8[-1])
+    ii = torch.from_numpy(idx).to(dev)
+    ei = torch.tensor(mine, dtype=torch.int64, device=dev)
+    p8 = dict(q=q[ii].contiguous(), sa=sa[ii].contiguous(), qw=qw[ei].contiguous(),
+              sw=sw[ei].contiguous(), off=t(off8),
+              y=torch.empty((R8, N), dtype=torch.int16, device=dev))
+    pp8 = {k: v.data_ptr() for k, v in p8.items()}
+    t8 = Row("ep8 share grouped", [pp8], lambda p, st: _ok(
+        L, L.bsb_grouped_gemm_w8a8_g128(p["q"], p["sa"], p["qw"], p["sw"], p["off"], 8, R8, N, K,
+                                        p["y"], 0, st))).time(torch, stream, 20, 3)
+    ne8 = int((per[mine] > 0).sum())
+    b8 = R8 * K + 4 * R8 + ne8 * (N * K + 4 * N * G) + 2 * R8 * N + 36
+    rows["ep8_share_moe_grouped"] = _rate(t8 * 1e3, ops=2 * R8 * N * K, byts=b8,
+                                          bound="mfma+hbm") | {
+        "gpu": gpu, "experts": mine, "rows": R8, "rows_per_gpu": [int(per[r::8].sum()) for r in range(8)]}
+    log(f"ep8 share (GPU {gpu}, {R8} rows): grouped {t8 * 1e3:.1f} us")
+    del p8, pp8, ii, ei
     # the glue either side: quantise the T tokens, gather into expert order,
     # (grouped GEMM), combine the top-k outputs per token
     T, topk = m["T"], m["topk"]

@@ -126,6 +126,20 @@ def test_decode_config_full():
         assert np.array_equal(host(bsb.gemm_w8a8_g128(qd, sd, qwd, swd)), yb)
 
 
+def test_tp8_share_of_the_decode_linear():
+    """One GPU's column share of the decode linear under 8-way tensor parallelism
+    (N = 3584), as the benchmark times it: full output against the oracle."""
+    d = require_gpu()
+    say("gemm decode share M=32 K=8192 N=3584")
+    cfg = synth.linear_inputs(32, 8192, 3584, outlier_p=0.005, outlier_f=30.0, seed=0)
+    q, sa = quantize_act_ref(cfg["x"])
+    qd, sd = bsb.quantize_act(dev_bf16(cfg["x"], d))
+    assert np.array_equal(host(qd), q) and np.array_equal(host(sd), sa)
+    y64, mag = gemm_ref(q, sa, cfg["qw"], cfg["sw"])
+    _, cb = gemm_fp32_ordered_ref(q, sa, cfg["qw"], cfg["sw"])
+    check_bf16(host(bsb.gemm_w8a8_g128(qd, sd, dev(cfg["qw"], d), dev(cfg["sw"], d))), y64, mag, cb)
+
+
 def test_prefill_config_sampled():
     """Prefill-shaped linear at full size; eight 128x128 output tiles checked against the oracle."""
     d = require_gpu()
