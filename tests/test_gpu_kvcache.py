@@ -343,3 +343,28 @@ def test_bf16_attention_matches_oracle(B, Hq, Hkv, T, lens, max_len):
             o64, mag = attention_bf16kv_ref(inp["q"][b:b + 1], inp["k"][b:b + 1], inp["v"][b:b + 1],
                                             np.minimum(lens[b:b + 1], max_len))
             _check(y[b:b + 1], o64, mag, dtype == torch.bfloat16)
+
+
+@pytest.mark.parametrize("route", ["int8", "bf16"])
+def test_attention_more_than_eight_splits(route):
+    """One sequence of 5120 tokens: ten 512-token splits, which the merge kernel reads
+    in two batches of eight (running maximum across batches)."""
+    from oracle import attention_bf16kv_ref
+    d = require_gpu()
+    B, Hq, Hkv, T = 2, 8, 1, 5120
+    lens = np.array([5120, 4700], np.int32)
+    say(f"attention {route}, ten splits")
+    inp = synth.kv_inputs(B, Hq, Hkv, T, lens=lens, q_gain=3.0, seed=77)
+    if route == "int8":
+        kc, ks = kv_quantize_ref(inp["k"])
+        vc, vs = kv_quantize_ref(inp["v"])
+        y = _run_attn(inp["q"], kc, ks, vc, vs, lens, T, torch.float32, d)
+        o64, mag = attention_int8kv_ref(inp["q"], kc, ks, vc, vs, lens)
+    else:
+        out = bsb.attention_decode_bf16kv(dev_bf16(inp["q"], d), dev_bf16(k16_encode(inp["k"]), d),
+                                          dev_bf16(v16_encode(inp["v"]), d), dev(lens, d), T,
+                                          out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        y = host(out).astype(np.float64)
+        o64, mag = attention_bf16kv_ref(inp["q"], inp["k"], inp["v"], lens)
+    _check(y, o64, mag, False)
