@@ -599,7 +599,7 @@ def kv_rows(torch, L, stream, dev, steps):
         p["q"], p["kc"], p["ks"], p["vc"], p["vs"], p["lens"], B, Hq, Hkv, T, D, T, p["work"],
         wbytes, p["out"], 0, st))).time(torch, stream, steps, 3)
     rows["kv_int8_attention_decode_b32_t4096"] = _rate(ta * 1e3, byts=a_bytes) | {
-        "kernel": "attn_split_kernel<8, 1> (one launch)", "traffic": measured_traffic("kv_attention")}
+        "kernel": "attn_split_kernel<0, 8, 1> (INT8 cache, one launch)", "traffic": measured_traffic("kv_attention")}
     log(f"kv attention (decode, 32 x 4096 tokens) {ta * 1e3:.1f} us")
     del asets, kc, ks, vc, vs, step, wsets
     torch.cuda.empty_cache()
@@ -617,7 +617,8 @@ def kv_rows(torch, L, stream, dev, steps):
         p["q"], p["kc"], p["vc"], p["lens"], B, Hq, Hkv, T, D, T, p["work"], wbytes, p["out"], 0,
         st))).time(torch, stream, steps, 3)
     rows["kv_bf16_attention_decode_b32_t4096"] = _rate(tbf * 1e3, byts=b_bytes) | {
-        "int8_kv_speedup": round(tbf / ta, 3)}
+        "kernel": "attn_split_kernel<1, 8, 1> (BF16 cache, one launch)",
+        "traffic": measured_traffic("kv_attention_bf16"), "int8_kv_speedup": round(tbf / ta, 3)}
     log(f"kv attention over a BF16 cache {tbf * 1e3:.1f} us (INT8 cache {tbf / ta:.2f}x faster)")
     del bsets, kb, vb
     torch.cuda.empty_cache()
