@@ -204,6 +204,13 @@ def test_attention_no_tokens_gives_zeros_and_is_deterministic():
     qb, kc, ks, vc, vs, lens, o64, mag = _attn_case(2, 8, 1, 128, [0, 0], 128, seed=5)
     y = _run_attn(qb, kc, ks, vc, vs, lens, 128, torch.float32, d)
     assert not y.any()
+    # a negative length is clamped to no tokens; the other sequence is unaffected
+    qb, kc, ks, vc, vs, _, _, _ = _attn_case(2, 8, 1, 128, [128, 128], 128, seed=8)
+    neg = np.array([-5, 128], np.int32)
+    y = _run_attn(qb, kc, ks, vc, vs, neg, 128, torch.float32, d)
+    assert not y[0].any()
+    o64, mag = attention_int8kv_ref(qb[1:], kc[1:], ks[1:], vc[1:], vs[1:], neg[1:])
+    _check(y[1:], o64, mag, False)
     y0 = _run_attn(qb, kc, ks, vc, vs, lens, 0, torch.bfloat16, d)     # max_len 0: no split runs
     assert not y0.any()
     qb, kc, ks, vc, vs, lens, o64, mag = _attn_case(2, 8, 1, 256, [256, 100], 256, seed=6)
