@@ -45,6 +45,7 @@ from .channel import gemm_channel_ref, gemm_channel_fp32_ordered_ref, channel_to
 from .a16 import gemm_w8a16_ref, gemm_bf16_ref, a16_tolerance, dequant_fp8_block_bf16_ref
 from .kvcache import (kv_quantize_ref, dequant_kv_ref, attention_int8kv_ref,
                       attention_bf16kv_ref, attention_tolerance)
+from .packed import packed_position_ref, repack_mfma_ref, unpack_mfma_ref
 
 __all__ = [
     "bf16_bits_to_f32", "quantize_rows_ref", "quantize_act_ref",
@@ -58,4 +59,5 @@ __all__ = [
     "gemm_w8a16_ref", "gemm_bf16_ref", "a16_tolerance", "dequant_fp8_block_bf16_ref",
     "kv_quantize_ref", "dequant_kv_ref", "attention_int8kv_ref", "attention_bf16kv_ref",
     "attention_tolerance",
+    "packed_position_ref", "repack_mfma_ref", "unpack_mfma_ref",
 ]
