@@ -4,15 +4,20 @@
 
 One step = one pass of the hot path over one batch: dynamic per-token INT8
 quantisation of the BF16 activations (bsb_quantize_act) followed by the W8A8
-per-group-128 GEMM with BF16 output (bsb_gemm_w8a8_g128), on the
-decode-shaped linear M=32 tokens, K=8192, N=28672 (seeded synthetic inputs:
-activations N(0,1) with 0.5 % outliers x30, INT8 weights uniform in
-[-127,127], lognormal group scales). All inputs are resident in HBM before
-timing starts; the weights are rotated over several copies (> 1 GB of
-traffic between reuses) so that the 256 MB last-level cache cannot serve them.
+per-group-128 GEMM with BF16 output on the decode-shaped linear M=32 tokens,
+K=8192, N=28672 (seeded synthetic inputs: activations N(0,1) with 0.5 %
+outliers x30, INT8 weights uniform in [-127,127], lognormal group scales). The
+GEMM reads the weights in the matrix cores' operand order
+(bsb_gemm_w8a8_g128_packed, bit-identical to bsb_gemm_w8a8_g128 on the
+row-major weights); they are repacked once per weight copy while the inputs
+are set up, as a serving stack does at load time, outside the timed region.
+All inputs are resident in HBM before timing starts; the weights are rotated
+over several copies (> 1 GB of traffic between reuses) so that the 256 MB
+last-level cache cannot serve them.
 
 Reported (one JSON line on stdout):
   value          algorithmic HBM bytes of the step / step time, GB/s
+  row_major      the same GEMM on the row-major weights (bsb_gemm_w8a8_g128)
   roofline       the GEMM kernel's algorithmic bytes per launch / its mean
                  duration (a timed region of back-to-back GEMM launches
                  between HIP events on the launch stream), against 8 TB/s;
@@ -89,10 +94,13 @@ def measured_traffic(kernel_key):
 class Linear:
     """Device-resident inputs/outputs of one linear layer, `copies` rotating copies."""
 
-    def __init__(self, torch, M, K, N, p, f, copies, device, seed=0):
+    def __init__(self, torch, M, K, N, p, f, copies, device, seed=0, L=None, stream=None):
+        """With L and stream given, each copy also holds its weights repacked into the
+        matrix cores' operand order, and the GEMM passes read those."""
         from block_scaled_bit_amd import synth
         d = synth.linear_inputs(M, K, N, outlier_p=p, outlier_f=f, seed=seed)
         self.M, self.K, self.N = M, K, N
+        self.packed = L is not None
         x = torch.from_numpy(d["x"].view("int16")).to(device)
         qw = torch.from_numpy(d["qw"]).to(device)
         sw = torch.from_numpy(d["sw"]).to(device)
@@ -102,13 +110,21 @@ class Linear:
                      q=torch.empty((M, K), dtype=torch.int8, device=device),
                      sa=torch.empty((M,), dtype=torch.float32, device=device),
                      y=torch.empty((M, N), dtype=torch.int16, device=device))
+            if self.packed:
+                b["qwp"] = torch.empty((N * K,), dtype=torch.int8, device=device)
+                s = L.bsb_repack_weights_mfma(b["qw"].data_ptr(), N, K, b["qwp"].data_ptr(),
+                                              stream)
+                if s:
+                    raise RuntimeError(L.bsb_status_string(s).decode())
             b["ptr"] = {k: v.data_ptr() for k, v in b.items()}
             self.bufs.append(b)
         del x, qw, sw
 
 
 def enqueue(L, lin, stream, n, what=("quant", "gemm")):
-    """Enqueue n passes over the rotating copies: the quantisation and/or the GEMM."""
+    """Enqueue n passes over the rotating copies: the quantisation and/or the GEMM
+    ("gemm": on the packed weights where the copies hold them; "gemm_rm": always on
+    the row-major weights)."""
     M, K, N = lin.M, lin.K, lin.N
     for i in range(n):
         p = lin.bufs[i % len(lin.bufs)]["ptr"]
@@ -116,7 +132,12 @@ def enqueue(L, lin, stream, n, what=("quant", "gemm")):
             s = L.bsb_quantize_act(p["x"], M, K, p["q"], p["sa"], stream)
             if s:
                 raise RuntimeError(L.bsb_status_string(s).decode())
-        if "gemm" in what:
+        if "gemm" in what and lin.packed:
+            s = L.bsb_gemm_w8a8_g128_packed(p["q"], p["sa"], p["qwp"], p["sw"], M, N, K, p["y"],
+                                            0, stream)
+            if s:
+                raise RuntimeError(L.bsb_status_string(s).decode())
+        elif "gemm" in what or "gemm_rm" in what:
             s = L.bsb_gemm_w8a8_g128(p["q"], p["sa"], p["qw"], p["sw"], M, N, K, p["y"], 0,
                                      stream)
             if s:
@@ -663,16 +684,19 @@ def main():
 
     # ---- decode-shaped linear: the step ----
     M, K, N = 32, 8192, 28672
-    lin = Linear(torch, M, K, N, 0.005, 30.0, args.copies, dev)
+    lin = Linear(torch, M, K, N, 0.005, 30.0, args.copies, dev, L=L, stream=stream)
     ms_step, wall = timed(torch, L, lin, stream, args.steps, args.warmup)
     # per-kernel mean durations: each kernel alone, back to back, same buffers
     g_avg, _ = timed(torch, L, lin, stream, args.steps, args.warmup, ("gemm",))
     q_avg, _ = timed(torch, L, lin, stream, args.steps, args.warmup, ("quant",))
+    rm_avg, _ = timed(torch, L, lin, stream, args.steps, args.warmup, ("gemm_rm",))
     step_bytes = quant_bytes(M, K) + gemm_bytes(M, N, K)
     g_bytes = gemm_bytes(M, N, K)
     achieved = g_bytes / (g_avg * 1e-3) / 1e9
+    rm_rate = g_bytes / (rm_avg * 1e-3) / 1e9
     log(f"decode step {ms_step * 1e3:.1f} us (wall {wall * 1e6:.1f} us/step); "
-        f"gemm {g_avg * 1e3:.1f} us = {achieved:.0f} GB/s; quant {q_avg * 1e3:.1f} us")
+        f"gemm {g_avg * 1e3:.1f} us = {achieved:.0f} GB/s; quant {q_avg * 1e3:.1f} us; "
+        f"row-major gemm {rm_avg * 1e3:.1f} us = {rm_rate:.0f} GB/s")
     del lin
     torch.cuda.empty_cache()
 
@@ -689,17 +713,21 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "decode-shaped W8A8-g128 linear: quantize_act + gemm_w8a8_g128 "
-                               "(BF16 out)", "M": M, "K": K, "N": N, "group": 128,
+        "config": {"workload": "decode-shaped W8A8-g128 linear: quantize_act + "
+                               "gemm_w8a8_g128_packed (weights in MFMA operand order, "
+                               "BF16 out)", "M": M, "K": K, "N": N, "group": 128,
                    "weight_copies": args.copies,
                    "tops": round(2.0 * M * N * K / (ms_step * 1e-3) / 1e12, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("gemm_decode"),
-                     "kernel": "gemm_smallm_kernel (M<=32)",
+                     "traffic": measured_traffic("gemm_decode_packed"),
+                     "kernel": "gemm_packed_kernel<2, 7, 0, true>",
                      "timing": "mean of back-to-back launches between HIP events on the launch stream",
                      "bytes_per_launch": g_bytes, "avg_us": round(g_avg * 1e3, 2),
                      "quant_avg_us": round(q_avg * 1e3, 2)},
+        "row_major": {"kernel": "gemm_smallm_kernel<2, 7, 0, ...>", "avg_us": round(rm_avg * 1e3, 2),
+                      "achieved": round(rm_rate, 1), "frac": round(rm_rate / HBM_PEAK_GBS, 4),
+                      "traffic": measured_traffic("gemm_decode")},
     }
 
     # ---- prefill-shaped GEMM ----

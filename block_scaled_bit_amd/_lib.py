@@ -28,6 +28,9 @@ _c_int = ctypes.c_int
 _SIGNATURES = {
     "bsb_quantize_act": [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "bsb_gemm_w8a8_g128": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
+    "bsb_repack_weights_mfma": [_c_p, _c_i64, _c_i64, _c_p, _c_p],
+    "bsb_gemm_w8a8_g128_packed": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int,
+                                  _c_p],
     "bsb_gemm_w8a8_channel": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_int,
                               _c_p],
     "bsb_grouped_gemm_w8a8_g128": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
@@ -157,6 +160,46 @@ def gemm_w8a8_g128(q: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torc
     with torch.cuda.device(dev):
         _check(lib().bsb_gemm_w8a8_g128(_ptr(q), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K,
                                         _ptr(out), code, _stream(dev)), "bsb_gemm_w8a8_g128")
+    return out
+
+
+def repack_weights_mfma(qw: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """packed [N*K] int8: qw [N,K] rearranged into the matrix cores' operand order (1 KB per
+    16-row x 64-column block), the weight form gemm_w8a8_g128_packed reads."""
+    _need(qw, "qw", (torch.int8,))
+    if qw.dim() != 2:
+        raise ValueError("qw [N,K] required")
+    N, K = qw.shape
+    dev = qw.device
+    out = torch.empty((N * K,), dtype=torch.int8, device=dev) if out is None else out
+    _need(out, "out", (torch.int8,), (N * K,), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_repack_weights_mfma(_ptr(qw), N, K, _ptr(out), _stream(dev)),
+               "bsb_repack_weights_mfma")
+    return out
+
+
+def gemm_w8a8_g128_packed(q: torch.Tensor, sa: torch.Tensor, packed: torch.Tensor,
+                          sw: torch.Tensor, out_dtype=torch.bfloat16,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gemm_w8a8_g128 (M <= 64) on weights from repack_weights_mfma; sw [N,K/128] unchanged.
+    Bit-identical to gemm_w8a8_g128 on the unpacked weights."""
+    _need(q, "q", (torch.int8,))
+    if q.dim() != 2 or sw.dim() != 2:
+        raise ValueError("q [M,K] and sw [N,K/128] required")
+    M, K = q.shape
+    N = sw.shape[0]
+    dev = q.device
+    _need(packed, "packed", (torch.int8,), (N * K,), dev)
+    _need(sa, "sa", (torch.float32,), (M,), dev)
+    _need(sw, "sw", (torch.float32,), (N, K // 128), dev)
+    code = _out_code(out_dtype)
+    out = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", (out_dtype,), (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_gemm_w8a8_g128_packed(_ptr(q), _ptr(sa), _ptr(packed), _ptr(sw), M, N,
+                                               K, _ptr(out), code, _stream(dev)),
+               "bsb_gemm_w8a8_g128_packed")
     return out
 
 

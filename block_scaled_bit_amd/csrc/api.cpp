@@ -35,6 +35,7 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 // Largest extents the 32-bit index arithmetic inside the kernels accepts.
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxElems = (int64_t)1 << 36;
+constexpr int64_t kMaxPackedK = (int64_t)1 << 24;
 
 // a * b * c <= limit for positive extents, without overflowing int64.
 inline bool prod_le(int64_t a, int64_t b, int64_t c, int64_t limit) {
@@ -109,6 +110,33 @@ bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa, const int8_t *qw
     if (bsb_status s = check_device()) return s;
     (void)hipGetLastError();
     return finish(bsb::launch_gemm(q, sa, qw, sw, M, N, K, y, (int)out, as_stream(stream)));
+}
+
+bsb_status bsb_repack_weights_mfma(const int8_t *qw, int64_t N, int64_t K, int8_t *packed,
+                                   void *stream) {
+    if (!dims_ok(0, N, K) || N % 16 || N * K > kMaxElems) return BSB_ERR_INVALID_ARG;
+    if (!qw || !packed) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(qw) || !aligned16(packed)) return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_repack_mfma(qw, N, K, packed, as_stream(stream)));
+}
+
+bsb_status bsb_gemm_w8a8_g128_packed(const int8_t *q, const float *sa, const int8_t *packed,
+                                     const float *sw, int64_t M, int64_t N, int64_t K, void *y,
+                                     bsb_out_dtype out, void *stream) {
+    // 32-bit buffer offsets: 64 activation rows of K bytes, 16*K weight bytes per wave
+    if (!dims_ok(M, N, K) || N % 16 || M > 64 || K > kMaxPackedK || N * K > kMaxElems)
+        return BSB_ERR_INVALID_ARG;
+    if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
+    if (M == 0) return BSB_OK;
+    if (!q || !sa || !packed || !sw || !y) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(sa) || !aligned16(packed) || !aligned16(sw) || !aligned16(y))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_gemm_packed(q, sa, packed, sw, M, N, K, y, (int)out,
+                                          as_stream(stream)));
 }
 
 bsb_status bsb_gemm_w8a8_channel(const int8_t *q, const float *sa, const int8_t *qw,

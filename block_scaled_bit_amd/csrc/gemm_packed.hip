@@ -1,0 +1,272 @@
+// W8A8 per-group-128 GEMM on INT8 weights stored in the matrix cores' operand
+// order (decode-shaped M <= 64).
+//
+// [P1] sec. 2: the serving stack rearranges quantised weights once, at load
+// time, into the layout the kernel that consumes them wants. Here that layout
+// is the B-operand order of v_mfma_i32_16x16x64_i8: the weight matrix qw[N,K]
+// is cut into 16-row x 64-column blocks, each stored as 1 KB,
+//
+//     packed[((n/16) * (K/64) + k/64) * 1024 + 16*l + j] = qw[n, k]
+//         with l = (n % 16) + 16 * ((k % 64) / 16),  j = k % 16,
+//
+// so lane l of a wave reads its 16 operand bytes of one instruction as one
+// 16-byte load and the wave's 64 lanes read 1 KB contiguous. A wave owns 16
+// weight rows; its whole weight stream (K/64 blocks) is contiguous.
+//
+// The arithmetic is the row-major kernel's, step for step ([P3] sec. 3.1):
+// per output element the exact INT32 sum of each 128-wide K group, then
+// acc = fmaf((float)P, sw[n,g], acc) for g ascending, then y = acc * sa[m];
+// the results are bit-identical to bsb_gemm_w8a8_g128 on the unpacked weights.
+//
+// Kernel: a workgroup of NW waves owns 16*NW weight rows and all M <= 16*MB
+// tokens. Each wave streams its weights straight into registers, PD groups
+// ahead (a ring of PD register buffers; groups past the end read zeros, which
+// add fmaf(0, 0, acc) = acc). The activations are shared through LDS: chunks of
+// PD groups, double-buffered, loaded one chunk ahead with LDS-destination
+// buffer loads, one barrier per chunk. Every wave runs the whole loop (waves
+// past N read through empty descriptors and store nothing) so the barriers
+// always complete.
+#include "device_common.h"
+#include "launch.h"
+
+namespace bsb {
+
+namespace {
+
+// One thread per 16-byte output chunk c: block c / 64, lane c % 64.
+__global__ void __launch_bounds__(256)
+repack_mfma_kernel(const int8_t *__restrict__ qw, int N, int K, int8_t *__restrict__ packed) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= (int64_t)N * K / 16) return;
+    const int l = (int)(c & 63);
+    const int64_t blk = c >> 6;
+    const int ks = K / 64;
+    const int64_t nb = blk / ks;
+    const int s = (int)(blk - nb * ks);
+    const int64_t n = nb * 16 + (l & 15);
+    const int64_t k = (int64_t)s * 64 + (l >> 4) * 16;
+    *reinterpret_cast<uint4 *>(packed + c * 16) = *reinterpret_cast<const uint4 *>(qw + n * K + k);
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_packed_out(void *y, int64_t idx, float v) {
+    if (OUT == 0)
+        reinterpret_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
+    else
+        reinterpret_cast<float *>(y)[idx] = v;
+}
+
+// Groups in flight per wave for MB token blocks. Each group costs 3 loads per
+// wave (2 weight, 1 scale) and a chunk of PD groups 2*PD*MB 1 KB activation
+// blocks per workgroup; at one wave per workgroup 3*PD + 2*PD*MB <= 63, the
+// number of loads a wave can have outstanding.
+template <int MB>
+constexpr int packed_depth() {
+    return MB == 1 ? 12 : MB == 2 ? 8 : 4;
+}
+
+// The pointer arguments carry no __restrict__: with it the compiler treats the
+// buffer loads as invariant and regroups them by kind across the fences below,
+// which breaks the one-group-per-step issue order the waits are counted for.
+template <int MB, int NW, int OUT, bool NT>
+__global__ void __launch_bounds__(64 * NW)
+gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const float *sw, int M,
+                   int N, int K, void *y) {
+    constexpr int PD = packed_depth<MB>();
+    constexpr int ROWS = 16 * MB;
+    constexpr int GT = ROWS * 128;           // one group of the activation tile (bytes)
+    constexpr int CT = PD * GT;              // one chunk
+    constexpr int TB = CT / 1024;            // 1 KB blocks per chunk
+    constexpr int AB = (TB + NW - 1) / NW;   // blocks per wave (the last waves may have fewer)
+    static_assert(3 * PD + 2 * PD * MB <= 63, "more loads than a wave can have outstanding");
+    __shared__ __align__(16) int8_t As[2][CT];
+    const int lane = threadIdx.x & 63;
+    const int wv = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nb = blockIdx.x * NW + wv;
+    const bool live = nb * 16 < N;
+    const int G = K / 128;
+    const int nch = (G + PD - 1) / PD;
+    const int col = lane & 15, slot = lane >> 4;
+    const auto wr = make_rsrc(live ? packed + (int64_t)nb * K * 16 : packed,
+                              live ? (uint32_t)(K * 16) : 0u);
+    const auto sr = make_rsrc(live ? sw + (int64_t)nb * 16 * G : sw,
+                              live ? (uint32_t)(16 * G * 4) : 0u);
+    const v4i ra = make_rsrc_words(q, (uint32_t)(M * K));   // rows >= M read zero
+    const uint32_t wl = (uint32_t)lane * 16;
+    const uint32_t sl = (uint32_t)(col * G * 4);
+
+    // Activation staging: block b of a chunk is group b / (ROWS/8), rows
+    // 8*rb .. 8*rb+7 with rb = b % (ROWS/8); chunk j of row r lands at position
+    // j ^ ((r>>1)&7) of its 128-byte LDS row, so the 16 rows one fragment read
+    // touches fall in distinct bank groups. Lane l of a block loads row
+    // 8*rb + l/8 at LDS position l%8; that row's pattern is
+    // (4*(rb&1) + l/16) & 7, so the lane part of the offset takes one of two
+    // values and the rest (8*rb*K + 128*g) is wave-uniform.
+    uint32_t avl[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        avl[e] = (uint32_t)((lane >> 3) * K + (((lane & 7) ^ ((4 * e + (lane >> 4)) & 7)) << 4));
+    auto lds_addr = [](const void *p) {
+        return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+    };
+    auto stage = [&](int c) {   // chunk c into buffer c & 1
+#pragma unroll
+        for (int i = 0; i < AB; ++i) {
+            const int b = wv + i * NW;
+            if (b < TB) {
+                const int gl = b / (ROWS / 8), rb = b % (ROWS / 8);
+                const int g = c * PD + gl;
+                buf_load16_lds(ra, lds_addr(&As[c & 1][gl * GT + rb * 1024]), avl[rb & 1],
+                               g < G ? (uint32_t)(g * 128 + rb * 8 * K) : kOOB);
+            }
+        }
+    };
+
+    v4i w[PD][2];
+    float s[PD];
+    auto load_w = [&](int d, int g) {
+        const uint32_t so = g < G ? (uint32_t)g * 2048u : kOOB;
+        w[d][0] = buf_load16s<NT ? kNonTemporal : 0>(wr, wl, so);
+        w[d][1] = buf_load16s<NT ? kNonTemporal : 0>(wr, wl + 1024, so);
+    };
+    auto load_s = [&](int d, int g) {
+        s[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             sr, (int)sl, g < G ? g * 4 : (int)kOOB, 0));
+    };
+    float facc[MB][4];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
+
+    // Issue order: chunk 0's activations, then groups 0 .. PD-1 one at a time.
+    stage(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < PD; ++d) {
+        load_w(d, d);
+        load_s(d, d);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int c = 0; c < nch; ++c) {
+        // Exactly 3*PD loads were issued after this wave's blocks of chunk c
+        // (the PD groups' weights and scales), and loads complete in order:
+        // the blocks have landed. The barrier then publishes every wave's and
+        // also means every wave is done reading chunk c-1's buffer, which
+        // chunk c+1 goes into.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PD) : "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 1 < nch) stage(c + 1);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const int8_t *buf = As[c & 1];
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+            const int g = c * PD + d;
+            v4i af[2][MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const int r = i * 16 + col;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int j = h * 4 + slot;   // K positions 64h + 16*slot .. +15
+                    af[h][i] = *reinterpret_cast<const v4i *>(buf + d * GT + r * 128 +
+                                                              ((j ^ ((r >> 1) & 7)) << 4));
+                }
+            }
+            v4i acc[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], w[d][0], v4i{0, 0, 0, 0},
+                                                               0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], w[d][1], acc[i], 0, 0, 0);
+            }
+            load_w(d, g + PD);
+            // C layout of 16x16: lane holds weight row `col`, tokens 4*slot + r
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    facc[i][r] = __builtin_fmaf((float)acc[i][r], s[d], facc[i][r]);
+            load_s(d, g + PD);   // after the epilogue: s[d] is reused in place
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (!live) return;
+    const int n = nb * 16 + col;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = i * 16 + slot * 4 + r;
+            if (m < M) store_packed_out<OUT>(y, (int64_t)m * N + n, facc[i][r] * sa[m]);
+        }
+}
+
+constexpr int kPackedCUs = 256;
+
+template <int MB, int NW, int OUT>
+hipError_t launch_packed_nw(const int8_t *q, const float *sa, const int8_t *packed,
+                            const float *sw, int M, int N, int K, void *y, hipStream_t stream) {
+    const dim3 grid((unsigned)((N / 16 + NW - 1) / NW));
+    // the non-temporal hint pays on weight streams far larger than the caches
+    if ((int64_t)N * K >= ((int64_t)1 << 27))
+        gemm_packed_kernel<MB, NW, OUT, true><<<grid, 64 * NW, 0, stream>>>(q, sa, packed, sw, M,
+                                                                            N, K, y);
+    else
+        gemm_packed_kernel<MB, NW, OUT, false><<<grid, 64 * NW, 0, stream>>>(q, sa, packed, sw, M,
+                                                                             N, K, y);
+    return hipGetLastError();
+}
+
+// Workgroup width: the 16-row blocks spread over whole rounds of one
+// workgroup per CU, at most 8 waves (the width the row-major kernel uses).
+template <int MB, int OUT>
+hipError_t launch_packed_mb(const int8_t *q, const float *sa, const int8_t *packed,
+                            const float *sw, int M, int N, int K, void *y, hipStream_t stream) {
+    const int64_t blocks16 = N / 16;
+    const int64_t rounds = (blocks16 + 8 * kPackedCUs - 1) / (8 * kPackedCUs);
+    const int nw = (int)((blocks16 + kPackedCUs * rounds - 1) / (kPackedCUs * rounds));
+    switch (nw) {
+        case 1: return launch_packed_nw<MB, 1, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+        case 2: return launch_packed_nw<MB, 2, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+        case 3: return launch_packed_nw<MB, 3, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+        case 4: return launch_packed_nw<MB, 4, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+        case 5: return launch_packed_nw<MB, 5, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+        case 6: return launch_packed_nw<MB, 6, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+        case 7: return launch_packed_nw<MB, 7, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+        default: return launch_packed_nw<MB, 8, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+    }
+}
+
+template <int OUT>
+hipError_t launch_packed_out(const int8_t *q, const float *sa, const int8_t *packed,
+                             const float *sw, int M, int N, int K, void *y, hipStream_t stream) {
+    if (M <= 16) return launch_packed_mb<1, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+    if (M <= 32) return launch_packed_mb<2, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+    return launch_packed_mb<4, OUT>(q, sa, packed, sw, M, N, K, y, stream);
+}
+
+}  // namespace
+
+hipError_t launch_repack_mfma(const int8_t *qw, int64_t N, int64_t K, int8_t *packed,
+                              hipStream_t stream) {
+    const int64_t chunks = N * K / 16;
+    repack_mfma_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, stream>>>(qw, (int)N, (int)K,
+                                                                             packed);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_packed(const int8_t *q, const float *sa, const int8_t *packed,
+                              const float *sw, int64_t M, int64_t N, int64_t K, void *y, int out,
+                              hipStream_t stream) {
+    return out == 0 ? launch_packed_out<0>(q, sa, packed, sw, (int)M, (int)N, (int)K, y, stream)
+                    : launch_packed_out<1>(q, sa, packed, sw, (int)M, (int)N, (int)K, y, stream);
+}
+
+}  // namespace bsb

@@ -27,6 +27,13 @@ hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw,
                        const float *sw, int64_t M, int64_t N, int64_t K, void *y,
                        int out, hipStream_t stream);
 
+// gemm_packed.hip: weights in the matrix cores' operand order (M <= 64)
+hipError_t launch_repack_mfma(const int8_t *qw, int64_t N, int64_t K, int8_t *packed,
+                              hipStream_t stream);
+hipError_t launch_gemm_packed(const int8_t *q, const float *sa, const int8_t *packed,
+                              const float *sw, int64_t M, int64_t N, int64_t K, void *y, int out,
+                              hipStream_t stream);
+
 // Per-channel (sw_stride 1, sw[N]) or per-tensor (sw_stride 0, sw[1]) weight
 // scales: out 0 = BF16, 1 = FP32.
 hipError_t launch_gemm_channel(const int8_t *q, const float *sa, const int8_t *qw,

@@ -107,6 +107,42 @@ bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa,
                               void *y, bsb_out_dtype out, void *stream);
 
 /*
+ * Load-time repack of INT8 weights into the matrix cores' operand order ([P1]
+ * sec. 2: quantised weights are rearranged once, when they are loaded, into the
+ * layout of the kernel that consumes them). The [N, K] matrix is cut into
+ * blocks of 16 rows x 64 columns, each stored as 1024 contiguous bytes:
+ *     packed[((n/16)*(K/64) + k/64)*1024 + 16*l + (k%16)] = qw[n, k]
+ *         with l = (n%16) + 16*((k%64)/16)
+ * (a permutation of the bytes: packed holds exactly N*K bytes). The scales sw
+ * keep their [N, G] layout.
+ *   qw      [N, K] int8 (read), 16-byte aligned
+ *   packed  [N*K] int8 (written), 16-byte aligned, caller-owned, must not
+ *           overlap qw
+ *   N       a multiple of 16;  K a multiple of 128
+ * Errors: BSB_ERR_INVALID_ARG for bad sizes or null pointers (N*K = 0 is not
+ * allowed), BSB_ERR_MISALIGNED, BSB_ERR_NO_DEVICE / BSB_ERR_LAUNCH.
+ */
+bsb_status bsb_repack_weights_mfma(const int8_t *qw, int64_t N, int64_t K,
+                                   int8_t *packed, void *stream);
+
+/*
+ * bsb_gemm_w8a8_g128 for decode-shaped M on weights repacked by
+ * bsb_repack_weights_mfma: the same arithmetic in the same order ([P3] sec. 3.1),
+ * so y is bit-identical to bsb_gemm_w8a8_g128(q, sa, qw, sw, ...) on the
+ * unpacked qw. Each wave streams its 16 rows' weights as contiguous 1 KB loads
+ * straight into its matrix-core operands.
+ *   packed  [N*K] int8 from bsb_repack_weights_mfma
+ *   M       0 .. 64 (M = 0: nothing to do);  N a multiple of 16;
+ *           K a multiple of 128, at most 2^24
+ * Other arguments, limits and errors as bsb_gemm_w8a8_g128; M > 64 is
+ * BSB_ERR_INVALID_ARG (use the row-major weights there).
+ */
+bsb_status bsb_gemm_w8a8_g128_packed(const int8_t *q, const float *sa,
+                                     const int8_t *packed, const float *sw,
+                                     int64_t M, int64_t N, int64_t K,
+                                     void *y, bsb_out_dtype out, void *stream);
+
+/*
  * W8A8 GEMM with one weight scale per output row (per-channel) or one for the
  * whole weight (per-tensor): the coarser granularities of [P3] sec. 3.1's
  * taxonomy, whose deployment checklist (sec. 6) runs per-tensor before moving

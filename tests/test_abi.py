@@ -219,3 +219,30 @@ def test_bf16_kv_cache_argument_checks(L):
     if not torch.cuda.is_available():
         assert at(A, A, A, A, 2, 16, 4, 128, 128, 128, A, need, A, 1, None) == UNSUPPORTED
         assert wr(A, A, A, A, 3, 2, 4, 128, 128, A, A, None) == UNSUPPORTED
+
+
+def test_packed_weight_argument_checks(L):
+    """Repack and packed GEMM: N a multiple of 16, K of 128, the GEMM at most 64
+    rows and K <= 2^24, the usual null, enum, alignment and empty-input rules;
+    with valid arguments and no gfx950 device they fail fast."""
+    rp, g = L.bsb_repack_weights_mfma, L.bsb_gemm_w8a8_g128_packed
+    assert rp(A, 24, 128, A, None) == INVALID            # N % 16
+    assert rp(A, 16, 192, A, None) == INVALID            # K % 128
+    assert rp(A, 0, 128, A, None) == INVALID             # empty weight
+    assert rp(None, 16, 128, A, None) == INVALID
+    assert rp(A, 16, 128, None, None) == INVALID
+    assert rp(U, 16, 128, A, None) == MISALIGNED
+    assert rp(A, 16, 128, U, None) == MISALIGNED
+    assert rp(A, 1 << 23, 1 << 14, A, None) == INVALID   # 2^37 bytes
+    assert g(A, A, A, A, 65, 16, 128, A, 0, None) == INVALID           # more than 64 rows
+    assert g(A, A, A, A, 4, 24, 128, A, 0, None) == INVALID            # N % 16
+    assert g(A, A, A, A, 4, 16, 130, A, 0, None) == INVALID            # K % 128
+    assert g(A, A, A, A, 4, 16, (1 << 24) + 128, A, 0, None) == INVALID   # K limit
+    assert g(A, A, A, A, -1, 16, 128, A, 0, None) == INVALID
+    assert g(A, A, A, A, 4, 16, 128, A, 7, None) == INVALID            # out enum
+    assert g(A, A, None, A, 4, 16, 128, A, 0, None) == INVALID
+    assert g(A, A, U, A, 4, 16, 128, A, 0, None) == MISALIGNED
+    assert g(None, None, None, None, 0, 16, 128, None, 0, None) == OK   # no rows
+    if not torch.cuda.is_available():
+        assert rp(A, 16, 128, A, None) == UNSUPPORTED
+        assert g(A, A, A, A, 64, 16, 1 << 24, A, 1, None) == UNSUPPORTED

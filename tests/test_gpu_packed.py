@@ -1,0 +1,133 @@
+"""GPU parity: weights repacked into the matrix cores' operand order, and the W8A8
+per-group-128 GEMM that reads them.
+
+The repack moves bytes, so it must match the oracle's layout bit for bit. The
+GEMM on packed weights keeps the stated float32 group order, so its FP32 and
+BF16 outputs must equal the oracle's float32 replay on the unpacked weights bit
+for bit (and lie within the float64 definition's tolerances).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_bit_amd as bsb
+from block_scaled_bit_amd import synth
+from oracle import (quantize_act_ref, gemm_ref, gemm_fp32_ordered_ref, repack_mfma_ref,
+                    packed_position_ref)
+from tests.gpu_util import require_gpu, dev, dev_bf16, host, say, Guarded, check_fp32, check_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(M, K, N, seed):
+    d = synth.linear_inputs(M, K, N, outlier_p=0.01, outlier_f=20.0, seed=seed)
+    q, sa = quantize_act_ref(d["x"])
+    return d, q, sa
+
+
+def _gpu_repack(qw, d):
+    N, K = qw.shape
+    g = Guarded((N * K,), torch.int8, d)
+    bsb.repack_weights_mfma(dev(qw, d), out=g.view)
+    torch.cuda.synchronize()
+    return g.check()
+
+
+def _gpu_packed_gemm(q, sa, packed_d, sw, dtype, d):
+    M, N = q.shape[0], sw.shape[0]
+    g = Guarded((M, N), dtype, d)
+    bsb.gemm_w8a8_g128_packed(dev(q, d), dev(sa, d), packed_d, dev(sw, d), out_dtype=dtype,
+                              out=g.view)
+    torch.cuda.synchronize()
+    return g.check()
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 1152), (1024, 7168), (144, 3584)])
+def test_repack_matches_the_layout(N, K):
+    d = require_gpu()
+    say(f"repack N={N} K={K}")
+    qw = np.random.default_rng(N + K).integers(-127, 128, (N, K), dtype=np.int8)
+    assert np.array_equal(_gpu_repack(qw, d), repack_mfma_ref(qw))
+
+
+# M spans one, two and four 16-row token blocks with ragged tails; K gives group
+# counts that do and do not fill the last chunk of the weight ring (12, 8 or 4
+# groups by token blocks); N from one 16-row block to wide enough for 2-8 waves
+# per workgroup.
+@pytest.mark.parametrize("M,N,K", [
+    (1, 16, 128), (5, 48, 3584), (16, 2048, 4096), (17, 1024, 1024), (32, 4096, 1536),
+    (33, 3584, 1152), (48, 272, 1152), (64, 4096, 7168), (7, 8192, 896),
+])
+def test_packed_gemm_matches_the_oracle(M, N, K):
+    d = require_gpu()
+    say(f"packed gemm M={M} N={N} K={K}")
+    cfg, q, sa = _inputs(M, K, N, M * 7 + N)
+    qw, sw = cfg["qw"], cfg["sw"]
+    packed = _gpu_repack(qw, d)
+    pd = dev(packed, d)
+    y64, mag = gemm_ref(q, sa, qw, sw)
+    c32, cb = gemm_fp32_ordered_ref(q, sa, qw, sw)
+    check_fp32(_gpu_packed_gemm(q, sa, pd, sw, torch.float32, d), y64, mag, c32)
+    check_bf16(_gpu_packed_gemm(q, sa, pd, sw, torch.bfloat16, d), y64, mag, cb)
+
+
+def test_waves_past_the_last_row_block():
+    """1795 row blocks over 8-wave workgroups: the last workgroup has five waves
+    with no weight rows; they still take part in every barrier and store nothing."""
+    d = require_gpu()
+    M, N, K = 32, 16 * 1795, 256
+    say(f"packed gemm dead waves M={M} N={N} K={K}")
+    cfg, q, sa = _inputs(M, K, N, 5)
+    qw, sw = cfg["qw"], cfg["sw"]
+    pd = bsb.repack_weights_mfma(dev(qw, d))
+    y64, mag = gemm_ref(q, sa, qw, sw)
+    c32, cb = gemm_fp32_ordered_ref(q, sa, qw, sw)
+    check_bf16(_gpu_packed_gemm(q, sa, pd, sw, torch.bfloat16, d), y64, mag, cb)
+
+
+def test_decode_config_full():
+    """The decode-shaped linear (32 x 8192 x 28672) at full size, in the launch
+    configuration the benchmark times: repack sampled against the layout, GEMM
+    bit-identical to the oracle's float32 replay and to the row-major kernel,
+    repeated launches identical."""
+    d = require_gpu()
+    say("packed gemm decode M=32 K=8192 N=28672 (full)")
+    cfg = synth.linear_config("decode")
+    qw, sw = cfg["qw"], cfg["sw"]
+    N, K = qw.shape
+    qd, sd = bsb.quantize_act(dev_bf16(cfg["x"], d))
+    q, sa = quantize_act_ref(cfg["x"])
+    assert np.array_equal(host(qd), q) and np.array_equal(host(sd), sa)
+    qwd, swd = dev(qw, d), dev(sw, d)
+    pd = bsb.repack_weights_mfma(qwd)
+    rng = np.random.default_rng(1)
+    n = rng.integers(0, N, 200000)
+    k = rng.integers(0, K, 200000)
+    pos = torch.from_numpy(packed_position_ref(n, k, K)).to(d)
+    assert np.array_equal(host(pd[pos]), qw[n, k])
+    y64, mag = gemm_ref(q, sa, qw, sw)
+    c32, cb = gemm_fp32_ordered_ref(q, sa, qw, sw)
+    yb = host(bsb.gemm_w8a8_g128_packed(qd, sd, pd, swd))
+    check_bf16(yb, y64, mag, cb)
+    y32 = host(bsb.gemm_w8a8_g128_packed(qd, sd, pd, swd, out_dtype=torch.float32))
+    check_fp32(y32, y64, mag, c32)
+    assert np.array_equal(host(bsb.gemm_w8a8_g128(qd, sd, qwd, swd)), yb)
+    for _ in range(2):
+        assert np.array_equal(host(bsb.gemm_w8a8_g128_packed(qd, sd, pd, swd)), yb)
+
+
+def test_empty_rows_and_limits():
+    d = require_gpu()
+    say("packed gemm M=0 and M=65")
+    qw = np.ones((16, 128), np.int8)
+    pd = bsb.repack_weights_mfma(dev(qw, d))
+    sw = dev(np.ones((16, 1), np.float32), d)
+    g = Guarded((0, 16), torch.bfloat16, d)
+    bsb.gemm_w8a8_g128_packed(torch.empty((0, 128), dtype=torch.int8, device=d),
+                              torch.empty((0,), dtype=torch.float32, device=d), pd, sw,
+                              out=g.view)
+    torch.cuda.synchronize()
+    g.check()
+    with pytest.raises(bsb.BsbError):
+        bsb.gemm_w8a8_g128_packed(torch.zeros((65, 128), dtype=torch.int8, device=d),
+                                  torch.ones((65,), dtype=torch.float32, device=d), pd, sw)
