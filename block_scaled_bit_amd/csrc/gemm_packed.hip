@@ -22,8 +22,8 @@
 // tokens. Each wave streams its weights straight into registers, PD groups
 // ahead (a ring of PD register buffers; groups past the end read zeros, which
 // add fmaf(0, 0, acc) = acc). The activations are shared through LDS: chunks of
-// PD groups, double-buffered, loaded one chunk ahead with LDS-destination
-// buffer loads, one barrier per chunk. Every wave runs the whole loop (waves
+// CG groups (PD or 2*PD), double-buffered, loaded one chunk ahead with
+// LDS-destination buffer loads, one barrier per chunk. Every wave runs the whole loop (waves
 // past N read through empty descriptors and store nothing) so the barriers
 // always complete.
 #include "device_common.h"
@@ -57,12 +57,23 @@ __device__ __forceinline__ void store_packed_out(void *y, int64_t idx, float v) 
 }
 
 // Groups in flight per wave for MB token blocks. Each group costs 3 loads per
-// wave (2 weight, 1 scale) and a chunk of PD groups 2*PD*MB 1 KB activation
-// blocks per workgroup; at one wave per workgroup 3*PD + 2*PD*MB <= 63, the
-// number of loads a wave can have outstanding.
+// wave (2 weight, 1 scale) and a chunk of CG groups 2*CG*MB 1 KB activation
+// blocks per workgroup, shared by its NW waves; a wave may have at most 63 loads
+// outstanding: 3*CG + ceil(2*CG*MB/NW) <= 63.
 template <int MB>
 constexpr int packed_depth() {
     return MB == 1 ? 12 : MB == 2 ? 8 : 4;
+}
+
+constexpr int packed_loads(int cg, int mb, int nw) { return 3 * cg + (2 * cg * mb + nw - 1) / nw; }
+
+// Groups per activation chunk: two rings' worth where that stays within the
+// outstanding-load limit (half the barriers: measured 1-2 % faster at 4 or
+// more waves), else one.
+template <int MB, int NW>
+constexpr int packed_chunk() {
+    return NW >= 4 && packed_loads(2 * packed_depth<MB>(), MB, NW) <= 63 ? 2 * packed_depth<MB>()
+                                                                          : packed_depth<MB>();
 }
 
 // The pointer arguments carry no __restrict__: with it the compiler treats the
@@ -73,19 +84,21 @@ __global__ void __launch_bounds__(64 * NW)
 gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const float *sw, int M,
                    int N, int K, void *y) {
     constexpr int PD = packed_depth<MB>();
+    constexpr int CG = packed_chunk<MB, NW>();
     constexpr int ROWS = 16 * MB;
     constexpr int GT = ROWS * 128;           // one group of the activation tile (bytes)
-    constexpr int CT = PD * GT;              // one chunk
+    constexpr int CT = CG * GT;              // one chunk
     constexpr int TB = CT / 1024;            // 1 KB blocks per chunk
     constexpr int AB = (TB + NW - 1) / NW;   // blocks per wave (the last waves may have fewer)
-    static_assert(3 * PD + 2 * PD * MB <= 63, "more loads than a wave can have outstanding");
+    static_assert(packed_loads(CG, MB, NW) <= 63 && CG % PD == 0,
+                  "more loads than a wave can have outstanding");
     __shared__ __align__(16) int8_t As[2][CT];
     const int lane = threadIdx.x & 63;
     const int wv = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int nb = blockIdx.x * NW + wv;
     const bool live = nb * 16 < N;
     const int G = K / 128;
-    const int nch = (G + PD - 1) / PD;
+    const int nch = (G + CG - 1) / CG;
     const int col = lane & 15, slot = lane >> 4;
     const auto wr = make_rsrc(live ? packed + (int64_t)nb * K * 16 : packed,
                               live ? (uint32_t)(K * 16) : 0u);
@@ -115,7 +128,7 @@ gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const
             const int b = wv + i * NW;
             if (b < TB) {
                 const int gl = b / (ROWS / 8), rb = b % (ROWS / 8);
-                const int g = c * PD + gl;
+                const int g = c * CG + gl;
                 buf_load16_lds(ra, lds_addr(&As[c & 1][gl * GT + rb * 1024]), avl[rb & 1],
                                g < G ? (uint32_t)(g * 128 + rb * 8 * K) : kOOB);
             }
@@ -151,12 +164,16 @@ gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const
         __builtin_amdgcn_sched_barrier(0);
     }
     for (int c = 0; c < nch; ++c) {
-        // Exactly 3*PD loads were issued after this wave's blocks of chunk c
-        // (the PD groups' weights and scales), and loads complete in order:
-        // the blocks have landed. The barrier then publishes every wave's and
-        // also means every wave is done reading chunk c-1's buffer, which
-        // chunk c+1 goes into.
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PD) : "memory");
+        // Exactly 3*CG loads (3*PD for chunk 0: the prologue's groups) were
+        // issued after this wave's blocks of chunk c, the weights and scales
+        // of the groups in between, and loads complete in order: the blocks
+        // have landed. The barrier then publishes every wave's and also means
+        // every wave is done reading chunk c-1's buffer, which chunk c+1 goes
+        // into.
+        if (c == 0)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PD) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * CG) : "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
@@ -165,8 +182,9 @@ gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const
         __builtin_amdgcn_sched_barrier(0);
         const int8_t *buf = As[c & 1];
 #pragma unroll
-        for (int d = 0; d < PD; ++d) {
-            const int g = c * PD + d;
+        for (int dd = 0; dd < CG; ++dd) {
+            const int d = dd % PD;           // weight ring slot
+            const int g = c * CG + dd;
             v4i af[2][MB];
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
@@ -174,7 +192,7 @@ gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int j = h * 4 + slot;   // K positions 64h + 16*slot .. +15
-                    af[h][i] = *reinterpret_cast<const v4i *>(buf + d * GT + r * 128 +
+                    af[h][i] = *reinterpret_cast<const v4i *>(buf + dd * GT + r * 128 +
                                                               ((j ^ ((r >> 1) & 7)) << 4));
                 }
             }
