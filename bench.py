@@ -257,7 +257,9 @@ def extra_rows(torch, L, stream, dev, steps):
     def t(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
-    def linear_rows(tag, M, K, N, p, f):
+    def linear_rows(tag, M, K, N, p, f, packed=False):
+        """Mean us of quantize_act and of the GEMM; with packed=True also of the GEMM on
+        weights repacked into the matrix cores' operand order (a third value)."""
         d = synth.linear_inputs(M, K, N, outlier_p=p, outlier_f=f, seed=0)
         gb = gemm_bytes(M, N, K)
         n = _copies(gb)
@@ -268,6 +270,10 @@ def extra_rows(torch, L, stream, dev, steps):
                      q=torch.empty((M, K), dtype=torch.int8, device=dev),
                      sa=torch.empty((M,), dtype=torch.float32, device=dev),
                      y=torch.empty((M, N), dtype=torch.int16, device=dev))
+            if packed:
+                b["qwp"] = torch.empty((N * K,), dtype=torch.int8, device=dev)
+                _ok(L, L.bsb_repack_weights_mfma(b["qw"].data_ptr(), N, K, b["qwp"].data_ptr(),
+                                                 stream))
             sets.append({k: v.data_ptr() for k, v in b.items()} | {"_keep": b})
         quant = Row(f"{tag} quantize_act", sets, lambda p, st: _ok(
             L, L.bsb_quantize_act(p["x"], M, K, p["q"], p["sa"], st)))
@@ -275,7 +281,14 @@ def extra_rows(torch, L, stream, dev, steps):
             L, L.bsb_gemm_w8a8_g128(p["q"], p["sa"], p["qw"], p["sw"], M, N, K, p["y"], 0, st)))
         tq = quant.time(torch, stream, steps, 3)
         tg = gemm.time(torch, stream, steps, 3)
-        return tq, tg
+        if not packed:
+            return tq, tg
+        for b in sets:   # the quantised activations the packed GEMM reads
+            _ok(L, L.bsb_quantize_act(b["x"], M, K, b["q"], b["sa"], stream))
+        tp = Row(f"{tag} gemm packed", sets, lambda p, st: _ok(
+            L, L.bsb_gemm_w8a8_g128_packed(p["q"], p["sa"], p["qwp"], p["sw"], M, N, K, p["y"], 0,
+                                           st))).time(torch, stream, steps, 3)
+        return tq, tg, tp
 
     # tiny linear: latency-bound, reported in microseconds
     tq, tg = linear_rows("tiny", 16, 1024, 1024, 0.01, 20.0)
@@ -288,10 +301,13 @@ def extra_rows(torch, L, stream, dev, steps):
 
     # one GPU's share of the decode linear under 8-way column (tensor) parallelism:
     # N / 8 = 3584 columns, 29 MB of weights (the exchange itself is not run)
-    tq, tg = linear_rows("tp8", 32, 8192, 3584, 0.005, 30.0)
+    tq, tg, tp = linear_rows("tp8", 32, 8192, 3584, 0.005, 30.0, packed=True)
     rows["tp8_share_decode_32x8192x3584_gemm"] = _rate(tg * 1e3, ops=2 * 32 * 3584 * 8192,
                                                        byts=gemm_bytes(32, 3584, 8192))
-    log(f"tp8 share of the decode linear: gemm {tg * 1e3:.1f} us")
+    rows["tp8_share_decode_32x8192x3584_gemm_packed"] = _rate(
+        tp * 1e3, ops=2 * 32 * 3584 * 8192, byts=gemm_bytes(32, 3584, 8192))
+    log(f"tp8 share of the decode linear: gemm {tg * 1e3:.1f} us, on packed weights "
+        f"{tp * 1e3:.1f} us")
     torch.cuda.empty_cache()
 
     # prefill-shaped quantisation (the GEMM is timed separately)

@@ -226,6 +226,96 @@ gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const
         }
 }
 
+// Narrow weights (at most one 16-row block per CU): one wave per workgroup and no
+// LDS. The wave reads its activations straight from L2 into registers, together
+// with its weights and scales, PD groups ahead. Loads retire in issue order, so
+// activations are fetched as far ahead as the weights, or a wait for one would
+// also wait for every older weight load. With this few waves the per-wave
+// activation re-reads are small and no barrier holds a wave back; at full width
+// they would move twice the weight bytes through L2.
+template <int MB, int OUT, bool NT>
+__global__ void __launch_bounds__(64)
+gemm_packed_narrow_kernel(const int8_t *q, const float *sa, const int8_t *packed, const float *sw,
+                          int M, int N, int K, void *y) {
+    constexpr int PD = packed_depth<MB>();
+    static_assert((3 + 2 * MB) * PD <= 63, "more loads than a wave can have outstanding");
+    const int lane = threadIdx.x;
+    const int nb = blockIdx.x;                // N is a multiple of 16: every block exists
+    const int G = K / 128;
+    const int col = lane & 15, slot = lane >> 4;
+    const auto wr = make_rsrc(packed + (int64_t)nb * K * 16, (uint32_t)(K * 16));
+    const auto ar = make_rsrc(q, (uint32_t)(M * K));   // rows >= M read zero
+    const auto sr = make_rsrc(sw + (int64_t)nb * 16 * G, (uint32_t)(16 * G * 4));
+    const uint32_t wl = (uint32_t)lane * 16;
+    const uint32_t sl = (uint32_t)(col * G * 4);
+    uint32_t al[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) al[i] = (uint32_t)((i * 16 + col) * K + slot * 16);
+
+    v4i w[PD][2];
+    v4i a[PD][2][MB];
+    float s[PD];
+    // group g (past the end: zeros, no bytes; fmaf(0, 0, acc) = acc)
+    auto load_wa = [&](int d, int g) {
+        const bool in = g < G;
+        const uint32_t so = in ? (uint32_t)g * 2048u : kOOB;
+        w[d][0] = buf_load16s<NT ? kNonTemporal : 0>(wr, wl, so);
+        w[d][1] = buf_load16s<NT ? kNonTemporal : 0>(wr, wl + 1024, so);
+        const uint32_t ao = in ? (uint32_t)g * 128u : kOOB;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            a[d][0][i] = buf_load16s(ar, al[i], ao);
+            a[d][1][i] = buf_load16s(ar, al[i] + 64, ao);
+        }
+    };
+    auto load_s = [&](int d, int g) {
+        s[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             sr, (int)sl, g < G ? g * 4 : (int)kOOB, 0));
+    };
+    float facc[MB][4];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < PD; ++d) {   // issued in group order
+        load_wa(d, d);
+        load_s(d, d);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int g0 = 0; g0 < G; g0 += PD) {
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+            const int g = g0 + d;
+            v4i acc[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d][0][i], w[d][0], v4i{0, 0, 0, 0},
+                                                               0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d][1][i], w[d][1], acc[i], 0, 0, 0);
+            }
+            load_wa(d, g + PD);
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    facc[i][r] = __builtin_fmaf((float)acc[i][r], s[d], facc[i][r]);
+            load_s(d, g + PD);   // after the epilogue: s[d] is reused in place
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    const int n = nb * 16 + col;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = i * 16 + slot * 4 + r;
+            if (m < M) store_packed_out<OUT>(y, (int64_t)m * N + n, facc[i][r] * sa[m]);
+        }
+}
+
 constexpr int kPackedCUs = 256;
 
 template <int MB, int NW, int OUT>
@@ -244,10 +334,21 @@ hipError_t launch_packed_nw(const int8_t *q, const float *sa, const int8_t *pack
 
 // Workgroup width: the 16-row blocks spread over whole rounds of one
 // workgroup per CU, at most 8 waves (the width the row-major kernel uses).
+// At most one block per CU: the narrow kernel.
 template <int MB, int OUT>
 hipError_t launch_packed_mb(const int8_t *q, const float *sa, const int8_t *packed,
                             const float *sw, int M, int N, int K, void *y, hipStream_t stream) {
     const int64_t blocks16 = N / 16;
+    if (blocks16 <= kPackedCUs) {   // narrow: one wave per block, activations from L2
+        const bool nt = (int64_t)N * K >= ((int64_t)1 << 27);
+        if (nt)
+            gemm_packed_narrow_kernel<MB, OUT, true><<<(unsigned)blocks16, 64, 0, stream>>>(
+                q, sa, packed, sw, M, N, K, y);
+        else
+            gemm_packed_narrow_kernel<MB, OUT, false><<<(unsigned)blocks16, 64, 0, stream>>>(
+                q, sa, packed, sw, M, N, K, y);
+        return hipGetLastError();
+    }
     const int64_t rounds = (blocks16 + 8 * kPackedCUs - 1) / (8 * kPackedCUs);
     const int nw = (int)((blocks16 + kPackedCUs * rounds - 1) / (kPackedCUs * rounds));
     switch (nw) {

@@ -52,11 +52,14 @@ def test_repack_matches_the_layout(N, K):
 
 # M spans one, two and four 16-row token blocks with ragged tails; K gives group
 # counts that do and do not fill the last chunk of the weight ring (12, 8 or 4
-# groups by token blocks); N from one 16-row block to wide enough for 2-8 waves
-# per workgroup.
+# groups by token blocks) or of the activation chunk (one or two rings). N up to
+# 4096 (at most one 16-row block per CU) runs the narrow one-wave kernel; wider N
+# the workgroup kernel with 2 to 8 waves.
 @pytest.mark.parametrize("M,N,K", [
     (1, 16, 128), (5, 48, 3584), (16, 2048, 4096), (17, 1024, 1024), (32, 4096, 1536),
-    (33, 3584, 1152), (48, 272, 1152), (64, 4096, 7168), (7, 8192, 896),
+    (33, 3584, 1152), (48, 272, 1152), (64, 4096, 7168),
+    (7, 8192, 896), (16, 8192, 1024), (1, 32768, 256), (64, 8192, 1152), (48, 16384, 768),
+    (33, 12288, 2176), (32, 20480, 3200),
 ])
 def test_packed_gemm_matches_the_oracle(M, N, K):
     d = require_gpu()
@@ -69,6 +72,21 @@ def test_packed_gemm_matches_the_oracle(M, N, K):
     c32, cb = gemm_fp32_ordered_ref(q, sa, qw, sw)
     check_fp32(_gpu_packed_gemm(q, sa, pd, sw, torch.float32, d), y64, mag, c32)
     check_bf16(_gpu_packed_gemm(q, sa, pd, sw, torch.bfloat16, d), y64, mag, cb)
+
+
+def test_tp8_share_of_the_decode_linear():
+    """One GPU's column share of the decode linear under 8-way tensor parallelism
+    (32 x 8192 x 3584, the narrow kernel) at full size against the oracle."""
+    d = require_gpu()
+    M, N, K = 32, 3584, 8192
+    say(f"packed gemm tp8 share M={M} N={N} K={K}")
+    cfg, q, sa = _inputs(M, K, N, 11)
+    qw, sw = cfg["qw"], cfg["sw"]
+    pd = bsb.repack_weights_mfma(dev(qw, d))
+    y64, mag = gemm_ref(q, sa, qw, sw)
+    c32, cb = gemm_fp32_ordered_ref(q, sa, qw, sw)
+    check_bf16(_gpu_packed_gemm(q, sa, pd, sw, torch.bfloat16, d), y64, mag, cb)
+    check_fp32(_gpu_packed_gemm(q, sa, pd, sw, torch.float32, d), y64, mag, c32)
 
 
 def test_waves_past_the_last_row_block():
