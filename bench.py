@@ -543,6 +543,10 @@ def extra_rows(torch, L, stream, dev, steps):
                      q=torch.empty((Mt, Kd), dtype=torch.int8, device=dev),
                      sa=torch.empty((Mt,), dtype=torch.float32, device=dev),
                      y=torch.empty((Mt, Nd), dtype=torch.int16, device=dev))
+            if Mt == 32:   # the decoded weight repacked at load time for the packed GEMM
+                o["qwp"] = torch.empty((Nd * Kd,), dtype=torch.int8, device=dev)
+                _ok(L, L.bsb_repack_weights_mfma(o["qw"].data_ptr(), Nd, Kd, o["qwp"].data_ptr(),
+                                                 stream))
             _ok(L, L.bsb_quantize_act(xd.data_ptr(), Mt, Kd, o["q"].data_ptr(),
                                       o["sa"].data_ptr(), stream))
             gs.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
@@ -563,6 +567,13 @@ def extra_rows(torch, L, stream, dev, steps):
         bound = "hbm" if Mt == 32 else "mfma"
         rows[f"blockfmt_gemm_m{Mt}_4096x7168"] = _rate(tg * 1e3, ops=2 * Mt * Nd * Kd,
                                                        byts=db, bound=bound)
+        if Mt == 32:
+            tp = Row("blockfmt gemm packed", gs, lambda p, st: _ok(
+                L, L.bsb_gemm_w8a8_g128_packed(p["q"], p["sa"], p["qwp"], p["sw"], Mt, Nd, Kd,
+                                               p["y"], 0, st))).time(torch, stream, steps, 3)
+            rows["blockfmt_gemm_m32_4096x7168_packed"] = _rate(tp * 1e3, ops=2 * Mt * Nd * Kd,
+                                                               byts=db, bound=bound)
+            log(f"blockfmt M=32: gemm on packed weights {tp * 1e3:.1f} us")
         rows[f"blockfmt_grouped_m{Mt}_8x2048x4096"] = _rate(te * 1e3, ops=2 * Re * Ne * Ke,
                                                             byts=eb, bound=bound)
         log(f"blockfmt M={Mt}: gemm {tg * 1e3:.1f} us, grouped {te * 1e3:.1f} us")
