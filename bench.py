@@ -488,6 +488,12 @@ def extra_rows(torch, L, stream, dev, steps):
             L, L.bsb_decode_fp8_block(p["w"], p["bs"], Nd, Kd, dl, p["qw"], p["sw"], st))).time(
             torch, stream, steps, 3)
         rows[f"blockfmt_decode_fp8_{dname}_4096x7168"] = _rate(td * 1e3, byts=fp8_bytes)
+        if dialect == 0:   # the same decode written in the packed GEMM's operand order
+            tdp = Row("decode fp8 packed", dsets, lambda p, st: _ok(
+                L, L.bsb_decode_fp8_block_packed(p["w"], p["bs"], Nd, Kd, 0, p["qw"], p["sw"],
+                                                 st))).time(torch, stream, steps, 3)
+            rows["blockfmt_decode_fp8_ocp_4096x7168_packed"] = _rate(tdp * 1e3, byts=fp8_bytes)
+            log(f"fp8 decode into the packed layout {tdp * 1e3:.1f} us")
         log(f"decode fp8 {dname} {td * 1e3:.1f} us")
     # the BF16 route's load-time dequantisation of the same FP8 blocks
     bf_bytes = Nd * Kd + (Nd // 128) * (Kd // 128) + 2 * Nd * Kd

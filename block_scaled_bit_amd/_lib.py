@@ -37,6 +37,7 @@ _SIGNATURES = {
                                    _c_p, _c_int, _c_p],
     "bsb_decode_fp8_block": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_p],
     "bsb_dequant_fp8_block_bf16": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p],
+    "bsb_decode_fp8_block_packed": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_p],
     "bsb_gemm_w8a16_g128": [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
     "bsb_gemm_bf16": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
     "bsb_decode_mxfp4": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
@@ -292,6 +293,30 @@ def decode_fp8_block(w: torch.Tensor, bs: torch.Tensor, dialect: int,
         _check(lib().bsb_decode_fp8_block(_ptr(w), _ptr(bs), N, K, dialect, _ptr(qw), _ptr(sw),
                                           _stream(dev)), "bsb_decode_fp8_block")
     return qw, sw
+
+
+def decode_fp8_block_packed(w: torch.Tensor, bs: torch.Tensor, dialect: int,
+                            packed: Optional[torch.Tensor] = None,
+                            sw: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """decode_fp8_block with the INT8 weight written in the matrix cores' operand order
+    (packed [N*K], as repack_weights_mfma would leave it) and sw [N,K/128]."""
+    _need(w, "w", (torch.uint8,))
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    N, K = w.shape
+    dev = w.device
+    _need(bs, "bs", (torch.uint8,), (N // 128, K // 128), dev)
+    if dialect not in (BSB_FP8_OCP, BSB_FP8_FNUZ):
+        raise ValueError("dialect must be BSB_FP8_OCP or BSB_FP8_FNUZ")
+    packed = torch.empty((N * K,), dtype=torch.int8, device=dev) if packed is None else packed
+    sw = torch.empty((N, K // 128), dtype=torch.float32, device=dev) if sw is None else sw
+    _need(packed, "packed", (torch.int8,), (N * K,), dev)
+    _need(sw, "sw", (torch.float32,), (N, K // 128), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_decode_fp8_block_packed(_ptr(w), _ptr(bs), N, K, dialect, _ptr(packed),
+                                                 _ptr(sw), _stream(dev)),
+               "bsb_decode_fp8_block_packed")
+    return packed, sw
 
 
 def dequant_fp8_block_bf16(w: torch.Tensor, bs: torch.Tensor, dialect: int,

@@ -202,6 +202,22 @@ bsb_status bsb_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t N, 
                                                sw, as_stream(stream)));
 }
 
+bsb_status bsb_decode_fp8_block_packed(const uint8_t *w, const uint8_t *bs, int64_t N,
+                                       int64_t K, bsb_fp8_dialect dialect, int8_t *packed,
+                                       float *sw, void *stream) {
+    if (N < 128 || N % 128 || K < 128 || K % 128 || N >= kMaxDim || K >= kMaxDim ||
+        N * K > kMaxDecodeElems)
+        return BSB_ERR_INVALID_ARG;
+    if (dialect != BSB_FP8_OCP && dialect != BSB_FP8_FNUZ) return BSB_ERR_INVALID_ARG;
+    if (!w || !bs || !packed || !sw) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(bs) || !aligned16(packed) || !aligned16(sw))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_decode_fp8_block(w, bs, N, K, dialect == BSB_FP8_FNUZ ? 1 : 0,
+                                               packed, sw, as_stream(stream), true));
+}
+
 bsb_status bsb_dequant_fp8_block_bf16(const uint8_t *w, const uint8_t *bs, int64_t N, int64_t K,
                                       bsb_fp8_dialect dialect, uint16_t *w_bf16, void *stream) {
     if (N < 128 || N % 128 || K < 128 || K % 128 || N >= kMaxDim || K >= kMaxDim ||

@@ -77,6 +77,13 @@ __device__ __forceinline__ void fp8x16_to_f32(uint4 v, int fnuz, float *f) {
     }
 }
 
+// PACKED: qw is written in the matrix cores' operand order (16-row x 64-column
+// blocks of 1 KB; 16 consecutive K positions of one row stay one 16-byte chunk),
+// the layout the packed GEMM reads; otherwise row-major [N, K]. The packed form
+// walks the chunks tile by tile (128 threads per 16 rows x one 128-wide group,
+// eight per row), so a wave reads whole 128-byte row segments and writes
+// 128-byte runs; eight consecutive lanes still hold one (row, group).
+template <bool PACKED>
 __global__ void __launch_bounds__(256)
 decode_fp8_block_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ bs,
                         uint32_t nchunks, uint32_t cpr, uint32_t gpr, int fnuz,
@@ -86,11 +93,19 @@ decode_fp8_block_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict
     const bool valid = chunk < nchunks;     // 8-lane groups are valid as a whole
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     float scale = 0.0f;
-    uint32_t n = 0, kc = 0;
+    uint32_t n = 0, kc = 0, src = chunk;
     if (valid) {
-        n = chunk / cpr;
-        kc = chunk - n * cpr;
-        v = reinterpret_cast<const uint4 *>(w)[chunk];
+        if (PACKED) {
+            const uint32_t tile = chunk >> 7, within = chunk & 127u;
+            const uint32_t nt = tile / gpr, gt = tile - nt * gpr;
+            n = nt * 16u + (within >> 3);
+            kc = gt * 8u + (within & 7u);
+            src = n * cpr + kc;
+        } else {
+            n = chunk / cpr;
+            kc = chunk - n * cpr;
+        }
+        v = reinterpret_cast<const uint4 *>(w)[src];
         scale = ue8m0_to_f32(bs[(n >> 7) * gpr + (kc >> 3)]);
     }
     // fnuz = OCP / 2: fold the half into the (power-of-two) block scale
@@ -108,7 +123,11 @@ decode_fp8_block_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict
     uint32_t o[4];
     quant16(f, s, amax, o);
     if (valid) {
-        reinterpret_cast<uint4 *>(qw)[chunk] = make_uint4(o[0], o[1], o[2], o[3]);
+        // packed: block (n/16, kc/4), lane n%16 + 16*(kc%4), in 16-byte chunks
+        const uint32_t dst = PACKED ? (((n >> 4) * (cpr >> 2) + (kc >> 2)) << 6) + (n & 15u) +
+                                          ((kc & 3u) << 4)
+                                    : chunk;
+        reinterpret_cast<uint4 *>(qw)[dst] = make_uint4(o[0], o[1], o[2], o[3]);
         if ((kc & 7u) == 0u) sw[n * gpr + (kc >> 3)] = s;
     }
 }
@@ -203,11 +222,16 @@ hipError_t launch_dequant_fp8_block_bf16(const uint8_t *w, const uint8_t *bs, in
 }
 
 hipError_t launch_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t N, int64_t K,
-                                   int fnuz, int8_t *qw, float *sw, hipStream_t stream) {
+                                   int fnuz, int8_t *qw, float *sw, hipStream_t stream,
+                                   bool packed) {
     const uint32_t nchunks = (uint32_t)(N * K / 16);
     const uint32_t blocks = (nchunks + 255u) / 256u;
-    decode_fp8_block_kernel<<<blocks, 256, 0, stream>>>(w, bs, nchunks, (uint32_t)(K / 16),
-                                                        (uint32_t)(K / 128), fnuz, qw, sw);
+    if (packed)
+        decode_fp8_block_kernel<true><<<blocks, 256, 0, stream>>>(
+            w, bs, nchunks, (uint32_t)(K / 16), (uint32_t)(K / 128), fnuz, qw, sw);
+    else
+        decode_fp8_block_kernel<false><<<blocks, 256, 0, stream>>>(
+            w, bs, nchunks, (uint32_t)(K / 16), (uint32_t)(K / 128), fnuz, qw, sw);
     return hipGetLastError();
 }
 

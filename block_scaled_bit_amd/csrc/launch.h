@@ -12,7 +12,7 @@ hipError_t launch_quantize_act(const uint16_t *x, int64_t M, int64_t K, int8_t *
 
 hipError_t launch_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t N,
                                    int64_t K, int fnuz, int8_t *qw, float *sw,
-                                   hipStream_t stream);
+                                   hipStream_t stream, bool packed = false);
 
 // FP8 e4m3 [N,K] with [N/128, K/128] UE8M0 block scales -> BF16 bits [N,K].
 hipError_t launch_dequant_fp8_block_bf16(const uint8_t *w, const uint8_t *bs, int64_t N,

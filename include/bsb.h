@@ -243,6 +243,17 @@ bsb_status bsb_decode_fp8_block(const uint8_t *w, const uint8_t *bs,
                                 int8_t *qw, float *sw, void *stream);
 
 /*
+ * bsb_decode_fp8_block with the INT8 weight written straight into the matrix
+ * cores' operand order of bsb_repack_weights_mfma (one load-time pass for the
+ * packed GEMM): packed = bsb_repack_weights_mfma(qw) of the qw that
+ * bsb_decode_fp8_block writes; sw is the same [N, G] array. Arguments, limits
+ * and errors as bsb_decode_fp8_block; packed [N*K] int8 (written).
+ */
+bsb_status bsb_decode_fp8_block_packed(const uint8_t *w, const uint8_t *bs,
+                                       int64_t N, int64_t K, bsb_fp8_dialect dialect,
+                                       int8_t *packed, float *sw, void *stream);
+
+/*
  * MXFP4 (E2M1 elements, 1x32 UE8M0 block scales along K) experts ([P1]
  * sec. 1) -> INT8 per-group-128 ([P1] sec. 2).
  *     W[e,n,k] = E2M1(nibble k of row (e,n)) * 2^(scale[e,n,k/32] - 127)

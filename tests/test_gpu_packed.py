@@ -149,3 +149,22 @@ def test_empty_rows_and_limits():
     with pytest.raises(bsb.BsbError):
         bsb.gemm_w8a8_g128_packed(torch.zeros((65, 128), dtype=torch.int8, device=d),
                                   torch.ones((65,), dtype=torch.float32, device=d), pd, sw)
+
+
+@pytest.mark.parametrize("N,K", [(128, 128), (256, 7168), (4096, 1152)])
+@pytest.mark.parametrize("dialect", [bsb.BSB_FP8_OCP, bsb.BSB_FP8_FNUZ])
+def test_fp8_decode_straight_into_the_packed_layout(N, K, dialect):
+    """The FP8 [128,128] UE8M0 decoder writing the operand order: the oracle's
+    decode, repacked by the oracle's layout, bit for bit; the scales as the
+    row-major decoder writes them."""
+    d = require_gpu()
+    say(f"decode fp8 packed N={N} K={K} dialect={dialect}")
+    from oracle import decode_fp8_block_ref
+    w, bs = synth.fp8_block_weights(np.random.default_rng(N + K + dialect), N, K)
+    pk = Guarded((N * K,), torch.int8, d)
+    sg = Guarded((N, K // 128), torch.float32, d)
+    bsb.decode_fp8_block_packed(dev(w, d), dev(bs, d), dialect, packed=pk.view, sw=sg.view)
+    torch.cuda.synchronize()
+    qr, sr = decode_fp8_block_ref(w, bs, dialect)
+    assert np.array_equal(pk.check(), repack_mfma_ref(qr))
+    assert np.array_equal(sg.check(), sr)
