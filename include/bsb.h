@@ -25,7 +25,10 @@
  *    mid-way, no scratch allocation).
  *  - All matrices are row-major and contiguous. K is the reduction dimension
  *    and is contiguous in both operands; G = K / 128 is the number of
- *    128-wide K groups.
+ *    128-wide K groups. Two exceptions, each with its layout stated at its
+ *    calls: the packed weight form (written by bsb_repack_weights_mfma and
+ *    bsb_decode_fp8_block_packed, read by bsb_gemm_w8a8_g128_packed) and the
+ *    INT8 KV cache's blocks.
  *  - Sizes: K % 128 == 0 and K > 0; N >= 1; M, R >= 0 (0 rows is a
  *    successful no-op that launches nothing). Every extent is below 2^30;
  *    a weight matrix (all experts together) holds at most 2^36 elements,
