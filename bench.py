@@ -561,6 +561,10 @@ def extra_rows(torch, L, stream, dev, steps):
                      q=torch.empty((Re, Ke), dtype=torch.int8, device=dev),
                      sa=torch.empty((Re,), dtype=torch.float32, device=dev),
                      y=torch.empty((Re, Ne), dtype=torch.int16, device=dev))
+            if Mt == 32:   # the stacked experts repacked at load time for the packed form
+                o["qwp"] = torch.empty((Ee * Ne * Ke,), dtype=torch.int8, device=dev)
+                _ok(L, L.bsb_repack_weights_mfma(o["qw"].data_ptr(), Ee * Ne, Ke,
+                                                 o["qwp"].data_ptr(), stream))
             _ok(L, L.bsb_quantize_act(xe.data_ptr(), Re, Ke, o["q"].data_ptr(),
                                       o["sa"].data_ptr(), stream))
             es.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
@@ -580,6 +584,13 @@ def extra_rows(torch, L, stream, dev, steps):
             rows["blockfmt_gemm_m32_4096x7168_packed"] = _rate(tp * 1e3, ops=2 * Mt * Nd * Kd,
                                                                byts=db, bound=bound)
             log(f"blockfmt M=32: gemm on packed weights {tp * 1e3:.1f} us")
+            tep = Row("blockfmt grouped packed", es, lambda p, st: _ok(
+                L, L.bsb_grouped_gemm_w8a8_g128_packed(p["q"], p["sa"], p["qwp"], p["sw"],
+                                                       p["off"], Ee, Re, Ne, Ke, p["y"], 0,
+                                                       st))).time(torch, stream, steps, 3)
+            rows["blockfmt_grouped_m32_8x2048x4096_packed"] = _rate(
+                tep * 1e3, ops=2 * Re * Ne * Ke, byts=eb, bound=bound)
+            log(f"blockfmt M=32: grouped on packed weights {tep * 1e3:.1f} us")
         rows[f"blockfmt_grouped_m{Mt}_8x2048x4096"] = _rate(te * 1e3, ops=2 * Re * Ne * Ke,
                                                             byts=eb, bound=bound)
         log(f"blockfmt M={Mt}: gemm {tg * 1e3:.1f} us, grouped {te * 1e3:.1f} us")

@@ -29,6 +29,8 @@ _SIGNATURES = {
     "bsb_quantize_act": [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "bsb_gemm_w8a8_g128": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
     "bsb_repack_weights_mfma": [_c_p, _c_i64, _c_i64, _c_p, _c_p],
+    "bsb_grouped_gemm_w8a8_g128_packed": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                          _c_i64, _c_p, _c_int, _c_p],
     "bsb_gemm_w8a8_g128_packed": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int,
                                   _c_p],
     "bsb_gemm_w8a8_channel": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_int,
@@ -270,6 +272,33 @@ def grouped_gemm_w8a8_g128(q: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, 
         _check(lib().bsb_grouped_gemm_w8a8_g128(_ptr(q), _ptr(sa), _ptr(qw), _ptr(sw),
                                                 _ptr(offsets), E, R, N, K, _ptr(out), code,
                                                 _stream(dev)), "bsb_grouped_gemm_w8a8_g128")
+    return out
+
+
+def grouped_gemm_w8a8_g128_packed(q: torch.Tensor, sa: torch.Tensor, packed: torch.Tensor,
+                                  sw: torch.Tensor, offsets: torch.Tensor,
+                                  out_dtype=torch.bfloat16,
+                                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """grouped_gemm_w8a8_g128 on packed expert weights: packed [E*N*K] is
+    repack_weights_mfma(qw.view(E*N, K)); sw [E,N,K/128]. Bit-identical results."""
+    _need(q, "q", (torch.int8,))
+    if q.dim() != 2 or sw.dim() != 3:
+        raise ValueError("q [R,K] and sw [E,N,K/128] required")
+    R, K = q.shape
+    E, N, _ = sw.shape
+    dev = q.device
+    _need(packed, "packed", (torch.int8,), (E * N * K,), dev)
+    _need(sa, "sa", (torch.float32,), (R,), dev)
+    _need(sw, "sw", (torch.float32,), (E, N, K // 128), dev)
+    _need(offsets, "offsets", (torch.int32,), (E + 1,), dev)
+    code = _out_code(out_dtype)
+    out = torch.empty((R, N), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", (out_dtype,), (R, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_grouped_gemm_w8a8_g128_packed(_ptr(q), _ptr(sa), _ptr(packed),
+                                                       _ptr(sw), _ptr(offsets), E, R, N, K,
+                                                       _ptr(out), code, _stream(dev)),
+               "bsb_grouped_gemm_w8a8_g128_packed")
     return out
 
 

@@ -139,6 +139,26 @@ bsb_status bsb_gemm_w8a8_g128_packed(const int8_t *q, const float *sa, const int
                                           as_stream(stream)));
 }
 
+bsb_status bsb_grouped_gemm_w8a8_g128_packed(const int8_t *q, const float *sa,
+                                             const int8_t *packed, const float *sw,
+                                             const int32_t *offsets, int64_t E, int64_t R,
+                                             int64_t N, int64_t K, void *y, bsb_out_dtype out,
+                                             void *stream) {
+    if (!dims_ok(R, N, K) || N % 16 || K > kMaxPackedK || E < 1 || E > 65535 ||
+        !prod_le(E, N, K, kMaxElems))
+        return BSB_ERR_INVALID_ARG;
+    if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
+    if (R == 0) return BSB_OK;
+    if (!q || !sa || !packed || !sw || !offsets || !y) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(sa) || !aligned16(packed) || !aligned16(sw) ||
+        !aligned16(offsets) || !aligned16(y))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_grouped_gemm_packed(q, sa, packed, sw, offsets, E, R, N, K, y,
+                                                  (int)out, as_stream(stream)));
+}
+
 bsb_status bsb_gemm_w8a8_channel(const int8_t *q, const float *sa, const int8_t *qw,
                                  const float *sw, int64_t sw_stride, int64_t M, int64_t N,
                                  int64_t K, void *y, bsb_out_dtype out, void *stream) {

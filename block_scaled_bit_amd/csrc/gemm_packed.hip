@@ -79,10 +79,14 @@ constexpr int packed_chunk() {
 // The pointer arguments carry no __restrict__: with it the compiler treats the
 // buffer loads as invariant and regroups them by kind across the fences below,
 // which breaks the one-group-per-step issue order the waits are counted for.
-template <int MB, int NW, int OUT, bool NT>
+// GROUPED (the MoE form): blockIdx.y is the expert e, its rows are
+// offsets[e] .. offsets[e+1]-1 of q / sa / y (clamped to [0, M]), its weights the
+// e-th [N, K] block of the packed array (the stacked [E*N, K] experts repacked),
+// its scales sw[e]; the rows are walked in passes of 16*MB.
+template <int MB, int NW, int OUT, bool NT, bool GROUPED = false>
 __global__ void __launch_bounds__(64 * NW)
 gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const float *sw, int M,
-                   int N, int K, void *y) {
+                   int N, int K, void *y, const int32_t *offsets = nullptr) {
     constexpr int PD = packed_depth<MB>();
     constexpr int CG = packed_chunk<MB, NW>();
     constexpr int ROWS = 16 * MB;
@@ -100,11 +104,22 @@ gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const
     const int G = K / 128;
     const int nch = (G + CG - 1) / CG;
     const int col = lane & 15, slot = lane >> 4;
+    int lo = 0, hi = M;
+    if (GROUPED) {
+        const int e = blockIdx.y;
+        lo = offsets[e];
+        hi = offsets[e + 1];
+        lo = lo < 0 ? 0 : (lo > M ? M : lo);
+        hi = hi < lo ? lo : (hi > M ? M : hi);
+        if (hi == lo) return;   // the whole workgroup: an empty expert
+        packed += (int64_t)e * N * K;
+        sw += (int64_t)e * N * G;
+    }
     const auto wr = make_rsrc(live ? packed + (int64_t)nb * K * 16 : packed,
                               live ? (uint32_t)(K * 16) : 0u);
     const auto sr = make_rsrc(live ? sw + (int64_t)nb * 16 * G : sw,
                               live ? (uint32_t)(16 * G * 4) : 0u);
-    const v4i ra = make_rsrc_words(q, (uint32_t)(M * K));   // rows >= M read zero
+    v4i ra;   // the pass's activation rows (rows past them read zero)
     const uint32_t wl = (uint32_t)lane * 16;
     const uint32_t sl = (uint32_t)(col * G * 4);
 
@@ -146,6 +161,9 @@ gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const
         s[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                              sr, (int)sl, g < G ? g * 4 : (int)kOOB, 0));
     };
+    for (int r0 = lo;; r0 += ROWS) {   // the dense form makes exactly one pass
+    const int rows = hi - r0 < ROWS ? hi - r0 : ROWS;
+    ra = make_rsrc_words(q + (int64_t)r0 * K, (uint32_t)(rows * K));
     float facc[MB][4];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -215,15 +233,24 @@ gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    if (!live) return;
-    const int n = nb * 16 + col;
+    if (live) {
+        const int n = nb * 16 + col;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = i * 16 + slot * 4 + r;
-            if (m < M) store_packed_out<OUT>(y, (int64_t)m * N + n, facc[i][r] * sa[m]);
-        }
+            for (int r = 0; r < 4; ++r) {
+                const int m = i * 16 + slot * 4 + r;
+                if (m < rows)
+                    store_packed_out<OUT>(y, (int64_t)(r0 + m) * N + n, facc[i][r] * sa[r0 + m]);
+            }
+    }
+    if (!GROUPED || r0 + ROWS >= hi) break;
+    // the next pass's chunk 0 goes into buffer 0, which the last chunk may still
+    // be read from: every wave finishes this pass first
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    }
 }
 
 // Narrow weights (at most one 16-row block per CU): one wave per workgroup and no
@@ -318,6 +345,40 @@ gemm_packed_narrow_kernel(const int8_t *q, const float *sa, const int8_t *packed
 
 constexpr int kPackedCUs = 256;
 
+template <int NW, int OUT>
+hipError_t launch_packed_grouped_nw(const int8_t *q, const float *sa, const int8_t *packed,
+                                    const float *sw, const int32_t *offsets, int E, int R, int N,
+                                    int K, void *y, hipStream_t stream) {
+    const dim3 grid((unsigned)((N / 16 + NW - 1) / NW), (unsigned)E);
+    if ((int64_t)E * N * K >= ((int64_t)1 << 27))
+        gemm_packed_kernel<2, NW, OUT, true, true><<<grid, 64 * NW, 0, stream>>>(
+            q, sa, packed, sw, R, N, K, y, offsets);
+    else
+        gemm_packed_kernel<2, NW, OUT, false, true><<<grid, 64 * NW, 0, stream>>>(
+            q, sa, packed, sw, R, N, K, y, offsets);
+    return hipGetLastError();
+}
+
+// Workgroup width as for the dense form, over all experts' 16-row blocks.
+template <int OUT>
+hipError_t launch_packed_grouped(const int8_t *q, const float *sa, const int8_t *packed,
+                                 const float *sw, const int32_t *offsets, int E, int R, int N,
+                                 int K, void *y, hipStream_t stream) {
+    const int64_t blocks16 = (int64_t)(N / 16) * E;
+    const int64_t rounds = (blocks16 + 8 * kPackedCUs - 1) / (8 * kPackedCUs);
+    int nw = (int)((blocks16 + kPackedCUs * rounds - 1) / (kPackedCUs * rounds));
+    nw = nw < 2 ? 2 : nw;
+    switch (nw) {
+        case 2: return launch_packed_grouped_nw<2, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
+        case 3: return launch_packed_grouped_nw<3, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
+        case 4: return launch_packed_grouped_nw<4, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
+        case 5: return launch_packed_grouped_nw<5, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
+        case 6: return launch_packed_grouped_nw<6, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
+        case 7: return launch_packed_grouped_nw<7, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
+        default: return launch_packed_grouped_nw<8, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
+    }
+}
+
 template <int MB, int NW, int OUT>
 hipError_t launch_packed_nw(const int8_t *q, const float *sa, const int8_t *packed,
                             const float *sw, int M, int N, int K, void *y, hipStream_t stream) {
@@ -379,6 +440,16 @@ hipError_t launch_repack_mfma(const int8_t *qw, int64_t N, int64_t K, int8_t *pa
     repack_mfma_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, stream>>>(qw, (int)N, (int)K,
                                                                              packed);
     return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_packed(const int8_t *q, const float *sa, const int8_t *packed,
+                                      const float *sw, const int32_t *offsets, int64_t E,
+                                      int64_t R, int64_t N, int64_t K, void *y, int out,
+                                      hipStream_t stream) {
+    return out == 0 ? launch_packed_grouped<0>(q, sa, packed, sw, offsets, (int)E, (int)R, (int)N,
+                                               (int)K, y, stream)
+                    : launch_packed_grouped<1>(q, sa, packed, sw, offsets, (int)E, (int)R, (int)N,
+                                               (int)K, y, stream);
 }
 
 hipError_t launch_gemm_packed(const int8_t *q, const float *sa, const int8_t *packed,

@@ -30,6 +30,10 @@ hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw,
 // gemm_packed.hip: weights in the matrix cores' operand order (M <= 64)
 hipError_t launch_repack_mfma(const int8_t *qw, int64_t N, int64_t K, int8_t *packed,
                               hipStream_t stream);
+hipError_t launch_grouped_gemm_packed(const int8_t *q, const float *sa, const int8_t *packed,
+                                      const float *sw, const int32_t *offsets, int64_t E,
+                                      int64_t R, int64_t N, int64_t K, void *y, int out,
+                                      hipStream_t stream);
 hipError_t launch_gemm_packed(const int8_t *q, const float *sa, const int8_t *packed,
                               const float *sw, int64_t M, int64_t N, int64_t K, void *y, int out,
                               hipStream_t stream);

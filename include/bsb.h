@@ -146,6 +146,23 @@ bsb_status bsb_gemm_w8a8_g128_packed(const int8_t *q, const float *sa,
                                      void *y, bsb_out_dtype out, void *stream);
 
 /*
+ * bsb_grouped_gemm_w8a8_g128 (the MoE form) on packed expert weights: the
+ * stacked experts qw [E*N, K] repacked by bsb_repack_weights_mfma (each expert's
+ * [N, K] block is then contiguous, N*K bytes at e*N*K), scales sw [E, N, K/128]
+ * unchanged. Same arithmetic and order, so y is bit-identical to
+ * bsb_grouped_gemm_w8a8_g128 on the unpacked weights. Built for decode-shaped
+ * MoE: each expert's rows are walked in passes of 32, and each pass streams the
+ * expert's weights once.
+ *   N a multiple of 16;  K a multiple of 128, at most 2^24;  E at most 65535
+ * Other arguments, limits and errors as bsb_grouped_gemm_w8a8_g128.
+ */
+bsb_status bsb_grouped_gemm_w8a8_g128_packed(const int8_t *q, const float *sa,
+                                             const int8_t *packed, const float *sw,
+                                             const int32_t *offsets, int64_t E, int64_t R,
+                                             int64_t N, int64_t K, void *y,
+                                             bsb_out_dtype out, void *stream);
+
+/*
  * W8A8 GEMM with one weight scale per output row (per-channel) or one for the
  * whole weight (per-tensor): the coarser granularities of [P3] sec. 3.1's
  * taxonomy, whose deployment checklist (sec. 6) runs per-tensor before moving

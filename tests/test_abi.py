@@ -243,6 +243,13 @@ def test_packed_weight_argument_checks(L):
     assert g(A, A, None, A, 4, 16, 128, A, 0, None) == INVALID
     assert g(A, A, U, A, 4, 16, 128, A, 0, None) == MISALIGNED
     assert g(None, None, None, None, 0, 16, 128, None, 0, None) == OK   # no rows
+    gp = L.bsb_grouped_gemm_w8a8_g128_packed
+    assert gp(A, A, A, A, A, 0, 4, 16, 128, A, 0, None) == INVALID       # no experts
+    assert gp(A, A, A, A, A, 65536, 4, 16, 128, A, 0, None) == INVALID   # too many experts
+    assert gp(A, A, A, A, A, 2, 4, 24, 128, A, 0, None) == INVALID       # N % 16
+    assert gp(A, A, A, A, None, 2, 4, 16, 128, A, 0, None) == INVALID    # offsets
+    assert gp(A, A, A, A, U, 2, 4, 16, 128, A, 0, None) == MISALIGNED
+    assert gp(None, None, None, None, None, 2, 0, 16, 128, None, 0, None) == OK   # no rows
     dp = L.bsb_decode_fp8_block_packed
     assert dp(A, A, 64, 128, 0, A, A, None) == INVALID        # N % 128
     assert dp(A, A, 128, 128, 2, A, A, None) == INVALID       # dialect
@@ -250,5 +257,6 @@ def test_packed_weight_argument_checks(L):
     assert dp(A, A, 128, 128, 0, U, A, None) == MISALIGNED
     if not torch.cuda.is_available():
         assert dp(A, A, 128, 128, 1, A, A, None) == UNSUPPORTED
+        assert gp(A, A, A, A, A, 2, 4, 16, 128, A, 1, None) == UNSUPPORTED
         assert rp(A, 16, 128, A, None) == UNSUPPORTED
         assert g(A, A, A, A, 64, 16, 1 << 24, A, 1, None) == UNSUPPORTED

@@ -168,3 +168,45 @@ def test_fp8_decode_straight_into_the_packed_layout(N, K, dialect):
     qr, sr = decode_fp8_block_ref(w, bs, dialect)
     assert np.array_equal(pk.check(), repack_mfma_ref(qr))
     assert np.array_equal(sg.check(), sr)
+
+
+def _grouped_case(lengths, N, K, seed):
+    rng = np.random.default_rng(seed)
+    E = len(lengths)
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(lengths)
+    x = synth.activations(rng, int(off[-1]), K, 0.01, 20.0)
+    qw = synth.int8_weights(rng, (E, N, K))
+    sw = synth.group_scales(rng, (E, N, K // 128))
+    return x, qw, sw, off
+
+
+# experts empty, of 1, 2, 31, 33, 64, 70 and 300 rows (passes of 32 rows); group
+# counts that do and do not fill the activation chunk; the MXFP4 expert shape
+@pytest.mark.parametrize("lengths,N,K", [
+    ([0, 0, 0, 64], 64, 128),
+    ([17] * 9, 256, 512),
+    ([0, 70, 1, 33, 0, 31, 2], 208, 384),
+    ([31, 0, 33, 1, 32, 5, 64, 2], 2048, 4224),
+    ([300, 0, 0, 2], 144, 1152),
+    ([32] * 8, 2048, 4096),
+])
+def test_grouped_packed_matches_the_oracle(lengths, N, K):
+    from oracle import grouped_gemm_ref, grouped_gemm_fp32_ordered_ref
+    d = require_gpu()
+    say(f"grouped packed lengths={lengths} N={N} K={K}")
+    x, qw, sw, off = _grouped_case(lengths, N, K, len(lengths) + N)
+    q, sa = quantize_act_ref(x)
+    E, R = len(lengths), q.shape[0]
+    pd = bsb.repack_weights_mfma(dev(qw.reshape(E * N, K), d))
+    y64, mag = grouped_gemm_ref(q, sa, qw, sw, off)
+    c32, cb = grouped_gemm_fp32_ordered_ref(q, sa, qw, sw, off)
+    for dtype in (torch.float32, torch.bfloat16):
+        g = Guarded((R, N), dtype, d)
+        bsb.grouped_gemm_w8a8_g128_packed(dev(q, d), dev(sa, d), pd, dev(sw, d), dev(off, d),
+                                          out_dtype=dtype, out=g.view)
+        torch.cuda.synchronize()
+        if dtype == torch.float32:
+            check_fp32(g.check(), y64, mag, c32)
+        else:
+            check_bf16(g.check(), y64, mag, cb)
