@@ -765,7 +765,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gemm_decode_packed"),
-                     "kernel": "gemm_packed_kernel<2, 7, 0, true>",
+                     "kernel": "gemm_packed_kernel<2, 7, 0, true, false>",
                      "timing": "mean of back-to-back launches between HIP events on the launch stream",
                      "bytes_per_launch": g_bytes, "avg_us": round(g_avg * 1e3, 2),
                      "quant_avg_us": round(q_avg * 1e3, 2)},
