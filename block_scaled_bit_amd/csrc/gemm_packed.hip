@@ -162,94 +162,96 @@ gemm_packed_kernel(const int8_t *q, const float *sa, const int8_t *packed, const
                                              sr, (int)sl, g < G ? g * 4 : (int)kOOB, 0));
     };
     for (int r0 = lo;; r0 += ROWS) {   // the dense form makes exactly one pass
-    const int rows = hi - r0 < ROWS ? hi - r0 : ROWS;
-    ra = make_rsrc_words(q + (int64_t)r0 * K, (uint32_t)(rows * K));
-    float facc[MB][4];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
-
-    // Issue order: chunk 0's activations, then groups 0 .. PD-1 one at a time.
-    stage(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int d = 0; d < PD; ++d) {
-        load_w(d, d);
-        load_s(d, d);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int c = 0; c < nch; ++c) {
-        // Exactly 3*CG loads (3*PD for chunk 0: the prologue's groups) were
-        // issued after this wave's blocks of chunk c, the weights and scales
-        // of the groups in between, and loads complete in order: the blocks
-        // have landed. The barrier then publishes every wave's and also means
-        // every wave is done reading chunk c-1's buffer, which chunk c+1 goes
-        // into.
-        if (c == 0)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PD) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * CG) : "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        if (c + 1 < nch) stage(c + 1);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        const int8_t *buf = As[c & 1];
-#pragma unroll
-        for (int dd = 0; dd < CG; ++dd) {
-            const int d = dd % PD;           // weight ring slot
-            const int g = c * CG + dd;
-            v4i af[2][MB];
-#pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                const int r = i * 16 + col;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int j = h * 4 + slot;   // K positions 64h + 16*slot .. +15
-                    af[h][i] = *reinterpret_cast<const v4i *>(buf + dd * GT + r * 128 +
-                                                              ((j ^ ((r >> 1) & 7)) << 4));
-                }
-            }
-            v4i acc[MB];
-#pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], w[d][0], v4i{0, 0, 0, 0},
-                                                               0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], w[d][1], acc[i], 0, 0, 0);
-            }
-            load_w(d, g + PD);
-            // C layout of 16x16: lane holds weight row `col`, tokens 4*slot + r
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    facc[i][r] = __builtin_fmaf((float)acc[i][r], s[d], facc[i][r]);
-            load_s(d, g + PD);   // after the epilogue: s[d] is reused in place
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    if (live) {
-        const int n = nb * 16 + col;
+        const int rows = hi - r0 < ROWS ? hi - r0 : ROWS;
+        ra = make_rsrc_words(q + (int64_t)r0 * K, (uint32_t)(rows * K));
+        float facc[MB][4];
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = i * 16 + slot * 4 + r;
-                if (m < rows)
-                    store_packed_out<OUT>(y, (int64_t)(r0 + m) * N + n, facc[i][r] * sa[r0 + m]);
+            for (int r = 0; r < 4; ++r) facc[i][r] = 0.0f;
+
+        // Issue order: chunk 0's activations, then groups 0 .. PD-1 one at a time.
+        stage(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+            load_w(d, d);
+            load_s(d, d);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int c = 0; c < nch; ++c) {
+            // Exactly 3*CG loads (3*PD for chunk 0: the prologue's groups) were
+            // issued after this wave's blocks of chunk c, the weights and scales
+            // of the groups in between, and loads complete in order: the blocks
+            // have landed. The barrier then publishes every wave's and also means
+            // every wave is done reading chunk c-1's buffer, which chunk c+1 goes
+            // into.
+            if (c == 0)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PD) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * CG) : "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (c + 1 < nch) stage(c + 1);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            const int8_t *buf = As[c & 1];
+#pragma unroll
+            for (int dd = 0; dd < CG; ++dd) {
+                const int d = dd % PD;           // weight ring slot
+                const int g = c * CG + dd;
+                v4i af[2][MB];
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const int r = i * 16 + col;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int j = h * 4 + slot;   // K positions 64h + 16*slot .. +15
+                        af[h][i] = *reinterpret_cast<const v4i *>(buf + dd * GT + r * 128 +
+                                                                  ((j ^ ((r >> 1) & 7)) << 4));
+                    }
+                }
+                v4i acc[MB];
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][i], w[d][0],
+                                                                   v4i{0, 0, 0, 0}, 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][i], w[d][1], acc[i],
+                                                                   0, 0, 0);
+                }
+                load_w(d, g + PD);
+                // C layout of 16x16: lane holds weight row `col`, tokens 4*slot + r
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        facc[i][r] = __builtin_fmaf((float)acc[i][r], s[d], facc[i][r]);
+                load_s(d, g + PD);   // after the epilogue: s[d] is reused in place
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
             }
-    }
-    if (!GROUPED || r0 + ROWS >= hi) break;
-    // the next pass's chunk 0 goes into buffer 0, which the last chunk may still
-    // be read from: every wave finishes this pass first
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+        }
+        if (live) {
+            const int n = nb * 16 + col;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = i * 16 + slot * 4 + r;
+                    if (m < rows)
+                        store_packed_out<OUT>(y, (int64_t)(r0 + m) * N + n,
+                                              facc[i][r] * sa[r0 + m]);
+                }
+        }
+        if (!GROUPED || r0 + ROWS >= hi) break;
+        // the next pass's chunk 0 goes into buffer 0, which the last chunk may still
+        // be read from: every wave finishes this pass first
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     }
 }
 
@@ -320,7 +322,8 @@ gemm_packed_narrow_kernel(const int8_t *q, const float *sa, const int8_t *packed
             for (int i = 0; i < MB; ++i) {
                 acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d][0][i], w[d][0], v4i{0, 0, 0, 0},
                                                                0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d][1][i], w[d][1], acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d][1][i], w[d][1], acc[i], 0, 0,
+                                                               0);
             }
             load_wa(d, g + PD);
 #pragma unroll
@@ -368,15 +371,20 @@ hipError_t launch_packed_grouped(const int8_t *q, const float *sa, const int8_t 
     const int64_t rounds = (blocks16 + 8 * kPackedCUs - 1) / (8 * kPackedCUs);
     int nw = (int)((blocks16 + kPackedCUs * rounds - 1) / (kPackedCUs * rounds));
     nw = nw < 2 ? 2 : nw;
+#define BSB_PACKED_GROUPED_CASE(W)                                                               \
+    case W:                                                                                      \
+        return launch_packed_grouped_nw<W, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
     switch (nw) {
-        case 2: return launch_packed_grouped_nw<2, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
-        case 3: return launch_packed_grouped_nw<3, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
-        case 4: return launch_packed_grouped_nw<4, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
-        case 5: return launch_packed_grouped_nw<5, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
-        case 6: return launch_packed_grouped_nw<6, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
-        case 7: return launch_packed_grouped_nw<7, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
-        default: return launch_packed_grouped_nw<8, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y, stream);
+        BSB_PACKED_GROUPED_CASE(2)
+        BSB_PACKED_GROUPED_CASE(3)
+        BSB_PACKED_GROUPED_CASE(4)
+        BSB_PACKED_GROUPED_CASE(5)
+        BSB_PACKED_GROUPED_CASE(6)
+        BSB_PACKED_GROUPED_CASE(7)
+        default: return launch_packed_grouped_nw<8, OUT>(q, sa, packed, sw, offsets, E, R, N, K, y,
+                                                          stream);
     }
+#undef BSB_PACKED_GROUPED_CASE
 }
 
 template <int MB, int NW, int OUT>
