@@ -30,42 +30,17 @@
 // assignment of K positions to (lane slot, instruction) that is identical for
 // A and B gives the same exact INT32 sum; each lane here owns a contiguous
 // span of the group so its loads are 16-byte aligned and contiguous.
-#include "device_common.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace bsb {
 
 namespace {
 
-// Output forms. The *_CH forms take one weight scale per row n of the weight
-// (or one for all rows: scale index n * sw_stride with stride 0): the INT32
-// total over the whole of K is formed and rescaled once at the end.
-enum { OUT_BF16 = 0, OUT_FP32 = 1, OUT_PARTIALS = 2, OUT_BF16_CH = 3, OUT_FP32_CH = 4 };
-
-template <int OUT>
-constexpr bool per_channel() {
-    return OUT == OUT_BF16_CH || OUT == OUT_FP32_CH;
-}
-
-// (float)P, times the weight scale, then the activation scale, each rounded
-// to float32 (the build does not contract multiplies into FMAs)
-__device__ __forceinline__ float channel_value(int32_t p, float swn, float sa) {
-    const float t = (float)p * swn;
-    return t * sa;
-}
-
 __device__ __forceinline__ v4i as_v4i(uint4 u) {
     v4i r;
     r[0] = (int)u.x; r[1] = (int)u.y; r[2] = (int)u.z; r[3] = (int)u.w;
     return r;
-}
-
-template <int OUT>
-__device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
-    if (OUT == OUT_BF16 || OUT == OUT_BF16_CH)
-        reinterpret_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
-    else
-        reinterpret_cast<float *>(y)[idx] = v;
 }
 
 // LDS position of 16-byte chunk j of row r is j ^ chunk_swizzle(r): rows of
@@ -766,337 +741,6 @@ gemm_tile_kernel(TileArgs p, int n_tiles) {
     }
 }
 
-// --------------------------------------------------------------------------
-// big: 256x256 output tile per workgroup of 8 waves (prefill-shaped M).
-// --------------------------------------------------------------------------
-// Waves form a 4 (M) x 2 (N) grid, each owning 64x128 outputs = 2 x 4 blocks
-// of v_mfma_i32_32x32x32_i8. Two waves per SIMD: while one converts and
-// rescales its finished INT32 block partials on the VALU, the other keeps the
-// matrix core busy. Per K group the A tile (256 rows x 128 B) and the B tile
-// (256 weight rows x 128 B) are staged through a double-buffered LDS tile
-// (128 KB) with an XOR swizzle (16-byte chunk j of row r at j ^ ((r>>1)&7)).
-// The next group's tiles are loaded straight into the other LDS buffer (buffer
-// loads with the LDS-destination bit, 8 lanes per 128-byte row line) while the
-// current group is multiplied, so the staging needs no registers; those loads
-// are waited for only at the end of the group (issued through inline assembly,
-// the compiler would otherwise wait for them before the group's first LDS
-// read and expose their whole latency every group). The group's 256 weight
-// scales are staged in LDS beside the tiles. One barrier per K group.
-// Workgroup ids are remapped so that each XCD works
-// on a contiguous run of tiles, ordered in groups of 4 tile rows, which keeps
-// the operand panels its workgroups share in that XCD's L2.
-constexpr int BBM = 256, BBN = 256;
-#ifndef BSB_GROUPED_COLUMN_MAJOR
-#define BSB_GROUPED_COLUMN_MAJOR 1
-#endif
-constexpr bool kGroupedColumnMajor = BSB_GROUPED_COLUMN_MAJOR;
-
-struct BigTiles {
-    int mt, nt;   // tile rows / columns
-};
-
-template <bool COLUMN_MAJOR>
-__device__ __forceinline__ void big_tile_of(int b, BigTiles t, int &bm, int &bn) {
-    const int num = t.mt * t.nt;
-    const int x = b & 7, per = num >> 3, rem = num & 7;
-    const int start = x * per + (x < rem ? x : rem);
-    const int tid = start + (b >> 3);                       // bijection onto [0, num)
-    if (COLUMN_MAJOR) {
-        // each XCD walks whole tile columns: consecutive row tiles share the
-        // weight panel of the column (per expert, in the grouped form)
-        bm = tid % t.mt;
-        bn = tid / t.mt;
-        return;
-    }
-    constexpr int GM = 4;
-    const int grp = tid / (GM * t.nt);
-    const int first = grp * GM;
-    const int gsz = min(t.mt - first, GM);
-    const int in = tid - grp * GM * t.nt;
-    bm = first + in % gsz;
-    bn = in / gsz;
-}
-
-// GROUPED: q holds R = M rows sorted by expert, rows [offsets[e], offsets[e+1])
-// multiply expert e's weights qw[e] / sw[e]; tile rows are laid out expert
-// after expert (a tile never spans two experts) and the host sizes the grid
-// for the most tiles any split of R rows over E experts can need.
-template <int OUT, bool GROUPED>
-__global__ void __launch_bounds__(512, 1)
-gemm_big_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
-                const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N, int K,
-                void *__restrict__ y, BigTiles tiles, const int32_t *__restrict__ offsets, int E,
-                int sw_stride) {
-    constexpr bool CHN = per_channel<OUT>();   // one scale per row, applied at the end
-    __shared__ __align__(16) int8_t smem[2][(BBM + BBN) * kGroup];   // 2 x 64 KB
-    __shared__ __align__(16) float sws[2][2 * BBN];   // second half: unused slots
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int l32 = lane & 31, half = lane >> 5;
-    const int G = K >> 7;
-    auto seg = [&](int e, int &lo, int &hi) {   // expert e's rows, clamped to [0, R]
-        lo = offsets[e];
-        hi = offsets[e + 1];
-        lo = lo < 0 ? 0 : (lo > M ? M : lo);
-        hi = hi < lo ? lo : (hi > M ? M : hi);
-    };
-    if (GROUPED) {
-        // The tiles that exist are known only here: count them and let the
-        // first mt*nt workgroups take them (the dispatcher deals workgroups
-        // round-robin to the XCDs, so the idle surplus spreads evenly).
-        // (Offsets that overlap, which the contract excludes, could count more
-        // than the host bound; the count is capped at it, so every tile stays
-        // inside [0, R).)
-        int64_t mt = 0;
-        for (int e = 0; e < E; ++e) {
-            int lo, hi;
-            seg(e, lo, hi);
-            mt += (hi - lo + BBM - 1) / BBM;
-        }
-        mt = mt < tiles.mt ? mt : tiles.mt;
-        if ((int64_t)blockIdx.x >= mt * tiles.nt) return;   // whole workgroup
-        tiles.mt = (int)mt;
-    }
-    int bm, bn;
-    big_tile_of<GROUPED && kGroupedColumnMajor>(blockIdx.x, tiles, bm, bn);
-    const int n0 = bn * BBN;
-    int m0, row_end;
-    if (GROUPED) {
-        // tile row bm -> (expert, 256-row block)
-        int t = bm, e = 0;
-        m0 = -1;
-        row_end = 0;
-        for (; e < E; ++e) {
-            int lo, hi;
-            seg(e, lo, hi);
-            const int nt = (hi - lo + BBM - 1) / BBM;
-            if (t < nt) {
-                m0 = lo + t * BBM;
-                row_end = hi;
-                break;
-            }
-            t -= nt;
-        }
-        if (m0 < 0) return;   // unreachable: bm < mt
-        qw += (int64_t)e * N * K;
-        sw += (int64_t)e * N * G;
-    } else {
-        m0 = bm * BBM;
-        row_end = M;
-    }
-    const int mrows = min(BBM, row_end - m0), ncols = min(BBN, N - n0);
-    // a wave whose 64 rows all lie past the tile's last row has nothing to
-    // multiply (short expert segments); it still stages tiles and meets the barriers
-    const bool active = wm * 64 < mrows;
-
-    const v4i ra = make_rsrc_words(q + (int64_t)m0 * K, (uint32_t)(mrows * K));
-    const v4i rb = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(ncols * K));
-    // no scales in the partials form (sw may be null): an empty descriptor
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(OUT == OUT_PARTIALS || CHN ? nullptr : sw + (int64_t)n0 * G,
-                  OUT == OUT_PARTIALS || CHN ? 0u : (uint32_t)(ncols * G * 4));
-
-    // Staging goes straight from global memory to LDS (buffer loads with the
-    // LDS-destination bit): each wave instruction fills one 1 KB block of the
-    // tile, lane l landing at byte 16*l of the block. Wave w fills blocks
-    // w*4 .. w*4+3 of the A tile and of the B tile (8 rows of 128 B each); a
-    // lane fetches the global chunk that the swizzle puts at its position.
-    // Rows 16 apart share the swizzle, so blocks i and i+2 differ by the
-    // uniform 16*K, which travels in the scalar offset.
-    const int drow = wave * 32 + (lane >> 3);            // + 8*i for block i
-    const int dpos = lane & 7;
-    uint32_t dvoff[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = drow + 8 * i;
-        dvoff[i] = (uint32_t)(row * K + ((dpos ^ ((row >> 1) & 7)) << 4));
-    }
-    // threads < 256 stage one scale each; the others read zero and write a
-    // spare slot, so neither the load nor the store is behind a branch
-    const uint32_t svoff = tid < BBN ? (uint32_t)(tid * G * 4) : kOOB;
-    const int sslot = tid < BBN ? (tid >> 7) * 128 + (tid & 31) * 4 + ((tid >> 5) & 3) : tid;
-    auto sgo = [&](int g) { return g < G ? (uint32_t)g * kGroup : kOOB; };
-
-    auto dma_group = [&](int buf, int g) {
-        const uint32_t so = sgo(g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t blk = __builtin_amdgcn_readfirstlane(
-                (uint32_t)(uintptr_t)(smem[buf] + (wave * 4 + i) * 1024));
-            const uint32_t s2 = g < G ? so + (uint32_t)((i >> 1) * 16 * K) : kOOB;
-            buf_load16_lds(ra, blk, dvoff[i & 1], s2);
-            buf_load16_lds(rb, blk + BBM * kGroup, dvoff[i & 1], s2);
-        }
-    };
-    float sreg = 0.0f;
-    auto load_scale = [&](int g) {
-        sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-            rs, (int)svoff, (int)(g < G ? (uint32_t)g * 4 : kOOB), 0));
-    };
-    auto store_scale = [&](int buf) {
-        // column t -> [wn][l32][j] so each lane reads its four block scales at once
-        sws[buf][sslot] = sreg;
-    };
-
-    v16f facc[2][4];
-    v16i pacc[2][4];   // per-channel form: the INT32 totals so far
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                facc[i][j][r] = 0.0f;
-                pacc[i][j][r] = 0;
-            }
-
-    auto frag = [&](const int8_t *tile, int row, int c) {
-        return *reinterpret_cast<const v4i *>(tile + row * kGroup + ((c ^ ((row >> 1) & 7)) << 4));
-    };
-
-    // Software pipeline over the 8 block units u = 2*j + i of a K group
-    // (column block j, row block i): the four MFMAs of unit u are interleaved
-    // with the epilogue of unit u-1 (its INT32 partials converted and FMA'd
-    // into the float accumulators), so the matrix core and the VALU work side
-    // by side; B fragments of column block j+1 are read from LDS while
-    // column block j is multiplied. The last unit's epilogue is deferred into
-    // the next group, behind that group's first fragment reads.
-    v16i acc[2];
-    v4i a[2][4], b[2][4];
-    float sc_last = 0.0f;          // scale of the deferred unit (column block 3)
-    int g_last = 0;
-
-    auto epilogue = [&](const v16i &p, int i, int j, float scale, int g) {
-        if (OUT == OUT_PARTIALS) {
-            const int n = n0 + wn * 128 + j * 32 + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (m < M && n < N)
-                    reinterpret_cast<int32_t *>(y)[((int64_t)m * N + n) * G + g] = p[r];
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                facc[i][j][r] = __builtin_fmaf((float)p[r], scale, facc[i][j][r]);
-        }
-    };
-
-    auto group = [&](int buf, int g, bool has_prev) {
-        const int8_t *As = smem[buf];
-        const int8_t *Bs = smem[buf] + BBM * kGroup;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) a[i][t] = frag(As, wm * 64 + i * 32 + l32, half * 4 + t);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[0][t] = frag(Bs, wn * 128 + l32, half * 4 + t);
-        const float *scl = &sws[buf][wn * 128 + l32 * 4];   // [j] = scale of column block j
-        float sc_prev = 0.0f, sc_cur = scl[0];
-        if (!CHN && has_prev) epilogue(acc[1], 1, 3, sc_last, g_last);   // unit 7 of the previous group
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = u >> 1, i = u & 1, cur = j & 1;
-            if (i == 0 && j < 3) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    b[cur ^ 1][t] = frag(Bs, wn * 128 + (j + 1) * 32 + l32, half * 4 + t);
-            }
-            if (i == 0 && j > 0) {
-                sc_prev = sc_cur;
-                sc_cur = scl[j];
-            }
-            v16i c = CHN ? pacc[i][j] : v16i{};
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][t], b[cur][t], c, 0, 0, 0);
-            if (CHN) {
-                pacc[i][j] = c;
-            } else if (u > 0) {
-                const int pj = (u - 1) >> 1, pi = (u - 1) & 1;
-                epilogue(acc[(u - 1) & 1], pi, pj, pj == j ? sc_cur : sc_prev, g);
-            }
-            acc[u & 1] = c;
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        sc_last = sc_cur;
-        g_last = g;
-    };
-
-    // prologue: group 0 into buffer 0
-    dma_group(0, 0);
-    if (!CHN) {
-        load_scale(0);
-        store_scale(0);
-    }
-    wait_vmem();
-    __syncthreads();
-
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        dma_group(buf ^ 1, g + 1);     // zeros past the end; lands while group g is multiplied
-        if (!CHN) load_scale(g + 1);
-        if (!GROUPED || active) group(buf, g, g > 0);
-        if (!CHN) store_scale(buf ^ 1);
-        wait_vmem();                   // the next group's tiles are in LDS ...
-        __syncthreads();               // ... for every wave: swap buffers
-    }
-    if (!CHN && (!GROUPED || active)) epilogue(acc[1], 1, 3, sc_last, g_last);
-
-    if (CHN) {
-        float swn[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + wn * 128 + j * 32 + l32;
-            swn[j] = n < N ? sw[(int64_t)n * sw_stride] : 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (m >= row_end) continue;
-                const float s = sa[m];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n = n0 + wn * 128 + j * 32 + l32;
-                    if (n < N)
-                        store_out<OUT>(y, (int64_t)m * N + n, channel_value(pacc[i][j][r], swn[j], s));
-                }
-            }
-    } else if (OUT != OUT_PARTIALS) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (m >= row_end) continue;
-                const float s = sa[m];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n = n0 + wn * 128 + j * 32 + l32;
-                    if (n < N) store_out<OUT>(y, (int64_t)m * N + n, facc[i][j][r] * s);
-                }
-            }
-    }
-}
-
-// Grouped: sum over experts of ceil(rows_e / 256) <= ceil(R / 256) + E tile rows.
-template <int OUT, bool GROUPED>
-hipError_t launch_big(const int8_t *q, const float *sa, const int8_t *qw, const float *sw, int M,
-                      int N, int K, void *y, const int32_t *offsets, int E, hipStream_t stream,
-                      int sw_stride = 1) {
-    const int64_t mt = (M + BBM - 1) / BBM + (GROUPED ? E : 0), nt = (N + BBN - 1) / BBN;
-    const int64_t total = mt * nt;
-    if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const BigTiles t{(int)mt, (int)nt};
-    gemm_big_kernel<OUT, GROUPED>
-        <<<dim3((unsigned)total), 512, 0, stream>>>(q, sa, qw, sw, M, N, K, y, t, offsets, E,
-                                                          sw_stride);
-    return hipGetLastError();
-}
-
 template <int OUT, bool GROUPED>
 hipError_t launch_tile(const TileArgs &a, int64_t row_tiles, hipStream_t stream) {
     const int64_t n_tiles = (a.N + TBN - 1) / TBN;
@@ -1211,10 +855,7 @@ hipError_t launch_smallm(const int8_t *q, const float *sa, const int8_t *qw, con
                                            sw_stride);
 }
 
-#ifndef BSB_BIG_MIN_M
-#define BSB_BIG_MIN_M 512
-#endif
-constexpr int kBigMinM = BSB_BIG_MIN_M;   // rows from which the 256x256 kernel is used
+constexpr int kBigMinM = 512;   // rows from which the 256x256 kernel is used
 
 template <int OUT>
 hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
@@ -1226,9 +867,9 @@ hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, cons
     // The 256x256 kernel (which addresses its operand panels with 32-bit
     // buffer offsets) when it has at least one tile per CU; below that the
     // 128x128 kernel's four times as many tiles finish sooner.
-    const int64_t big_tiles = (int64_t)((M + BBM - 1) / BBM) * ((N + BBN - 1) / BBN);
-    if (M >= kBigMinM && (int64_t)256 * K < ((int64_t)1 << 31) && big_tiles >= kCUs)
-        return launch_big<OUT, false>(q, sa, qw, sw, M, N, K, y, nullptr, 0, stream, sw_stride);
+    const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+    if (M >= kBigMinM && big_gemm_fits(K) && big_tiles >= kCUs)
+        return launch_gemm_big(q, sa, qw, sw, M, N, K, y, OUT, nullptr, 0, sw_stride, stream);
     TileArgs a{q, sa, qw, sw, nullptr, y, M, N, K, 0, sw_stride};
     return launch_tile<OUT, false>(a, (M + TBM - 1) / TBM, stream);
 }
@@ -1292,14 +933,10 @@ hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *q
     // Rows per expert are known only on the device; the mean decides. With
     // at least 128 rows per expert on average, and enough rows for a tile per
     // CU, the 256x256 kernel is used.
-    const int64_t big_tiles = ((R + BBM - 1) / BBM) * ((N + BBN - 1) / BBN);
-    if (R >= 128 * E && big_tiles >= kCUs && (int64_t)256 * K < ((int64_t)1 << 31)) {
-        if (out == OUT_BF16)
-            return launch_big<OUT_BF16, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y, offsets,
-                                              (int)E, stream);
-        return launch_big<OUT_FP32, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y, offsets,
-                                          (int)E, stream);
-    }
+    const int64_t big_tiles = ((R + 255) / 256) * ((N + 255) / 256);
+    if (R >= 128 * E && big_tiles >= kCUs && big_gemm_fits(K))
+        return launch_gemm_big(q, sa, qw, sw, (int)R, (int)N, (int)K, y, out, offsets, (int)E, 1,
+                               stream);
     // At most 32 rows per expert on average (decode-shaped MoE): stream each
     // expert's weights once per 32 of its rows.
     if (R <= 32 * E && E <= 65535 && (int64_t)128 * K < ((int64_t)1 << 31)) {

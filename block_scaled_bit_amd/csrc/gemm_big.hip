@@ -1,0 +1,472 @@
+// W8A8 per-group-128 GEMM for prefill-shaped M (and the grouped MoE form with
+// many rows per expert) on gfx950: 256x256 output tile per workgroup.
+//
+// [P3] sec. 3.1: INT8 x INT8 multiply-accumulate into INT32 inside the
+// matmul, the FP32 scales applied last. Per output element:
+//     acc = 0
+//     for g = 0 .. K/128-1:                  (ascending, never split)
+//         P   = sum_{k in group g} q[m,k]*qw[n,k]        (INT32, MFMA)
+//         acc = fmaf((float)P, sw[n,g], acc)             (VALU epilogue)
+//     y = acc * sa[m]  -> BF16 (RNE) or FP32
+//
+// Workgroup: 8 waves in a 4 (M) x 2 (N) grid, two per SIMD, each owning
+// 64 x 128 outputs = 2 x 4 blocks of v_mfma_i32_32x32x32_i8. Per K group a
+// block takes four MFMAs (32 K each) into a fresh INT32 accumulator, then 16
+// conversions and 16 fused multiply-adds fold it into the float32 totals.
+// Those 32 VALU instructions take as long as the block's four MFMAs, so the
+// kernel is built to keep both units issuing side by side: every MFMA is
+// followed by a quarter of the previous block's epilogue (8 VALU
+// instructions), and nothing else runs on the VALU inside the main loop. LDS
+// fragment addresses are fixed per lane and differ between stages, blocks
+// and K steps only by constants, so every fragment read is one ds_read_b128
+// with an immediate offset.
+//
+// Staging: per K group the A tile (256 rows x 128 B) and the B tile (256
+// weight rows x 128 B) go from global memory straight into LDS (buffer loads
+// with the LDS-destination bit, 1 KB per wave instruction, 8 lanes per
+// 128-byte row line, 16-byte chunk j of row r at j ^ ((r >> 1) & 7)), with the
+// group's 256 weight scales beside them, in two stages (128 KB + 4 KB).
+// One barrier per group, placed before the last column block: at that point
+// every wave holds the fragments it still needs of group g in registers, so
+// the barrier (a) publishes group g+1, whose fragments are then read while
+// the last column block of g is multiplied (each A fragment right after its
+// last use, each B fragment after its last use in that block), and (b) frees
+// group g's stage, into which group g+2 is loaded at once: the loads have
+// about one group of work to land. The last block's epilogue moves into the
+// next group, behind its first MFMA.
+//
+// Out-of-range rows, columns and groups read zero through the buffer
+// descriptors (a zero group adds fmaf(0, 0, acc) = acc), so no load sits
+// behind a branch; stores are masked by the real extents.
+#include <type_traits>
+
+#include "gemm_common.h"
+#include "launch.h"
+
+namespace bsb {
+
+namespace {
+
+constexpr int kBigTM = 256, kBigTN = 256;        // output tile per workgroup
+constexpr int kBigStage = 256 * kGroup;          // one operand tile of one K group (bytes)
+constexpr int kBigLdsA = 0;                      // A tiles of stages 0, 1
+constexpr int kBigLdsB = 2 * kBigStage;          // B tiles of stages 0, 1
+constexpr int kBigLdsS = 4 * kBigStage;          // scales of stages 0, 1
+constexpr int kBigScaleStage = 512 * 4;          // 256 scales + 256 slots for the spare loads
+constexpr int kBigLds = kBigLdsS + 2 * kBigScaleStage;   // 135168 bytes of 160 KB
+
+struct BigTiles {
+    int mt, nt;   // tile rows / columns
+};
+
+// Workgroup -> tile. The dispatcher deals workgroups to the 8 XCDs round
+// robin; the remap gives each XCD a contiguous run of tiles, walked in groups
+// of 4 tile rows (dense: the 4 A panels and the B panels of a run stay in
+// that XCD's L2) or down whole tile columns (grouped: the row tiles of one
+// expert share its weight panel).
+template <bool COLUMN_MAJOR>
+__device__ __forceinline__ void big_tile_of(int b, BigTiles t, int &bm, int &bn) {
+    const int num = t.mt * t.nt;
+    const int x = b & 7, per = num >> 3, rem = num & 7;
+    const int start = x * per + (x < rem ? x : rem);
+    const int tid = start + (b >> 3);                       // bijection onto [0, num)
+    if (COLUMN_MAJOR) {
+        bm = tid % t.mt;
+        bn = tid / t.mt;
+        return;
+    }
+    constexpr int GM = 4;
+    const int grp = tid / (GM * t.nt);
+    const int first = grp * GM;
+    const int gsz = min(t.mt - first, GM);
+    const int in = tid - grp * GM * t.nt;
+    bm = first + in % gsz;
+    bn = in / gsz;
+}
+
+__device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
+
+// GROUPED: q holds R = M rows sorted by expert, rows [offsets[e], offsets[e+1])
+// multiply expert e's weights qw[e] / sw[e]; tile rows are laid out expert
+// after expert (a tile never spans two experts) and the host sizes the grid
+// for the most tiles any split of R rows over E experts can need.
+template <int OUT, bool GROUPED>
+__global__ void __launch_bounds__(512, 1)
+gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float *sw, int M, int N,
+                int K, void *y, BigTiles tiles, const int32_t *offsets, int E, int sw_stride) {
+    constexpr bool CHN = per_channel<OUT>();             // one scale per row, applied at the end
+    constexpr bool SCALES = !CHN && OUT != OUT_PARTIALS;   // per-group scales staged in LDS
+    __shared__ __align__(16) int8_t lds[kBigLds];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int G = K >> 7;
+    auto seg = [&](int e, int &lo, int &hi) {   // expert e's rows, clamped to [0, R]
+        lo = offsets[e];
+        hi = offsets[e + 1];
+        lo = lo < 0 ? 0 : (lo > M ? M : lo);
+        hi = hi < lo ? lo : (hi > M ? M : hi);
+    };
+    if (GROUPED) {
+        // The tiles that exist are known only here: count them and let the
+        // first mt*nt workgroups take them (the dispatcher deals workgroups
+        // round-robin to the XCDs, so the idle surplus spreads evenly).
+        // (Offsets that overlap, which the contract excludes, could count more
+        // than the host bound; the count is capped at it, so every tile stays
+        // inside [0, R).)
+        int64_t mt = 0;
+        for (int e = 0; e < E; ++e) {
+            int lo, hi;
+            seg(e, lo, hi);
+            mt += (hi - lo + kBigTM - 1) / kBigTM;
+        }
+        mt = mt < tiles.mt ? mt : tiles.mt;
+        if ((int64_t)blockIdx.x >= mt * tiles.nt) return;   // whole workgroup
+        tiles.mt = (int)mt;
+    }
+    int bm, bn;
+    big_tile_of<GROUPED>(blockIdx.x, tiles, bm, bn);
+    const int n0 = bn * kBigTN;
+    int m0, row_end;
+    if (GROUPED) {
+        // tile row bm -> (expert, 256-row block)
+        int t = bm, e = 0;
+        m0 = -1;
+        row_end = 0;
+        for (; e < E; ++e) {
+            int lo, hi;
+            seg(e, lo, hi);
+            const int nt = (hi - lo + kBigTM - 1) / kBigTM;
+            if (t < nt) {
+                m0 = lo + t * kBigTM;
+                row_end = hi;
+                break;
+            }
+            t -= nt;
+        }
+        if (m0 < 0) return;   // unreachable: bm < mt
+        qw += (int64_t)e * N * K;
+        sw += (int64_t)e * N * G;
+    } else {
+        m0 = bm * kBigTM;
+        row_end = M;
+    }
+    const int mrows = min(kBigTM, row_end - m0), ncols = min(kBigTN, N - n0);
+
+    const v4i ra = make_rsrc_words(q + (int64_t)m0 * K, (uint32_t)(mrows * K));
+    const v4i rb = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(ncols * K));
+    const v4i rs = make_rsrc_words(SCALES ? sw + (int64_t)n0 * G : nullptr,
+                                   SCALES ? (uint32_t)(ncols * G * 4) : 0u);
+
+    // ---- staging (global -> LDS) ----
+    // Wave w fills 1 KB blocks 4w .. 4w+3 of each tile (8 rows of 128 B each);
+    // lane l lands at byte 16*l of a block and fetches the global chunk that
+    // the swizzle puts there. Blocks i and i+2 are 16 rows apart, which share
+    // the swizzle, so they differ by the uniform 16*K in the scalar offset.
+    uint32_t dvoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = wave * 32 + 8 * i + (lane >> 3);
+        dvoff[i] = (uint32_t)(row * K + (((lane & 7) ^ big_swz(row)) << 4));
+    }
+    // Scales: waves 0-3 load the group's 256 scales, one per lane, into the
+    // order [wn][l32][cb] (column n = 128 wn + 32 cb + l32), so that each lane
+    // later reads its four column blocks' scales in one 16-byte read; waves
+    // 4-7 issue the same load past the end into spare slots, which keeps every
+    // wave's load count per group equal (9).
+    const int sp = wave * 64 + lane;
+    const uint32_t svoff =
+        wave < 4 ? (uint32_t)((((sp >> 7) << 7) + ((sp & 3) << 5) + ((sp >> 2) & 31)) * G * 4) : 0u;
+    const uint32_t lbase = (uint32_t)(uintptr_t)lds;
+
+    auto dma = [&](int st, int g) {
+        const bool in = g < G;
+        const uint32_t so0 = in ? (uint32_t)g * kGroup : kOOB;
+        const uint32_t so1 = in ? so0 + (uint32_t)(16 * K) : kOOB;
+        const uint32_t sso = (in && wave < 4) ? (uint32_t)g * 4 : kOOB;
+        const uint32_t ma = lbase + kBigLdsA + st * kBigStage + wave * 4096;
+        const uint32_t mb = lbase + kBigLdsB + st * kBigStage + wave * 4096;
+        const uint32_t ms = lbase + kBigLdsS + st * kBigScaleStage + wave * 256;
+        uint32_t m0_out;   // M0 is written inside: declared as an output
+        // One statement, so nothing the compiler emits lands between the loads.
+        // s_nop 4: a VALU write of an SGPR read by a vector memory instruction
+        // needs five wait states (the compiler may form the descriptors or
+        // offsets with v_readfirstlane right before); s_nop 0 after each M0
+        // write: one wait state before an LDS-destination load reads M0.
+        asm volatile(
+            "s_nop 4\n\t"
+            "s_mov_b32 m0, %[a0]\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %[v0], %[ra], %[s0] offen lds\n\t"
+            "s_mov_b32 m0, %[a1]\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %[v1], %[ra], %[s0] offen lds\n\t"
+            "s_mov_b32 m0, %[a2]\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %[v0], %[ra], %[s1] offen lds\n\t"
+            "s_mov_b32 m0, %[a3]\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %[v1], %[ra], %[s1] offen lds\n\t"
+            "s_mov_b32 m0, %[b0]\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %[v0], %[rb], %[s0] offen lds\n\t"
+            "s_mov_b32 m0, %[b1]\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %[v1], %[rb], %[s0] offen lds\n\t"
+            "s_mov_b32 m0, %[b2]\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %[v0], %[rb], %[s1] offen lds\n\t"
+            "s_mov_b32 m0, %[b3]\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %[v1], %[rb], %[s1] offen lds\n\t"
+            "s_mov_b32 m0, %[c0]\n\ts_nop 0\n\t"
+            "buffer_load_dword %[vs], %[rs], %[ss] offen lds"
+            : "=&{m0}"(m0_out)
+            : [a0] "s"(ma), [a1] "s"(ma + 1024), [a2] "s"(ma + 2048), [a3] "s"(ma + 3072),
+              [b0] "s"(mb), [b1] "s"(mb + 1024), [b2] "s"(mb + 2048), [b3] "s"(mb + 3072),
+              [c0] "s"(ms), [v0] "v"(dvoff[0]), [v1] "v"(dvoff[1]), [vs] "v"(svoff),
+              [ra] "s"(ra), [rb] "s"(rb), [rs] "s"(rs), [s0] "s"(so0), [s1] "s"(so1),
+              [ss] "s"(sso)
+            : "memory");
+        (void)m0_out;
+    };
+
+    // ---- fragment reads (LDS -> registers) ----
+    // A fragment (row block rb, K step ks) of lane l: 16 bytes of row
+    // 64 wm + 32 rb + l32 at K bytes 32 ks + 16 half; B likewise for weight row
+    // 128 wn + 32 cb + l32. Rows 32 apart share the swizzle, so stage, block
+    // and K-step offsets beyond the per-(ks) lane base are constants.
+    uint32_t fa[4], fb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int r_a = wm * 64 + l32, r_b = wn * 128 + l32;
+        fa[ks] = kBigLdsA + r_a * kGroup + (((2 * ks + half) ^ big_swz(r_a)) << 4);
+        fb[ks] = kBigLdsB + r_b * kGroup + (((2 * ks + half) ^ big_swz(r_b)) << 4);
+    }
+    const uint32_t fs = kBigLdsS + (wn * 128 + l32 * 4) * 4;
+    auto ldA = [&](int st, int rb_, int ks) {
+        return *reinterpret_cast<const v4i *>(lds + fa[ks] + st * kBigStage + rb_ * 4096);
+    };
+    auto ldB = [&](int st, int cb, int ks) {
+        return *reinterpret_cast<const v4i *>(lds + fb[ks] + st * kBigStage + cb * 4096);
+    };
+    auto ldS = [&](int st) {
+        return *reinterpret_cast<const v4f *>(lds + fs + st * kBigScaleStage);
+    };
+
+    const bool active = wm * 64 < mrows;   // rows of this wave exist in the tile
+
+    v16f facc[2][4];   // float32 totals (per-group forms)
+    v16i pacc[2][4];   // INT32 totals (per-channel forms)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                facc[i][j][r] = 0.0f;
+                pacc[i][j][r] = 0;
+            }
+
+    // prologue: groups 0 and 1 into stages 0 and 1; wait for group 0
+    dma(0, 0);
+    dma(1, 1);
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    __syncthreads();
+
+    if (active) {
+        v4i a[2][4], b[4];
+        v4f sc = ldS(0), scn;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) a[i][ks] = ldA(0, i, ks);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) b[ks] = ldB(0, 0, ks);
+        v16i prev;         // INT32 partials of the block whose epilogue is pending
+        float prev_s = 0;  // its weight scale (0 with zero partials before the first group)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) prev[r] = 0;
+
+        // Epilogue quarter qt of the pending block (row block pi, column block pj).
+        auto epi = [&](int pi, int pj, int qt, int g) {
+            if (OUT == OUT_PARTIALS) {
+                if (g < 0) return;
+                const int n = n0 + wn * 128 + pj * 32 + l32;
+#pragma unroll
+                for (int r = 4 * qt; r < 4 * qt + 4; ++r) {
+                    const int m = m0 + wm * 64 + pi * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (m < row_end && n < N)
+                        reinterpret_cast<int32_t *>(y)[((int64_t)m * N + n) * G + g] = prev[r];
+                }
+            } else if (SCALES) {
+#pragma unroll
+                for (int r = 4 * qt; r < 4 * qt + 4; ++r)
+                    facc[pi][pj][r] = __builtin_fmaf((float)prev[r], prev_s, facc[pi][pj][r]);
+            }
+        };
+
+        // One K group on stage st (group g): column blocks cb = 0..3, row
+        // blocks rb = 0..1, four MFMAs each.
+        auto step = [&](auto stc, int g) {
+            constexpr int st = decltype(stc)::value;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+                for (int rb_ = 0; rb_ < 2; ++rb_) {
+                    const int j = 2 * cb + rb_;   // block unit; its predecessor's epilogue runs beside it
+                    const int pi = j == 0 ? 1 : (j - 1) & 1, pj = j == 0 ? 3 : (j - 1) >> 1;
+                    v16i c;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) c[r] = CHN ? pacc[rb_][cb][r] : 0;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rb_][ks], b[ks], c, 0, 0, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (cb == 3) {   // fragments of group g+1 after their last use in g
+                            a[rb_][ks] = ldA(st ^ 1, rb_, ks);
+                            if (rb_ == 1) {
+                                b[ks] = ldB(st ^ 1, 0, ks);
+                                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                            } else {
+                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                            }
+                        } else if (rb_ == 1) {   // next column block of this group
+                            b[ks] = ldB(st, cb + 1, ks);
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        }
+                        epi(pi, pj, ks, j == 0 ? g - 1 : g);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                    }
+                    if (CHN) pacc[rb_][cb] = c;
+                    prev = c;
+                    prev_s = sc[cb];
+                }
+                if (cb == 2) {
+                    // every wave holds group g's remaining fragments: publish
+                    // g+1, free this stage, load g+2 into it
+                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                    __syncthreads();
+                    dma(st, g + 2);
+                    scn = ldS(st ^ 1);
+                }
+            }
+            sc = scn;
+        };
+
+        int g = 0;
+        for (; g + 1 < G; g += 2) {
+            step(std::integral_constant<int, 0>{}, g);
+            step(std::integral_constant<int, 1>{}, g + 1);
+        }
+        if (g < G) step(std::integral_constant<int, 0>{}, g);
+        epi(1, 3, 0, G - 1);
+        epi(1, 3, 1, G - 1);
+        epi(1, 3, 2, G - 1);
+        epi(1, 3, 3, G - 1);
+    } else {
+        // rows past the tile's end: stage this wave's share and meet every barrier
+        int g = 0;
+        for (; g + 1 < G; g += 2) {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+            dma(0, g + 2);
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+            dma(1, g + 3);
+        }
+        if (g < G) {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+            dma(0, g + 2);
+        }
+    }
+    // loads past the last group still write (zeros) into LDS: let them land
+    // before the workgroup's LDS can be handed to another one
+    wait_vmem();
+    if (!active) return;
+
+    if (CHN) {
+        float swn[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wn * 128 + j * 32 + l32;
+            swn[j] = n < N ? sw[(int64_t)n * sw_stride] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (m >= row_end) continue;
+                const float s = sa[m];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = n0 + wn * 128 + j * 32 + l32;
+                    if (n < N)
+                        store_out<OUT>(y, (int64_t)m * N + n, channel_value(pacc[i][j][r], swn[j], s));
+                }
+            }
+    } else if (OUT != OUT_PARTIALS) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (m >= row_end) continue;
+                const float s = sa[m];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = n0 + wn * 128 + j * 32 + l32;
+                    if (n < N) store_out<OUT>(y, (int64_t)m * N + n, facc[i][j][r] * s);
+                }
+            }
+    }
+}
+
+template <int OUT, bool GROUPED>
+hipError_t launch_big_t(const int8_t *q, const float *sa, const int8_t *qw, const float *sw, int M,
+                        int N, int K, void *y, const int32_t *offsets, int E, int sw_stride,
+                        hipStream_t stream) {
+    // Grouped: sum over experts of ceil(rows_e / 256) <= ceil(R / 256) + E tile rows.
+    const int64_t mt = (M + kBigTM - 1) / kBigTM + (GROUPED ? E : 0), nt = (N + kBigTN - 1) / kBigTN;
+    const int64_t total = mt * nt;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const BigTiles t{(int)mt, (int)nt};
+    gemm_big_kernel<OUT, GROUPED><<<dim3((unsigned)total), 512, 0, stream>>>(
+        q, sa, qw, sw, M, N, K, y, t, offsets, E, sw_stride);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool big_gemm_fits(int64_t K) {
+    // 32-bit buffer offsets: a lane's row of a 256-row panel plus 16 rows and a group
+    return (int64_t)(kBigTM + 16) * K + kGroup < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_big(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
+                           int M, int N, int K, void *y, int out, const int32_t *offsets, int E,
+                           int sw_stride, hipStream_t stream) {
+    if (offsets) {
+        switch (out) {
+            case OUT_BF16:
+                return launch_big_t<OUT_BF16, true>(q, sa, qw, sw, M, N, K, y, offsets, E, 1, stream);
+            case OUT_FP32:
+                return launch_big_t<OUT_FP32, true>(q, sa, qw, sw, M, N, K, y, offsets, E, 1, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (out) {
+        case OUT_BF16:
+            return launch_big_t<OUT_BF16, false>(q, sa, qw, sw, M, N, K, y, nullptr, 0, 1, stream);
+        case OUT_FP32:
+            return launch_big_t<OUT_FP32, false>(q, sa, qw, sw, M, N, K, y, nullptr, 0, 1, stream);
+        case OUT_PARTIALS:
+            return launch_big_t<OUT_PARTIALS, false>(q, sa, qw, sw, M, N, K, y, nullptr, 0, 1,
+                                                     stream);
+        case OUT_BF16_CH:
+            return launch_big_t<OUT_BF16_CH, false>(q, sa, qw, sw, M, N, K, y, nullptr, 0,
+                                                    sw_stride, stream);
+        case OUT_FP32_CH:
+            return launch_big_t<OUT_FP32_CH, false>(q, sa, qw, sw, M, N, K, y, nullptr, 0,
+                                                    sw_stride, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace bsb

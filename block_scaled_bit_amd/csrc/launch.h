@@ -27,6 +27,13 @@ hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw,
                        const float *sw, int64_t M, int64_t N, int64_t K, void *y,
                        int out, hipStream_t stream);
 
+// gemm_big.hip: 256x256 tiles for prefill-shaped M. out as gemm_common.h's
+// OUT_* forms; offsets non-null selects the grouped form (BF16 / FP32 only).
+bool big_gemm_fits(int64_t K);
+hipError_t launch_gemm_big(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
+                           int M, int N, int K, void *y, int out, const int32_t *offsets, int E,
+                           int sw_stride, hipStream_t stream);
+
 // gemm_packed.hip: weights in the matrix cores' operand order (M <= 64)
 hipError_t launch_repack_mfma(const int8_t *qw, int64_t N, int64_t K, int8_t *packed,
                               hipStream_t stream);
