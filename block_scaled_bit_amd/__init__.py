@@ -11,6 +11,7 @@ from ._lib import (quantize_act, gemm_w8a8_g128, gemm_w8a8_g128_partials,  # noq
                    gemm_w8a8_channel, gemm_w8a16_g128, gemm_bf16, dequant_fp8_block_bf16,
                    grouped_gemm_w8a8_g128, decode_fp8_block, decode_mxfp4, gather_rows,
                    moe_combine, kv_cache_empty, kv_cache_write, attention_workspace_bytes,
-                   attention_decode_int8kv, kv_cache_empty_bf16, kv_cache_write_bf16,
+                   attention_decode_int8kv, attention_decode_int8kv_noalloc,
+                   kv_cache_empty_bf16, kv_cache_write_bf16,
                    attention_decode_bf16kv, BsbError,
                    BSB_OUT_BF16, BSB_OUT_FP32, BSB_FP8_OCP, BSB_FP8_FNUZ, lib, LIB_PATH)

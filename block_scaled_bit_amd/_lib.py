@@ -50,6 +50,8 @@ _SIGNATURES = {
                            _c_p, _c_p, _c_p, _c_p],
     "bsb_attention_decode_int8kv": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
                                     _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_int, _c_p],
+    "bsb_attention_decode_int8kv_noalloc": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64,
+                                            _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
     "bsb_kv_cache_write_bf16": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                 _c_p, _c_p, _c_p],
     "bsb_attention_decode_bf16kv": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
@@ -528,6 +530,32 @@ def attention_workspace_bytes(B: int, Hq: int, max_len: int) -> int:
     if n < 0:
         raise ValueError("invalid attention sizes")
     return n
+
+
+ATTENTION_NOALLOC_MAX_BYTES = 32 << 20   # BSB_ATTENTION_NOALLOC_MAX_BYTES
+
+
+def attention_decode_int8kv_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
+                                    k_scale: torch.Tensor, v_cache: torch.Tensor,
+                                    v_scale: torch.Tensor, lens: torch.Tensor, max_len: int,
+                                    out: torch.Tensor) -> torch.Tensor:
+    """attention_decode_int8kv with the library's static per-device workspace instead of a
+    caller's (bsb_attention_decode_int8kv_noalloc): allocates nothing, so `out` [B, Hq, 128]
+    (BF16 or float32) is required. Calls that overlap on one device race."""
+    B, Hkv, T, dev = _kv_shapes(k_cache, k_scale, v_cache, v_scale)
+    _need(q, "q", _BF16_BITS, None, dev)
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != KV_HEAD_DIM:
+        raise ValueError("q must be [B, Hq, 128]")
+    Hq = q.shape[1]
+    _need(lens, "lens", (torch.int32,), (B,), dev)
+    code = _out_code(out.dtype)
+    _need(out, "out", (out.dtype,), (B, Hq, KV_HEAD_DIM), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_attention_decode_int8kv_noalloc(
+            _ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(lens),
+            B, Hq, Hkv, T, KV_HEAD_DIM, max_len, _ptr(out), code, _stream(dev)),
+            "bsb_attention_decode_int8kv_noalloc")
+    return out
 
 
 def attention_decode_int8kv(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor,

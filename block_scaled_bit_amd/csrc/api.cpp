@@ -10,6 +10,9 @@
 #include "../../include/bsb.h"
 #include "launch.h"
 
+static_assert(BSB_ATTENTION_NOALLOC_MAX_BYTES == bsb::kNoAllocScratchBytes,
+              "the header's limit is the size of the static workspace");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -367,20 +370,30 @@ int64_t bsb_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t max_len) {
 
 namespace {
 
-// Checks shared by the two attention entry points (caches checked by the caller).
-bsb_status attention_checks(const uint16_t *q, const int32_t *lens, int64_t B, int64_t Hq,
-                            int64_t Hkv, int64_t T, int64_t D, int64_t max_len, const float *work,
-                            int64_t work_bytes, const void *out, bsb_out_dtype out_dtype) noexcept {
+// Shape, dtype and pointer checks shared by the attention entry points
+// (caches checked by the caller, the workspace by attention_checks).
+bsb_status attention_shape_checks(const uint16_t *q, const int32_t *lens, int64_t B, int64_t Hq,
+                                  int64_t Hkv, int64_t T, int64_t D, int64_t max_len,
+                                  const void *out, bsb_out_dtype out_dtype) noexcept {
     if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || Hq / Hkv > 16 || B * Hkv > 65535 ||
         B * Hq >= ((int64_t)1 << 31) || D != kKvHeadDim || T < 64 || T % 64 ||
         T >= kMaxKvSlots || max_len < 0 || max_len > T || !prod_le(B, Hkv, T, kMaxElems))
         return BSB_ERR_INVALID_ARG;
     if (out_dtype != BSB_OUT_BF16 && out_dtype != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
+    if (!q || !lens || !out) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(lens) || !aligned16(out)) return BSB_ERR_MISALIGNED;
+    return BSB_OK;
+}
+
+bsb_status attention_checks(const uint16_t *q, const int32_t *lens, int64_t B, int64_t Hq,
+                            int64_t Hkv, int64_t T, int64_t D, int64_t max_len, const float *work,
+                            int64_t work_bytes, const void *out, bsb_out_dtype out_dtype) noexcept {
+    if (bsb_status s = attention_shape_checks(q, lens, B, Hq, Hkv, T, D, max_len, out, out_dtype))
+        return s;
     const int64_t need = bsb_attention_workspace_bytes(B, Hq, max_len);
     if (need < 0 || work_bytes < need) return BSB_ERR_INVALID_ARG;
-    if (!q || !lens || !out || (need > 0 && !work)) return BSB_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(lens) || !aligned16(out) || (work && !aligned16(work)))
-        return BSB_ERR_MISALIGNED;
+    if (need > 0 && !work) return BSB_ERR_INVALID_ARG;
+    if (work && !aligned16(work)) return BSB_ERR_MISALIGNED;
     return BSB_OK;
 }
 
@@ -406,6 +419,27 @@ bsb_status bsb_attention_decode_int8kv(const uint16_t *q_bf16, const int8_t *k_c
                                                (int)B, (int)Hq, (int)Hkv, (int)T, (int)max_len,
                                                work, out, out_dtype == BSB_OUT_BF16 ? 1 : 0,
                                                as_stream(stream)));
+}
+
+bsb_status bsb_attention_decode_int8kv_noalloc(const uint16_t *q_bf16, const int8_t *k_cache,
+                                               const float *k_scale, const int8_t *v_cache,
+                                               const float *v_scale, const int32_t *lens,
+                                               int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                                               int64_t D, int64_t max_len, void *out,
+                                               bsb_out_dtype out_dtype, void *stream) {
+    if (bsb_status s = attention_shape_checks(q_bf16, lens, B, Hq, Hkv, T, D, max_len, out,
+                                              out_dtype))
+        return s;
+    const int64_t need = bsb_attention_workspace_bytes(B, Hq, max_len);
+    if (need < 0 || need > BSB_ATTENTION_NOALLOC_MAX_BYTES) return BSB_ERR_INVALID_ARG;
+    if (!k_cache || !k_scale || !v_cache || !v_scale) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(k_scale) || !aligned16(v_cache) || !aligned16(v_scale))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_attention_decode_noalloc(
+        q_bf16, k_cache, k_scale, v_cache, v_scale, lens, (int)B, (int)Hq, (int)Hkv, (int)T,
+        (int)max_len, out, out_dtype == BSB_OUT_BF16 ? 1 : 0, as_stream(stream)));
 }
 
 bsb_status bsb_kv_cache_write_bf16(const uint16_t *k_bf16, const uint16_t *v_bf16,

@@ -37,6 +37,8 @@
 // replaces, kept as the comparison route): 2-byte elements in blocks of the
 // same operand order, no conversion and no scales.
 #include "device_common.h"
+#include <atomic>
+
 #include "launch.h"
 
 namespace bsb {
@@ -545,6 +547,55 @@ hipError_t attention_decode(const uint16_t *q, const void *kc, const float *ks, 
 }  // namespace
 
 int64_t attention_splits(int64_t max_len) { return (max_len + kSplitTok - 1) / kSplitTok; }
+
+// ---- the allocation-free entry point's workspace ----
+// The split partials of bsb_attention_decode_int8kv_noalloc live in this
+// array instead of a caller-provided workspace; each device the library runs
+// on holds its own copy until the process ends. Every partial the merge reads
+// is written by the split kernel of the same call, so nothing is cleared
+// between calls; calls that overlap on one device share it and race.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / 4];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<float *> g_scratch[kMaxScratchDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device. In host code the array's name is a host-side stand-in, never a
+// device address, so kernels only ever receive this pointer.
+hipError_t scratch_ptr(float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    float *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void *a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (a == nullptr) return hipErrorInvalidSymbol;
+        p = static_cast<float *>(a);
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attention_decode_noalloc(const uint16_t *q, const int8_t *kc, const float *ks,
+                                           const int8_t *vc, const float *vs, const int32_t *lens,
+                                           int B, int Hq, int Hkv, int T, int max_len, void *out,
+                                           int out_bf16, hipStream_t stream) {
+    if (attention_workspace_floats(B, Hq, max_len) * 4 > kNoAllocScratchBytes)
+        return hipErrorInvalidValue;   // the entry point rejects these sizes first
+    float *work = nullptr;
+    hipError_t e = scratch_ptr(&work);
+    if (e != hipSuccess) return e;
+    return attention_decode<kKvInt8>(q, kc, ks, vc, vs, lens, B, Hq, Hkv, T, max_len, work, out,
+                                     out_bf16, stream);
+}
 
 int64_t attention_workspace_floats(int64_t B, int64_t Hq, int64_t max_len) {
     return B * Hq * attention_splits(max_len) * kPart;

@@ -82,6 +82,15 @@ hipError_t launch_attention_decode(const uint16_t *q, const int8_t *kc, const fl
                                    int Hq, int Hkv, int T, int max_len, float *work, void *out,
                                    int out_bf16, hipStream_t stream);
 
+// The same attention with its split partials in a static per-device array of
+// kNoAllocScratchBytes (no workspace argument, nothing allocated); sizes whose
+// workspace exceeds it are rejected by the caller.
+constexpr int64_t kNoAllocScratchBytes = (int64_t)32 << 20;
+hipError_t launch_attention_decode_noalloc(const uint16_t *q, const int8_t *kc, const float *ks,
+                                           const int8_t *vc, const float *vs, const int32_t *lens,
+                                           int B, int Hq, int Hkv, int T, int max_len, void *out,
+                                           int out_bf16, hipStream_t stream);
+
 // The BF16 KV cache of the comparison route (same blocks, 2-byte elements, no scales).
 hipError_t launch_kv_cache_write_bf16(const uint16_t *k, const uint16_t *v, const int32_t *seq,
                                       const int32_t *pos, int64_t n, int B, int Hkv, int T,

@@ -45,7 +45,9 @@
  *    kernel surface at the caller's next synchronisation, as usual for HIP.
  *  - Outputs are written exactly once for every in-range element; nothing
  *    outside the documented output extents is written.
- *  - Calls are reentrant; calls on different streams do not share state.
+ *  - Calls are reentrant; calls on different streams do not share state,
+ *    except bsb_attention_decode_int8kv_noalloc, whose calls on one device
+ *    share a static workspace (stated at its declaration).
  *  - No C++ exception crosses this boundary.
  */
 #ifndef BSB_H
@@ -392,6 +394,30 @@ bsb_status bsb_attention_decode_int8kv(const uint16_t *q_bf16,
                                        int64_t Hkv, int64_t T, int64_t D, int64_t max_len,
                                        float *work, int64_t work_bytes,
                                        void *out, bsb_out_dtype out_dtype, void *stream);
+
+/*
+ * bsb_attention_decode_int8kv for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops and harnesses that forbid hipMalloc.
+ * Same arguments, arithmetic and results (bit for bit) without the workspace:
+ * the split partials live in a static array of BSB_ATTENTION_NOALLOC_MAX_BYTES
+ * that each device the library runs on holds until the process ends, found
+ * on the first call on a device (with that device current). The call
+ * allocates and frees nothing. Sizes whose workspace,
+ * bsb_attention_workspace_bytes(B, Hq, max_len), exceeds the limit return
+ * BSB_ERR_INVALID_ARG and launch nothing. Calls on one device share the array:
+ * calls that overlap on a device (different streams, or graphs replayed
+ * concurrently) race and give undefined outputs; serialise them. Every value
+ * the call reads back from the array is written earlier in the same call.
+ */
+#define BSB_ATTENTION_NOALLOC_MAX_BYTES ((int64_t)32 << 20)
+
+bsb_status bsb_attention_decode_int8kv_noalloc(const uint16_t *q_bf16,
+                                               const int8_t *k_cache, const float *k_scale,
+                                               const int8_t *v_cache, const float *v_scale,
+                                               const int32_t *lens, int64_t B, int64_t Hq,
+                                               int64_t Hkv, int64_t T, int64_t D,
+                                               int64_t max_len, void *out,
+                                               bsb_out_dtype out_dtype, void *stream);
 
 /*
  * The comparison route of the INT8 KV cache: the same cache and attention with

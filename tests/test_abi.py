@@ -202,6 +202,39 @@ def test_kv_cache_argument_checks(L):
         assert wr(A, A, A, A, 3, 2, 4, 128, 128, A, A, A, A, None) == UNSUPPORTED
 
 
+def test_noalloc_attention_argument_checks(L):
+    """The allocation-free decode attention: the attention's checks without a
+    workspace argument, and sizes whose workspace exceeds the static array's
+    BSB_ATTENTION_NOALLOC_MAX_BYTES are refused before anything is launched."""
+    na, wb = L.bsb_attention_decode_int8kv_noalloc, L.bsb_attention_workspace_bytes
+    limit = _lib.ATTENTION_NOALLOC_MAX_BYTES
+    assert limit == 32 << 20
+    names = ["q", "kc", "ks", "vc", "vs", "lens", "B", "Hq", "Hkv", "T", "D", "max_len", "out",
+             "dtype", "stream"]
+    ok = (A, A, A, A, A, A, 2, 16, 4, 128, 128, 128, A, 0, None)
+
+    def call(**kw):
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return na(*[args[n] for n in names])
+
+    assert call(Hq=15) == INVALID
+    assert call(D=64) == INVALID
+    assert call(max_len=129) == INVALID
+    assert call(dtype=2) == INVALID
+    assert call(out=None) == INVALID
+    assert call(kc=None) == INVALID
+    assert call(vs=U) == MISALIGNED
+    # 1024 sequences x 64 heads x 2 splits of 512 tokens: 68 MB of partials, over the limit
+    assert wb(1024, 64, 1024) > limit
+    assert call(B=1024, Hq=64, Hkv=64, T=1024, max_len=1024) == INVALID
+    # the largest workspace under the limit is accepted up to the device check
+    assert wb(32, 64, 8192) <= limit
+    if not torch.cuda.is_available():
+        assert call() == UNSUPPORTED
+        assert call(B=32, Hq=64, Hkv=8, T=8192, max_len=8192) == UNSUPPORTED
+
+
 def test_bf16_kv_cache_argument_checks(L):
     wr, at, wb = L.bsb_kv_cache_write_bf16, L.bsb_attention_decode_bf16kv, L.bsb_attention_workspace_bytes
     assert wr(A, A, A, A, 3, 2, 4, 128, 64, A, A, None) == INVALID          # D != 128
