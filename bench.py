@@ -52,6 +52,7 @@ METRIC = "W8A8-g128 GEMM TOPS & HBM GB/s (M=32 decode, M=4096 prefill), % roofli
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
 CSRC = os.path.join(ROOT, "block_scaled_bit_amd", "csrc")
 
 
@@ -160,35 +161,190 @@ def timed(torch, L, lin, stream, steps, warmup, what=("quant", "gemm")):
     return start.elapsed_time(end) / steps, wall / steps
 
 
-def cpu_baseline(budget_s=10.0):
-    """The oracle as it stands, on the decode workload, on this host's cores."""
+def percall(torch, call, n, warmup):
+    """Per-call durations: a HIP event pair around each of n calls on the launch
+    stream (torch's current stream), after `warmup` untimed calls. Returns a dict
+    of median / p10 / p90 / mean in microseconds."""
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+    def q(f):
+        return round(t[min(n - 1, int(f * (n - 1) + 0.5))], 2)
+    return {"median_us": q(0.5), "p10_us": q(0.1), "p90_us": q(0.9),
+            "mean_us": round(sum(t) / n, 2), "calls": n}
+
+
+def read_sclk_mhz():
+    """The GPU's current shader clock from sysfs (None where it is not readable)."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(f) as h:
+                for line in h:
+                    if line.startswith("S:") or line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def sampled_sclk(torch, call, seconds=0.4):
+    """Shader clocks sampled from sysfs while `call` runs back to back for about
+    `seconds`: (median, min, max) in MHz, or None."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            v = read_sclk_mhz()
+            if v is not None:
+                samples.append(v)
+            stop.wait(0.01)
+    call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    call()
+    b.record()
+    torch.cuda.synchronize()
+    n = max(1, int(seconds / max(1e-6, a.elapsed_time(b) * 1e-3)))
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    for _ in range(n):
+        call()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    busy = [v for v in samples if v > 600] or samples   # drop idle readings at the edges
+    if not busy:
+        return None
+    busy.sort()
+    return {"median_mhz": busy[len(busy) // 2], "min_mhz": busy[0], "max_mhz": busy[-1],
+            "samples": len(busy), "source": "sysfs pp_dpm_sclk"}
+
+
+def measured_peaks(torch, L, stream, dev, a_bytes=None, b_bytes=None):
+    """What this part sustains, measured with the library's probes: a streaming
+    HBM read of 2 GiB (8x the last-level cache) and INT8 MFMA-only loops on
+    uniform random codes and (when given) on the prefill workload's own
+    activation and weight bytes (the matrix cores' rate depends on the operand bits)."""
+    out = torch.empty((131072,), dtype=torch.int32, device=dev)
+    nbytes = 2 << 30
+    src = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    src.fill_(0x5A)
+
+    def hbm():
+        _ok(L, L.bsb_probe_hbm_read(src.data_ptr(), nbytes, out.data_ptr(), stream))
+    h = percall(torch, hbm, 10, 2)
+    del src
+    torch.cuda.empty_cache()
+    res = {"hbm_read_gbs": round(nbytes / (h["median_us"] * 1e-6) / 1e9, 1),
+           "hbm_read_probe": "2 GiB streamed once per call, median of 10 calls"}
+    rounds = 512   # about a millisecond of matrix-core work per call
+    ops = 2048 * rounds * 64 * 65536   # 131072 threads = 2048 waves of 64 MFMAs per round
+
+    def mfma_rate(a, b):
+        def call():
+            _ok(L, L.bsb_probe_mfma_i8(a.data_ptr(), b.data_ptr(), a.numel(), rounds,
+                                       out.data_ptr(), stream))
+        m = percall(torch, call, 10, 3)
+        return round(ops / (m["median_us"] * 1e-6) / 1e12, 1)
+    g = torch.Generator(device="cpu").manual_seed(0)
+    u8 = 8 << 20
+    ua = torch.randint(-127, 128, (u8,), dtype=torch.int8, generator=g).to(dev)
+    ub = torch.randint(-127, 128, (u8,), dtype=torch.int8, generator=g).to(dev)
+    res["mfma_i8_tops_uniform"] = mfma_rate(ua, ub)
+    if a_bytes is not None and b_bytes is not None:
+        n = min(u8, a_bytes.numel(), b_bytes.numel()) // 16 * 16
+        res["mfma_i8_tops_workload"] = mfma_rate(a_bytes.reshape(-1)[:n], b_bytes.reshape(-1)[:n])
+    res["mfma_probe"] = ("only v_mfma_i32_32x32x32_i8, 2 waves per SIMD on every CU, operands "
+                         "cycled over 8 register sets; median of 10 calls")
+    return res
+
+
+def counter_summary(kernel_key):
+    """INT8 MFMA counters of one kernel from the committed rocprofv3 runs, if they
+    match these sources: ops counted by SQ_INSTS_VALU_MFMA_MOPS_I8 against 2MNK, the
+    F16/BF16/F8 MFMA op counts, and utilisation = MFMA busy cycles per SIMD / the
+    kernel's cycles at the clock GRBM_GUI_ACTIVE gives."""
+    try:
+        with open(COUNTER_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources") != sources_digest():
+        return None
+    return t.get("kernels", {}).get(kernel_key)
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands, on the decode workload, on this host's cores,
+    stage by stage: quantisation, the exact INT32 group partials (float64 BLAS),
+    the float64 definition with its magnitude, and the float32 replay in the
+    stated order (what the strict parity checks compare against)."""
     import numpy as np
     from block_scaled_bit_amd import synth
     import oracle
+    cores = len(os.sched_getaffinity(0))
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        blas = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        blas = None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     M, K, N = 32, 8192, 28672
     Ns = 7168                                # a quarter of the output columns
     d = synth.linear_inputs(M, K, Ns, outlier_p=0.005, outlier_f=30.0, seed=0)
+    stages = {"quantize_act_ref": 0.0, "group_partials_ref": 0.0, "gemm_ref": 0.0,
+              "gemm_fp32_ordered_ref": 0.0}
     runs, t_tot = 0, 0.0
     while t_tot < budget_s and runs < 1000:
         t0 = time.perf_counter()
         q, sa = oracle.quantize_act_ref(d["x"])
+        t1 = time.perf_counter()
         oracle.gemm_fp32_ordered_ref(q, sa, d["qw"], d["sw"])
-        t_tot += time.perf_counter() - t0
+        t2 = time.perf_counter()
+        stages["quantize_act_ref"] += t1 - t0
+        stages["gemm_fp32_ordered_ref"] += t2 - t1
+        t_tot += t2 - t0
         runs += 1
+    # the other two stages once each, outside the throughput figure
+    t0 = time.perf_counter()
+    oracle.group_partials_ref(q, d["qw"])
+    t1 = time.perf_counter()
+    oracle.gemm_ref(q, sa, d["qw"], d["sw"])
+    t2 = time.perf_counter()
     t = t_tot / runs
     byts = quant_bytes(M, K) + gemm_bytes(M, Ns, K)
-    return {"value": round(byts / t / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    return {"value": round(byts / t / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": (f"oracle quantize_act_ref + gemm_fp32_ordered_ref on M={M}, K={K} and "
                        f"{Ns} of the {N} output columns (same per-column work as the full "
                        f"layer), mean of {runs} runs = {t:.3f} s; GB/s = that sample's "
-                       f"algorithmic bytes / time")}
+                       f"algorithmic bytes / time"),
+            "cores_affinity": cores, "blas_threads": blas, "cpu_model": model,
+            "stage_s": {"quantize_act_ref": round(stages["quantize_act_ref"] / runs, 4),
+                        "gemm_fp32_ordered_ref": round(stages["gemm_fp32_ordered_ref"] / runs, 4),
+                        "group_partials_ref": round(t1 - t0, 4),
+                        "gemm_ref": round(t2 - t1, 4)}}
 
 
 class Row:
@@ -411,6 +567,9 @@ def extra_rows(torch, L, stream, dev, steps):
     rows["moe_4096tok_top8_64e_grouped"] = _rate(tg * 1e3, ops=2 * R * N * K, byts=gbytes,
                                                  bound="mfma+hbm")
     rows["moe_4096tok_top8_64e_grouped"].update(rows=R, experts_nonempty=nonempty)
+    cs = counter_summary("gemm_big_kernel<0, true> [grid 786432]")
+    if cs:
+        rows["moe_4096tok_top8_64e_grouped"].update(counters=cs, mfma_util=cs.get("mfma_util"))
     log(f"moe: quant {tq * 1e3:.1f} us, grouped {tg * 1e3:.1f} us")
     # one GPU's share under 8-way expert parallelism (experts e with e % 8 == r on
     # GPU r): the grouped GEMM over the 8 experts of the GPU with the most rows,
@@ -734,6 +893,15 @@ def main():
     g_avg, _ = timed(torch, L, lin, stream, args.steps, args.warmup, ("gemm",))
     q_avg, _ = timed(torch, L, lin, stream, args.steps, args.warmup, ("quant",))
     rm_avg, _ = timed(torch, L, lin, stream, args.steps, args.warmup, ("gemm_rm",))
+    # per-call HIP events around the packed GEMM (copies rotated as in the step)
+    it = [0]
+
+    def one_gemm():
+        p = lin.bufs[it[0] % len(lin.bufs)]["ptr"]
+        it[0] += 1
+        _ok(L, L.bsb_gemm_w8a8_g128_packed(p["q"], p["sa"], p["qwp"], p["sw"], M, N, K, p["y"], 0,
+                                           stream))
+    g_calls = percall(torch, one_gemm, max(20, min(200, args.steps)), 10)
     step_bytes = quant_bytes(M, K) + gemm_bytes(M, N, K)
     g_bytes = gemm_bytes(M, N, K)
     achieved = g_bytes / (g_avg * 1e-3) / 1e9
@@ -768,6 +936,7 @@ def main():
                      "kernel": "gemm_packed_kernel<2, 7, 0, true, false>",
                      "timing": "mean of back-to-back launches between HIP events on the launch stream",
                      "bytes_per_launch": g_bytes, "avg_us": round(g_avg * 1e3, 2),
+                     "per_call": g_calls,
                      "quant_avg_us": round(q_avg * 1e3, 2)},
         "row_major": {"kernel": "gemm_smallm_kernel<2, 7, 0, ...>", "avg_us": round(rm_avg * 1e3, 2),
                       "achieved": round(rm_rate, 1), "frac": round(rm_rate / HBM_PEAK_GBS, 4),
@@ -782,14 +951,39 @@ def main():
         for b in pre.bufs:
             L.bsb_quantize_act(b["ptr"]["x"], Mp, Kp, b["ptr"]["q"], b["ptr"]["sa"], stream)
         psteps = max(5, min(50, args.steps // 4))
-        pg, _ = timed(torch, L, pre, stream, psteps, max(2, args.warmup // 4), ("gemm",))
-        tops = 2.0 * Mp * Np * Kp / (pg * 1e-3) / 1e12
-        log(f"prefill gemm {pg * 1e3:.1f} us = {tops:.0f} TOPS")
-        out["prefill"] = {"M": Mp, "K": Kp, "N": Np, "avg_us": round(pg * 1e3, 2),
+        pg, _ = timed(torch, L, pre, stream, psteps, 10, ("gemm",))
+        pit = [0]
+
+        def one_prefill():
+            p = pre.bufs[pit[0] % len(pre.bufs)]["ptr"]
+            pit[0] += 1
+            _ok(L, L.bsb_gemm_w8a8_g128(p["q"], p["sa"], p["qw"], p["sw"], Mp, Np, Kp, p["y"], 0,
+                                        stream))
+        pc = percall(torch, one_prefill, max(10, min(40, args.steps // 5)), 5)
+        ops = 2.0 * Mp * Np * Kp
+        tops = ops / (pc["median_us"] * 1e-6) / 1e12
+        log(f"prefill gemm median {pc['median_us']:.1f} us (p10 {pc['p10_us']:.1f}, p90 "
+            f"{pc['p90_us']:.1f}; back-to-back mean {pg * 1e3:.1f} us) = {tops:.0f} TOPS")
+        peaks = measured_peaks(torch, L, stream, dev, pre.bufs[0]["q"], pre.bufs[0]["qw"])
+        clk = sampled_sclk(torch, one_prefill)
+        log(f"measured peaks {peaks}; prefill clock {clk}")
+        out["prefill"] = {"M": Mp, "K": Kp, "N": Np, "median_us": pc["median_us"],
+                          "p10_us": pc["p10_us"], "p90_us": pc["p90_us"],
+                          "back_to_back_mean_us": round(pg * 1e3, 2),
                           "tops": round(tops, 1), "peak_tops": INT8_PEAK_TOPS,
                           "frac": round(tops / INT8_PEAK_TOPS, 4), "bound": "mfma",
-                          "kernel": "gemm_big_kernel 256x256",
+                          "frac_of_measured_mfma_workload": round(
+                              tops / peaks["mfma_i8_tops_workload"], 4),
+                          "frac_of_measured_mfma_uniform": round(
+                              tops / peaks["mfma_i8_tops_uniform"], 4),
+                          "kernel": "gemm_big_kernel<0, false> (256x256)",
+                          "sclk": clk,
+                          "counters": counter_summary("gemm_big_kernel<0, false> [grid 262144]"),
                           "traffic": measured_traffic("gemm_prefill")}
+        if out["prefill"]["counters"]:
+            out["prefill"]["mfma_util"] = out["prefill"]["counters"].get("mfma_util")
+        out["measured_peaks"] = peaks
+        out["roofline"]["frac_of_measured_hbm"] = round(achieved / peaks["hbm_read_gbs"], 4)
         del pre
         torch.cuda.empty_cache()
 

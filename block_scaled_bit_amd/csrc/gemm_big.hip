@@ -21,19 +21,27 @@
 // and K steps only by constants, so every fragment read is one ds_read_b128
 // with an immediate offset.
 //
-// Staging: per K group the A tile (256 rows x 128 B) and the B tile (256
-// weight rows x 128 B) go from global memory straight into LDS (buffer loads
-// with the LDS-destination bit, 1 KB per wave instruction, 8 lanes per
-// 128-byte row line, 16-byte chunk j of row r at j ^ ((r >> 1) & 7)), with the
-// group's 256 weight scales beside them, in two stages (128 KB + 4 KB).
-// One barrier per group, placed before the last column block: at that point
-// every wave holds the fragments it still needs of group g in registers, so
-// the barrier (a) publishes group g+1, whose fragments are then read while
-// the last column block of g is multiplied (each A fragment right after its
-// last use, each B fragment after its last use in that block), and (b) frees
-// group g's stage, into which group g+2 is loaded at once: the loads have
-// about one group of work to land. The last block's epilogue moves into the
-// next group, behind its first MFMA.
+// Staging: per K group the A tile (256 rows x 128 B), the B tile (256 weight
+// rows x 128 B) and the group's 256 weight scales go from global memory
+// straight into LDS (buffer loads with the LDS-destination bit, 1 KB per wave
+// instruction, 8 lanes per 128-byte row line, 16-byte chunk j of row r at
+// j ^ ((r >> 1) & 7)), each in two stages. The B tile is staged as two
+// halves: B01 holds the rows of every wave's column blocks 0 and 1, B23 those
+// of blocks 2 and 3. Two barriers per group, after column block 0 (S) and
+// after column block 2 (M), each preceded by a wait for the stages it
+// publishes:
+//   S(g): publishes B23[g] (read from block 1 on); frees the stages of A[g]
+//         (read during block 3 of g-1) and B01[g] (read up to block 0), into
+//         which A[g+2] and B01[g+2] are loaded at once;
+//   M(g): publishes A[g+1], B01[g+1] and the scales of g+1, whose fragments are
+//         read while block 3 of g is multiplied (each A fragment right after
+//         its last use, each B fragment after its last use in that block);
+//         frees B23[g] and the scales of g, into which B23[g+2] and the scales
+//         of g+2 are loaded.
+// A and B01 thus have one and a half groups of work to land, B23 one and a
+// quarter, instead of one. Loads complete in issue order, so each wait is a
+// single vmcnt that leaves the later stages in flight. 132 KB of LDS. The last
+// block's epilogue moves into the next group, behind its first MFMA.
 //
 // Out-of-range rows, columns and groups read zero through the buffer
 // descriptors (a zero group adds fmaf(0, 0, acc) = acc), so no load sits
@@ -48,10 +56,12 @@ namespace bsb {
 namespace {
 
 constexpr int kBigTM = 256, kBigTN = 256;        // output tile per workgroup
-constexpr int kBigStage = 256 * kGroup;          // one operand tile of one K group (bytes)
+constexpr int kBigStage = 256 * kGroup;          // A tile of one K group (bytes)
+constexpr int kBigHalf = 128 * kGroup;           // half a B tile (B01 or B23) of one K group
 constexpr int kBigLdsA = 0;                      // A tiles of stages 0, 1
-constexpr int kBigLdsB = 2 * kBigStage;          // B tiles of stages 0, 1
-constexpr int kBigLdsS = 4 * kBigStage;          // scales of stages 0, 1
+constexpr int kBigLdsB01 = 2 * kBigStage;        // B01 halves of stages 0, 1
+constexpr int kBigLdsB23 = kBigLdsB01 + 2 * kBigHalf;   // B23 halves of stages 0, 1
+constexpr int kBigLdsS = kBigLdsB23 + 2 * kBigHalf;     // scales of stages 0, 1
 constexpr int kBigScaleStage = 512 * 4;          // 256 scales + 256 slots for the spare loads
 constexpr int kBigLds = kBigLdsS + 2 * kBigScaleStage;   // 135168 bytes of 160 KB
 
@@ -161,40 +171,47 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
                                    SCALES ? (uint32_t)(ncols * G * 4) : 0u);
 
     // ---- staging (global -> LDS) ----
-    // Wave w fills 1 KB blocks 4w .. 4w+3 of each tile (8 rows of 128 B each);
-    // lane l lands at byte 16*l of a block and fetches the global chunk that
-    // the swizzle puts there. Blocks i and i+2 are 16 rows apart, which share
-    // the swizzle, so they differ by the uniform 16*K in the scalar offset.
+    // Each tile is filled in 1 KB blocks of 8 rows x 128 B; lane l lands at
+    // byte 16*l of a block and fetches the global chunk that the swizzle puts
+    // there. Wave w fills blocks 2w and 2w+1 of each region (LDS rows
+    // 16w .. 16w+15), and of the A tile also blocks 16+2w, 17+2w (rows 128
+    // further on). Rows 16 apart share the swizzle, so every block of a wave
+    // uses one of two per-lane offsets and differs only in the scalar offset.
+    // B01 row r holds tile row r + (r >= 64 ? 64 : 0), B23 row r tile row
+    // r + 64 + (r >= 64 ? 64 : 0): the rows of column blocks 0-1 and 2-3 of
+    // both waves' 128-row halves.
     uint32_t dvoff[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = wave * 32 + 8 * i + (lane >> 3);
-        dvoff[i] = (uint32_t)(row * K + (((lane & 7) ^ big_swz(row)) << 4));
+    for (int j = 0; j < 2; ++j) {
+        const int row = wave * 16 + 8 * j + (lane >> 3);
+        dvoff[j] = (uint32_t)(row * K + (((lane & 7) ^ big_swz(row)) << 4));
     }
+    const uint32_t boff01 = (uint32_t)((wave >= 4 ? 64 : 0) * K);
+    const uint32_t boff23 = (uint32_t)((wave >= 4 ? 128 : 64) * K);
     // Scales: waves 0-3 load the group's 256 scales, one per lane, into the
     // order [wn][l32][cb] (column n = 128 wn + 32 cb + l32), so that each lane
     // later reads its four column blocks' scales in one 16-byte read; waves
     // 4-7 issue the same load past the end into spare slots, which keeps every
-    // wave's load count per group equal (9).
+    // wave's load count per stage equal.
     const int sp = wave * 64 + lane;
     const uint32_t svoff =
         wave < 4 ? (uint32_t)((((sp >> 7) << 7) + ((sp & 3) << 5) + ((sp >> 2) & 31)) * G * 4) : 0u;
     const uint32_t lbase = (uint32_t)(uintptr_t)lds;
 
-    auto dma = [&](int st, int g) {
+    // Each batch is one statement, so nothing the compiler emits lands between
+    // the loads. s_nop 4: a VALU write of an SGPR read by a vector memory
+    // instruction needs five wait states (the compiler may form the
+    // descriptors or offsets with v_readfirstlane right before); s_nop 0 after
+    // each M0 write: one wait state before an LDS-destination load reads M0.
+    // S batch of group g into stage st: A (4 loads) and B01 (2 loads).
+    auto dma_s = [&](int st, int g) {
         const bool in = g < G;
-        const uint32_t so0 = in ? (uint32_t)g * kGroup : kOOB;
-        const uint32_t so1 = in ? so0 + (uint32_t)(16 * K) : kOOB;
-        const uint32_t sso = (in && wave < 4) ? (uint32_t)g * 4 : kOOB;
-        const uint32_t ma = lbase + kBigLdsA + st * kBigStage + wave * 4096;
-        const uint32_t mb = lbase + kBigLdsB + st * kBigStage + wave * 4096;
-        const uint32_t ms = lbase + kBigLdsS + st * kBigScaleStage + wave * 256;
+        const uint32_t so = in ? (uint32_t)g * kGroup : kOOB;
+        const uint32_t sa2 = in ? so + (uint32_t)(128 * K) : kOOB;
+        const uint32_t sb = in ? so + boff01 : kOOB;
+        const uint32_t ma = lbase + kBigLdsA + st * kBigStage + wave * 2048;
+        const uint32_t mb = lbase + kBigLdsB01 + st * kBigHalf + wave * 2048;
         uint32_t m0_out;   // M0 is written inside: declared as an output
-        // One statement, so nothing the compiler emits lands between the loads.
-        // s_nop 4: a VALU write of an SGPR read by a vector memory instruction
-        // needs five wait states (the compiler may form the descriptors or
-        // offsets with v_readfirstlane right before); s_nop 0 after each M0
-        // write: one wait state before an LDS-destination load reads M0.
         asm volatile(
             "s_nop 4\n\t"
             "s_mov_b32 m0, %[a0]\n\ts_nop 0\n\t"
@@ -206,43 +223,69 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             "s_mov_b32 m0, %[a3]\n\ts_nop 0\n\t"
             "buffer_load_dwordx4 %[v1], %[ra], %[s1] offen lds\n\t"
             "s_mov_b32 m0, %[b0]\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %[v0], %[rb], %[s0] offen lds\n\t"
+            "buffer_load_dwordx4 %[v0], %[rb], %[s2] offen lds\n\t"
             "s_mov_b32 m0, %[b1]\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %[v1], %[rb], %[s0] offen lds\n\t"
-            "s_mov_b32 m0, %[b2]\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %[v0], %[rb], %[s1] offen lds\n\t"
-            "s_mov_b32 m0, %[b3]\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %[v1], %[rb], %[s1] offen lds\n\t"
-            "s_mov_b32 m0, %[c0]\n\ts_nop 0\n\t"
-            "buffer_load_dword %[vs], %[rs], %[ss] offen lds"
+            "buffer_load_dwordx4 %[v1], %[rb], %[s2] offen lds"
             : "=&{m0}"(m0_out)
-            : [a0] "s"(ma), [a1] "s"(ma + 1024), [a2] "s"(ma + 2048), [a3] "s"(ma + 3072),
-              [b0] "s"(mb), [b1] "s"(mb + 1024), [b2] "s"(mb + 2048), [b3] "s"(mb + 3072),
-              [c0] "s"(ms), [v0] "v"(dvoff[0]), [v1] "v"(dvoff[1]), [vs] "v"(svoff),
-              [ra] "s"(ra), [rb] "s"(rb), [rs] "s"(rs), [s0] "s"(so0), [s1] "s"(so1),
+            : [a0] "s"(ma), [a1] "s"(ma + 1024), [a2] "s"(ma + 16384), [a3] "s"(ma + 17408),
+              [b0] "s"(mb), [b1] "s"(mb + 1024), [v0] "v"(dvoff[0]), [v1] "v"(dvoff[1]),
+              [ra] "s"(ra), [rb] "s"(rb), [s0] "s"(so), [s1] "s"(sa2), [s2] "s"(sb)
+            : "memory");
+        (void)m0_out;
+    };
+    // M batch of group g into stage st: the scales (1 load) and B23 (2 loads).
+    auto dma_m = [&](int st, int g) {
+        const bool in = g < G;
+        const uint32_t sb = in ? (uint32_t)g * kGroup + boff23 : kOOB;
+        const uint32_t sso = (in && wave < 4) ? (uint32_t)g * 4 : kOOB;
+        const uint32_t mb = lbase + kBigLdsB23 + st * kBigHalf + wave * 2048;
+        const uint32_t ms = lbase + kBigLdsS + st * kBigScaleStage + wave * 256;
+        uint32_t m0_out;
+        asm volatile(
+            "s_nop 4\n\t"
+            "s_mov_b32 m0, %[c0]\n\ts_nop 0\n\t"
+            "buffer_load_dword %[vs], %[rs], %[ss] offen lds\n\t"
+            "s_mov_b32 m0, %[b0]\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %[v0], %[rb], %[s2] offen lds\n\t"
+            "s_mov_b32 m0, %[b1]\n\ts_nop 0\n\t"
+            "buffer_load_dwordx4 %[v1], %[rb], %[s2] offen lds"
+            : "=&{m0}"(m0_out)
+            : [c0] "s"(ms), [b0] "s"(mb), [b1] "s"(mb + 1024), [v0] "v"(dvoff[0]),
+              [v1] "v"(dvoff[1]), [vs] "v"(svoff), [rb] "s"(rb), [rs] "s"(rs), [s2] "s"(sb),
               [ss] "s"(sso)
             : "memory");
         (void)m0_out;
     };
+    // Loads per wave: 6 in an S batch, 3 in an M batch (scales first).
+    // At S(g) B23[g] (end of the M batch of g-2) must have landed: the S and M
+    // batches of g-1 (9 loads) may still be in flight. At M(g) the S batch of
+    // g-1 and the scales of g+1 (first load of the M batch of g-1) must have
+    // landed: B23[g+1] and the S batch of g (8 loads) may be in flight.
+    auto wait_s = [&]() { asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)" ::: "memory"); };
+    auto wait_m = [&]() { asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); };
 
     // ---- fragment reads (LDS -> registers) ----
     // A fragment (row block rb, K step ks) of lane l: 16 bytes of row
     // 64 wm + 32 rb + l32 at K bytes 32 ks + 16 half; B likewise for weight row
     // 128 wn + 32 cb + l32. Rows 32 apart share the swizzle, so stage, block
     // and K-step offsets beyond the per-(ks) lane base are constants.
+    // B fragments of column blocks 0-1 come from B01 row 64 wn + 32 cb + l32,
+    // those of blocks 2-3 from the same row of B23 (one lane base for both).
     uint32_t fa[4], fb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        const int r_a = wm * 64 + l32, r_b = wn * 128 + l32;
+        const int r_a = wm * 64 + l32, r_b = wn * 64 + l32;
         fa[ks] = kBigLdsA + r_a * kGroup + (((2 * ks + half) ^ big_swz(r_a)) << 4);
-        fb[ks] = kBigLdsB + r_b * kGroup + (((2 * ks + half) ^ big_swz(r_b)) << 4);
+        fb[ks] = kBigLdsB01 + r_b * kGroup + (((2 * ks + half) ^ big_swz(r_b)) << 4);
     }
     const uint32_t fs = kBigLdsS + (wn * 128 + l32 * 4) * 4;
     auto ldA = [&](int st, int rb_, int ks) {
         return *reinterpret_cast<const v4i *>(lds + fa[ks] + st * kBigStage + rb_ * 4096);
     };
     auto ldB = [&](int st, int cb, int ks) {
-        return *reinterpret_cast<const v4i *>(lds + fb[ks] + st * kBigStage + cb * 4096);
+        const int off = cb < 2 ? st * kBigHalf + cb * 4096
+                               : (kBigLdsB23 - kBigLdsB01) + st * kBigHalf + (cb - 2) * 4096;
+        return *reinterpret_cast<const v4i *>(lds + fb[ks] + off);
     };
     auto ldS = [&](int st) {
         return *reinterpret_cast<const v4f *>(lds + fs + st * kBigScaleStage);
@@ -262,10 +305,13 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
                 pacc[i][j][r] = 0;
             }
 
-    // prologue: groups 0 and 1 into stages 0 and 1; wait for group 0
-    dma(0, 0);
-    dma(1, 1);
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    // prologue: groups 0 and 1 into stages 0 and 1; wait for A[0], B01[0]
+    // and the scales of group 0 (B23[0] and group 1 may stay in flight)
+    dma_s(0, 0);
+    dma_m(0, 0);
+    dma_s(1, 1);
+    dma_m(1, 1);
+    asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
     __syncthreads();
 
     if (active) {
@@ -336,18 +382,28 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
                     prev = c;
                     prev_s = sc[cb];
                 }
-                if (cb == 2) {
-                    // every wave holds group g's remaining fragments: publish
-                    // g+1, free this stage, load g+2 into it
-                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                // Around the barriers the wave drops to the default priority, so a
+                // wave of the same SIMD that is still multiplying issues first.
+                if (cb == 0 || cb == 2) __builtin_amdgcn_s_setprio(0);
+                if (cb == 0) {
+                    // S(g): publish B23[g]; A[g] and B01[g] are read: load g+2 there
+                    wait_s();
                     __syncthreads();
-                    dma(st, g + 2);
+                    dma_s(st, g + 2);
+                } else if (cb == 2) {
+                    // M(g): publish A, B01 and the scales of g+1; B23[g] and the
+                    // scales of g are read: load g+2 there
+                    wait_m();
+                    __syncthreads();
+                    dma_m(st, g + 2);
                     scn = ldS(st ^ 1);
                 }
+                if (cb == 0 || cb == 2) __builtin_amdgcn_s_setprio(2);
             }
             sc = scn;
         };
 
+        __builtin_amdgcn_s_setprio(2);   // the multiplying phases run at the raised priority
         int g = 0;
         for (; g + 1 < G; g += 2) {
             step(std::integral_constant<int, 0>{}, g);
@@ -358,21 +414,17 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
         epi(1, 3, 1, G - 1);
         epi(1, 3, 2, G - 1);
         epi(1, 3, 3, G - 1);
+        __builtin_amdgcn_s_setprio(0);
     } else {
         // rows past the tile's end: stage this wave's share and meet every barrier
-        int g = 0;
-        for (; g + 1 < G; g += 2) {
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        for (int g = 0; g < G; ++g) {
+            const int st = g & 1;
+            wait_s();
             __syncthreads();
-            dma(0, g + 2);
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            dma_s(st, g + 2);
+            wait_m();
             __syncthreads();
-            dma(1, g + 3);
-        }
-        if (g < G) {
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            __syncthreads();
-            dma(0, g + 2);
+            dma_m(st, g + 2);
         }
     }
     // loads past the last group still write (zeros) into LDS: let them land

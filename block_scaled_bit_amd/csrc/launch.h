@@ -91,6 +91,13 @@ hipError_t launch_attention_decode_noalloc(const uint16_t *q, const int8_t *kc, 
                                            int B, int Hq, int Hkv, int T, int max_len, void *out,
                                            int out_bf16, hipStream_t stream);
 
+// probe.hip: measurement probes (threads per launch; each writes one int32 to out)
+constexpr int kProbeThreads = 131072;
+hipError_t launch_probe_mfma_i8(const int8_t *a, const int8_t *b, int64_t bytes, int64_t rounds,
+                                int32_t *out, hipStream_t stream);
+hipError_t launch_probe_hbm_read(const void *src, int64_t bytes, int32_t *out,
+                                 hipStream_t stream);
+
 // The BF16 KV cache of the comparison route (same blocks, 2-byte elements, no scales).
 hipError_t launch_kv_cache_write_bf16(const uint16_t *k, const uint16_t *v, const int32_t *seq,
                                       const int32_t *pos, int64_t n, int B, int Hkv, int T,

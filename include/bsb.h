@@ -447,6 +447,32 @@ bsb_status bsb_attention_decode_bf16kv(const uint16_t *q_bf16,
                                        float *work, int64_t work_bytes,
                                        void *out, bsb_out_dtype out_dtype, void *stream);
 
+/*
+ * Measurement probes. Not steps of the method: they measure what this part
+ * sustains, so that the benchmark can state its rooflines against measured
+ * ceilings beside the published peaks ([P3] sec. 4.1 and its sec. 6
+ * checklist: confirm by measurement what the INT8 path really achieves).
+ * Each launches BSB_PROBE_THREADS threads, and each thread writes one int32 of
+ * `out` (a value derived from what it read or computed, so nothing is skipped).
+ *
+ * bsb_probe_mfma_i8: only v_mfma_i32_32x32x32_i8, two waves per SIMD on 256
+ * compute units, rounds * 64 MFMAs per wave; ops = BSB_PROBE_THREADS / 64 *
+ * rounds * 64 * 65536. Operands are 16-byte chunks of `a` and `b` (each
+ * `bytes` long), so the rate reflects those bytes (the matrix cores draw more
+ * power on dense bit patterns and the clock follows).
+ *   bytes a multiple of 16, 16 .. 2^31;  1 <= rounds <= 2^24
+ * bsb_probe_hbm_read: reads `bytes` of src once, 16 bytes per lane, four
+ * loads in flight per lane, non-temporal.
+ *   bytes a multiple of 16 * BSB_PROBE_THREADS (2 MiB), at most 2^40
+ * out [BSB_PROBE_THREADS] int32 (written). Errors as bsb_gemm_w8a8_g128.
+ */
+#define BSB_PROBE_THREADS 131072
+
+bsb_status bsb_probe_mfma_i8(const int8_t *a, const int8_t *b, int64_t bytes, int64_t rounds,
+                             int32_t *out, void *stream);
+
+bsb_status bsb_probe_hbm_read(const void *src, int64_t bytes, int32_t *out, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *bsb_status_string(bsb_status s);
 

@@ -235,6 +235,26 @@ def test_noalloc_attention_argument_checks(L):
         assert call(B=32, Hq=64, Hkv=8, T=8192, max_len=8192) == UNSUPPORTED
 
 
+def test_probe_argument_checks(L):
+    """Measurement probes: sizes outside their stated ranges are refused before
+    anything is launched; valid calls without a gfx950 device fail fast."""
+    mf, hb = L.bsb_probe_mfma_i8, L.bsb_probe_hbm_read
+    assert mf(A, A, 8, 1, A, None) == INVALID            # under 16 bytes
+    assert mf(A, A, 24, 1, A, None) == INVALID           # not a multiple of 16
+    assert mf(A, A, 1024, 0, A, None) == INVALID         # no rounds
+    assert mf(A, A, (1 << 31) + 16, 1, A, None) == INVALID
+    assert mf(None, A, 1024, 1, A, None) == INVALID
+    assert mf(A, A, 1024, 1, U, None) == MISALIGNED
+    sweep = 16 * 131072
+    assert hb(A, sweep - 16, A, None) == INVALID
+    assert hb(A, sweep + 16, A, None) == INVALID
+    assert hb(None, sweep, A, None) == INVALID
+    assert hb(U, sweep, A, None) == MISALIGNED
+    if not torch.cuda.is_available():
+        assert mf(A, A, 1024, 1, A, None) == UNSUPPORTED
+        assert hb(A, 2 * sweep, A, None) == UNSUPPORTED
+
+
 def test_bf16_kv_cache_argument_checks(L):
     wr, at, wb = L.bsb_kv_cache_write_bf16, L.bsb_attention_decode_bf16kv, L.bsb_attention_workspace_bytes
     assert wr(A, A, A, A, 3, 2, 4, 128, 64, A, A, None) == INVALID          # D != 128
