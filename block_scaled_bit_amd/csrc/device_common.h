@@ -167,12 +167,9 @@ __device__ __forceinline__ void buf_load16_lds(v4i rsrc, uint32_t lds, uint32_t 
 }
 
 // The same with the non-temporal hint (data streamed once).
-#ifndef BSB_STREAM_POLICY
-#define BSB_STREAM_POLICY "nt"
-#endif
 __device__ __forceinline__ void buf_load16_lds_nt(v4i rsrc, uint32_t lds, uint32_t voff,
                                                   uint32_t soff) {
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen " BSB_STREAM_POLICY " lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                  :: "{m0}"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 

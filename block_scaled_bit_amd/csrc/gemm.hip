@@ -99,10 +99,6 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
 // workgroup walks that expert's rows [offsets[e], offsets[e+1]) in passes of
 // 16*MB rows against its slice of the expert's weights.
 constexpr int kScaleChunk = 16;   // groups per staged chunk of weight scales
-#ifndef BSB_SMALLM_NOSPARE
-#define BSB_SMALLM_NOSPARE 1
-#endif
-constexpr bool kSmallNoSpare = BSB_SMALLM_NOSPARE;
 
 template <int NW>
 constexpr bool smallm_chunked_scales() {
@@ -158,7 +154,7 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     // means the oldest stage has landed whatever this wave issued after it.
     // (workgroups of 4 or more waves; narrower ones, with at most one spare,
     // measured faster keeping it)
-    constexpr bool NOSPARE = kSmallNoSpare && NW >= 4;
+    constexpr bool NOSPARE = NW >= 4;
     constexpr int A_MIN = TBLK - (NW - 1) * ABLK > 0 ? TBLK - (NW - 1) * ABLK : 0;
     constexpr int NLD_MIN = NOSPARE ? WBLK + A_MIN : NLD;
     constexpr int SCH = kScaleChunk;
@@ -750,14 +746,8 @@ hipError_t launch_tile(const TileArgs &a, int64_t row_tiles, hipStream_t stream)
     return hipGetLastError();
 }
 
-#ifndef BSB_SMALLM_S
-#define BSB_SMALLM_S 2
-#endif
-#ifndef BSB_SMALLM_D
-#define BSB_SMALLM_D 4
-#endif
-constexpr int kSmallS = BSB_SMALLM_S;     // K groups per stage
-constexpr int kSmallD = BSB_SMALLM_D;     // LDS stage buffers (D-1 stages in flight)
+constexpr int kSmallS = 2;     // K groups per stage
+constexpr int kSmallD = 4;     // LDS stage buffers (D-1 stages in flight)
 
 // Ring depth: as many stage buffers as fit in the 160 KB of LDS beside the
 // scale chunks, at most kSmallD.
@@ -785,11 +775,8 @@ hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, 
     const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW)), GROUPED ? (unsigned)E : 1u);
     // the non-temporal hint pays on weight streams far larger than the caches
     // (measured: faster at 235 MB, slower at 29 MB)
-#ifndef BSB_NT_MIN
-#define BSB_NT_MIN (1LL << 27)
-#endif
-    const bool nt = (int64_t)N * K * (GROUPED ? E : 1) * (AM == AM_BF16 ? 2 : 1) >=
-                    (int64_t)BSB_NT_MIN;
+    constexpr int64_t kNtMin = (int64_t)1 << 27;
+    const bool nt = (int64_t)N * K * (GROUPED ? E : 1) * (AM == AM_BF16 ? 2 : 1) >= kNtMin;
     if (nt)
         gemm_smallm_kernel<MB, NW, OUT, S, D, GROUPED, true, AM>
             <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets, sw_stride);
@@ -819,17 +806,11 @@ hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, 
     nw = nw < min_nw ? min_nw : nw;
     // 64 rows across 8 waves would leave room for only two stage buffers
     if (MB >= 4 && nw > 7) nw = 7;
-#ifdef BSB_SMALLM_NW
-    nw = BSB_SMALLM_NW;
-#endif
 #define BSB_SMALLM_CASE(W)                                                                       \
     case W:                                                                                      \
         return launch_smallm_mb<MB, W, OUT, GROUPED, AM>(q, sa, qw, sw, M, N, K, y, offsets, E,   \
                                                          stream, sw_stride);
     switch (nw) {
-#ifdef BSB_SMALLM_NW
-        BSB_SMALLM_CASE(1)
-#endif
         BSB_SMALLM_CASE(2)
         BSB_SMALLM_CASE(3)
         BSB_SMALLM_CASE(4)

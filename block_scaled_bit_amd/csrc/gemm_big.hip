@@ -119,50 +119,84 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
         lo = lo < 0 ? 0 : (lo > M ? M : lo);
         hi = hi < lo ? lo : (hi > M ? M : hi);
     };
+    int m0, row_end, bm, bn;
     if (GROUPED) {
-        // The tiles that exist are known only here: count them and let the
-        // first mt*nt workgroups take them (the dispatcher deals workgroups
-        // round-robin to the XCDs, so the idle surplus spreads evenly).
-        // (Offsets that overlap, which the contract excludes, could count more
-        // than the host bound; the count is capped at it, so every tile stays
-        // inside [0, R).)
-        int64_t mt = 0;
-        for (int e = 0; e < E; ++e) {
+        // The tiles that exist are known only here. Each thread takes one expert of
+        // a chunk of 512 (one coalesced load of its bounds per chunk); a block-wide
+        // sum gives the tile rows that exist, and the first mt*nt workgroups take
+        // them (the dispatcher deals workgroups round-robin to the XCDs, so the idle
+        // surplus spreads evenly). A block-wide exclusive scan then finds the expert
+        // holding this workgroup's tile row. (Offsets that overlap, which the
+        // contract excludes, could count more than the host bound; the count is
+        // capped at it, so every tile stays inside [0, R).)
+        __shared__ int s_red[8];
+        __shared__ int s_hit[2];
+        auto tiles_of = [&](int e) {
+            if (e >= E) return 0;
             int lo, hi;
             seg(e, lo, hi);
-            mt += (hi - lo + kBigTM - 1) / kBigTM;
+            return (hi - lo + kBigTM - 1) / kBigTM;
+        };
+        // inclusive scan of v over the 512 threads; also returns the block total
+        auto block_scan = [&](int v, int &total) {
+            int x = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o, kWave);
+                if (lane >= o) x += y;
+            }
+            if (lane == 63) s_red[wave] = x;
+            __syncthreads();
+            int before = 0;
+            total = 0;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const int t = s_red[w];
+                before += w < wave ? t : 0;
+                total += t;
+            }
+            __syncthreads();
+            return x + before;
+        };
+        int64_t mt = 0;
+        for (int base = 0; base < E; base += 512) {
+            int tot;
+            block_scan(tiles_of(base + tid), tot);
+            mt += tot;
         }
         mt = mt < tiles.mt ? mt : tiles.mt;
         if ((int64_t)blockIdx.x >= mt * tiles.nt) return;   // whole workgroup
         tiles.mt = (int)mt;
-    }
-    int bm, bn;
-    big_tile_of<GROUPED>(blockIdx.x, tiles, bm, bn);
-    const int n0 = bn * kBigTN;
-    int m0, row_end;
-    if (GROUPED) {
+        big_tile_of<GROUPED>(blockIdx.x, tiles, bm, bn);
         // tile row bm -> (expert, 256-row block)
-        int t = bm, e = 0;
-        m0 = -1;
-        row_end = 0;
-        for (; e < E; ++e) {
-            int lo, hi;
-            seg(e, lo, hi);
-            const int nt = (hi - lo + kBigTM - 1) / kBigTM;
-            if (t < nt) {
-                m0 = lo + t * kBigTM;
-                row_end = hi;
-                break;
+        if (tid == 0) s_hit[0] = -1;
+        int run = 0;
+        for (int base = 0; base < E; base += 512) {
+            const int e = base + tid, c = tiles_of(e);
+            int tot;
+            const int incl = block_scan(c, tot) + run;
+            if (c > 0 && incl - c <= bm && bm < incl) {
+                s_hit[0] = e;
+                s_hit[1] = bm - (incl - c);
             }
-            t -= nt;
+            run += tot;
+            __syncthreads();
+            if (s_hit[0] >= 0 || run > bm) break;   // uniform: every thread reads the same
         }
-        if (m0 < 0) return;   // unreachable: bm < mt
+        const int e = s_hit[0];
+        if (e < 0) return;   // unreachable: bm < mt
+        int lo, hi;
+        seg(e, lo, hi);
+        m0 = lo + s_hit[1] * kBigTM;
+        row_end = hi;
         qw += (int64_t)e * N * K;
         sw += (int64_t)e * N * G;
     } else {
+        big_tile_of<GROUPED>(blockIdx.x, tiles, bm, bn);
         m0 = bm * kBigTM;
         row_end = M;
     }
+    const int n0 = bn * kBigTN;
     const int mrows = min(kBigTM, row_end - m0), ncols = min(kBigTN, N - n0);
 
     const v4i ra = make_rsrc_words(q + (int64_t)m0 * K, (uint32_t)(mrows * K));

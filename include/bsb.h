@@ -26,8 +26,9 @@
  *  - All matrices are row-major and contiguous. K is the reduction dimension
  *    and is contiguous in both operands; G = K / 128 is the number of
  *    128-wide K groups. Two exceptions, each with its layout stated at its
- *    calls: the packed weight form (written by bsb_repack_weights_mfma and
- *    bsb_decode_fp8_block_packed, read by bsb_gemm_w8a8_g128_packed) and the
+ *    calls: the packed weight form (written by bsb_repack_weights_mfma,
+ *    bsb_decode_fp8_block_packed and bsb_decode_mxfp4_packed, read by
+ *    bsb_gemm_w8a8_g128_packed and bsb_grouped_gemm_w8a8_g128_packed) and the
  *    INT8 KV cache's blocks.
  *  - Sizes: K % 128 == 0 and K > 0; N >= 1; M, R >= 0 (0 rows is a
  *    successful no-op that launches nothing). Every extent is below 2^30;
@@ -125,7 +126,7 @@ bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa,
  *           overlap qw
  *   N       a multiple of 16;  K a multiple of 128
  * Errors: BSB_ERR_INVALID_ARG for bad sizes or null pointers (N*K = 0 is not
- * allowed), BSB_ERR_MISALIGNED, BSB_ERR_NO_DEVICE / BSB_ERR_LAUNCH.
+ * allowed), BSB_ERR_MISALIGNED, BSB_ERR_UNSUPPORTED_DEVICE, BSB_ERR_LAUNCH.
  */
 bsb_status bsb_repack_weights_mfma(const int8_t *qw, int64_t N, int64_t K,
                                    int8_t *packed, void *stream);
@@ -148,7 +149,9 @@ bsb_status bsb_gemm_w8a8_g128_packed(const int8_t *q, const float *sa,
                                      void *y, bsb_out_dtype out, void *stream);
 
 /*
- * bsb_grouped_gemm_w8a8_g128 (the MoE form) on packed expert weights: the
+ * The MoE form ([P3] sec. 1.3: experts resident, each token runs through a few
+ * of them; [P1] sec. 2: weights rearranged once at load time into the layout
+ * of the kernel that consumes them) on packed expert weights: the
  * stacked experts qw [E*N, K] repacked by bsb_repack_weights_mfma (each expert's
  * [N, K] block is then contiguous, N*K bytes at e*N*K), scales sw [E, N, K/128]
  * unchanged. Same arithmetic and order, so y is bit-identical to
@@ -265,9 +268,11 @@ bsb_status bsb_decode_fp8_block(const uint8_t *w, const uint8_t *bs,
                                 int8_t *qw, float *sw, void *stream);
 
 /*
- * bsb_decode_fp8_block with the INT8 weight written straight into the matrix
- * cores' operand order of bsb_repack_weights_mfma (one load-time pass for the
- * packed GEMM): packed = bsb_repack_weights_mfma(qw) of the qw that
+ * FP8 [128,128]-block weights decoded to INT8 per-group-128 ([P1] sec. 1-2; the
+ * dialect as in [P2] "FP8 dialect clash") with the INT8 weight written straight
+ * into the matrix cores' operand order of bsb_repack_weights_mfma, the one
+ * load-time rearrangement [P1] sec. 2 describes done in the same pass as the
+ * decode: packed = bsb_repack_weights_mfma(qw) of the qw that
  * bsb_decode_fp8_block writes; sw is the same [N, G] array. Arguments, limits
  * and errors as bsb_decode_fp8_block; packed [N*K] int8 (written).
  */

@@ -162,6 +162,33 @@ def test_prefill_config_sampled():
         assert np.array_equal(host(P[rs, cs]), group_partials_ref(q[rs], qw[cs]))
 
 
+def test_prefill_config_every_tile_row_and_column():
+    """Prefill-shaped linear at full size: one whole output row in every 256-row tile
+    row (16 rows x 8192 columns) and one whole output column in every 256-column tile
+    (32 columns x 4096 rows), so every workgroup of the 256x256 kernel is checked, in
+    BF16 and FP32, strictly against the stated float32 order. The row and column
+    inside each tile move from tile to tile so that every wave position is hit."""
+    d = require_gpu()
+    say("gemm prefill M=4096 K=8192 N=8192 (full, a row per tile row, a column per tile)")
+    cfg = synth.linear_config("prefill")
+    q, sa = quantize_act_ref(cfg["x"])
+    qd, sd = bsb.quantize_act(dev_bf16(cfg["x"], d))
+    qw, sw = cfg["qw"], cfg["sw"]
+    qwd, swd = dev(qw, d), dev(sw, d)
+    yb = host(bsb.gemm_w8a8_g128(qd, sd, qwd, swd))
+    y32 = host(bsb.gemm_w8a8_g128(qd, sd, qwd, swd, out_dtype=torch.float32))
+    rows = np.array([256 * t + (t * 37 + 5) % 256 for t in range(16)])
+    cols = np.array([256 * t + (t * 53 + 11) % 256 for t in range(32)])
+    y64, mag = gemm_ref(q[rows], sa[rows], qw, sw)
+    c32, cb = gemm_fp32_ordered_ref(q[rows], sa[rows], qw, sw)
+    check_bf16(yb[rows], y64, mag, cb)
+    check_fp32(y32[rows], y64, mag, c32)
+    y64, mag = gemm_ref(q, sa, qw[cols], sw[cols])
+    c32, cb = gemm_fp32_ordered_ref(q, sa, qw[cols], sw[cols])
+    check_bf16(yb[:, cols], y64, mag, cb)
+    check_fp32(y32[:, cols], y64, mag, c32)
+
+
 @pytest.mark.parametrize("M", [32, 1024])
 def test_blockfmt_dense_decode_then_gemm(M):
     """FP8 [128,128]-block weights decoded on the GPU, then the GEMM at M tokens. The

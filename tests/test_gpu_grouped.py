@@ -99,15 +99,21 @@ def test_moe_config_sampled_rows():
     yb = host(bsb.grouped_gemm_w8a8_g128(qd, sd, qwd, swd, offd))
     yb2 = host(bsb.grouped_gemm_w8a8_g128(qd, sd, qwd, swd, offd))
     assert np.array_equal(yb, yb2)
+    y32 = host(bsb.grouped_gemm_w8a8_g128(qd, sd, qwd, swd, offd, out_dtype=torch.float32))
     rng = np.random.default_rng(1)
     for e in range(64):
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
             continue
-        rows = sorted(set([lo, hi - 1] + rng.integers(lo, hi, 3).tolist()))
+        # segment ends, random rows, and the rows either side of every 64-row wave
+        # boundary and 256-row tile boundary inside the segment
+        edges = [lo + b + d for b in range(64, hi - lo, 64) for d in (-1, 0)]
+        rows = sorted(set([lo, hi - 1] + rng.integers(lo, hi, 3).tolist() +
+                          [r for r in edges if lo <= r < hi]))
         y64, mag = gemm_ref(q[rows], sa[rows], qw[e], sw[e])
-        _, cb = gemm_fp32_ordered_ref(q[rows], sa[rows], qw[e], sw[e])
+        c32, cb = gemm_fp32_ordered_ref(q[rows], sa[rows], qw[e], sw[e])
         check_bf16(yb[rows], y64, mag, cb)
+        check_fp32(y32[rows], y64, mag, c32)
 
 
 @pytest.mark.parametrize("M", [32, 1024])
