@@ -347,6 +347,53 @@ def cpu_baseline(budget_s=12.0):
                         "gemm_ref": round(t2 - t1, 4)}}
 
 
+def _decoders_at_load_size(torch, L, stream, steps, dev, rows, log):
+    """The two decoders over a whole layer's weights at once (a 16384 x 7168 FP8
+    linear; 32 MXFP4 experts of 2048 x 4096), where the fixed cost of a launch
+    (a few microseconds) is small against the stream; random bytes with finite
+    UE8M0 exponents (the decoders' time does not depend on the values)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    N, K = 16384, 7168
+    byts = N * K + (N // 128) * (K // 128) + N * K + 4 * N * (K // 128)
+    sets = []
+    for _ in range(_copies(byts)):
+        o = dict(w=torch.randint(0, 256, (N, K), dtype=torch.uint8, device=dev, generator=g),
+                 bs=torch.randint(100, 140, (N // 128, K // 128), dtype=torch.uint8, device=dev,
+                                  generator=g),
+                 qw=torch.empty((N, K), dtype=torch.int8, device=dev),
+                 sw=torch.empty((N, K // 128), dtype=torch.float32, device=dev))
+        o["w"][(o["w"] & 0x7F) == 0x7F] = 0   # OCP NaN bytes are outside the domain
+        sets.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
+    tf = Row("decode fp8 (layer)", sets, lambda p, st: _ok(
+        L, L.bsb_decode_fp8_block(p["w"], p["bs"], N, K, 0, p["qw"], p["sw"], st))).time(
+        torch, stream, steps, 3)
+    rows[f"blockfmt_decode_fp8_ocp_{N}x{K}"] = _rate(tf * 1e3, byts=byts)
+    log(f"decode fp8 {N}x{K} {tf * 1e3:.1f} us")
+    del sets
+    torch.cuda.empty_cache()
+    E, N, K = 32, 2048, 4096
+    byts = E * N * K // 2 + E * N * K // 32 + E * N * K + 4 * E * N * (K // 128)
+    sets = []
+    for _ in range(_copies(byts)):
+        o = dict(pk=torch.randint(0, 256, (E, N, K // 2), dtype=torch.uint8, device=dev,
+                                  generator=g),
+                 sc=torch.randint(100, 140, (E, N, K // 32), dtype=torch.uint8, device=dev,
+                                  generator=g),
+                 qw=torch.empty((E * N * K,), dtype=torch.int8, device=dev),
+                 sw=torch.empty((E, N, K // 128), dtype=torch.float32, device=dev))
+        sets.append({k: v.data_ptr() for k, v in o.items()} | {"_keep": o})
+    for packed in (False, True):
+        fn = L.bsb_decode_mxfp4_packed if packed else L.bsb_decode_mxfp4
+        tx = Row("decode mxfp4 (layer)", sets, lambda p, st, fn=fn: _ok(
+            L, fn(p["pk"], p["sc"], E, N, K, p["qw"], p["sw"], st))).time(torch, stream, steps, 3)
+        key = f"blockfmt_decode_mxfp4_{E}x{N}x{K}" + ("_packed" if packed else "")
+        rows[key] = _rate(tx * 1e3, byts=byts)
+        log(f"decode mxfp4 {E}x{N}x{K}{' packed' if packed else ''} {tx * 1e3:.1f} us")
+    del sets
+    torch.cuda.empty_cache()
+
+
 class Row:
     """One measured workload: device-resident inputs in `copies` rotating sets
     and a raw C-ABI call that enqueues one pass over set i."""
@@ -687,12 +734,19 @@ def extra_rows(torch, L, stream, dev, steps):
         torch, stream, steps, 3)
     rows["blockfmt_decode_mxfp4_8x2048x4096"] = _rate(tm * 1e3, byts=mx_bytes)
     log(f"decode mxfp4 {tm * 1e3:.1f} us")
+    # the same decode written in the grouped packed GEMM's operand order
+    tmp = Row("decode mxfp4 packed", msets, lambda p, st: _ok(
+        L, L.bsb_decode_mxfp4_packed(p["pk"], p["sc"], Ee, Ne, Ke, p["qw"], p["sw"], st))).time(
+        torch, stream, steps, 3)
+    rows["blockfmt_decode_mxfp4_8x2048x4096_packed"] = _rate(tmp * 1e3, byts=mx_bytes)
+    log(f"decode mxfp4 into the packed layout {tmp * 1e3:.1f} us")
     qwe = torch.empty((Ee, Ne, Ke), dtype=torch.int8, device=dev)
     swe = torch.empty((Ee, Ne, Ge), dtype=torch.float32, device=dev)
     _ok(L, L.bsb_decode_mxfp4(pk.data_ptr(), sc.data_ptr(), Ee, Ne, Ke, qwe.data_ptr(),
                               swe.data_ptr(), stream))
     del msets, pk, sc
     torch.cuda.empty_cache()
+    _decoders_at_load_size(torch, L, stream, steps, dev, rows, log)
 
     # GEMMs on the decoded weights, M = 32 and 1024 tokens (per expert for the grouped one)
     for Mt in (32, 1024):

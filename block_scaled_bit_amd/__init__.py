@@ -9,7 +9,8 @@ from ._lib import (quantize_act, gemm_w8a8_g128, gemm_w8a8_g128_partials,  # noq
                    repack_weights_mfma, gemm_w8a8_g128_packed, decode_fp8_block_packed,
                    grouped_gemm_w8a8_g128_packed,
                    gemm_w8a8_channel, gemm_w8a16_g128, gemm_bf16, dequant_fp8_block_bf16,
-                   grouped_gemm_w8a8_g128, decode_fp8_block, decode_mxfp4, gather_rows,
+                   grouped_gemm_w8a8_g128, decode_fp8_block, decode_mxfp4, decode_mxfp4_packed,
+                   gather_rows,
                    moe_combine, kv_cache_empty, kv_cache_write, attention_workspace_bytes,
                    attention_decode_int8kv, attention_decode_int8kv_noalloc,
                    kv_cache_empty_bf16, kv_cache_write_bf16,

@@ -43,6 +43,7 @@ _SIGNATURES = {
     "bsb_gemm_w8a16_g128": [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
     "bsb_gemm_bf16": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
     "bsb_decode_mxfp4": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
+    "bsb_decode_mxfp4_packed": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "bsb_gemm_w8a8_g128_partials": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
     "bsb_gather_rows": [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "bsb_moe_combine": [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p],
@@ -430,6 +431,29 @@ def decode_mxfp4(packed: torch.Tensor, scale: torch.Tensor,
         _check(lib().bsb_decode_mxfp4(_ptr(packed), _ptr(scale), E, N, K, _ptr(qw), _ptr(sw),
                                       _stream(dev)), "bsb_decode_mxfp4")
     return qw, sw
+
+
+def decode_mxfp4_packed(packed: torch.Tensor, scale: torch.Tensor,
+                        packed_qw: Optional[torch.Tensor] = None,
+                        sw: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """decode_mxfp4 with the INT8 weight written in the matrix cores' operand order: packed_qw
+    [E*N*K] as repack_weights_mfma leaves the stacked [E*N, K] weights, and sw [E,N,K/128]."""
+    _need(packed, "packed", (torch.uint8,))
+    if packed.dim() != 3:
+        raise ValueError("packed must be [E, N, K/2]")
+    E, N, Kh = packed.shape
+    K = 2 * Kh
+    dev = packed.device
+    _need(scale, "scale", (torch.uint8,), (E, N, K // 32), dev)
+    packed_qw = (torch.empty((E * N * K,), dtype=torch.int8, device=dev) if packed_qw is None
+                 else packed_qw)
+    sw = torch.empty((E, N, K // 128), dtype=torch.float32, device=dev) if sw is None else sw
+    _need(packed_qw, "packed_qw", (torch.int8,), (E * N * K,), dev)
+    _need(sw, "sw", (torch.float32,), (E, N, K // 128), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_decode_mxfp4_packed(_ptr(packed), _ptr(scale), E, N, K, _ptr(packed_qw),
+                                             _ptr(sw), _stream(dev)), "bsb_decode_mxfp4_packed")
+    return packed_qw, sw
 
 
 def gather_rows(q: torch.Tensor, sa: torch.Tensor, index: torch.Tensor,

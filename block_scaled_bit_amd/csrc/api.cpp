@@ -307,6 +307,21 @@ bsb_status bsb_decode_mxfp4(const uint8_t *packed, const uint8_t *scale, int64_t
     return finish(bsb::launch_decode_mxfp4(packed, scale, E, N, K, qw, sw, as_stream(stream)));
 }
 
+bsb_status bsb_decode_mxfp4_packed(const uint8_t *packed, const uint8_t *scale, int64_t E,
+                                   int64_t N, int64_t K, int8_t *packed_qw, float *sw,
+                                   void *stream) {
+    if (E < 1 || N < 16 || N % 16 || K < 128 || K % 128 || E >= kMaxDim || N >= kMaxDim ||
+        K >= kMaxDim || !prod_le(E, N, K, kMaxDecodeElems))
+        return BSB_ERR_INVALID_ARG;
+    if (!packed || !scale || !packed_qw || !sw) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(packed) || !aligned16(scale) || !aligned16(packed_qw) || !aligned16(sw))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_decode_mxfp4(packed, scale, E, N, K, packed_qw, sw,
+                                           as_stream(stream), true));
+}
+
 bsb_status bsb_gather_rows(const int8_t *q, const float *sa, const int32_t *index, int64_t R,
                            int64_t T, int64_t K, int8_t *q_out, float *sa_out, void *stream) {
     if (R < 0 || R >= kMaxDim || T < 1 || T >= kMaxDim || K < 128 || K % 128 || K >= kMaxDim ||

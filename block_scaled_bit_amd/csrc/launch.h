@@ -20,7 +20,7 @@ hipError_t launch_dequant_fp8_block_bf16(const uint8_t *w, const uint8_t *bs, in
 
 hipError_t launch_decode_mxfp4(const uint8_t *packed, const uint8_t *scale, int64_t E,
                                int64_t N, int64_t K, int8_t *qw, float *sw,
-                               hipStream_t stream);
+                               hipStream_t stream, bool packed_out = false);
 
 // out: 0 = BF16, 1 = FP32, 2 = INT32 group partials [M, N, G]
 hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw,

@@ -295,6 +295,21 @@ bsb_status bsb_decode_mxfp4(const uint8_t *packed, const uint8_t *scale,
                             int8_t *qw, float *sw, void *stream);
 
 /*
+ * MXFP4 experts ([P1] sec. 1: E2M1 elements with one UE8M0 exponent per 32
+ * along K) decoded to INT8 per-group-128 with the INT8 weight written in the
+ * matrix cores' operand order, ready for bsb_grouped_gemm_w8a8_g128_packed:
+ * the decode of bsb_decode_mxfp4 and the load-time rearrangement of [P1]
+ * sec. 2 in one pass. packed_qw = bsb_repack_weights_mfma of the stacked
+ * [E*N, K] qw that bsb_decode_mxfp4 writes (expert e's block at e*N*K);
+ * sw is the same [E, N, G] array.
+ *   N a multiple of 16; other arguments, limits and errors as bsb_decode_mxfp4;
+ *   packed_qw [E*N*K] int8 (written).
+ */
+bsb_status bsb_decode_mxfp4_packed(const uint8_t *packed, const uint8_t *scale,
+                                   int64_t E, int64_t N, int64_t K,
+                                   int8_t *packed_qw, float *sw, void *stream);
+
+/*
  * Inspection form of bsb_gemm_w8a8_g128 for tests: the same kernels and
  * main loop selected by the same M, with the epilogue replaced by a store of
  * the exact INT32 group partials ([P3] sec. 3.1 INT32 accumulator).

@@ -308,7 +308,14 @@ def test_packed_weight_argument_checks(L):
     assert dp(A, A, 128, 128, 2, A, A, None) == INVALID       # dialect
     assert dp(A, A, 128, 128, 0, None, A, None) == INVALID
     assert dp(A, A, 128, 128, 0, U, A, None) == MISALIGNED
+    mp = L.bsb_decode_mxfp4_packed
+    assert mp(A, A, 1, 24, 128, A, A, None) == INVALID        # N % 16
+    assert mp(A, A, 0, 16, 128, A, A, None) == INVALID        # no experts
+    assert mp(A, A, 1, 16, 96, A, A, None) == INVALID         # K % 128
+    assert mp(A, A, 1, 16, 128, None, A, None) == INVALID
+    assert mp(A, A, 1, 16, 128, A, U, None) == MISALIGNED
     if not torch.cuda.is_available():
+        assert mp(A, A, 1, 16, 128, A, A, None) == UNSUPPORTED
         assert dp(A, A, 128, 128, 1, A, A, None) == UNSUPPORTED
         assert gp(A, A, A, A, A, 2, 4, 16, 128, A, 1, None) == UNSUPPORTED
         assert rp(A, 16, 128, A, None) == UNSUPPORTED

@@ -170,6 +170,34 @@ def test_fp8_decode_straight_into_the_packed_layout(N, K, dialect):
     assert np.array_equal(sg.check(), sr)
 
 
+# one expert of one 16-row block (one partly filled workgroup); K/32 = 12 and 4
+# input chunks per row (64-byte row segments), 8 and 128 (128-byte ones); the
+# MXFP4 expert shape
+@pytest.mark.parametrize("E,N,K", [(1, 16, 128), (3, 48, 384), (2, 32, 256), (5, 80, 1152),
+                                   (8, 2048, 4096)])
+def test_mxfp4_decode_straight_into_the_packed_layout(E, N, K):
+    """The MXFP4 decoder writing the operand order: the oracle's decode of the
+    stacked [E*N, K] experts, repacked by the oracle's layout, bit for bit; the
+    scales as the row-major decoder writes them. Every UE8M0 exponent with a
+    finite scale occurs at the small shapes."""
+    d = require_gpu()
+    say(f"decode mxfp4 packed E={E} N={N} K={K}")
+    from oracle import decode_mxfp4_ref
+    rng = np.random.default_rng(E * 1000 + N + K)
+    if E * N * K <= 1 << 20:
+        packed = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+        sc = rng.integers(0, 251, size=(E, N, K // 32)).astype(np.uint8)
+    else:
+        packed, sc = synth.mxfp4_weights(rng, E, N, K)
+    pk = Guarded((E * N * K,), torch.int8, d)
+    sg = Guarded((E, N, K // 128), torch.float32, d)
+    bsb.decode_mxfp4_packed(dev(packed, d), dev(sc, d), packed_qw=pk.view, sw=sg.view)
+    torch.cuda.synchronize()
+    qr, sr = decode_mxfp4_ref(packed, sc)
+    assert np.array_equal(pk.check(), repack_mfma_ref(qr.reshape(E * N, K)))
+    assert np.array_equal(sg.check().view(np.uint32), sr.view(np.uint32))
+
+
 def _grouped_case(lengths, N, K, seed):
     rng = np.random.default_rng(seed)
     E = len(lengths)
