@@ -53,6 +53,10 @@ constexpr int64_t kMaxDecodeElems = (int64_t)1 << 35;
 // whole of K stays in range (127 * 127 * 131072 < 2^31).
 constexpr int64_t kMaxChannelK = 131072;
 
+// K accepted by the row-major W8A8 GEMMs: the kernels address a 128-row operand
+// panel with 32-bit buffer offsets (128 * K + 128 < 2^31).
+constexpr int64_t kGemmKLimit = (int64_t)1 << 24;   // K must be below it
+
 // Rows of the BF16-activation GEMMs (the decode-shaped kernel).
 constexpr int64_t kMaxA16Rows = 64;
 
@@ -104,7 +108,7 @@ bsb_status bsb_quantize_act(const uint16_t *x_bf16, int64_t M, int64_t K, int8_t
 bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                               int64_t M, int64_t N, int64_t K, void *y, bsb_out_dtype out,
                               void *stream) {
-    if (!dims_ok(M, N, K) || N * K > kMaxElems) return BSB_ERR_INVALID_ARG;
+    if (!dims_ok(M, N, K) || N * K > kMaxElems || K >= kGemmKLimit) return BSB_ERR_INVALID_ARG;
     if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
     if (M == 0) return BSB_OK;
     if (!q || !sa || !qw || !sw || !y) return BSB_ERR_INVALID_ARG;
@@ -181,7 +185,7 @@ bsb_status bsb_gemm_w8a8_channel(const int8_t *q, const float *sa, const int8_t 
 
 bsb_status bsb_gemm_w8a8_g128_partials(const int8_t *q, const int8_t *qw, int64_t M, int64_t N,
                                        int64_t K, int32_t *P, void *stream) {
-    if (!dims_ok(M, N, K) || N * K > kMaxElems ||
+    if (!dims_ok(M, N, K) || N * K > kMaxElems || K >= kGemmKLimit ||
         (M > 0 && !prod_le(M, N, K / 128, kMaxElems)))
         return BSB_ERR_INVALID_ARG;
     if (M == 0) return BSB_OK;
@@ -196,7 +200,8 @@ bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa, const in
                                       const float *sw, const int32_t *offsets, int64_t E,
                                       int64_t R, int64_t N, int64_t K, void *y,
                                       bsb_out_dtype out, void *stream) {
-    if (!dims_ok(R, N, K) || E < 1 || E >= (1 << 20) || !prod_le(E, N, K, kMaxElems))
+    if (!dims_ok(R, N, K) || K >= kGemmKLimit || E < 1 || E >= (1 << 20) ||
+        !prod_le(E, N, K, kMaxElems))
         return BSB_ERR_INVALID_ARG;
     if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
     if (R == 0) return BSB_OK;

@@ -8,7 +8,7 @@
 //         acc = fmaf((float)P, sw[n,g], acc)             (VALU epilogue)
 //     y = acc * sa[m]  -> BF16 (RNE) or FP32
 //
-// Two kernels share that per-group structure:
+// The kernels share that per-group structure:
 //
 //  * smallm (M <= 64, decode-shaped): the weight matrix is the stream. A
 //    workgroup of 4 waves owns 64 output columns; each wave owns 16 columns
@@ -18,12 +18,9 @@
 //    ahead straight into registers, so every weight byte is read from HBM
 //    once with many bytes in flight per wave.
 //
-//  * tile (large M, prefill-shaped, and the grouped MoE kernel): 128x128
-//    output tile per workgroup of 4 waves (2x2, 64x64 per wave, four
-//    v_mfma_i32_32x32x32_i8 blocks). A and B tiles of one K group are staged
-//    through double-buffered LDS (rows padded to 144 B against bank
-//    conflicts), the next group's tiles are loaded into registers while the
-//    current one is multiplied.
+//  * the tiled kernels for larger M (gemm_mid.hip, 128x128 tiles, and
+//    gemm_big.hip, 256x256 tiles for prefill-shaped M and the grouped MoE
+//    form with many rows per expert), selected by the launchers below.
 //
 // MFMA operand pairing: lane l supplies 16 bytes of row (l % 16 or l % 32)
 // of A and the same 16 K positions of column (l % 16 or l % 32) of B. Any
@@ -519,233 +516,6 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
     }
 }
 
-// --------------------------------------------------------------------------
-// tile: 128x128 per workgroup, dense or grouped.
-// --------------------------------------------------------------------------
-struct TileArgs {
-    const int8_t *q;
-    const float *sa;
-    const int8_t *qw;
-    const float *sw;
-    const int32_t *offsets;   // grouped only
-    void *y;
-    int M;                    // dense rows, or R for grouped
-    int N, K, E;
-    int sw_stride;            // per-channel forms: scale index n * sw_stride
-};
-
-constexpr int TBM = 128, TBN = 128, TLD = kGroup + 16;
-
-constexpr int kTileSmem = 2 * (TBM + TBN) * TLD;   // 73728 bytes (gfx950 allows 160 KB)
-
-// Grid: one workgroup per (row tile, column tile), flattened so that
-// consecutive workgroups share a row tile: bm = id / n_tiles, bn = id % n_tiles.
-template <int OUT, bool GROUPED>
-__global__ void __launch_bounds__(256, 2)
-gemm_tile_kernel(TileArgs p, int n_tiles) {
-    constexpr bool CHN = per_channel<OUT>();   // one scale per row, applied at the end
-    __shared__ __align__(16) int8_t smem[kTileSmem];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int N = p.N, K = p.K, G = K >> 7;
-    const int bm = (int)(blockIdx.x / (unsigned)n_tiles);
-    const int n0 = (int)(blockIdx.x - (unsigned)bm * (unsigned)n_tiles) * TBN;
-
-    // Row range of this tile and the weight slice it multiplies.
-    int row0, row_end;
-    const int8_t *qw = p.qw;
-    const float *sw = p.sw;
-    if (GROUPED) {
-        // Tile index -> (expert, row block): walk the expert segments in order.
-        // Segments are clamped to [0, R] so malformed offsets stay in bounds.
-        int t = bm, e = 0;
-        row0 = -1;
-        row_end = 0;
-        for (; e < p.E; ++e) {
-            int lo = p.offsets[e], hi = p.offsets[e + 1];
-            lo = lo < 0 ? 0 : (lo > p.M ? p.M : lo);
-            hi = hi < lo ? lo : (hi > p.M ? p.M : hi);
-            const int nt = (hi - lo + TBM - 1) / TBM;
-            if (t < nt) {
-                row0 = lo + t * TBM;
-                row_end = hi;
-                break;
-            }
-            t -= nt;
-        }
-        if (row0 < 0) return;   // surplus tile of the host-sized grid
-        qw += (int64_t)e * N * K;
-        sw += (int64_t)e * N * G;
-    } else {
-        row0 = bm * TBM;
-        row_end = p.M;
-    }
-
-    // Global -> register staging: 2048 chunks of 16 B per group (A then B).
-    uint4 st[8];
-    auto load_stage = [&](int g) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = tid + 256 * (i & 3);
-            const int r = c >> 3, cc = c & 7;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (i < 4) {
-                if (row0 + r < row_end)
-                    v = *reinterpret_cast<const uint4 *>(p.q + (int64_t)(row0 + r) * K +
-                                                         g * kGroup + cc * 16);
-            } else {
-                if (n0 + r < N)
-                    v = *reinterpret_cast<const uint4 *>(qw + (int64_t)(n0 + r) * K +
-                                                         g * kGroup + cc * 16);
-            }
-            st[i] = v;
-        }
-    };
-    auto store_stage = [&](int buf) {
-        int8_t *base = smem + buf * (TBM + TBN) * TLD;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = tid + 256 * (i & 3);
-            const int r = (c >> 3) + (i < 4 ? 0 : TBM), cc = c & 7;
-            *reinterpret_cast<uint4 *>(base + r * TLD + cc * 16) = st[i];
-        }
-    };
-
-    const int l32 = lane & 31, half = lane >> 5;
-    // Per-lane output columns of the two 32-wide column blocks.
-    int ncol[2];
-    bool nok[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        ncol[j] = n0 + wn * 64 + j * 32 + l32;
-        nok[j] = ncol[j] < N;
-    }
-
-    v16f facc[2][2];
-    v16i pacc[2][2];   // per-channel form: the INT32 totals so far
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                facc[i][j][r] = 0.0f;
-                pacc[i][j][r] = 0;
-            }
-
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-
-    for (int g = 0; g < G; ++g) {
-        if (g + 1 < G) load_stage(g + 1);
-        float swv[2] = {0.0f, 0.0f};   // the partials form has no scales (sw may be null)
-        if (OUT != OUT_PARTIALS && !CHN) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) swv[j] = nok[j] ? sw[(int64_t)ncol[j] * G + g] : 0.0f;
-        }
-
-        const int8_t *As = smem + (g & 1) * (TBM + TBN) * TLD;
-        const int8_t *Bs = As + TBM * TLD;
-        v16i acc[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = CHN ? pacc[i][j][r] : 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            v4i a[2], b[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                a[i] = as_v4i(*reinterpret_cast<const uint4 *>(
-                    As + (wm * 64 + i * 32 + l32) * TLD + half * 64 + t * 16));
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[j] = as_v4i(*reinterpret_cast<const uint4 *>(
-                    Bs + (wn * 64 + j * 32 + l32) * TLD + half * 64 + t * 16));
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-
-        if (CHN) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) pacc[i][j] = acc[i][j];
-        } else if (OUT == OUT_PARTIALS) {
-            // C layout of 32x32: lane holds column l32, rows 8*(r/4) + 4*half + r%4.
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                        if (m < row_end && nok[j])
-                            reinterpret_cast<int32_t *>(p.y)[((int64_t)m * N + ncol[j]) * G + g] =
-                                acc[i][j][r];
-                    }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        facc[i][j][r] = __builtin_fmaf((float)acc[i][j][r], swv[j], facc[i][j][r]);
-        }
-
-        if (g + 1 < G) store_stage((g + 1) & 1);
-        __syncthreads();
-    }
-
-    if (CHN) {
-        float swn[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) swn[j] = nok[j] ? p.sw[(int64_t)ncol[j] * p.sw_stride] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (m >= row_end) continue;
-                const float s = p.sa[m];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    if (nok[j])
-                        store_out<OUT>(p.y, (int64_t)m * N + ncol[j],
-                                       channel_value(pacc[i][j][r], swn[j], s));
-            }
-    } else if (OUT != OUT_PARTIALS) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (m >= row_end) continue;
-                const float s = p.sa[m];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    if (nok[j]) store_out<OUT>(p.y, (int64_t)m * N + ncol[j], facc[i][j][r] * s);
-            }
-    }
-}
-
-template <int OUT, bool GROUPED>
-hipError_t launch_tile(const TileArgs &a, int64_t row_tiles, hipStream_t stream) {
-    const int64_t n_tiles = (a.N + TBN - 1) / TBN;
-    const int64_t total = row_tiles * n_tiles;
-    if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    gemm_tile_kernel<OUT, GROUPED><<<dim3((unsigned)total), 256, 0, stream>>>(a, (int)n_tiles);
-    return hipGetLastError();
-}
-
 constexpr int kSmallS = 2;     // K groups per stage
 constexpr int kSmallD = 4;     // LDS stage buffers (D-1 stages in flight)
 
@@ -847,12 +617,12 @@ hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, cons
         return launch_smallm<OUT>(q, sa, qw, sw, M, N, K, y, stream, sw_stride);
     // The 256x256 kernel (which addresses its operand panels with 32-bit
     // buffer offsets) when it has at least one tile per CU; below that the
-    // 128x128 kernel's four times as many tiles finish sooner.
+    // 128x128 kernels' four times as many tiles finish sooner.
     const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
     if (M >= kBigMinM && big_gemm_fits(K) && big_tiles >= kCUs)
         return launch_gemm_big(q, sa, qw, sw, M, N, K, y, OUT, nullptr, 0, sw_stride, stream);
-    TileArgs a{q, sa, qw, sw, nullptr, y, M, N, K, 0, sw_stride};
-    return launch_tile<OUT, false>(a, (M + TBM - 1) / TBM, stream);
+    if (!mid_gemm_fits(K)) return hipErrorInvalidValue;   // excluded by the C ABI's checks
+    return launch_gemm_mid(q, sa, qw, sw, M, N, K, y, OUT, nullptr, 0, sw_stride, stream);
 }
 
 }  // namespace
@@ -927,11 +697,9 @@ hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *q
         return launch_smallm_nw<2, OUT_FP32, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y,
                                                    offsets, (int)E, stream);
     }
-    TileArgs a{q, sa, qw, sw, offsets, y, (int)R, (int)N, (int)K, (int)E, 1};
-    // Upper bound on the row tiles over all segments, from host values only.
-    const int64_t row_tiles = (R + TBM - 1) / TBM + E;
-    if (out == OUT_BF16) return launch_tile<OUT_BF16, true>(a, row_tiles, stream);
-    return launch_tile<OUT_FP32, true>(a, row_tiles, stream);
+    if (!mid_gemm_fits(K)) return hipErrorInvalidValue;   // excluded by the C ABI's checks
+    return launch_gemm_mid(q, sa, qw, sw, (int)R, (int)N, (int)K, y, out, offsets, (int)E, 1,
+                           stream);
 }
 
 }  // namespace bsb

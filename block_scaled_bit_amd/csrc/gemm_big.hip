@@ -65,33 +65,6 @@ constexpr int kBigLdsS = kBigLdsB23 + 2 * kBigHalf;     // scales of stages 0, 1
 constexpr int kBigScaleStage = 512 * 4;          // 256 scales + 256 slots for the spare loads
 constexpr int kBigLds = kBigLdsS + 2 * kBigScaleStage;   // 135168 bytes of 160 KB
 
-struct BigTiles {
-    int mt, nt;   // tile rows / columns
-};
-
-// Workgroup -> tile. The dispatcher deals workgroups to the 8 XCDs round
-// robin; the remap gives each XCD a contiguous run of tiles, walked in groups
-// of 4 tile rows, column after column, so that the tiles an XCD runs at once
-// share their A panels (each read for all tile columns while it is in that
-// XCD's L2) and their B panels (four tile rows at a time; in the grouped form
-// the rows of one expert, which share its weight panel). Walking whole tile
-// columns instead re-reads every A panel once per column from HBM: measured
-// on the 64-expert MoE layer, the grouped launch took 545 us that way against
-// 457 us with groups of 2 to 16 tile rows.
-__device__ __forceinline__ void big_tile_of(int b, BigTiles t, int &bm, int &bn) {
-    const int num = t.mt * t.nt;
-    const int x = b & 7, per = num >> 3, rem = num & 7;
-    const int start = x * per + (x < rem ? x : rem);
-    const int tid = start + (b >> 3);                       // bijection onto [0, num)
-    constexpr int GM = 4;
-    const int grp = tid / (GM * t.nt);
-    const int first = grp * GM;
-    const int gsz = min(t.mt - first, GM);
-    const int in = tid - grp * GM * t.nt;
-    bm = first + in % gsz;
-    bn = in / gsz;
-}
-
 __device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
 
 // GROUPED: q holds R = M rows sorted by expert, rows [offsets[e], offsets[e+1])
@@ -101,7 +74,7 @@ __device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
 template <int OUT, bool GROUPED>
 __global__ void __launch_bounds__(512, 1)
 gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float *sw, int M, int N,
-                int K, void *y, BigTiles tiles, const int32_t *offsets, int E, int sw_stride) {
+                int K, void *y, TileGrid tiles, const int32_t *offsets, int E, int sw_stride) {
     constexpr bool CHN = per_channel<OUT>();             // one scale per row, applied at the end
     constexpr bool SCALES = !CHN && OUT != OUT_PARTIALS;   // per-group scales staged in LDS
     __shared__ __align__(16) int8_t lds[kBigLds];
@@ -111,86 +84,14 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, half = lane >> 5;
     const int G = K >> 7;
-    auto seg = [&](int e, int &lo, int &hi) {   // expert e's rows, clamped to [0, R]
-        lo = offsets[e];
-        hi = offsets[e + 1];
-        lo = lo < 0 ? 0 : (lo > M ? M : lo);
-        hi = hi < lo ? lo : (hi > M ? M : hi);
-    };
     int m0, row_end, bm, bn;
     if (GROUPED) {
-        // The tiles that exist are known only here. Each thread takes one expert of
-        // a chunk of 512 (one coalesced load of its bounds per chunk); a block-wide
-        // sum gives the tile rows that exist, and the first mt*nt workgroups take
-        // them (the dispatcher deals workgroups round-robin to the XCDs, so the idle
-        // surplus spreads evenly). A block-wide exclusive scan then finds the expert
-        // holding this workgroup's tile row. (Offsets that overlap, which the
-        // contract excludes, could count more than the host bound; the count is
-        // capped at it, so every tile stays inside [0, R).)
-        __shared__ int s_red[8];
-        __shared__ int s_hit[2];
-        auto tiles_of = [&](int e) {
-            if (e >= E) return 0;
-            int lo, hi;
-            seg(e, lo, hi);
-            return (hi - lo + kBigTM - 1) / kBigTM;
-        };
-        // inclusive scan of v over the 512 threads; also returns the block total
-        auto block_scan = [&](int v, int &total) {
-            int x = v;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o, kWave);
-                if (lane >= o) x += y;
-            }
-            if (lane == 63) s_red[wave] = x;
-            __syncthreads();
-            int before = 0;
-            total = 0;
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const int t = s_red[w];
-                before += w < wave ? t : 0;
-                total += t;
-            }
-            __syncthreads();
-            return x + before;
-        };
-        int64_t mt = 0;
-        for (int base = 0; base < E; base += 512) {
-            int tot;
-            block_scan(tiles_of(base + tid), tot);
-            mt += tot;
-        }
-        mt = mt < tiles.mt ? mt : tiles.mt;
-        if ((int64_t)blockIdx.x >= mt * tiles.nt) return;   // whole workgroup
-        tiles.mt = (int)mt;
-        big_tile_of(blockIdx.x, tiles, bm, bn);
-        // tile row bm -> (expert, 256-row block)
-        if (tid == 0) s_hit[0] = -1;
-        int run = 0;
-        for (int base = 0; base < E; base += 512) {
-            const int e = base + tid, c = tiles_of(e);
-            int tot;
-            const int incl = block_scan(c, tot) + run;
-            if (c > 0 && incl - c <= bm && bm < incl) {
-                s_hit[0] = e;
-                s_hit[1] = bm - (incl - c);
-            }
-            run += tot;
-            __syncthreads();
-            if (s_hit[0] >= 0 || run > bm) break;   // uniform: every thread reads the same
-        }
-        const int e = s_hit[0];
-        if (e < 0) return;   // unreachable: bm < mt
-        int lo, hi;
-        seg(e, lo, hi);
-        m0 = lo + s_hit[1] * kBigTM;
-        row_end = hi;
+        int e;
+        if (!grouped_tile<kBigTM>(offsets, E, M, tiles, e, m0, row_end, bm, bn)) return;
         qw += (int64_t)e * N * K;
         sw += (int64_t)e * N * G;
     } else {
-        big_tile_of(blockIdx.x, tiles, bm, bn);
+        xcd_tile_of(blockIdx.x, tiles, bm, bn);
         m0 = bm * kBigTM;
         row_end = M;
     }
@@ -510,7 +411,7 @@ hipError_t launch_big_t(const int8_t *q, const float *sa, const int8_t *qw, cons
     const int64_t mt = (M + kBigTM - 1) / kBigTM + (GROUPED ? E : 0), nt = (N + kBigTN - 1) / kBigTN;
     const int64_t total = mt * nt;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const BigTiles t{(int)mt, (int)nt};
+    const TileGrid t{(int)mt, (int)nt};
     gemm_big_kernel<OUT, GROUPED><<<dim3((unsigned)total), 512, 0, stream>>>(
         q, sa, qw, sw, M, N, K, y, t, offsets, E, sw_stride);
     return hipGetLastError();

@@ -31,4 +31,118 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
         reinterpret_cast<float *>(y)[idx] = v;
 }
 
+// Output tiles of a launch: mt tile rows x nt tile columns.
+struct TileGrid {
+    int mt, nt;
+};
+
+// Workgroup -> tile. The dispatcher deals workgroups to the 8 XCDs round
+// robin; the remap gives each XCD a contiguous run of tiles, walked in groups
+// of 4 tile rows, column after column, so that the tiles an XCD runs at once
+// share their A panels (each read for all tile columns while it is in that
+// XCD's L2) and their B panels (four tile rows at a time; in the grouped form
+// the rows of one expert, which share its weight panel).
+__device__ __forceinline__ void xcd_tile_of(int b, TileGrid t, int &bm, int &bn) {
+    const int num = t.mt * t.nt;
+    const int x = b & 7, per = num >> 3, rem = num & 7;
+    const int start = x * per + (x < rem ? x : rem);
+    const int tid = start + (b >> 3);                       // bijection onto [0, num)
+    constexpr int GM = 4;
+    const int grp = tid / (GM * t.nt);
+    const int first = grp * GM;
+    const int gsz = min(t.mt - first, GM);
+    const int in = tid - grp * GM * t.nt;
+    bm = first + in % gsz;
+    bn = in / gsz;
+}
+
+// The tile of this workgroup in a grouped launch of 512-thread workgroups:
+// rows [offsets[e], offsets[e+1]) of R sorted rows belong to expert e, tile
+// rows of TM rows are laid out expert after expert (a tile never spans two
+// experts), and the host sized the grid for the most tile rows any split of R
+// rows can need (tiles.mt). The tiles that exist are known only here. Each
+// thread takes one expert of a chunk of 512 (one coalesced load of its bounds
+// per chunk); a block-wide sum gives the tile rows that exist, and the first
+// mt*nt workgroups take them (the dispatcher deals workgroups round-robin to
+// the XCDs, so the idle surplus spreads evenly). A block-wide exclusive scan
+// then finds the expert holding this workgroup's tile row. (Offsets that
+// overlap, which the contract excludes, could count more than the host bound;
+// the count is capped at it, so every tile stays inside [0, R).) Returns false,
+// for the whole workgroup, when it has no tile.
+template <int TM>
+__device__ __forceinline__ bool grouped_tile(const int32_t *offsets, int E, int R, TileGrid tiles,
+                                             int &e_out, int &m0, int &row_end, int &bm,
+                                             int &bn) {
+    __shared__ int s_red[8];
+    __shared__ int s_hit[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    auto seg = [&](int e, int &lo, int &hi) {   // expert e's rows, clamped to [0, R]
+        lo = offsets[e];
+        hi = offsets[e + 1];
+        lo = lo < 0 ? 0 : (lo > R ? R : lo);
+        hi = hi < lo ? lo : (hi > R ? R : hi);
+    };
+    auto tiles_of = [&](int e) {
+        if (e >= E) return 0;
+        int lo, hi;
+        seg(e, lo, hi);
+        return (hi - lo + TM - 1) / TM;
+    };
+    // inclusive scan of v over the 512 threads; also returns the block total
+    auto block_scan = [&](int v, int &total) {
+        int x = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, kWave);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) s_red[wave] = x;
+        __syncthreads();
+        int before = 0;
+        total = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const int t = s_red[w];
+            before += w < wave ? t : 0;
+            total += t;
+        }
+        __syncthreads();
+        return x + before;
+    };
+    int64_t mt = 0;
+    for (int base = 0; base < E; base += 512) {
+        int tot;
+        block_scan(tiles_of(base + tid), tot);
+        mt += tot;
+    }
+    mt = mt < tiles.mt ? mt : tiles.mt;
+    if ((int64_t)blockIdx.x >= mt * tiles.nt) return false;
+    tiles.mt = (int)mt;
+    xcd_tile_of(blockIdx.x, tiles, bm, bn);
+    // tile row bm -> (expert, TM-row block)
+    if (tid == 0) s_hit[0] = -1;
+    int run = 0;
+    for (int base = 0; base < E; base += 512) {
+        const int e = base + tid, c = tiles_of(e);
+        int tot;
+        const int incl = block_scan(c, tot) + run;
+        if (c > 0 && incl - c <= bm && bm < incl) {
+            s_hit[0] = e;
+            s_hit[1] = bm - (incl - c);
+        }
+        run += tot;
+        __syncthreads();
+        if (s_hit[0] >= 0 || run > bm) break;   // uniform: every thread reads the same
+    }
+    const int e = s_hit[0];
+    if (e < 0) return false;   // unreachable: bm < mt
+    int lo, hi;
+    seg(e, lo, hi);
+    e_out = e;
+    m0 = lo + s_hit[1] * TM;
+    row_end = hi;
+    return true;
+}
+
 }  // namespace bsb

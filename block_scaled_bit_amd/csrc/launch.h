@@ -33,6 +33,11 @@ bool big_gemm_fits(int64_t K);
 hipError_t launch_gemm_big(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                            int M, int N, int K, void *y, int out, const int32_t *offsets, int E,
                            int sw_stride, hipStream_t stream);
+// gemm_mid.hip: 128x128 tiles for mid-sized M (same arguments and forms)
+bool mid_gemm_fits(int64_t K);
+hipError_t launch_gemm_mid(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
+                           int M, int N, int K, void *y, int out, const int32_t *offsets, int E,
+                           int sw_stride, hipStream_t stream);
 
 // gemm_packed.hip: weights in the matrix cores' operand order (M <= 64)
 hipError_t launch_repack_mfma(const int8_t *qw, int64_t N, int64_t K, int8_t *packed,

@@ -106,6 +106,7 @@ bsb_status bsb_quantize_act(const uint16_t *x_bf16, int64_t M, int64_t K,
  *   q   [M, K] int8, sa [M] float32       (output of bsb_quantize_act)
  *   qw  [N, K] int8, sw [N, G] float32    (weights, [out, in] layout)
  *   y   [M, N] BF16 bits or float32 per `out`
+ *   K   a multiple of 128 below 2^24 (also for the partials and grouped forms)
  */
 bsb_status bsb_gemm_w8a8_g128(const int8_t *q, const float *sa,
                               const int8_t *qw, const float *sw,
@@ -203,8 +204,10 @@ bsb_status bsb_gemm_w8a8_channel(const int8_t *q, const float *sa,
  *           y but never an out-of-bounds access.
  *   y       [R, N] BF16 bits or float32
  * The launch grid is sized from host values only (the row tiles any split of
- * R rows over E experts can need); with R >= 128*E the kernel uses 256-row
- * tiles, otherwise 128-row tiles. Neither choice changes a result bit.
+ * R rows over E experts can need); with R >= 128*E (and a 256x256 tile per
+ * CU) the kernel uses 256-row tiles, with R <= 32*E it walks each expert's
+ * rows in passes of 32, otherwise it uses 128-row tiles. No choice changes a
+ * result bit.
  */
 bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa,
                                       const int8_t *qw, const float *sw,

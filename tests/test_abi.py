@@ -61,6 +61,10 @@ def test_invalid_sizes_return_invalid_arg(L):
     assert L.bsb_decode_mxfp4(A, A, big, big, big, A, A, None) == INVALID
     assert L.bsb_gemm_w8a8_g128_partials(A, A, big, big, 1 << 20, A, None) == INVALID
     assert L.bsb_decode_fp8_block(A, A, 1 << 23, 1 << 13, 0, A, A, None) == INVALID   # 2^36
+    # K below 2^24 for the row-major W8A8 GEMMs (128-row panels, 32-bit offsets)
+    assert L.bsb_gemm_w8a8_g128(A, A, A, A, 4, 8, 1 << 24, A, 0, None) == INVALID
+    assert L.bsb_gemm_w8a8_g128_partials(A, A, 4, 8, 1 << 24, A, None) == INVALID
+    assert L.bsb_grouped_gemm_w8a8_g128(A, A, A, A, A, 1, 4, 8, 1 << 24, A, 0, None) == INVALID
     assert L.bsb_gather_rows(A, A, A, 4, 0, 128, A, A, None) == INVALID          # no tokens
     assert L.bsb_gather_rows(A, A, A, 4, 8, 100, A, A, None) == INVALID          # K % 128
     assert L.bsb_moe_combine(A, A, A, 4, 0, 16, 64, A, None) == INVALID          # topk 0
