@@ -51,6 +51,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W8A8-g128 GEMM TOPS & HBM GB/s (M=32 decode, M=4096 prefill), % roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COUNTER_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
 CSRC = os.path.join(ROOT, "block_scaled_bit_amd", "csrc")
@@ -427,8 +428,10 @@ def _copies(bytes_per_set, floor=1 << 30, cap=64):
     return max(1, min(cap, -(-floor // max(1, bytes_per_set)) + 1))
 
 
-def _rate(us, ops=None, byts=None, bound="hbm"):
-    """avg_us plus achieved TOPS / GB/s against the published peaks."""
+def _rate(us, ops=None, byts=None, bound="hbm", peak_tops=None):
+    """avg_us plus achieved TOPS / GB/s against the published peaks (the matrix
+    peak of the path's own type: INT8 unless peak_tops says otherwise)."""
+    peak_tops = INT8_PEAK_TOPS if peak_tops is None else peak_tops
     r = {"avg_us": round(us, 2), "bound": bound}
     t = us * 1e-6
     if byts is not None:
@@ -438,10 +441,12 @@ def _rate(us, ops=None, byts=None, bound="hbm"):
     if ops is not None:
         r["ops"] = int(ops)
         r["tops"] = round(ops / t / 1e12, 1)
-        r["mfma_frac"] = round(ops / t / 1e12 / INT8_PEAK_TOPS, 4)
+        r["mfma_frac"] = round(ops / t / 1e12 / peak_tops, 4)
+        if peak_tops != INT8_PEAK_TOPS:
+            r["peak_tops"] = peak_tops
     if ops is not None and byts is not None:
         # a kernel bound by both: the slower roofline over the measured time
-        r["frac"] = round(max(ops / (INT8_PEAK_TOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9)) / t, 4)
+        r["frac"] = round(max(ops / (peak_tops * 1e12), byts / (HBM_PEAK_GBS * 1e9)) / t, 4)
     else:
         r["frac"] = r.get("mfma_frac" if bound == "mfma" else "hbm_frac")
     return r
@@ -573,7 +578,8 @@ def extra_rows(torch, L, stream, dev, steps):
     tg = Row("w8a16 decode", sets, lambda p, st: _ok(
         L, L.bsb_gemm_w8a16_g128(p["x"], p["qw"], p["sw"], M, N, K, p["y"], 0, st))).time(
         torch, stream, steps, 3)
-    rows["w8a16_decode_32x8192x28672"] = _rate(tg * 1e3, ops=2 * M * N * K, byts=byts)
+    rows["w8a16_decode_32x8192x28672"] = _rate(tg * 1e3, ops=2 * M * N * K, byts=byts,
+                                               peak_tops=BF16_PEAK_TFLOPS)
     log(f"w8a16 decode: gemm {tg * 1e3:.1f} us")
     del sets, qw, sw
     torch.cuda.empty_cache()
@@ -586,9 +592,35 @@ def extra_rows(torch, L, stream, dev, steps):
         sets.append({k: v.data_ptr() for k, v in b.items()} | {"_keep": b})
     tg = Row("bf16 decode", sets, lambda p, st: _ok(
         L, L.bsb_gemm_bf16(p["x"], p["w"], M, N, K, p["y"], 0, st))).time(torch, stream, steps, 3)
-    rows["bf16_decode_32x8192x28672"] = _rate(tg * 1e3, ops=2 * M * N * K, byts=byts)
+    rows["bf16_decode_32x8192x28672"] = _rate(tg * 1e3, ops=2 * M * N * K, byts=byts,
+                                              peak_tops=BF16_PEAK_TFLOPS)
     log(f"bf16 decode: gemm {tg * 1e3:.1f} us")
     del sets, wb, x
+    torch.cuda.empty_cache()
+
+    # the same two routes at the prefill shape (BF16 matrix instructions, 128x128 tiles)
+    M, K, N = 4096, 8192, 8192
+    d = synth.linear_inputs(M, K, N, outlier_p=0.005, outlier_f=30.0, seed=0)
+    x, qw, sw = t(d["x"].view(np.int16)), t(d["qw"]), t(d["sw"])
+    wb = t((np.random.default_rng(0).standard_normal((N, K), dtype=np.float32) * 0.02)
+           ).to(torch.bfloat16).view(torch.int16)
+    y = torch.empty((M, N), dtype=torch.int16, device=dev)
+    p = {"x": x.data_ptr(), "qw": qw.data_ptr(), "sw": sw.data_ptr(), "w": wb.data_ptr(),
+         "y": y.data_ptr()}
+    ops = 2 * M * N * K
+    tg = Row("w8a16 prefill", [p], lambda p, st: _ok(
+        L, L.bsb_gemm_w8a16_g128(p["x"], p["qw"], p["sw"], M, N, K, p["y"], 0, st))).time(
+        torch, stream, 10, 3)
+    rows["w8a16_prefill_4096x8192x8192"] = _rate(
+        tg * 1e3, ops=ops, byts=2 * M * K + N * K + 4 * N * K // 128 + 2 * M * N, bound="mfma",
+        peak_tops=BF16_PEAK_TFLOPS)
+    tb = Row("bf16 prefill", [p], lambda p, st: _ok(
+        L, L.bsb_gemm_bf16(p["x"], p["w"], M, N, K, p["y"], 0, st))).time(torch, stream, 10, 3)
+    rows["bf16_prefill_4096x8192x8192"] = _rate(
+        tb * 1e3, ops=ops, byts=2 * M * K + 2 * N * K + 2 * M * N, bound="mfma",
+        peak_tops=BF16_PEAK_TFLOPS)
+    log(f"prefill 4096x8192x8192: w8a16 {tg * 1e3:.1f} us, bf16 {tb * 1e3:.1f} us")
+    del x, qw, sw, wb, y, p
     torch.cuda.empty_cache()
 
     # routed MoE layer: 4096 tokens, top-8 of 64 experts (Zipf, 4 empty), K=4096, N=2048

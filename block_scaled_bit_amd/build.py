@@ -23,7 +23,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsb.so")
-SOURCES = ["quant.hip", "decode.hip", "gemm.hip", "gemm_big.hip", "gemm_mid.hip", "gemm_packed.hip", "moe.hip", "attn.hip", "probe.hip", "api.cpp"]
+SOURCES = ["quant.hip", "decode.hip", "gemm.hip", "gemm_big.hip", "gemm_mid.hip", "gemm_a16.hip", "gemm_packed.hip", "moe.hip", "attn.hip", "probe.hip", "api.cpp"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -57,9 +57,6 @@ constexpr int64_t kMaxChannelK = 131072;
 // panel with 32-bit buffer offsets (128 * K + 128 < 2^31).
 constexpr int64_t kGemmKLimit = (int64_t)1 << 24;   // K must be below it
 
-// Rows of the BF16-activation GEMMs (the decode-shaped kernel).
-constexpr int64_t kMaxA16Rows = 64;
-
 // Experts per token accepted by the combine.
 constexpr int64_t kMaxTopk = 256;
 
@@ -262,11 +259,10 @@ bsb_status bsb_dequant_fp8_block_bf16(const uint8_t *w, const uint8_t *bs, int64
 
 namespace {
 
-// The BF16-activation GEMMs run the decode-shaped kernel: at most 64 rows, and
-// 128 weight rows of 2K bytes addressed with 32-bit offsets.
+// The BF16-activation GEMMs address 128 rows of 2K bytes (weights in the
+// decode-shaped kernel, activations in the tiled one) with 32-bit offsets.
 bsb_status a16_checks(int64_t M, int64_t N, int64_t K, bsb_out_dtype out) {
-    if (!dims_ok(M, N, K) || M > kMaxA16Rows || N * K > kMaxElems ||
-        (int64_t)256 * K >= ((int64_t)1 << 31))
+    if (!dims_ok(M, N, K) || N * K > kMaxElems || (int64_t)256 * K >= ((int64_t)1 << 31))
         return BSB_ERR_INVALID_ARG;
     if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
     return BSB_OK;

@@ -658,6 +658,11 @@ hipError_t launch_a16_rows(const uint16_t *x, const void *w, const float *sw, in
 
 hipError_t launch_gemm_a16(const uint16_t *x, const void *w, const float *sw, int64_t M,
                            int64_t N, int64_t K, void *y, int out, int am, hipStream_t stream) {
+    // beyond the decode-shaped range: 128x128 tiles (gemm_a16.hip)
+    if (M > 64) {
+        if (!a16_tiles_fit(K)) return hipErrorInvalidValue;   // excluded by the C ABI's checks
+        return launch_gemm_a16_tiles(x, w, sw, (int)M, (int)N, (int)K, y, out, am, stream);
+    }
     if (am == 1) {
         if (out == OUT_BF16)
             return launch_a16_rows<OUT_BF16, AM_W8A16>(x, w, sw, (int)M, (int)N, (int)K, y, stream);

@@ -39,6 +39,12 @@ hipError_t launch_gemm_mid(const int8_t *q, const float *sa, const int8_t *qw, c
                            int M, int N, int K, void *y, int out, const int32_t *offsets, int E,
                            int sw_stride, hipStream_t stream);
 
+// gemm_a16.hip: BF16 activations beyond 64 rows, 128x128 tiles; am 1 = INT8
+// weights with group scales (W8A16), 2 = BF16 weights
+bool a16_tiles_fit(int64_t K);
+hipError_t launch_gemm_a16_tiles(const uint16_t *x, const void *w, const float *sw, int M, int N,
+                                 int K, void *y, int out, int am, hipStream_t stream);
+
 // gemm_packed.hip: weights in the matrix cores' operand order (M <= 64)
 hipError_t launch_repack_mfma(const int8_t *qw, int64_t N, int64_t K, int8_t *packed,
                               hipStream_t stream);

@@ -219,8 +219,9 @@ bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa,
  * The routes the pages run beside W8A8 ([P1] sec. 1-2): weight-only INT8
  * ("WNA16": INT8 weights with the per-group scales above, BF16 activations)
  * and BF16 weights dequantised from FP8 at load time. Both take BF16
- * activations as they are (no activation quantisation) and are built for
- * decode-shaped M:
+ * activations as they are (no activation quantisation); up to 64 rows the
+ * weights are streamed once (decode-shaped M), beyond that 128x128 output
+ * tiles are used:
  *     W8A16: y[m,n] = sum_g sw[n,g] * sum_{k in g} x[m,k] * qw[n,k]
  *     BF16:  y[m,n] = sum_k x[m,k] * w[n,k]
  * Products are exact in float32; the matrix core sums each group's 128
@@ -228,12 +229,12 @@ bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa,
  * order (a fused multiply-add with sw[n,g], or a float32 add), so results are
  * within (127 + G) * 2^-24 * sum |terms| of the exact value and do not depend
  * on the launch shape.
- *   x_bf16  [M, K] BF16 bits, 0 <= M <= 64
+ *   x_bf16  [M, K] BF16 bits
  *   qw      [N, K] int8, sw [N, G] float32   (W8A16)
  *   w_bf16  [N, K] BF16 bits                 (BF16)
  *   y       [M, N] BF16 bits or float32 per `out`
  * K a multiple of 128 and below 2^23; other limits and errors as
- * bsb_gemm_w8a8_g128; M > 64 -> BSB_ERR_INVALID_ARG.
+ * bsb_gemm_w8a8_g128.
  */
 bsb_status bsb_gemm_w8a16_g128(const uint16_t *x_bf16, const int8_t *qw, const float *sw,
                                int64_t M, int64_t N, int64_t K,

@@ -144,12 +144,16 @@ def test_channel_gemm_argument_checks(L):
 
 
 def test_bf16_activation_routes_argument_checks(L):
-    """W8A16 / BF16 GEMMs: at most 64 rows, K a multiple of 128 below 2^23; the FP8 -> BF16
+    """W8A16 / BF16 GEMMs: K a multiple of 128 below 2^23, any number of rows; the FP8 -> BF16
     dequantisation: the decoder's size and dialect rules."""
     w16, b16, dq = L.bsb_gemm_w8a16_g128, L.bsb_gemm_bf16, L.bsb_dequant_fp8_block_bf16
-    assert w16(A, A, A, 65, 8, 128, A, 0, None) == INVALID          # M > 64
-    assert b16(A, A, 65, 8, 128, A, 0, None) == INVALID
+    assert w16(A, A, A, -1, 8, 128, A, 0, None) == INVALID
+    assert b16(A, A, 1 << 30, 8, 128, A, 0, None) == INVALID        # rows below 2^30
     assert w16(A, A, A, 4, 8, 1 << 23, A, 0, None) == INVALID       # 256*K >= 2^31
+    assert w16(A, A, A, 100, 8, 1 << 23, A, 0, None) == INVALID
+    if not torch.cuda.is_available():
+        assert w16(A, A, A, 65, 8, 128, A, 0, None) == UNSUPPORTED   # tiled kernel beyond 64 rows
+        assert b16(A, A, 65, 8, 128, A, 0, None) == UNSUPPORTED
     assert b16(A, A, 4, 8, 130, A, 0, None) == INVALID
     assert w16(A, A, A, 4, 8, 128, A, 3, None) == INVALID           # out enum
     assert w16(A, None, A, 4, 8, 128, A, 0, None) == INVALID

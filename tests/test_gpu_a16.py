@@ -73,6 +73,55 @@ def test_bf16_ragged(M, N, K):
     _check(_bf16(cfg["x"], wb, torch.bfloat16, d), y64, mag, K, True)
 
 
+# beyond 64 rows: 128x128 tiles; partial tiles in M and N, group counts 1 to 17
+# (the stage loop's unrolled body and its two-stage remainder)
+TILED = [(65, 1, 128), (100, 257, 384), (130, 128, 256), (257, 100, 1152), (600, 300, 640),
+         (1000, 520, 2176)]
+
+
+@pytest.mark.parametrize("M,N,K", TILED)
+def test_w8a16_tiled_ragged(M, N, K):
+    test_w8a16_ragged(M, N, K)
+
+
+@pytest.mark.parametrize("M,N,K", TILED)
+def test_bf16_tiled_ragged(M, N, K):
+    test_bf16_ragged(M, N, K)
+
+
+@pytest.mark.parametrize("route", ["w8a16", "bf16"])
+def test_prefill_config_every_tile_row_and_column(route):
+    """The prefill-shaped linear (4096 x 8192 x 8192) on both BF16-activation routes: one
+    whole output row in every 128-row tile row and one whole column in every 128-column
+    tile, against the float64 definition with the order-independent bound."""
+    d = require_gpu()
+    say(f"{route} prefill M=4096 K=8192 N=8192 (a row per tile row, a column per tile)")
+    cfg = synth.linear_config("prefill")
+    x = cfg["x"]
+    xd = dev_bf16(x, d)
+    rows = np.array([128 * t + (t * 37 + 5) % 128 for t in range(32)])
+    cols = np.array([128 * t + (t * 53 + 11) % 128 for t in range(64)])
+    if route == "w8a16":
+        qw, sw = cfg["qw"], cfg["sw"]
+        y32 = host(bsb.gemm_w8a16_g128(xd, dev(qw, d), dev(sw, d), out_dtype=torch.float32))
+        yb = host(bsb.gemm_w8a16_g128(xd, dev(qw, d), dev(sw, d)))
+        ref_rows = gemm_w8a16_ref(x[rows], qw, sw)
+        ref_cols = gemm_w8a16_ref(x, qw[cols], sw[cols])
+    else:
+        rng = np.random.default_rng(4)
+        wb = synth.to_bf16_bits(rng.standard_normal((8192, 8192), dtype=np.float32) *
+                                np.float32(0.02))
+        wd = dev_bf16(wb, d)
+        y32 = host(bsb.gemm_bf16(xd, wd, out_dtype=torch.float32))
+        yb = host(bsb.gemm_bf16(xd, wd))
+        ref_rows = gemm_bf16_ref(x[rows], wb)
+        ref_cols = gemm_bf16_ref(x, wb[cols])
+    _check(y32[rows], *ref_rows, 8192, False)
+    _check(yb[rows], *ref_rows, 8192, True)
+    _check(y32[:, cols], *ref_cols, 8192, False)
+    _check(yb[:, cols], *ref_cols, 8192, True)
+
+
 def test_w8a16_decode_config():
     """The decode-shaped linear (32 x 8192 x 28672) on its INT8 weights, BF16 activations
     as they are; every output checked."""
