@@ -162,12 +162,31 @@ def timed(torch, L, lin, stream, steps, warmup, what=("quant", "gemm")):
     return start.elapsed_time(end) / steps, wall / steps
 
 
+WARM_MS = 25.0   # untimed work before each timed row: the clock settles under load
+
+
+def warm_up(torch, call, calls, ms=WARM_MS):
+    """At least `calls` untimed calls, and more until `ms` of GPU time have passed
+    (the first milliseconds of a workload run at a lower, rising clock)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    done = 0
+    while True:
+        for _ in range(max(1, calls - done)):
+            call()
+            done += 1
+        b.record()
+        torch.cuda.synchronize()
+        if a.elapsed_time(b) >= ms or done >= 10000:
+            return
+
+
 def percall(torch, call, n, warmup):
     """Per-call durations: a HIP event pair around each of n calls on the launch
-    stream (torch's current stream), after `warmup` untimed calls. Returns a dict
-    of median / p10 / p90 / mean in microseconds."""
-    for _ in range(warmup):
-        call()
+    stream (torch's current stream), after `warmup` untimed calls (and at least
+    WARM_MS of untimed work). Returns a dict of median / p10 / p90 / mean in
+    microseconds."""
+    warm_up(torch, call, warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
     torch.cuda.synchronize()
@@ -246,10 +265,34 @@ def measured_peaks(torch, L, stream, dev, a_bytes=None, b_bytes=None):
     def hbm():
         _ok(L, L.bsb_probe_hbm_read(src.data_ptr(), nbytes, out.data_ptr(), stream))
     h = percall(torch, hbm, 10, 2)
-    del src
+    # the same read at the decode GEMM's size (its weights: 232 MiB), windows of the
+    # 2 GiB buffer in turn so that no call finds its bytes in a cache
+    small = 232 << 20
+    win = [0]
+
+    def hbm_small():
+        off = (win[0] % (nbytes // small)) * small
+        win[0] += 1
+        _ok(L, L.bsb_probe_hbm_read(src.data_ptr() + off, small, out.data_ptr(), stream))
+    hs = percall(torch, hbm_small, 10, 2)
+    # a read + write stream, as the decoders run: 512 MiB copied by the copy probe
+    cb = 512 << 20
+    dst = torch.empty((cb,), dtype=torch.uint8, device=dev)
+    cwin = [0]
+
+    def copy():
+        off = (cwin[0] % (nbytes // cb)) * cb
+        cwin[0] += 1
+        _ok(L, L.bsb_probe_hbm_copy(src.data_ptr() + off, dst.data_ptr(), cb, stream))
+    cs = percall(torch, copy, 10, 2)
+    del src, dst
     torch.cuda.empty_cache()
     res = {"hbm_read_gbs": round(nbytes / (h["median_us"] * 1e-6) / 1e9, 1),
-           "hbm_read_probe": "2 GiB streamed once per call, median of 10 calls"}
+           "hbm_read_probe": "2 GiB streamed once per call, median of 10 calls",
+           "hbm_read_gbs_232mib": round(small / (hs["median_us"] * 1e-6) / 1e9, 1),
+           "copy_gbs": round(2 * cb / (cs["median_us"] * 1e-6) / 1e9, 1),
+           "copy_probe": ("bsb_probe_hbm_copy of 512 MiB windows of the 2 GiB buffer (read + "
+                          "write bytes, non-temporal), median of 10")}
     rounds = 512   # about a millisecond of matrix-core work per call
     ops = 2048 * rounds * 64 * 65536   # 131072 threads = 2048 waves of 64 MFMAs per round
 
@@ -406,8 +449,12 @@ class Row:
         """Mean ms per pass over `steps` back-to-back passes between HIP events
         recorded on the launch stream."""
         n = len(self.sets)
-        for i in range(warmup):
-            self.call(self.sets[i % n], stream)
+        k = [0]
+
+        def one():
+            self.call(self.sets[k[0] % n], stream)
+            k[0] += 1
+        warm_up(torch, one, warmup)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record()
@@ -1069,12 +1116,23 @@ def main():
         if out["prefill"]["counters"]:
             out["prefill"]["mfma_util"] = out["prefill"]["counters"].get("mfma_util")
         out["measured_peaks"] = peaks
-        out["roofline"]["frac_of_measured_hbm"] = round(achieved / peaks["hbm_read_gbs"], 4)
+        # against the read probe at the same size (its weights' 232 MiB), and at 2 GiB
+        out["roofline"]["frac_of_measured_hbm"] = round(achieved / peaks["hbm_read_gbs_232mib"], 4)
+        out["roofline"]["frac_of_measured_hbm_2gib"] = round(achieved / peaks["hbm_read_gbs"], 4)
         del pre
         torch.cuda.empty_cache()
 
     if not args.no_rows:
         out["rows"] = extra_rows(torch, L, stream, dev, max(10, min(50, args.steps // 4)))
+        peaks = out.get("measured_peaks")
+        if peaks:
+            # streams against what this part sustains for the same kind of stream:
+            # the decoders read and write (the copy probe), attention reads
+            for k, r in out["rows"].items():
+                if k.startswith("blockfmt_decode") or k.startswith("blockfmt_dequant"):
+                    r["frac_of_measured_copy"] = round(r["gbs"] / peaks["copy_gbs"], 4)
+                elif k.startswith("kv_") and "attention" in k:
+                    r["frac_of_measured_hbm"] = round(r["gbs"] / peaks["hbm_read_gbs"], 4)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

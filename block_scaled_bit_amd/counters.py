@@ -107,6 +107,12 @@ TRAFFIC_KEYS = {
     "moe_grouped": ("gemm_big_kernel<0, true>", 786432, 787611908),
     "kv_attention": ("attn_split_kernel<0, 8, 1>", 131072, 277872640),
     "kv_attention_bf16": ("attn_split_kernel<1, 8, 1>", 131072, 537919488),
+    "gemm_mid_m1024": ("gemm_mid_kernel<0, false>", 131072, 46010368),
+    "w8a16_prefill": ("gemm_a16_kernel<0, 1>", 1048576, 203423744),
+    "bf16_prefill": ("gemm_a16_kernel<0, 2>", 1048576, 268435456),
+    "decode_fp8": ("decode_fp8_block_kernel<false>", 917504, 59639552),
+    "decode_fp8_layer": ("decode_fp8_block_kernel<false>", 3670016, 238558208),
+    "decode_mxfp4": ("decode_mxfp4_kernel<false>", 1048576, 104857600),
 }
 CAL_BYTES = 512 << 20
 

@@ -516,4 +516,14 @@ bsb_status bsb_probe_hbm_read(const void *src, int64_t bytes, int32_t *out, void
     return finish(bsb::launch_probe_hbm_read(src, bytes, out, as_stream(stream)));
 }
 
+bsb_status bsb_probe_hbm_copy(const void *src, void *dst, int64_t bytes, void *stream) {
+    const int64_t sweep = (int64_t)16 * bsb::kProbeThreads;
+    if (bytes < sweep || bytes % sweep || bytes > ((int64_t)1 << 40)) return BSB_ERR_INVALID_ARG;
+    if (!src || !dst) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(src) || !aligned16(dst)) return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_probe_hbm_copy(src, dst, bytes, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -108,6 +108,7 @@ hipError_t launch_probe_mfma_i8(const int8_t *a, const int8_t *b, int64_t bytes,
                                 int32_t *out, hipStream_t stream);
 hipError_t launch_probe_hbm_read(const void *src, int64_t bytes, int32_t *out,
                                  hipStream_t stream);
+hipError_t launch_probe_hbm_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
 // The BF16 KV cache of the comparison route (same blocks, 2-byte elements, no scales).
 hipError_t launch_kv_cache_write_bf16(const uint16_t *k, const uint16_t *v, const int32_t *seq,

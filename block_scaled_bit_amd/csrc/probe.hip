@@ -9,6 +9,9 @@
 //    operands allow.
 //  * hbm_read_probe_kernel: a streaming read of a buffer larger than the
 //    last-level cache, 16 bytes per lane, four loads in flight, non-temporal.
+//  * hbm_copy_probe_kernel: the same walk copying into a second buffer
+//    (non-temporal stores): the rate of a read + write stream, the kind the
+//    weight decoders run.
 #include "device_common.h"
 #include "launch.h"
 
@@ -79,7 +82,41 @@ hbm_read_probe_kernel(const void *src, uint32_t sweeps, int32_t *out) {
     out[gt] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Same walk as the read probe; every chunk read is stored at the same offset of dst.
+__global__ void __launch_bounds__(256)
+hbm_copy_probe_kernel(const void *src, void *dst, uint32_t sweeps) {
+    const uint32_t gt = blockIdx.x * 256u + threadIdx.x;
+    for (uint32_t w = 0; w < sweeps; w += 512) {
+        const uint32_t n = sweeps - w < 512 ? sweeps - w : 512;
+        const uint64_t base = (uint64_t)w * kProbeThreads;   // in 16-byte chunks
+        const v4u *s4 = reinterpret_cast<const v4u *>(src) + base;
+        v4u *d4 = reinterpret_cast<v4u *>(dst) + base;
+        uint32_t s = 0;
+        for (; s + 4 <= n; s += 4) {
+            const v4u v0 = __builtin_nontemporal_load(s4 + gt + (s + 0) * kProbeThreads);
+            const v4u v1 = __builtin_nontemporal_load(s4 + gt + (s + 1) * kProbeThreads);
+            const v4u v2 = __builtin_nontemporal_load(s4 + gt + (s + 2) * kProbeThreads);
+            const v4u v3 = __builtin_nontemporal_load(s4 + gt + (s + 3) * kProbeThreads);
+            __builtin_nontemporal_store(v0, d4 + gt + (s + 0) * kProbeThreads);
+            __builtin_nontemporal_store(v1, d4 + gt + (s + 1) * kProbeThreads);
+            __builtin_nontemporal_store(v2, d4 + gt + (s + 2) * kProbeThreads);
+            __builtin_nontemporal_store(v3, d4 + gt + (s + 3) * kProbeThreads);
+        }
+        for (; s < n; ++s)
+            __builtin_nontemporal_store(__builtin_nontemporal_load(s4 + gt + s * kProbeThreads),
+                                        d4 + gt + s * kProbeThreads);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_probe_hbm_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream) {
+    hbm_copy_probe_kernel<<<dim3(kProbeThreads / 256), 256, 0, stream>>>(
+        src, dst, (uint32_t)(bytes / (16 * (int64_t)kProbeThreads)));
+    return hipGetLastError();
+}
 
 hipError_t launch_probe_mfma_i8(const int8_t *a, const int8_t *b, int64_t bytes, int64_t rounds,
                                 int32_t *out, hipStream_t stream) {

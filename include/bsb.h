@@ -489,6 +489,10 @@ bsb_status bsb_attention_decode_bf16kv(const uint16_t *q_bf16,
  * loads in flight per lane, non-temporal.
  *   bytes a multiple of 16 * BSB_PROBE_THREADS (2 MiB), at most 2^40
  * out [BSB_PROBE_THREADS] int32 (written). Errors as bsb_gemm_w8a8_g128.
+ * bsb_probe_hbm_copy: the same walk copying src to dst (`bytes` read and
+ * `bytes` written, non-temporal loads and stores): a read + write stream.
+ * Sizes as bsb_probe_hbm_read; src and dst must not overlap (the copied values
+ * are otherwise unspecified); nothing is written to `out`.
  */
 #define BSB_PROBE_THREADS 131072
 
@@ -496,6 +500,8 @@ bsb_status bsb_probe_mfma_i8(const int8_t *a, const int8_t *b, int64_t bytes, in
                              int32_t *out, void *stream);
 
 bsb_status bsb_probe_hbm_read(const void *src, int64_t bytes, int32_t *out, void *stream);
+
+bsb_status bsb_probe_hbm_copy(const void *src, void *dst, int64_t bytes, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *bsb_status_string(bsb_status s);

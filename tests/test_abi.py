@@ -258,9 +258,14 @@ def test_probe_argument_checks(L):
     assert hb(A, sweep + 16, A, None) == INVALID
     assert hb(None, sweep, A, None) == INVALID
     assert hb(U, sweep, A, None) == MISALIGNED
+    cp = L.bsb_probe_hbm_copy
+    assert cp(A, A, sweep + 16, None) == INVALID
+    assert cp(A, None, sweep, None) == INVALID
+    assert cp(A, U, sweep, None) == MISALIGNED
     if not torch.cuda.is_available():
         assert mf(A, A, 1024, 1, A, None) == UNSUPPORTED
         assert hb(A, 2 * sweep, A, None) == UNSUPPORTED
+        assert cp(A, A, 2 * sweep, None) == UNSUPPORTED
 
 
 def test_bf16_kv_cache_argument_checks(L):
