@@ -11,12 +11,14 @@
 //   k_cache [B, Hkv, T/16, 2048] INT8: 16-token blocks; token tau of a block,
 //           dimension d at byte ((d/16)%2)*1024 + ((d/32)*16 + tau)*16 + d%16
 //   v_cache [B, Hkv, T/32, 4096] INT8: 32-token blocks; token tau of a block,
-//           dimension d at byte (((tau%16)/4)*16 + d%16)*64 + (d/16)*8 + (tau/16)*4 + tau%4
+//           dimension d at byte (d/32)*1024 + (((tau%16)/4)*16 + d%16)*16 +
+//           ((d/16)%2)*8 + (tau/16)*4 + tau%4
 //   k_scale, v_scale [B, Hkv, T] float32
 // Both block orders are the matrix cores' operand orders (lane l of a wave
-// reads bytes 16l .. 16l+15 of each 1 KB half of a K block and bytes 64l ..
-// 64l+63 of a V block), so every load instruction reads 1 KB contiguous and
-// nothing is transposed.
+// reads bytes 16l .. 16l+15 of each 1 KB quarter or half of a block), so every
+// load instruction reads 1 KB contiguous and nothing is transposed. (A V
+// order in which each lane's 64 bytes were contiguous made every load
+// instruction touch 4 KB at a 64-byte stride; measured 1-2 % slower.)
 //
 // Decode attention (one query token per sequence, grouped-query heads, up to
 // 16 query heads per KV head): a workgroup of 8 waves takes a split of the
@@ -67,8 +69,12 @@ __device__ __forceinline__ int kblk_off(int tau, int d) {
     return ((d >> 4) & 1) * 1024 + ((d >> 5) * 16 + tau) * 16 + (d & 15);
 }
 
+// byte of (token tau in a 32-token block, dim d) in a 4 KB V block: lane
+// 16((tau%16)/4) + d%16 holds, in quarter d/32 of the block, the 16 bytes of
+// dims d and d+16 (of that 32-dim slab) for its tokens 4 (tau/16) + tau%4
 __device__ __forceinline__ int vblk_off(int tau, int d) {
-    return ((((tau & 15) >> 2) * 16 + (d & 15)) * 64) + (d >> 4) * 8 + (tau >> 4) * 4 + (tau & 3);
+    return (d >> 5) * 1024 + ((((tau & 15) >> 2) * 16 + (d & 15)) * 16) + ((d >> 4) & 1) * 8 +
+           (tau >> 4) * 4 + (tau & 3);
 }
 
 // The BF16 cache of the comparison route keeps the same blocks with 2-byte
@@ -221,7 +227,7 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
     const __amdgpu_buffer_rsrc_t rv =
         make_rsrc(reinterpret_cast<const uint8_t *>(vc) + (int64_t)bh * tb, tb);
     const uint32_t kvo = (uint32_t)lane * 16;
-    const uint32_t vvo = (uint32_t)lane * (I8 ? 64 : 16);
+    const uint32_t vvo = (uint32_t)lane * 16;
 
     auto load = [&](KvChunk<KVT> &ch, int r) {
         const int t0 = t0_of(r);
@@ -237,7 +243,7 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    ch.vd[s][j] = buf_load16s(rv, vvo, ok ? so + s * (kVBlk * kHD) + 16 * j : kOOB);
+                    ch.vd[s][j] = buf_load16s(rv, vvo, ok ? so + s * (kVBlk * kHD) + 1024 * j : kOOB);
             const __amdgpu_buffer_rsrc_t rks = make_rsrc(ks + (int64_t)bh * T, (uint32_t)T * 4);
             const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vs + (int64_t)bh * T, (uint32_t)T * 4);
             const uint32_t ss = ok ? (uint32_t)t0 * 4 : kOOB;

@@ -363,7 +363,8 @@ bsb_status bsb_moe_combine(const uint16_t *y, const int32_t *row_of_pair,
  *           ((d/16)%2)*1024 + ((d/32)*16 + tau)*16 + d%16
  *   v_cache [B, Hkv, T/32, 4096] int8: blocks of 32 tokens; token tau of a
  *           block and dimension d sit at byte
- *           (((tau%16)/4)*16 + d%16)*64 + (d/16)*8 + (tau/16)*4 + tau%4
+ *           (d/32)*1024 + (((tau%16)/4)*16 + d%16)*16 + ((d/16)%2)*8 +
+ *           (tau/16)*4 + tau%4
  *   k_scale, v_scale [B, Hkv, T] float32
  * The caller allocates and owns every buffer; nothing is written outside the
  * slots named by (seq, pos).

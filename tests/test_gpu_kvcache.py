@@ -24,7 +24,8 @@ _d = np.arange(D)[None, :]
 _kt = np.arange(KB)[:, None]
 K_OFF = ((_d // 16) % 2) * 1024 + ((_d // 32) * 16 + _kt) * 16 + _d % 16
 _tau = np.arange(VB)[:, None]
-V_OFF = (((_tau % 16) // 4) * 16 + _d % 16) * 64 + (_d // 16) * 8 + (_tau // 16) * 4 + _tau % 4
+V_OFF = ((_d // 32) * 1024 + (((_tau % 16) // 4) * 16 + _d % 16) * 16 + ((_d // 16) % 2) * 8 +
+         (_tau // 16) * 4 + _tau % 4)
 
 
 def k_encode(kc):
