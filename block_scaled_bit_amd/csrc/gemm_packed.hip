@@ -346,6 +346,115 @@ gemm_packed_narrow_kernel(const int8_t *q, const float *sa, const int8_t *packed
         }
 }
 
+// Narrow weights, K split across the waves of a workgroup: KW waves share one
+// 16-row block, wave w taking the groups g = KW*t + w (t = 0, 1, ...), each
+// streaming its weights, activations and scales PD of its groups ahead like
+// the one-wave kernel above (KW times the bytes in flight per block). The
+// float32 fold must still run over g in ascending order for every output:
+// after each round t every wave writes its group's INT32 partials and scales to
+// LDS (double-buffered), one barrier, and then each wave folds all KW groups of
+// the round, in order, into its own share of the block's outputs (MB of the
+// 4*MB accumulator positions of every lane), which it stores at the end.
+// Groups past the end read zeros and add fmaf(0, 0, acc) = acc.
+template <int MB, int KW, int OUT, bool NT>
+__global__ void __launch_bounds__(64 * KW)
+gemm_packed_split_kernel(const int8_t *q, const float *sa, const int8_t *packed, const float *sw,
+                         int M, int N, int K, void *y) {
+    static_assert(KW == 4, "the KW waves' shares cover the 4*MB positions of a lane");
+    constexpr int PD = packed_depth<MB>();
+    constexpr int NP = 4 * MB;   // accumulator positions per lane: (token block i, row r)
+    static_assert((3 + 2 * MB) * PD <= 63, "more loads than a wave can have outstanding");
+    __shared__ __align__(16) int32_t xp[2][KW][64][NP];   // partials: [buffer][wave][lane][pos]
+    __shared__ float xs[2][KW][16];                        // scales: [buffer][wave][col]
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nb = blockIdx.x;                // N is a multiple of 16: every block exists
+    const int G = K / 128;
+    const int rounds = (G + KW - 1) / KW;
+    const int col = lane & 15, slot = lane >> 4;
+    const auto wr = make_rsrc(packed + (int64_t)nb * K * 16, (uint32_t)(K * 16));
+    const auto ar = make_rsrc(q, (uint32_t)(M * K));   // rows >= M read zero
+    const auto sr = make_rsrc(sw + (int64_t)nb * 16 * G, (uint32_t)(16 * G * 4));
+    const uint32_t wl = (uint32_t)lane * 16;
+    const uint32_t sl = (uint32_t)(col * G * 4);
+    uint32_t al[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) al[i] = (uint32_t)((i * 16 + col) * K + slot * 16);
+
+    v4i w[PD][2];
+    v4i a[PD][2][MB];
+    float s[PD];
+    // this wave's t-th group (g = KW*t + wv; past the end: zeros, no bytes)
+    auto load_wa = [&](int d, int t) {
+        const int g = KW * t + wv;
+        const bool in = g < G;
+        const uint32_t so = in ? (uint32_t)g * 2048u : kOOB;
+        w[d][0] = buf_load16s<NT ? kNonTemporal : 0>(wr, wl, so);
+        w[d][1] = buf_load16s<NT ? kNonTemporal : 0>(wr, wl + 1024, so);
+        const uint32_t ao = in ? (uint32_t)g * 128u : kOOB;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            a[d][0][i] = buf_load16s(ar, al[i], ao);
+            a[d][1][i] = buf_load16s(ar, al[i] + 64, ao);
+        }
+    };
+    auto load_s = [&](int d, int t) {
+        const int g = KW * t + wv;
+        s[d] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             sr, (int)sl, g < G ? g * 4 : (int)kOOB, 0));
+    };
+    float facc[MB];   // this wave's share: positions MB*wv .. MB*wv + MB-1
+#pragma unroll
+    for (int p = 0; p < MB; ++p) facc[p] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < PD; ++d) {   // issued in group order
+        load_wa(d, d);
+        load_s(d, d);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int t0 = 0; t0 < rounds; t0 += PD) {
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+            const int t = t0 + d;
+            if (t >= rounds) break;   // uniform over the workgroup
+            v4i acc[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d][0][i], w[d][0], v4i{0, 0, 0, 0},
+                                                               0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d][1][i], w[d][1], acc[i], 0, 0,
+                                                               0);
+            }
+            const int b = t & 1;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                *reinterpret_cast<v4i *>(&xp[b][wv][lane][4 * i]) = acc[i];
+            if (lane < 16) xs[b][wv][lane] = s[d];
+            load_wa(d, t + PD);
+            load_s(d, t + PD);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            // fold the round's KW groups in ascending order into this wave's share
+#pragma unroll
+            for (int u = 0; u < KW; ++u) {
+                const float su = xs[b][u][col];
+#pragma unroll
+                for (int p = 0; p < MB; ++p)
+                    facc[p] = __builtin_fmaf((float)xp[b][u][lane][MB * wv + p], su, facc[p]);
+            }
+        }
+    }
+    const int n = nb * 16 + col;
+#pragma unroll
+    for (int p = 0; p < MB; ++p) {
+        const int pos = MB * wv + p, i = pos >> 2, r = pos & 3;
+        const int m = i * 16 + slot * 4 + r;
+        if (m < M) store_packed_out<OUT>(y, (int64_t)m * N + n, facc[p] * sa[m]);
+    }
+}
+
 constexpr int kPackedCUs = 256;
 
 template <int NW, int OUT>
@@ -408,8 +517,21 @@ template <int MB, int OUT>
 hipError_t launch_packed_mb(const int8_t *q, const float *sa, const int8_t *packed,
                             const float *sw, int M, int N, int K, void *y, hipStream_t stream) {
     const int64_t blocks16 = N / 16;
-    if (blocks16 <= kPackedCUs) {   // narrow: one wave per block, activations from L2
+    if (blocks16 <= kPackedCUs) {   // narrow: at most one 16-row block per CU
         const bool nt = (int64_t)N * K >= ((int64_t)1 << 27);
+        // up to 16 tokens, or few groups, the K split across four waves (measured at
+        // N = 2048-4096: M = 1 12 -> 6 us, M = 16 12.2 -> 10 us, K = 1152 11.6 -> 6 us);
+        // more tokens on long K run faster on one wave (M = 32, K = 7168: 12.2 against
+        // 13.7 us, the per-round exchange and barrier costing more than they hide)
+        if (MB == 1 || K / 128 <= 16) {
+            if (nt)
+                gemm_packed_split_kernel<MB, 4, OUT, true><<<(unsigned)blocks16, 256, 0, stream>>>(
+                    q, sa, packed, sw, M, N, K, y);
+            else
+                gemm_packed_split_kernel<MB, 4, OUT, false><<<(unsigned)blocks16, 256, 0, stream>>>(
+                    q, sa, packed, sw, M, N, K, y);
+            return hipGetLastError();
+        }
         if (nt)
             gemm_packed_narrow_kernel<MB, OUT, true><<<(unsigned)blocks16, 64, 0, stream>>>(
                 q, sa, packed, sw, M, N, K, y);
