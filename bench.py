@@ -1124,6 +1124,26 @@ def main():
 
     if not args.no_rows:
         out["rows"] = extra_rows(torch, L, stream, dev, max(10, min(50, args.steps // 4)))
+        # the committed counter runs of these rows' kernels (null once the sources change)
+        for key, ck, tk in (
+                ("moe_4096tok_top8_64e_grouped", None, "moe_grouped"),
+                ("w8a16_prefill_4096x8192x8192", "gemm_a16_kernel<0, 1> [grid 1048576]",
+                 "w8a16_prefill"),
+                ("bf16_prefill_4096x8192x8192", "gemm_a16_kernel<0, 2> [grid 1048576]",
+                 "bf16_prefill"),
+                ("blockfmt_gemm_m1024_4096x7168", "gemm_mid_kernel<0, false> [grid 131072]",
+                 "gemm_mid_m1024"),
+                ("blockfmt_decode_fp8_ocp_4096x7168", None, "decode_fp8"),
+                ("blockfmt_decode_fp8_ocp_16384x7168", None, "decode_fp8_layer"),
+                ("blockfmt_decode_mxfp4_8x2048x4096", None, "decode_mxfp4")):
+            r = out["rows"].get(key)
+            if r is None:
+                continue
+            if ck:
+                cs = counter_summary(ck)
+                r["counters"] = cs
+                r["mfma_util"] = cs.get("mfma_util") if cs else None
+            r["traffic"] = measured_traffic(tk)
         peaks = out.get("measured_peaks")
         if peaks:
             # streams against what this part sustains for the same kind of stream:
