@@ -44,7 +44,8 @@ from .moe import gather_rows_ref, moe_combine_ref, moe_combine_fp32_ordered_ref
 from .channel import gemm_channel_ref, gemm_channel_fp32_ordered_ref, channel_total_ref
 from .a16 import gemm_w8a16_ref, gemm_bf16_ref, a16_tolerance, dequant_fp8_block_bf16_ref
 from .kvcache import (kv_quantize_ref, dequant_kv_ref, attention_int8kv_ref,
-                      attention_bf16kv_ref, attention_tolerance)
+                      attention_bf16kv_ref, attention_tolerance, chunk_lengths_ref,
+                      attention_int8kv_chunk_ref)
 from .packed import packed_position_ref, repack_mfma_ref, unpack_mfma_ref
 
 __all__ = [
@@ -57,7 +58,7 @@ __all__ = [
     "gather_rows_ref", "moe_combine_ref", "moe_combine_fp32_ordered_ref",
     "gemm_channel_ref", "gemm_channel_fp32_ordered_ref", "channel_total_ref",
     "gemm_w8a16_ref", "gemm_bf16_ref", "a16_tolerance", "dequant_fp8_block_bf16_ref",
-    "kv_quantize_ref", "dequant_kv_ref", "attention_int8kv_ref", "attention_bf16kv_ref",
+    "kv_quantize_ref", "dequant_kv_ref", "attention_int8kv_chunk_ref", "chunk_lengths_ref", "attention_int8kv_ref", "attention_bf16kv_ref",
     "attention_tolerance",
     "packed_position_ref", "repack_mfma_ref", "unpack_mfma_ref",
 ]

@@ -95,6 +95,39 @@ def attention_int8kv_ref(q_bits, k_codes, k_scales, v_codes, v_scales, lens):
     return o, mag
 
 
+def chunk_lengths_ref(lens, Qn: int) -> np.ndarray:
+    """Tokens attended by each of the Qn newest tokens of every sequence: query i sits at
+    position lens[b] - Qn + i and attends to tokens 0 .. that position. [B, Qn] int."""
+    lens = np.asarray(lens, np.int64)
+    L = lens[:, None] - Qn + np.arange(Qn)[None, :] + 1
+    return np.clip(L, 0, lens[:, None])
+
+
+def attention_int8kv_chunk_ref(q_bits, k_codes, k_scales, v_codes, v_scales, lens):
+    """Attention of the Qn newest tokens of each sequence over the INT8 cache, causal.
+
+    Reading (the pages name a blockwise attention that dequantises the INT8 cache, sec.
+    4.1, and give no formula for several query tokens): the Qn query tokens of sequence
+    b are its last Qn positions, lens[b] - Qn .. lens[b] - 1, whose keys and values are
+    already in the cache (written before the attention, as a decode step writes its
+    token first); query i attends to tokens 0 .. lens[b] - Qn + i (chunked prefill or
+    verifying Qn drafted tokens). A query with no such token (lens[b] < Qn - i) gives 0.
+    Each query is the decode attention above over its own prefix.
+
+    q_bits BF16 bits [B, Qn, Hq, D]; cache and lens as attention_int8kv_ref.
+    Returns (o [B, Qn, Hq, D], mag [B, Qn, Hq, D]) float64.
+    """
+    q_bits = np.asarray(q_bits)
+    B, Qn, Hq, D = q_bits.shape
+    Ls = chunk_lengths_ref(lens, Qn)
+    o = np.zeros((B, Qn, Hq, D))
+    mag = np.zeros((B, Qn, Hq, D))
+    for i in range(Qn):
+        o[:, i], mag[:, i] = attention_int8kv_ref(q_bits[:, i], k_codes, k_scales, v_codes,
+                                                  v_scales, Ls[:, i])
+    return o, mag
+
+
 def attention_bf16kv_ref(q_bits, k_bits, v_bits, lens):
     """The same attention over a BF16 cache (the cache the INT8 one replaces): K and V
     are the cached BF16 values, exact in float64. Arguments as attention_int8kv_ref

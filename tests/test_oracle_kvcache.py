@@ -15,7 +15,8 @@ import torch
 
 from block_scaled_bit_amd import synth
 from oracle import (kv_quantize_ref, dequant_kv_ref, attention_int8kv_ref, attention_tolerance,
-                    bf16_bits_to_f32_ref, f32_to_bf16_bits_ref)
+                    bf16_bits_to_f32_ref, f32_to_bf16_bits_ref, attention_int8kv_chunk_ref,
+                    chunk_lengths_ref)
 from tests.exact import F, quant_rule_exact, f32_bits
 
 
@@ -242,3 +243,53 @@ def test_bf16_cache_of_exact_int8_values_is_the_int8_attention():
     o8, m8 = attention_int8kv_ref(d["q"], kc, ks, vc, vs, d["lens"])
     o16, m16 = attention_bf16kv_ref(d["q"], kb, vb, d["lens"])
     assert np.allclose(o8, o16, rtol=1e-13, atol=1e-15) and np.allclose(m8, m16, rtol=1e-13)
+
+
+@pytest.mark.parametrize("Qn,Hq,Hkv", [(2, 16, 2), (4, 8, 2), (16, 4, 4), (3, 6, 3)])
+def test_chunk_attention_matches_causal_sdpa(Qn, Hq, Hkv):
+    """Several query tokens per sequence: query i at position L - Qn + i against torch's
+    attention in float64 with the causal mask written as a boolean matrix (a different
+    construction from the oracle's per-query prefixes); queries with no token give 0
+    (sequences shorter than the chunk)."""
+    B, T, D = 3, 64, 128
+    lens = [64, 2, 37]
+    d, kc, ks, vc, vs = _cache(30 + Qn, B, Hq, Hkv, T, lens=lens, q_gain=2.0)
+    rng = np.random.default_rng(Qn)
+    qb = f32_to_bf16_bits_ref(rng.standard_normal((B, Qn, Hq, D)).astype(np.float32) * 2)
+    o, mag = attention_int8kv_chunk_ref(qb, kc, ks, vc, vs, lens)
+    q = torch.from_numpy(bf16_bits_to_f32_ref(qb).astype(np.float64))
+    K = torch.from_numpy(dequant_kv_ref(kc, ks))
+    V = torch.from_numpy(dequant_kv_ref(vc, vs))
+    G = Hq // Hkv
+    for b, L in enumerate(lens):
+        pos = L - Qn + np.arange(Qn)                                  # the queries' positions
+        mask = torch.from_numpy(np.arange(L)[None, :] <= pos[:, None])  # [Qn, L]
+        Kb = K[b, :, :L].repeat_interleave(G, dim=0)[None]
+        Vb = V[b, :, :L].repeat_interleave(G, dim=0)[None]
+        qq = q[b].permute(1, 0, 2)[None]                              # [1, Hq, Qn, D]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, Kb, Vb, attn_mask=mask)
+        ref = ref[0].permute(1, 0, 2).numpy()                         # [Qn, Hq, D]
+        for i in range(Qn):
+            if pos[i] < 0:
+                assert not o[b, i].any() and not mag[b, i].any()
+            else:
+                assert np.allclose(o[b, i], ref[i], rtol=1e-12, atol=1e-14)
+    # one query: the decode attention itself
+    o1, _ = attention_int8kv_chunk_ref(qb[:, -1:], kc, ks, vc, vs, lens)
+    od, _ = attention_int8kv_ref(qb[:, -1], kc, ks, vc, vs, lens)
+    assert np.array_equal(o1[:, 0], od)
+
+
+def test_chunk_lengths_and_an_off_by_one_boundary_is_caught():
+    assert chunk_lengths_ref([5, 1, 0], 3).tolist() == [[3, 4, 5], [0, 0, 1], [0, 0, 0]]
+    # zero queries: each output is the mean of the attended values, so a prefix one
+    # token too long or too short moves it by ~|V| / 13, far past the bound
+    B, Qn, Hq, Hkv, T, D = 1, 4, 2, 1, 16, 128
+    d, kc, ks, vc, vs = _cache(40, B, Hq, Hkv, T, lens=[16])
+    qb = np.zeros((B, Qn, Hq, D), np.uint16)
+    o, mag = attention_int8kv_chunk_ref(qb, kc, ks, vc, vs, [16])
+    mean13 = dequant_kv_ref(vc, vs)[0, 0, :13].mean(axis=0)
+    assert np.allclose(o[0, 0, 0], mean13, rtol=1e-12, atol=1e-14)   # query 0 sees 13 tokens
+    for L in (12, 14):
+        other, _ = attention_int8kv_ref(qb[:, 0], kc, ks, vc, vs, [L])
+        assert np.abs(other - o[:, 0]).max() > attention_tolerance(False) * mag[:, 0].max()
