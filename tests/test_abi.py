@@ -1,5 +1,9 @@
 """C-ABI checks that need no GPU: the library loads, exports what include/bsb.h
-declares, and rejects bad arguments before anything is launched."""
+declares, and rejects bad arguments before anything is launched.
+
+The argument checks pass fake device addresses. They run only where no GPU is
+visible: with one, a call whose checks regressed would launch a kernel on those
+addresses."""
 import ctypes
 import os
 import re
@@ -14,6 +18,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bsb.h")
 
 OK, INVALID, UNSUPPORTED, MISALIGNED = 0, 1, 2, 3
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="passes fake device addresses: host checks only, no GPU visible")
 A = 0x10000          # fake, 16-byte aligned, never dereferenced
 U = 0x10008          # fake, misaligned
 
@@ -44,6 +50,7 @@ def test_version_and_status_strings(L):
     assert L.bsb_status_string(99).decode() == "BSB_ERR_UNKNOWN"
 
 
+@no_gpu
 def test_invalid_sizes_return_invalid_arg(L):
     # K not a multiple of 128, negative sizes, empty N
     assert L.bsb_quantize_act(A, 4, 100, A, A, None) == INVALID
@@ -72,12 +79,14 @@ def test_invalid_sizes_return_invalid_arg(L):
     assert L.bsb_moe_combine(A, A, A, 4, 2, 16, 60, A, None) == INVALID          # N % 8
 
 
+@no_gpu
 def test_bad_enums_return_invalid_arg(L):
     assert L.bsb_gemm_w8a8_g128(A, A, A, A, 4, 8, 128, A, 7, None) == INVALID
     assert L.bsb_grouped_gemm_w8a8_g128(A, A, A, A, A, 2, 4, 8, 128, A, -1, None) == INVALID
     assert L.bsb_decode_fp8_block(A, A, 128, 128, 2, A, A, None) == INVALID
 
 
+@no_gpu
 def test_null_pointers_return_invalid_arg(L):
     assert L.bsb_quantize_act(None, 4, 128, A, A, None) == INVALID
     assert L.bsb_gemm_w8a8_g128(A, None, A, A, 4, 8, 128, A, 0, None) == INVALID
@@ -89,6 +98,7 @@ def test_null_pointers_return_invalid_arg(L):
     assert L.bsb_moe_combine(A, None, A, 4, 2, 16, 64, A, None) == INVALID
 
 
+@no_gpu
 def test_misaligned_pointers(L):
     assert L.bsb_quantize_act(U, 4, 128, A, A, None) == MISALIGNED
     assert L.bsb_gemm_w8a8_g128(A, A, A, U, 4, 8, 128, A, 1, None) == MISALIGNED
@@ -98,6 +108,7 @@ def test_misaligned_pointers(L):
     assert L.bsb_moe_combine(A, A, U, 4, 2, 16, 64, A, None) == MISALIGNED
 
 
+@no_gpu
 def test_empty_rows_are_a_successful_no_op(L):
     # M = 0 / R = 0: nothing to do, nothing launched, null pointers allowed
     assert L.bsb_quantize_act(None, 0, 128, None, None, None) == OK
@@ -125,6 +136,7 @@ def test_python_binding_validates_before_calling():
         bsb.gemm_w8a8_g128(torch.zeros(4, 128, dtype=torch.int8), None, None, None)
 
 
+@no_gpu
 def test_channel_gemm_argument_checks(L):
     """Per-channel / per-tensor GEMM: stride 0 or 1 only, K within the INT32 total's
     bound, sw 4-byte aligned (one float for per-tensor), the usual null, enum and
@@ -143,6 +155,7 @@ def test_channel_gemm_argument_checks(L):
         assert f(A, A, A, A + 4, 0, 4, 8, 131072, A, 1, None) == UNSUPPORTED
 
 
+@no_gpu
 def test_bf16_activation_routes_argument_checks(L):
     """W8A16 / BF16 GEMMs: K a multiple of 128 below 2^23, any number of rows; the FP8 -> BF16
     dequantisation: the decoder's size and dialect rules."""
@@ -171,6 +184,7 @@ def test_bf16_activation_routes_argument_checks(L):
         assert dq(A, A, 128, 128, 1, A, None) == UNSUPPORTED
 
 
+@no_gpu
 def test_kv_cache_argument_checks(L):
     """KV cache write and decode attention: head dimension 128, T a multiple of 64,
     at most 16 query heads per KV head, max_len <= T, a large enough workspace;
@@ -210,6 +224,42 @@ def test_kv_cache_argument_checks(L):
         assert wr(A, A, A, A, 3, 2, 4, 128, 128, A, A, A, A, None) == UNSUPPORTED
 
 
+@no_gpu
+def test_chunk_attention_argument_checks(L):
+    """Attention of several query tokens per sequence: the decode attention's checks
+    plus 1 <= Qn and Qn * Hq / Hkv <= 16, a workspace sized for B * Qn query heads;
+    with valid arguments and no gfx950 device it fails fast."""
+    ch, wb = L.bsb_attention_chunk_int8kv, L.bsb_attention_workspace_bytes
+    names = ["q", "kc", "ks", "vc", "vs", "lens", "B", "Qn", "Hq", "Hkv", "T", "D", "max_len",
+             "work", "work_bytes", "out", "dtype", "stream"]
+    need = wb(2, 4 * 8, 1000)
+    ok = (A, A, A, A, A, A, 2, 4, 8, 2, 1024, 128, 1000, A, need, A, 0, None)
+
+    def call(**kw):
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return ch(*[args[n] for n in names])
+
+    assert call(Qn=0) == INVALID
+    assert call(Qn=5) == INVALID                                    # 5 tokens x 4 heads > 16
+    assert call(Qn=17, Hq=2) == INVALID
+    assert call(work_bytes=wb(2, 8, 1000)) == INVALID               # sized for one token
+    assert call(Hq=7) == INVALID                                    # Hq % Hkv
+    assert call(D=64) == INVALID
+    assert call(T=1000) == INVALID
+    assert call(max_len=1025) == INVALID
+    assert call(work_bytes=need - 4) == INVALID
+    assert call(dtype=2) == INVALID
+    assert call(q=None) == INVALID
+    assert call(vs=U) == MISALIGNED
+    if not torch.cuda.is_available():
+        assert call() == UNSUPPORTED
+        assert call(Qn=8, Hq=4) == UNSUPPORTED                       # 8 x 2 columns
+        assert call(Qn=16, Hq=2) == UNSUPPORTED                      # 16 x 1
+        assert call(max_len=0, work=None, work_bytes=0) == UNSUPPORTED
+
+
+@no_gpu
 def test_noalloc_attention_argument_checks(L):
     """The allocation-free decode attention: the attention's checks without a
     workspace argument, and sizes whose workspace exceeds the static array's
@@ -243,6 +293,7 @@ def test_noalloc_attention_argument_checks(L):
         assert call(B=32, Hq=64, Hkv=8, T=8192, max_len=8192) == UNSUPPORTED
 
 
+@no_gpu
 def test_probe_argument_checks(L):
     """Measurement probes: sizes outside their stated ranges are refused before
     anything is launched; valid calls without a gfx950 device fail fast."""
@@ -268,6 +319,7 @@ def test_probe_argument_checks(L):
         assert cp(A, A, 2 * sweep, None) == UNSUPPORTED
 
 
+@no_gpu
 def test_bf16_kv_cache_argument_checks(L):
     wr, at, wb = L.bsb_kv_cache_write_bf16, L.bsb_attention_decode_bf16kv, L.bsb_attention_workspace_bytes
     assert wr(A, A, A, A, 3, 2, 4, 128, 64, A, A, None) == INVALID          # D != 128
@@ -276,17 +328,18 @@ def test_bf16_kv_cache_argument_checks(L):
     assert wr(A, A, A, A, 3, 2, 4, 128, 128, U, A, None) == MISALIGNED
     assert wr(None, None, None, None, 0, 2, 4, 128, 128, None, None, None) == OK
     need = wb(2, 16, 128)
-    assert at(A, A, A, A, 2, 16, 4, 128, 128, 128, A, need, A, 0, None) in (OK, UNSUPPORTED)
     assert at(A, A, A, A, 2, 15, 4, 128, 128, 128, A, need, A, 0, None) == INVALID
     assert at(A, A, A, A, 2, 16, 4, 128, 128, 129, A, need, A, 0, None) == INVALID
     assert at(A, A, A, A, 2, 16, 4, 128, 128, 128, A, need - 4, A, 0, None) == INVALID
     assert at(A, None, A, A, 2, 16, 4, 128, 128, 128, A, need, A, 0, None) == INVALID
     assert at(A, A, U, A, 2, 16, 4, 128, 128, 128, A, need, A, 0, None) == MISALIGNED
     if not torch.cuda.is_available():
+        assert at(A, A, A, A, 2, 16, 4, 128, 128, 128, A, need, A, 0, None) == UNSUPPORTED
         assert at(A, A, A, A, 2, 16, 4, 128, 128, 128, A, need, A, 1, None) == UNSUPPORTED
         assert wr(A, A, A, A, 3, 2, 4, 128, 128, A, A, None) == UNSUPPORTED
 
 
+@no_gpu
 def test_packed_weight_argument_checks(L):
     """Repack and packed GEMM: N a multiple of 16, K of 128, the GEMM at most 64
     rows and K <= 2^24, the usual null, enum, alignment and empty-input rules;
