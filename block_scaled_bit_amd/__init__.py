@@ -13,6 +13,7 @@ from ._lib import (quantize_act, gemm_w8a8_g128, gemm_w8a8_g128_partials,  # noq
                    gather_rows,
                    moe_combine, kv_cache_empty, kv_cache_write, attention_workspace_bytes,
                    attention_decode_int8kv, attention_decode_int8kv_noalloc,
+                   attention_chunk_int8kv,
                    kv_cache_empty_bf16, kv_cache_write_bf16,
                    attention_decode_bf16kv, BsbError,
                    BSB_OUT_BF16, BSB_OUT_FP32, BSB_FP8_OCP, BSB_FP8_FNUZ, lib, LIB_PATH)

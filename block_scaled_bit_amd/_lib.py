@@ -51,6 +51,9 @@ _SIGNATURES = {
                            _c_p, _c_p, _c_p, _c_p],
     "bsb_attention_decode_int8kv": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
                                     _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_int, _c_p],
+    "bsb_attention_chunk_int8kv": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64,
+                                   _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_int,
+                                   _c_p],
     "bsb_attention_decode_int8kv_noalloc": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64,
                                             _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
     "bsb_probe_mfma_i8": [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p],
@@ -610,6 +613,36 @@ def attention_decode_int8kv(q: torch.Tensor, k_cache: torch.Tensor, k_scale: tor
             _ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(lens),
             B, Hq, Hkv, T, KV_HEAD_DIM, max_len, _ptr(work), work.numel() * 4, _ptr(out), code,
             _stream(dev)), "bsb_attention_decode_int8kv")
+    return out
+
+
+def attention_chunk_int8kv(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor,
+                           v_cache: torch.Tensor, v_scale: torch.Tensor, lens: torch.Tensor,
+                           max_len: int, out_dtype=torch.bfloat16,
+                           out: Optional[torch.Tensor] = None,
+                           work: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal attention of the newest Qn tokens of each sequence, q [B, Qn, Hq, 128] (BF16),
+    over the INT8 cache (their keys and values already written; lens counts them);
+    returns out [B, Qn, Hq, 128]."""
+    B, Hkv, T, dev = _kv_shapes(k_cache, k_scale, v_cache, v_scale)
+    _need(q, "q", _BF16_BITS, None, dev)
+    if q.dim() != 4 or q.shape[0] != B or q.shape[3] != KV_HEAD_DIM:
+        raise ValueError("q must be [B, Qn, Hq, 128]")
+    Qn, Hq = q.shape[1], q.shape[2]
+    _need(lens, "lens", (torch.int32,), (B,), dev)
+    code = _out_code(out_dtype)
+    out = (torch.empty((B, Qn, Hq, KV_HEAD_DIM), dtype=out_dtype, device=dev) if out is None
+           else out)
+    _need(out, "out", (out_dtype,), (B, Qn, Hq, KV_HEAD_DIM), dev)
+    nbytes = attention_workspace_bytes(B, Qn * Hq, max_len)
+    if work is None:
+        work = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=dev)
+    _need(work, "work", (torch.float32,), None, dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_attention_chunk_int8kv(
+            _ptr(q), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(lens),
+            B, Qn, Hq, Hkv, T, KV_HEAD_DIM, max_len, _ptr(work), work.numel() * 4, _ptr(out), code,
+            _stream(dev)), "bsb_attention_chunk_int8kv")
     return out
 
 

@@ -437,6 +437,34 @@ bsb_status bsb_attention_decode_int8kv(const uint16_t *q_bf16, const int8_t *k_c
                                                as_stream(stream)));
 }
 
+bsb_status bsb_attention_chunk_int8kv(const uint16_t *q_bf16, const int8_t *k_cache,
+                                      const float *k_scale, const int8_t *v_cache,
+                                      const float *v_scale, const int32_t *lens, int64_t B,
+                                      int64_t Qn, int64_t Hq, int64_t Hkv, int64_t T, int64_t D,
+                                      int64_t max_len, float *work, int64_t work_bytes, void *out,
+                                      bsb_out_dtype out_dtype, void *stream) {
+    if (bsb_status s = attention_shape_checks(q_bf16, lens, B, Hq, Hkv, T, D, max_len, out,
+                                              out_dtype))
+        return s;
+    // Qn query tokens x Hq / Hkv heads share the 16 query columns of a KV head
+    if (Qn < 1 || Qn > 16 || Qn * (Hq / Hkv) > 16 || B * Qn * Hq >= ((int64_t)1 << 31))
+        return BSB_ERR_INVALID_ARG;
+    const int64_t need = bsb_attention_workspace_bytes(B, Qn * Hq, max_len);
+    if (need < 0 || work_bytes < need) return BSB_ERR_INVALID_ARG;
+    if (need > 0 && !work) return BSB_ERR_INVALID_ARG;
+    if (work && !aligned16(work)) return BSB_ERR_MISALIGNED;
+    if (!k_cache || !k_scale || !v_cache || !v_scale) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(k_scale) || !aligned16(v_cache) || !aligned16(v_scale))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_attention_chunk(q_bf16, k_cache, k_scale, v_cache, v_scale, lens,
+                                              (int)B, (int)Qn, (int)Hq, (int)Hkv, (int)T,
+                                              (int)max_len, work, out,
+                                              out_dtype == BSB_OUT_BF16 ? 1 : 0,
+                                              as_stream(stream)));
+}
+
 bsb_status bsb_attention_decode_int8kv_noalloc(const uint16_t *q_bf16, const int8_t *k_cache,
                                                const float *k_scale, const int8_t *v_cache,
                                                const float *v_scale, const int32_t *lens,

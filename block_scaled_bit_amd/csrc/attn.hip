@@ -38,6 +38,13 @@
 // The same kernel also runs over a BF16 cache (the cache the INT8 one
 // replaces, kept as the comparison route): 2-byte elements in blocks of the
 // same operand order, no conversion and no scales.
+//
+// Several query tokens per sequence (chunked prefill, verifying drafted
+// tokens; [P3] sec. 4.1's blockwise attention): the matrix instructions'
+// 16 query columns hold (query token, head) pairs, Qn tokens x G heads <= 16,
+// so the cache is still read once per (sequence, KV head) for all of them.
+// Query i of Qn is the sequence's token at position L - Qn + i and attends to
+// tokens 0 .. L - Qn + i: each column carries its own length in the masks.
 #include "device_common.h"
 #include <atomic>
 
@@ -200,7 +207,7 @@ __global__ void __launch_bounds__(512)
 attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
                   const float *__restrict__ ks, const void *__restrict__ vc,
                   const float *__restrict__ vs, const int32_t *__restrict__ lens, int Hq, int Hkv,
-                  int T, int max_len, float *__restrict__ part, void *__restrict__ out) {
+                  int T, int max_len, int Qn, float *__restrict__ part, void *__restrict__ out) {
     constexpr bool I8 = KVT == kKvInt8;
     constexpr int EB = I8 ? 1 : 2;                     // bytes per cached element
     __shared__ __align__(16) float s_o[kAttnWaves][16][kORow];
@@ -209,13 +216,17 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
     const int split = blockIdx.x, nsplit = gridDim.x;
     const int bh = blockIdx.y;
     const int b = bh / Hkv, hk = bh - b * Hkv;
-    const int G = Hq / Hkv;
+    const int G = Hq / Hkv, NC = Qn * G;   // query columns: (token qi, head hh) = (c / G, c % G)
     // wave index as a uniform value, so the offsets derived from it stay scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 15, grp = lane >> 4;
     int L = lens[b];
     const int lim = max_len < T ? max_len : T;
     L = L < 0 ? 0 : (L > lim ? lim : L);
+    // this lane's column: its query token and head, and the tokens it attends
+    const int qi = col / G, hh = col - qi * G;
+    int Lc = L - Qn + qi + 1;
+    Lc = Lc < 0 ? 0 : (Lc > L ? L : Lc);
     const int base = split * kSplitTok * R + wave * kWaveTok;
     auto t0_of = [&](int r) { return base + r * kSplitTok; };
 
@@ -268,11 +279,12 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // queries: head hk*G + col (zero rows for col >= G), dims 32grp .. 32grp+31
+    // queries: token qi, head hk*G + hh (zero rows for col >= NC), dims 32grp .. 32grp+31
     uint4 qd[4];
     {
-        const bool hv = col < G;
-        const uint16_t *qr = q + ((int64_t)b * Hq + hk * G + (hv ? col : 0)) * kHD + 32 * grp;
+        const bool hv = col < NC;
+        const uint16_t *qr =
+            q + (((int64_t)b * Qn + (hv ? qi : 0)) * Hq + hk * G + (hv ? hh : 0)) * kHD + 32 * grp;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             qd[j] = hv ? *reinterpret_cast<const uint4 *>(qr + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
@@ -309,14 +321,17 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
                 float sv;
                 if constexpr (I8) sv = (acc[r] * __shfl(ch.skl, tt, kWave)) * kScoreScale;
                 else sv = acc[r] * kScoreScale;
-                x[c][r] = (t0 + tt < L) ? sv : kNegInf;
+                x[c][r] = (t0 + tt < Lc) ? sv : kNegInf;
                 mc = __builtin_fmaxf(mc, x[c][r]);
             }
         }
         mc = __builtin_fmaxf(mc, __shfl_xor(mc, 16, kWave));
-        mc = __builtin_fmaxf(mc, __shfl_xor(mc, 32, kWave));   // finite: token t0 is valid
+        mc = __builtin_fmaxf(mc, __shfl_xor(mc, 32, kWave));
         const float mn = __builtin_fmaxf(m, mc);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first chunk
+        // a column none of whose tokens so far is attended (a chunk's earlier
+        // queries) keeps m = -inf: exponents against 0 then give 0, not NaN
+        const float ms = mn == kNegInf ? 0.0f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m - ms);   // 0 on the first chunk
         m = mn;
         lpart *= alpha;
 #pragma unroll
@@ -326,7 +341,7 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[c][r] = __builtin_amdgcn_exp2f(x[c][r] - mn);
+                p[c][r] = __builtin_amdgcn_exp2f(x[c][r] - ms);
                 lpart += p[c][r];
             }
         // P.V over two 32-token blocks; slot j < 4 is token 32s + 4grp + j,
@@ -342,8 +357,8 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
                     pa *= __shfl(ch.svl, ta + j, kWave);
                     pb2 *= __shfl(ch.svl, tbk + j, kWave);
                 }
-                pw[j] = (__bf16)(t0 + ta + j < L ? pa : 0.0f);
-                pw[4 + j] = (__bf16)(t0 + tbk + j < L ? pb2 : 0.0f);
+                pw[j] = (__bf16)(t0 + ta + j < Lc ? pa : 0.0f);
+                pw[4 + j] = (__bf16)(t0 + tbk + j < Lc ? pb2 : 0.0f);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -395,8 +410,8 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
         *reinterpret_cast<float4 *>(&s_o[wave][col][16 * i + 4 * grp]) =
             make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
     __syncthreads();
-    float *pb = part + ((int64_t)bh * nsplit + split) * G * kPart;
-    for (int idx = threadIdx.x; idx < G * kHD; idx += kAttnWaves * kWave) {
+    float *pb = part + ((int64_t)bh * nsplit + split) * NC * kPart;
+    for (int idx = threadIdx.x; idx < NC * kHD; idx += kAttnWaves * kWave) {
         const int h = idx / kHD, d = idx - h * kHD;
         float M = kNegInf;
 #pragma unroll
@@ -419,7 +434,8 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
         } else {
             // the only split: this is the whole sequence, finish here
             const float y = M != kNegInf ? O / Ls : 0.0f;
-            const int64_t oi = ((int64_t)b * Hq + hk * G + h) * kHD + d;
+            const int hq = h / G, hhd = h - hq * G;   // column h: query token hq, head hhd
+            const int64_t oi = (((int64_t)b * Qn + hq) * Hq + hk * G + hhd) * kHD + d;
             if (OUT == kDirectBf16)
                 reinterpret_cast<uint16_t *>(out)[oi] = (uint16_t)f32_to_bf16_rne(y);
             else
@@ -428,21 +444,23 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
     }
 }
 
-// one wave per (sequence, query head); lane holds dimensions 2 lane, 2 lane + 1.
+// one wave per (sequence, query token, query head); lane holds dimensions 2 lane,
+// 2 lane + 1.
 // Splits are read eight at a time, all loads of a batch issued together, and
 // merged with a running maximum.
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(64)
-attn_combine_kernel(const float *__restrict__ part, int Hq, int Hkv, int nsplit,
+attn_combine_kernel(const float *__restrict__ part, int Hq, int Hkv, int Qn, int nsplit,
                     void *__restrict__ out) {
     constexpr int kBatch = 8;
-    const int bq = blockIdx.x;
+    const int bq = blockIdx.x;             // (sequence, query token, query head), row-major
     const int G = Hq / Hkv;
-    const int b = bq / Hq, hq = bq - b * Hq;
+    const int b = bq / (Qn * Hq), rq = bq - b * Qn * Hq;
+    const int qi = rq / Hq, hq = rq - qi * Hq;
     const int hk = hq / G, h = hq - hk * G;
     const int lane = threadIdx.x;
-    const int64_t stride = (int64_t)G * kPart;
-    const float *pp = part + ((int64_t)(b * Hkv + hk) * nsplit) * stride + h * kPart;
+    const int64_t stride = (int64_t)Qn * G * kPart;
+    const float *pp = part + ((int64_t)(b * Hkv + hk) * nsplit) * stride + (qi * G + h) * kPart;
     float M = kNegInf, Lt = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
         float ms[kBatch], ls[kBatch];
@@ -490,21 +508,21 @@ attn_combine_kernel(const float *__restrict__ part, int Hq, int Hkv, int nsplit,
 template <int KVT, int R, int OUT>
 hipError_t launch_split(dim3 grid, const uint16_t *q, const void *kc, const float *ks,
                         const void *vc, const float *vs, const int32_t *lens, int Hq, int Hkv,
-                        int T, int max_len, float *work, void *out, hipStream_t stream) {
+                        int T, int max_len, int Qn, float *work, void *out, hipStream_t stream) {
     attn_split_kernel<KVT, R, OUT><<<grid, kAttnWaves * kWave, 0, stream>>>(
-        q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out);
+        q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, Qn, work, out);
     return hipGetLastError();
 }
 
 template <int KVT, int OUT>
 hipError_t launch_split_o(int R, dim3 grid, const uint16_t *q, const void *kc, const float *ks,
                           const void *vc, const float *vs, const int32_t *lens, int Hq, int Hkv,
-                          int T, int max_len, float *work, void *out, hipStream_t stream) {
+                          int T, int max_len, int Qn, float *work, void *out, hipStream_t stream) {
     switch (R) {
-        case 1: return launch_split<KVT, 1, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
-        case 2: return launch_split<KVT, 2, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
-        case 4: return launch_split<KVT, 4, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
-        default: return launch_split<KVT, 8, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        case 1: return launch_split<KVT, 1, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, Qn, work, out, stream);
+        case 2: return launch_split<KVT, 2, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, Qn, work, out, stream);
+        case 4: return launch_split<KVT, 4, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, Qn, work, out, stream);
+        default: return launch_split<KVT, 8, OUT>(grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, Qn, work, out, stream);
     }
 }
 
@@ -512,21 +530,24 @@ hipError_t launch_split_o(int R, dim3 grid, const uint16_t *q, const void *kc, c
 template <int KVT>
 hipError_t launch_split_r(int R, int out_mode, const uint16_t *q, const void *kc, const float *ks,
                           const void *vc, const float *vs, const int32_t *lens, int B, int Hq,
-                          int Hkv, int T, int max_len, float *work, void *out, hipStream_t stream) {
+                          int Hkv, int T, int max_len, int Qn, float *work, void *out,
+                          hipStream_t stream) {
     const int64_t ns = (max_len + (int64_t)kSplitTok * R - 1) / ((int64_t)kSplitTok * R);
     const dim3 grid((unsigned)ns, (unsigned)(B * Hkv));
     if (out_mode == kDirectBf16)
-        return launch_split_o<KVT, kDirectBf16>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        return launch_split_o<KVT, kDirectBf16>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, Qn, work, out, stream);
     if (out_mode == kDirectF32)
-        return launch_split_o<KVT, kDirectF32>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
-    return launch_split_o<KVT, kPartials>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, work, out, stream);
+        return launch_split_o<KVT, kDirectF32>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, Qn, work, out, stream);
+    return launch_split_o<KVT, kPartials>(R, grid, q, kc, ks, vc, vs, lens, Hq, Hkv, T, max_len, Qn, work, out, stream);
 }
 
 // Both cache types: R chunks per wave, one or several splits, then the merge.
+// Qn query tokens per sequence (1 for decode), Qn * Hq / Hkv <= 16.
 template <int KVT>
 hipError_t attention_decode(const uint16_t *q, const void *kc, const float *ks, const void *vc,
                             const float *vs, const int32_t *lens, int B, int Hq, int Hkv, int T,
-                            int max_len, float *work, void *out, int out_bf16, hipStream_t stream) {
+                            int max_len, float *work, void *out, int out_bf16, hipStream_t stream,
+                            int Qn = 1) {
     // chunks per wave (1, 2, 4 or 8): the most that keep at least kMinWorkgroups
     // workgroups in the grid (long-lived waves, fewer partials to merge)
     const int64_t units = (int64_t)B * Hkv * attention_splits(max_len);
@@ -535,18 +556,17 @@ hipError_t attention_decode(const uint16_t *q, const void *kc, const float *ks, 
     const int64_t ns = (max_len + kSplitTok * R - 1) / (kSplitTok * R);
     if (ns == 1)   // one split holds every sequence: it writes the output, no merge
         return launch_split_r<KVT>(R, out_bf16 ? kDirectBf16 : kDirectF32, q, kc, ks, vc, vs, lens,
-                                   B, Hq, Hkv, T, max_len, work, out, stream);
+                                   B, Hq, Hkv, T, max_len, Qn, work, out, stream);
     if (ns > 0) {   // max_len == 0: no split to run, the combine writes zeros
         hipError_t e = launch_split_r<KVT>(R, kPartials, q, kc, ks, vc, vs, lens, B, Hq, Hkv, T,
-                                           max_len, work, out, stream);
+                                           max_len, Qn, work, out, stream);
         if (e != hipSuccess) return e;
     }
+    const dim3 rows((unsigned)((int64_t)B * Qn * Hq));
     if (out_bf16)
-        attn_combine_kernel<true><<<dim3((unsigned)(B * Hq)), 64, 0, stream>>>(work, Hq, Hkv,
-                                                                               (int)ns, out);
+        attn_combine_kernel<true><<<rows, 64, 0, stream>>>(work, Hq, Hkv, Qn, (int)ns, out);
     else
-        attn_combine_kernel<false><<<dim3((unsigned)(B * Hq)), 64, 0, stream>>>(work, Hq, Hkv,
-                                                                                (int)ns, out);
+        attn_combine_kernel<false><<<rows, 64, 0, stream>>>(work, Hq, Hkv, Qn, (int)ns, out);
     return hipGetLastError();
 }
 
@@ -624,6 +644,14 @@ hipError_t launch_attention_decode(const uint16_t *q, const int8_t *kc, const fl
                                    int out_bf16, hipStream_t stream) {
     return attention_decode<kKvInt8>(q, kc, ks, vc, vs, lens, B, Hq, Hkv, T, max_len, work, out,
                                      out_bf16, stream);
+}
+
+hipError_t launch_attention_chunk(const uint16_t *q, const int8_t *kc, const float *ks,
+                                  const int8_t *vc, const float *vs, const int32_t *lens, int B,
+                                  int Qn, int Hq, int Hkv, int T, int max_len, float *work,
+                                  void *out, int out_bf16, hipStream_t stream) {
+    return attention_decode<kKvInt8>(q, kc, ks, vc, vs, lens, B, Hq, Hkv, T, max_len, work, out,
+                                     out_bf16, stream, Qn);
 }
 
 hipError_t launch_kv_cache_write_bf16(const uint16_t *k, const uint16_t *v, const int32_t *seq,

@@ -93,6 +93,13 @@ hipError_t launch_attention_decode(const uint16_t *q, const int8_t *kc, const fl
                                    int Hq, int Hkv, int T, int max_len, float *work, void *out,
                                    int out_bf16, hipStream_t stream);
 
+// Attention of the Qn newest tokens of each sequence (causal), Qn * Hq / Hkv <= 16;
+// q and out [B, Qn, Hq, 128]; work: attention_workspace_floats(B, Qn * Hq, max_len).
+hipError_t launch_attention_chunk(const uint16_t *q, const int8_t *kc, const float *ks,
+                                  const int8_t *vc, const float *vs, const int32_t *lens, int B,
+                                  int Qn, int Hq, int Hkv, int T, int max_len, float *work,
+                                  void *out, int out_bf16, hipStream_t stream);
+
 // The same attention with its split partials in a static per-device array of
 // kNoAllocScratchBytes (no workspace argument, nothing allocated); sizes whose
 // workspace exceeds it are rejected by the caller.

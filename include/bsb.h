@@ -421,6 +421,32 @@ bsb_status bsb_attention_decode_int8kv(const uint16_t *q_bf16,
                                        void *out, bsb_out_dtype out_dtype, void *stream);
 
 /*
+ * Attention of several query tokens per sequence over the INT8 cache: the
+ * blockwise attention of [P3] sec. 4.1 with the dequantisation fused as in
+ * bsb_attention_decode_int8kv, for chunked prefill or for checking drafted
+ * tokens. The Qn query tokens of sequence b are its newest Qn tokens, at
+ * positions lens[b] - Qn .. lens[b] - 1, whose keys and values are already in
+ * the cache; query i attends to tokens 0 .. lens[b] - Qn + i (causal):
+ *     out[b, i, h, :] = the attention of bsb_attention_decode_int8kv for
+ *                       query q[b, i, h, :] over tokens t <= lens[b] - Qn + i
+ * and a query with no such token (lens[b] < Qn - i) gives zeros. All Qn
+ * queries of a sequence share one read of its cache.
+ *   q_bf16   [B, Qn, Hq, 128] BF16 bits; 1 <= Qn and Qn * Hq / Hkv <= 16
+ *   work     float32 scratch of bsb_attention_workspace_bytes(B, Qn * Hq,
+ *            max_len) bytes; work_bytes its size
+ *   out      [B, Qn, Hq, 128] BF16 bits or float32 per `out_dtype` (written)
+ * Other arguments, the bound and the errors as bsb_attention_decode_int8kv
+ * (B * Qn * Hq < 2^31).
+ */
+bsb_status bsb_attention_chunk_int8kv(const uint16_t *q_bf16,
+                                      const int8_t *k_cache, const float *k_scale,
+                                      const int8_t *v_cache, const float *v_scale,
+                                      const int32_t *lens, int64_t B, int64_t Qn, int64_t Hq,
+                                      int64_t Hkv, int64_t T, int64_t D, int64_t max_len,
+                                      float *work, int64_t work_bytes,
+                                      void *out, bsb_out_dtype out_dtype, void *stream);
+
+/*
  * bsb_attention_decode_int8kv for callers that cannot allocate: code under
  * HIP graph capture, tight serving loops and harnesses that forbid hipMalloc.
  * Same arguments, arithmetic and results (bit for bit) without the workspace:

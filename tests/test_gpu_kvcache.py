@@ -14,7 +14,7 @@ import torch
 import block_scaled_bit_amd as bsb
 from block_scaled_bit_amd import synth
 from oracle import (kv_quantize_ref, attention_int8kv_ref, attention_tolerance,
-                    bf16_bits_to_f32_ref)
+                    bf16_bits_to_f32_ref, attention_int8kv_chunk_ref, f32_to_bf16_bits_ref)
 from tests.gpu_util import require_gpu, dev, dev_bf16, host, say
 
 pytestmark = pytest.mark.gpu
@@ -376,3 +376,47 @@ def test_attention_more_than_eight_splits(route):
         y = host(out).astype(np.float64)
         o64, mag = attention_bf16kv_ref(inp["q"], inp["k"], inp["v"], lens)
     _check(y, o64, mag, False)
+
+
+# several query tokens per sequence: B, Qn, Hq, Hkv, T, lens, max_len
+CHUNK_CASES = [
+    (2, 2, 16, 2, 128, [128, 77], 128),          # 2 tokens x 8 heads: all 16 columns
+    (3, 4, 8, 2, 576, [576, 2, 300], 576),       # two splits; a sequence shorter than the chunk
+    (2, 16, 2, 2, 1088, [1088, 513], 1088),      # 16 tokens x 1 head; three splits
+    (3, 3, 12, 3, 640, [640, 0, 601], 600),      # G = 4, 12 columns; max_len below T; empty
+    (1, 5, 3, 1, 192, [191], 192),               # G = 3, 15 columns
+    (32, 2, 64, 8, 512, [512] * 32, 512),        # many (sequence, KV head) pairs: several chunks per wave
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_chunk_attention_matches_oracle(case, dtype):
+    """Causal attention of the newest Qn tokens over the INT8 cache: every query against
+    the oracle's per-query prefix within the attention bound; queries with no token give 0."""
+    d = require_gpu()
+    B, Qn, Hq, Hkv, T, lens, max_len = case
+    say(f"chunk attention B={B} Qn={Qn} Hq={Hq} Hkv={Hkv} T={T} lens={lens} max_len={max_len} {dtype}")
+    _, kc, ks, vc, vs, lens, _, _ = _attn_case(B, Hq, Hkv, T, lens, max_len, seed=B + Qn + Hq + T)
+    rng = np.random.default_rng(B * Qn + T)
+    qb = f32_to_bf16_bits_ref(rng.standard_normal((B, Qn, Hq, D)).astype(np.float32) * 2)
+    eff = np.minimum(lens, max_len)
+    o64, mag = attention_int8kv_chunk_ref(qb, kc, ks, vc, vs, eff)
+    out = bsb.attention_chunk_int8kv(dev_bf16(qb, d), *_upload_cache(kc, ks, vc, vs, d),
+                                     dev(lens, d), max_len, out_dtype=dtype)
+    torch.cuda.synchronize()
+    y = host(out)
+    y = (bf16_bits_to_f32_ref(y) if dtype == torch.bfloat16 else y).astype(np.float64)
+    _check(y, o64, mag, dtype == torch.bfloat16)
+
+
+def test_chunk_attention_of_one_token_is_the_decode_attention():
+    """Qn = 1 runs the decode kernel's arithmetic: bit-identical outputs."""
+    d = require_gpu()
+    qb, kc, ks, vc, vs, lens, _, _ = _attn_case(3, 16, 2, 1088, [1088, 1, 500], 1088, seed=77)
+    cache = _upload_cache(kc, ks, vc, vs, d)
+    q = dev_bf16(qb, d)
+    a = bsb.attention_decode_int8kv(q, *cache, dev(lens, d), 1088, out_dtype=torch.float32)
+    c = bsb.attention_chunk_int8kv(q[:, None], *cache, dev(lens, d), 1088, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c[:, 0])
