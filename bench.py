@@ -902,6 +902,7 @@ def kv_rows(torch, L, stream, dev, steps):
     and value, the BF16 queries and the BF16 output."""
     import numpy as np
     from block_scaled_bit_amd import synth
+    from block_scaled_bit_amd import _lib as bsb_lib
     rows = {}
     c = synth.KV_CONFIG
     B, Hq, Hkv, T, D = c["B"], c["Hq"], c["Hkv"], c["T"], c["D"]
@@ -914,16 +915,12 @@ def kv_rows(torch, L, stream, dev, steps):
     vt = t(inp["v"].view(np.int16)).permute(0, 2, 1, 3).reshape(B * T, Hkv, D).contiguous()
     seq = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(T)
     pos = torch.arange(T, dtype=torch.int32, device=dev).repeat(B)
-    kc = torch.empty((B, Hkv, T // 16, 16 * D), dtype=torch.int8, device=dev)
-    ks = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
-    vc = torch.empty((B, Hkv, T // 32, 32 * D), dtype=torch.int8, device=dev)
-    vs = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+    kc, ks, vc, vs = bsb_lib.kv_cache_empty(B, Hkv, T, dev)
     _ok(L, L.bsb_kv_cache_write(kt.data_ptr(), vt.data_ptr(), seq.data_ptr(), pos.data_ptr(),
                                 B * T, B, Hkv, T, D, kc.data_ptr(), ks.data_ptr(), vc.data_ptr(),
                                 vs.data_ptr(), stream))
     # the BF16 cache the INT8 one replaces, written from the same keys and values
-    kb = torch.empty((B, Hkv, T // 16, 16 * D), dtype=torch.int16, device=dev)
-    vb = torch.empty((B, Hkv, T // 32, 32 * D), dtype=torch.int16, device=dev)
+    kb, vb = (c.view(torch.int16) for c in bsb_lib.kv_cache_empty_bf16(B, Hkv, T, dev))
     _ok(L, L.bsb_kv_cache_write_bf16(kt.data_ptr(), vt.data_ptr(), seq.data_ptr(), pos.data_ptr(),
                                      B * T, B, Hkv, T, D, kb.data_ptr(), vb.data_ptr(), stream))
     # one decode step: the last slot of every sequence rewritten with its own key / value
@@ -958,6 +955,29 @@ def kv_rows(torch, L, stream, dev, steps):
     rows["kv_int8_attention_decode_b32_t4096"] = _rate(ta * 1e3, byts=a_bytes) | {
         "kernel": "attn_split_kernel<0, 8, 1> (INT8 cache, one launch)", "traffic": measured_traffic("kv_attention")}
     log(f"kv attention (decode, 32 x 4096 tokens) {ta * 1e3:.1f} us")
+
+    # two query tokens per sequence (checking a drafted token, a prefill chunk):
+    # 2 x G = 16 query columns per KV head, the cache still read once
+    Qn = 16 // (Hq // Hkv)
+    if Qn > 1:
+        c_bytes = 2 * B * Hkv * T * D + 8 * B * Hkv * T + 4 * B * Qn * Hq * D
+        cw = L.bsb_attention_workspace_bytes(B, Qn * Hq, T)
+        qc = t(synth.to_bf16_bits(np.random.default_rng(5).standard_normal(
+            (B, Qn, Hq, D), dtype=np.float32)).view(np.int16))
+        csets = []
+        for i, a in enumerate(asets):
+            o = dict(q=qc.clone(), out=torch.empty((B, Qn, Hq, D), dtype=torch.int16, device=dev),
+                     work=torch.empty((cw // 4,), dtype=torch.float32, device=dev))
+            csets.append(a | {k: v.data_ptr() for k, v in o.items()} | {"_keep2": o})
+        tc = Row("kv attention chunk", csets, lambda p, st: _ok(L, L.bsb_attention_chunk_int8kv(
+            p["q"], p["kc"], p["ks"], p["vc"], p["vs"], p["lens"], B, Qn, Hq, Hkv, T, D, T,
+            p["work"], cw, p["out"], 0, st))).time(torch, stream, steps, 3)
+        rows[f"kv_int8_attention_chunk{Qn}_b32_t4096"] = _rate(tc * 1e3, byts=c_bytes) | {
+            "kernel": "attn_split_kernel<0, 8, 1> (INT8 cache, one launch)",
+            "query_tokens": Qn, "vs_decode_time": round(tc / ta, 3)}
+        log(f"kv attention ({Qn} query tokens per sequence) {tc * 1e3:.1f} us "
+            f"({tc / ta:.2f}x the one-token time)")
+        del csets
     del asets, kc, ks, vc, vs, step, wsets
     torch.cuda.empty_cache()
 

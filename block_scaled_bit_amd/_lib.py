@@ -506,8 +506,7 @@ def moe_combine(y: torch.Tensor, row_of_pair: torch.Tensor, gate: torch.Tensor,
 
 
 KV_HEAD_DIM = 128
-KV_KBLOCK = 16
-KV_VBLOCK = 32
+KV_CHUNK = 64          # tokens per cache row: caches are [T/64, B, Hkv, 64 * 128]
 
 
 def kv_cache_empty(B: int, Hkv: int, T: int, device) -> Tuple[torch.Tensor, ...]:
@@ -515,23 +514,22 @@ def kv_cache_empty(B: int, Hkv: int, T: int, device) -> Tuple[torch.Tensor, ...]
     slots (T a multiple of 64) over Hkv heads of dimension 128, in the layout of
     bsb_kv_cache_write (contents undefined until written)."""
     dev = torch.device(device)
-    return (torch.empty((B, Hkv, T // KV_KBLOCK, KV_KBLOCK * KV_HEAD_DIM), dtype=torch.int8,
-                        device=dev),
+    rows = (T // KV_CHUNK, B, Hkv, KV_CHUNK * KV_HEAD_DIM)
+    return (torch.empty(rows, dtype=torch.int8, device=dev),
             torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
-            torch.empty((B, Hkv, T // KV_VBLOCK, KV_VBLOCK * KV_HEAD_DIM), dtype=torch.int8,
-                        device=dev),
+            torch.empty(rows, dtype=torch.int8, device=dev),
             torch.empty((B, Hkv, T), dtype=torch.float32, device=dev))
 
 
 def _kv_shapes(k_cache, k_scale, v_cache, v_scale):
     _need(k_cache, "k_cache", (torch.int8,))
-    if k_cache.dim() != 4 or k_cache.shape[3] != KV_KBLOCK * KV_HEAD_DIM:
-        raise ValueError("k_cache must be [B, Hkv, T/16, 2048]")
-    B, Hkv, nb, _ = k_cache.shape
-    T = nb * KV_KBLOCK
+    if k_cache.dim() != 4 or k_cache.shape[3] != KV_CHUNK * KV_HEAD_DIM:
+        raise ValueError("k_cache must be [T/64, B, Hkv, 8192]")
+    nc, B, Hkv, _ = k_cache.shape
+    T = nc * KV_CHUNK
     dev = k_cache.device
     _need(k_scale, "k_scale", (torch.float32,), (B, Hkv, T), dev)
-    _need(v_cache, "v_cache", (torch.int8,), (B, Hkv, T // KV_VBLOCK, KV_VBLOCK * KV_HEAD_DIM), dev)
+    _need(v_cache, "v_cache", (torch.int8,), tuple(k_cache.shape), dev)
     _need(v_scale, "v_scale", (torch.float32,), (B, Hkv, T), dev)
     return B, Hkv, T, dev
 
@@ -650,20 +648,19 @@ def kv_cache_empty_bf16(B: int, Hkv: int, T: int, device) -> Tuple[torch.Tensor,
     """Allocate the BF16 comparison cache (k_cache, v_cache) in the layout of
     bsb_kv_cache_write_bf16 (contents undefined until written)."""
     dev = torch.device(device)
-    return (torch.empty((B, Hkv, T // KV_KBLOCK, KV_KBLOCK * KV_HEAD_DIM), dtype=torch.bfloat16,
-                        device=dev),
-            torch.empty((B, Hkv, T // KV_VBLOCK, KV_VBLOCK * KV_HEAD_DIM), dtype=torch.bfloat16,
-                        device=dev))
+    rows = (T // KV_CHUNK, B, Hkv, KV_CHUNK * KV_HEAD_DIM)
+    return (torch.empty(rows, dtype=torch.bfloat16, device=dev),
+            torch.empty(rows, dtype=torch.bfloat16, device=dev))
 
 
 def _kv16_shapes(k_cache, v_cache):
     _need(k_cache, "k_cache", _BF16_BITS)
-    if k_cache.dim() != 4 or k_cache.shape[3] != KV_KBLOCK * KV_HEAD_DIM:
-        raise ValueError("k_cache must be [B, Hkv, T/16, 2048]")
-    B, Hkv, nb, _ = k_cache.shape
-    T = nb * KV_KBLOCK
+    if k_cache.dim() != 4 or k_cache.shape[3] != KV_CHUNK * KV_HEAD_DIM:
+        raise ValueError("k_cache must be [T/64, B, Hkv, 8192]")
+    nc, B, Hkv, _ = k_cache.shape
+    T = nc * KV_CHUNK
     dev = k_cache.device
-    _need(v_cache, "v_cache", _BF16_BITS, (B, Hkv, T // KV_VBLOCK, KV_VBLOCK * KV_HEAD_DIM), dev)
+    _need(v_cache, "v_cache", _BF16_BITS, tuple(k_cache.shape), dev)
     return B, Hkv, T, dev
 
 

@@ -8,17 +8,24 @@
 // read once and never expanded in memory.
 //
 // Cache layout (head dimension 128; T = token slots per sequence, a multiple of 64):
-//   k_cache [B, Hkv, T/16, 2048] INT8: 16-token blocks; token tau of a block,
+//   k_cache [T/64, B, Hkv, 8192] INT8: the 64-token chunk c of (sequence b, KV
+//           head h) is row (c, b, h), chunks of every (b, h) interleaved; a
+//           chunk is four 16-token blocks of 2 KB; token tau of a block,
 //           dimension d at byte ((d/16)%2)*1024 + ((d/32)*16 + tau)*16 + d%16
-//   v_cache [B, Hkv, T/32, 4096] INT8: 32-token blocks; token tau of a block,
-//           dimension d at byte (d/32)*1024 + (((tau%16)/4)*16 + d%16)*16 +
-//           ((d/16)%2)*8 + (tau/16)*4 + tau%4
+//   v_cache [T/64, B, Hkv, 8192] INT8: a chunk is two 32-token blocks of 4 KB;
+//           token tau of a block, dimension d at byte (d/32)*1024 +
+//           (((tau%16)/4)*16 + d%16)*16 + ((d/16)%2)*8 + (tau/16)*4 + tau%4
 //   k_scale, v_scale [B, Hkv, T] float32
 // Both block orders are the matrix cores' operand orders (lane l of a wave
 // reads bytes 16l .. 16l+15 of each 1 KB quarter or half of a block), so every
 // load instruction reads 1 KB contiguous and nothing is transposed. (A V
 // order in which each lane's 64 bytes were contiguous made every load
 // instruction touch 4 KB at a 64-byte stride; measured 1-2 % slower.)
+// Chunk-major order puts the chunks that the workgroups of one launch read at
+// the same time (the same chunk of every (sequence, KV head)) next to each
+// other in memory: at 32 sequences x 8 KV heads x 4096 tokens the attention
+// ran 53-54 us with each (sequence, head) contiguous and 50-52 us chunk-major
+// (with the non-temporal hint below, 48-50 us).
 //
 // Decode attention (one query token per sequence, grouped-query heads, up to
 // 16 query heads per KV head): a workgroup of 8 waves takes a split of the
@@ -56,6 +63,7 @@ namespace {
 
 constexpr int kHD = 128;                       // head dimension
 constexpr int kVBlk = 32;                      // tokens per V block
+constexpr int kChunk = 64;                     // tokens per cache chunk (row of the layout)
 constexpr int kAttnWaves = 8;                  // waves per attention workgroup
 constexpr int kWaveTok = 64;                   // tokens per wave
 constexpr int kSplitTok = kAttnWaves * kWaveTok;   // tokens per split per chunk step
@@ -97,6 +105,12 @@ __device__ __forceinline__ int vblk16_off(int tau, int d) {
     return (d >> 4) * 1024 + (((tau & 15) >> 2) * 16 + (d & 15)) * 16 + ((tau >> 4) * 4 + (tau & 3)) * 2;
 }
 
+// Byte offset of the chunk holding token t of (sequence, KV head) bh in a cache
+// of BH = B * Hkv rows per chunk index, chunk_bytes per chunk.
+__device__ __forceinline__ int64_t chunk_at(int64_t bh, int64_t BH, int t, int chunk_bytes) {
+    return ((int64_t)(t / kChunk) * BH + bh) * chunk_bytes;
+}
+
 // eight INT8 codes (little-endian in two dwords) -> eight BF16 values (exact)
 __device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
     bf16x8 r;
@@ -133,14 +147,15 @@ kv_write_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
         c0 = quant_elem(bf16_to_f32(w & 0xFFFFu), s);
         c1 = quant_elem(bf16_to_f32(w >> 16), s);
     }
-    const int64_t vec = ((int64_t)b * Hkv + h) * T + t;
+    const int64_t bh = (int64_t)b * Hkv + h, vec = bh * T + t;
+    const int64_t chunk = chunk_at(bh, (int64_t)B * Hkv, t, kChunk * kHD);
     if (which == 0) {
         const uint16_t pair = (uint16_t)((uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8));
-        int8_t *blk = kc + (((int64_t)b * Hkv + h) * T + (t & ~15)) * kHD;
+        int8_t *blk = kc + chunk + ((t % kChunk) / 16) * (16 * kHD);
         *reinterpret_cast<uint16_t *>(blk + kblk_off(t & 15, 2 * lane)) = pair;
         if (lane == 0) ks[vec] = s;
     } else {
-        int8_t *blk = vc + (((int64_t)b * Hkv + h) * (T / kVBlk) + t / kVBlk) * (kVBlk * kHD);
+        int8_t *blk = vc + chunk + ((t % kChunk) / kVBlk) * (kVBlk * kHD);
         const int tau = t % kVBlk;
         blk[vblk_off(tau, 2 * lane)] = (int8_t)c0;
         blk[vblk_off(tau, 2 * lane + 1)] = (int8_t)c1;
@@ -165,11 +180,12 @@ kv_write_bf16_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict_
     if (b < 0 || b >= B || t < 0 || t >= T) return;     // whole wave: nothing written
     const uint32_t w = reinterpret_cast<const uint32_t *>((which ? v : k) + th * kHD)[lane];
     const int64_t bh = (int64_t)b * Hkv + h;
+    const int64_t chunk = chunk_at(bh, (int64_t)B * Hkv, t, kChunk * 2 * kHD);
     if (which == 0) {
-        uint8_t *blk = reinterpret_cast<uint8_t *>(kc) + (bh * T + (t & ~15)) * (2 * kHD);
+        uint8_t *blk = reinterpret_cast<uint8_t *>(kc) + chunk + ((t % kChunk) / 16) * (16 * 2 * kHD);
         *reinterpret_cast<uint32_t *>(blk + kblk16_off(t & 15, 2 * lane)) = w;   // d, d+1 adjacent
     } else {
-        uint8_t *blk = reinterpret_cast<uint8_t *>(vc) + (bh * T + (t & ~31)) * (2 * kHD);
+        uint8_t *blk = reinterpret_cast<uint8_t *>(vc) + chunk + ((t % kChunk) / kVBlk) * (kVBlk * 2 * kHD);
         *reinterpret_cast<uint16_t *>(blk + vblk16_off(t & 31, 2 * lane)) = (uint16_t)(w & 0xFFFFu);
         *reinterpret_cast<uint16_t *>(blk + vblk16_off(t & 31, 2 * lane + 1)) = (uint16_t)(w >> 16);
     }
@@ -230,31 +246,39 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
     const int base = split * kSplitTok * R + wave * kWaveTok;
     auto t0_of = [&](int r) { return base + r * kSplitTok; };
 
-    // this (sequence, KV head)'s slice of the cache, range-checked by the buffer
-    // descriptors; the lane's part of an offset is in a VGPR, the rest scalar
-    const uint32_t tb = (uint32_t)T * kHD * EB;
-    const __amdgpu_buffer_rsrc_t rk =
-        make_rsrc(reinterpret_cast<const uint8_t *>(kc) + (int64_t)bh * tb, tb);
-    const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc(reinterpret_cast<const uint8_t *>(vc) + (int64_t)bh * tb, tb);
+    // one chunk of keys and one of values per load step, each through a buffer
+    // descriptor over that chunk (range-checked; offset kOOB reads zeros); the
+    // lane's part of an offset is in a VGPR, the rest scalar. INT8 chunks are
+    // read once and carry the non-temporal hint (measured 2-3 us faster at 32
+    // sequences x 4096 tokens; with the (sequence, head)-contiguous layout the
+    // hint had cost 12-15 us).
+    constexpr int kCB = kChunk * kHD * EB;   // bytes per chunk
+    constexpr int kAux = I8 ? kNonTemporal : 0;
+    const int64_t BH = (int64_t)gridDim.y;
     const uint32_t kvo = (uint32_t)lane * 16;
     const uint32_t vvo = (uint32_t)lane * 16;
 
     auto load = [&](KvChunk<KVT> &ch, int r) {
         const int t0 = t0_of(r);
         const bool ok = r < R && t0 < L;
-        const uint32_t so = ok ? (uint32_t)t0 * kHD * EB : kOOB;
+        const uint32_t so = ok ? 0u : kOOB;
+        const int64_t cb = chunk_at(bh, BH, ok ? t0 : 0, kCB);
+        const __amdgpu_buffer_rsrc_t rk =
+            make_rsrc(reinterpret_cast<const uint8_t *>(kc) + cb, (uint32_t)kCB);
+        const __amdgpu_buffer_rsrc_t rv =
+            make_rsrc(reinterpret_cast<const uint8_t *>(vc) + cb, (uint32_t)kCB);
         if constexpr (I8) {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    ch.kd[c][j] = buf_load16s(rk, kvo, ok ? so + c * 2048 + j * 1024 : kOOB);
+                    ch.kd[c][j] = buf_load16s<kAux>(rk, kvo, ok ? so + c * 2048 + j * 1024 : kOOB);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    ch.vd[s][j] = buf_load16s(rv, vvo, ok ? so + s * (kVBlk * kHD) + 1024 * j : kOOB);
+                    ch.vd[s][j] =
+                        buf_load16s<kAux>(rv, vvo, ok ? so + s * (kVBlk * kHD) + 1024 * j : kOOB);
             const __amdgpu_buffer_rsrc_t rks = make_rsrc(ks + (int64_t)bh * T, (uint32_t)T * 4);
             const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vs + (int64_t)bh * T, (uint32_t)T * 4);
             const uint32_t ss = ok ? (uint32_t)t0 * 4 : kOOB;

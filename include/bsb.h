@@ -358,13 +358,16 @@ bsb_status bsb_moe_combine(const uint16_t *y, const int32_t *row_of_pair,
  * per value vector (one token of one KV head, D = 128 values), taken on write
  * by the rule of bsb_quantize_act over those 128 values.
  * Cache layout (T = token slots per sequence, a multiple of 64, 64 <= T < 2^24):
- *   k_cache [B, Hkv, T/16, 2048] int8: blocks of 16 tokens; token tau of a
- *           block and dimension d sit at byte
- *           ((d/16)%2)*1024 + ((d/32)*16 + tau)*16 + d%16
- *   v_cache [B, Hkv, T/32, 4096] int8: blocks of 32 tokens; token tau of a
- *           block and dimension d sit at byte
- *           (d/32)*1024 + (((tau%16)/4)*16 + d%16)*16 + ((d/16)%2)*8 +
- *           (tau/16)*4 + tau%4
+ *   k_cache [T/64, B, Hkv, 8192] int8: row (c, b, h) holds tokens 64c .. 64c+63
+ *           of sequence b, KV head h (the same chunk of every sequence and head
+ *           is adjacent, which is the order the attention reads them in), as
+ *           four blocks of 16 tokens, 2048 bytes each; token tau of a block and
+ *           dimension d sit at byte
+ *           ((d/16)%2)*1024 + ((d/32)*16 + tau)*16 + d%16 of the block
+ *   v_cache [T/64, B, Hkv, 8192] int8: rows as k_cache, each two blocks of 32
+ *           tokens, 4096 bytes each; token tau of a block and dimension d sit
+ *           at byte (d/32)*1024 + (((tau%16)/4)*16 + d%16)*16 + ((d/16)%2)*8 +
+ *           (tau/16)*4 + tau%4 of the block
  *   k_scale, v_scale [B, Hkv, T] float32
  * The caller allocates and owns every buffer; nothing is written outside the
  * slots named by (seq, pos).
@@ -475,11 +478,12 @@ bsb_status bsb_attention_decode_int8kv_noalloc(const uint16_t *q_bf16,
  * BF16 keys and values (no scales, nothing quantised), the cache the INT8 one
  * replaces ([P3] sec. 2.2 counts it at 2 bytes per element).
  * Cache layout (T as above):
- *   k_cache [B, Hkv, T/16, 2048] BF16 bits: blocks of 16 tokens; token tau and
- *           dimension d at element ((d/8)%4)*512 + ((d/32)*16 + tau)*8 + d%8
- *   v_cache [B, Hkv, T/32, 4096] BF16 bits: blocks of 32 tokens; token tau and
- *           dimension d at element (d/16)*512 + (((tau%16)/4)*16 + d%16)*8 +
- *           (tau/16)*4 + tau%4
+ *   k_cache [T/64, B, Hkv, 8192] BF16 bits: rows as the INT8 cache, each four
+ *           blocks of 16 tokens (2048 elements); token tau and dimension d at
+ *           element ((d/8)%4)*512 + ((d/32)*16 + tau)*8 + d%8 of the block
+ *   v_cache [T/64, B, Hkv, 8192] BF16 bits: rows of two blocks of 32 tokens
+ *           (4096 elements); token tau and dimension d at element
+ *           (d/16)*512 + (((tau%16)/4)*16 + d%16)*8 + (tau/16)*4 + tau%4
  * bsb_kv_cache_write_bf16 copies n tokens' keys and values into their slots
  * (arguments as bsb_kv_cache_write, without scales);
  * bsb_attention_decode_bf16kv computes the attention of

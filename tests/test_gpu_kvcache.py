@@ -28,28 +28,47 @@ V_OFF = ((_d // 32) * 1024 + (((_tau % 16) // 4) * 16 + _d % 16) * 16 + ((_d // 
          (_tau // 16) * 4 + _tau % 4)
 
 
+CH = 64          # tokens per cache row
+
+
+def _rows(blocks):
+    """[B, H, T/blk, blk elements] -> the cache rows [T/64, B, H, 64*128]: row (c, b, h)
+    holds the blocks of tokens 64c .. 64c+63 of (b, h) in token order."""
+    B, H, N, W = blocks.shape
+    per = CH * D // W
+    return np.ascontiguousarray(blocks.reshape(B, H, N // per, per * W).transpose(2, 0, 1, 3))
+
+
+def _blocks(rows, W):
+    """Inverse of _rows for blocks of W elements."""
+    C, B, H, R = rows.shape
+    return rows.transpose(1, 2, 0, 3).reshape(B, H, C * R // W, W)
+
+
 def k_encode(kc):
-    """[B, H, T, 128] int8 -> the K block layout [B, H, T/16, 2048]."""
+    """[B, H, T, 128] int8 -> k_cache [T/64, B, H, 8192] (16-token blocks of 2 KB)."""
     B, H, T, _ = kc.shape
     out = np.empty((B, H, T // KB, KB * D), np.int8)
     out[..., K_OFF] = kc.reshape(B, H, T // KB, KB, D)
-    return out
+    return _rows(out)
 
 
 def k_decode(kb):
+    kb = _blocks(np.asarray(kb), KB * D)
     B, H, NB, _ = kb.shape
     return kb[..., K_OFF].reshape(B, H, NB * KB, D)
 
 
 def v_encode(vc):
-    """[B, H, T, 128] int8 -> the V block layout [B, H, T/32, 4096]."""
+    """[B, H, T, 128] int8 -> v_cache [T/64, B, H, 8192] (32-token blocks of 4 KB)."""
     B, H, T, _ = vc.shape
     out = np.empty((B, H, T // VB, VB * D), np.int8)
     out[..., V_OFF] = vc.reshape(B, H, T // VB, VB, D)
-    return out
+    return _rows(out)
 
 
 def v_decode(vb):
+    vb = _blocks(np.asarray(vb), VB * D)
     B, H, NB, _ = vb.shape
     return vb[..., V_OFF].reshape(B, H, NB * VB, D)
 
@@ -60,6 +79,10 @@ def test_kv_layouts_are_permutations():
     x = np.random.default_rng(0).integers(-127, 128, size=(2, 3, 64, D)).astype(np.int8)
     assert np.array_equal(k_decode(k_encode(x)), x)
     assert np.array_equal(v_decode(v_encode(x)), x)
+    # rows are chunk-major: token 64 of (b, h) starts row (1, b, h)
+    y = np.zeros((2, 3, 128, D), np.int8)
+    y[1, 2, 64, 0] = 7
+    assert k_encode(y)[1, 1, 2, 0] == 7 and v_encode(y)[1, 1, 2, 0] == 7
 
 
 def _poisoned_cache(B, H, T, d):
@@ -243,8 +266,8 @@ def test_full_size_decode_attention_sampled():
     for b in (0, 17, 31):
         qk, sk = kv_quantize_ref(inp["k"][b:b + 1])
         qv, sv = kv_quantize_ref(inp["v"][b:b + 1])
-        assert np.array_equal(k_decode(host(kc[b:b + 1])), qk)
-        assert np.array_equal(v_decode(host(vc[b:b + 1])), qv)
+        assert np.array_equal(k_decode(host(kc[:, b:b + 1])), qk)
+        assert np.array_equal(v_decode(host(vc[:, b:b + 1])), qv)
         assert np.array_equal(host(ks[b:b + 1]), sk) and np.array_equal(host(vs[b:b + 1]), sv)
         o64, mag = attention_int8kv_ref(inp["q"][b:b + 1], qk, sk, qv, sv, inp["lens"][b:b + 1])
         _check(y[b:b + 1], o64, mag, True)
@@ -289,19 +312,22 @@ def k16_encode(k):
     B, H, T, _ = k.shape
     out = np.empty((B, H, T // KB, KB * D), np.uint16)
     out[..., K16_OFF] = k.reshape(B, H, T // KB, KB, D)
-    return out
+    return _rows(out)
 
 
 def v16_encode(v):
     B, H, T, _ = v.shape
     out = np.empty((B, H, T // VB, VB * D), np.uint16)
     out[..., V16_OFF] = v.reshape(B, H, T // VB, VB, D)
-    return out
+    return _rows(out)
 
 
 def test_bf16_layouts_are_permutations():
     assert np.array_equal(np.sort(K16_OFF.ravel()), np.arange(KB * D))
     assert np.array_equal(np.sort(V16_OFF.ravel()), np.arange(VB * D))
+    x = np.random.default_rng(1).integers(0, 1 << 16, size=(2, 3, 128, D)).astype(np.uint16)
+    assert np.array_equal(_blocks(k16_encode(x), KB * D)[..., K16_OFF].reshape(x.shape), x)
+    assert np.array_equal(_blocks(v16_encode(x), VB * D)[..., V16_OFF].reshape(x.shape), x)
 
 
 def test_bf16_write_copies_into_the_layout():
@@ -318,8 +344,8 @@ def test_bf16_write_copies_into_the_layout():
     vn = np.stack([inp["v"][b, :, t] for b, t in slots] + [inp["v"][0, :, 0]])
     bsb.kv_cache_write_bf16(dev_bf16(kn, d), dev_bf16(vn, d), dev(seq, d), dev(pos, d), kc, vc)
     torch.cuda.synchronize()
-    gk = host(kc)[..., K16_OFF].reshape(B, H, T, D)
-    gv = host(vc)[..., V16_OFF].reshape(B, H, T, D)
+    gk = _blocks(host(kc), KB * D)[..., K16_OFF].reshape(B, H, T, D)
+    gv = _blocks(host(vc), VB * D)[..., V16_OFF].reshape(B, H, T, D)
     for b in range(B):
         for t in range(T):
             if (b + t) % 3:
