@@ -248,12 +248,12 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
 
     // one chunk of keys and one of values per load step, each through a buffer
     // descriptor over that chunk (range-checked; offset kOOB reads zeros); the
-    // lane's part of an offset is in a VGPR, the rest scalar. INT8 chunks are
-    // read once and carry the non-temporal hint (measured 2-3 us faster at 32
-    // sequences x 4096 tokens; with the (sequence, head)-contiguous layout the
-    // hint had cost 12-15 us).
+    // lane's part of an offset is in a VGPR, the rest scalar. Chunks are read
+    // once and carry the non-temporal hint (at 32 sequences x 4096 tokens: INT8
+    // 2-3 us faster, BF16 92.6 -> 82.7 us; with the (sequence, head)-contiguous
+    // layout the hint had cost the INT8 cache 12-15 us).
     constexpr int kCB = kChunk * kHD * EB;   // bytes per chunk
-    constexpr int kAux = I8 ? kNonTemporal : 0;
+    constexpr int kAux = kNonTemporal;
     const int64_t BH = (int64_t)gridDim.y;
     const uint32_t kvo = (uint32_t)lane * 16;
     const uint32_t vvo = (uint32_t)lane * 16;
@@ -291,12 +291,12 @@ attn_split_kernel(const uint16_t *__restrict__ q, const void *__restrict__ kc,
             for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    ch.kd[c][s] = buf_load16s(rk, kvo, ok ? so + c * 4096 + s * 1024 : kOOB);
+                    ch.kd[c][s] = buf_load16s<kAux>(rk, kvo, ok ? so + c * 4096 + s * 1024 : kOOB);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    ch.vd[s][i] = buf_load16s(rv, vvo, ok ? so + s * 8192 + i * 1024 : kOOB);
+                    ch.vd[s][i] = buf_load16s<kAux>(rv, vvo, ok ? so + s * 8192 + i * 1024 : kOOB);
         }
         // keep the whole chunk's loads here, ahead of the computation that follows
         asm volatile("" ::: "memory");
