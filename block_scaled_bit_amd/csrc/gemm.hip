@@ -607,6 +607,12 @@ hipError_t launch_smallm(const int8_t *q, const float *sa, const int8_t *qw, con
 }
 
 constexpr int kBigMinM = 512;   // rows from which the 256x256 kernel is used
+// The 256x256 kernel once the 128x128 kernel's four times as many tiles would
+// take more than two rounds of the CUs: more than 128 of its own tiles. Both
+// give the same bits; measured at N = 4096, K = 7168 (and 8192 x 8192):
+// 128 tiles 122 against 98 us for the 128x128 kernel, 160 tiles 130 against
+// 145, 192 tiles 136 against 154, 224 tiles 154 against 189.
+constexpr int64_t kBigMinTiles = kCUs / 2 + 1;
 
 template <int OUT>
 hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
@@ -616,10 +622,10 @@ hipError_t launch_dense(const int8_t *q, const float *sa, const int8_t *qw, cons
     if (M <= 64 && (int64_t)128 * K < ((int64_t)1 << 31))
         return launch_smallm<OUT>(q, sa, qw, sw, M, N, K, y, stream, sw_stride);
     // The 256x256 kernel (which addresses its operand panels with 32-bit
-    // buffer offsets) when it has at least one tile per CU; below that the
-    // 128x128 kernels' four times as many tiles finish sooner.
+    // buffer offsets) from kBigMinTiles of its tiles; below that the 128x128
+    // kernel's four times as many tiles finish sooner.
     const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-    if (M >= kBigMinM && big_gemm_fits(K) && big_tiles >= kCUs)
+    if (M >= kBigMinM && big_gemm_fits(K) && big_tiles >= kBigMinTiles)
         return launch_gemm_big(q, sa, qw, sw, M, N, K, y, OUT, nullptr, 0, sw_stride, stream);
     if (!mid_gemm_fits(K)) return hipErrorInvalidValue;   // excluded by the C ABI's checks
     return launch_gemm_mid(q, sa, qw, sw, M, N, K, y, OUT, nullptr, 0, sw_stride, stream);
@@ -687,10 +693,12 @@ hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *q
                                const float *sw, const int32_t *offsets, int64_t E, int64_t R,
                                int64_t N, int64_t K, void *y, int out, hipStream_t stream) {
     // Rows per expert are known only on the device; the mean decides. With
-    // at least 128 rows per expert on average, and enough rows for a tile per
-    // CU, the 256x256 kernel is used.
+    // at least 128 rows per expert on average, and at least kBigMinTiles tiles
+    // (counted without the experts' partial tiles, a lower bound), the 256x256
+    // kernel is used (the busiest GPU's share of the MoE layer under 8-way
+    // expert parallelism, 240 tiles: 93 against 136 us).
     const int64_t big_tiles = ((R + 255) / 256) * ((N + 255) / 256);
-    if (R >= 128 * E && big_tiles >= kCUs && big_gemm_fits(K))
+    if (R >= 128 * E && big_tiles >= kBigMinTiles && big_gemm_fits(K))
         return launch_gemm_big(q, sa, qw, sw, (int)R, (int)N, (int)K, y, out, offsets, (int)E, 1,
                                stream);
     // At most 32 rows per expert on average (decode-shaped MoE): stream each

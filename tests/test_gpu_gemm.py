@@ -69,15 +69,15 @@ def test_tiny_config():
     (33, 64, 256), (64, 130, 640), (65, 129, 256), (100, 300, 384), (128, 128, 128),
     (130, 257, 512), (257, 1, 256), (300, 96, 1024),
     (512, 256, 256), (600, 300, 384), (777, 1000, 256), (1024, 520, 128), (513, 7, 1152),
-    (2049, 7425, 256), (2305, 7000, 384),
+    (2049, 7425, 256), (2305, 7000, 384), (1537, 5000, 256),
     # M <= 64 with at least 4 waves per workgroup (scales staged in 16-group
     # chunks): a ragged last chunk, less than one chunk, odd N
     (33, 12400, 2176), (1, 20000, 1152), (64, 13001, 4224),
     (17, 12900, 2560)])     # G a multiple of 4: 16-row scale pieces, partial last chunk
 def test_ragged_shapes(M, N, K):
-    """Every kernel (M <= 64; 128x128 tiles; 256x256 tiles from 512 rows when there is at
-    least one such tile per CU, the last two shapes), partial tiles in M and N, several
-    groups."""
+    """Every kernel (M <= 64; 128x128 tiles; 256x256 tiles from 512 rows when there are
+    more than 128 such tiles: 2049 x 7425, 2305 x 7000 and 1537 x 5000, the last 140 tiles),
+    partial tiles in M and N, several groups."""
     d = require_gpu()
     say(f"gemm ragged M={M} N={N} K={K}")
     cfg, q, sa = _inputs(M, K, N, M * 1000 + N + K)

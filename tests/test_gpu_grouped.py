@@ -45,11 +45,16 @@ def _gpu_grouped(q, sa, qw, sw, off, dtype, d):
     # up to 128 rows per expert on average: 128x128 tiles
     ([0, 1, 127, 128, 129, 0, 5], 96, 256),     # segment ends at 0, 1, BM-1, BM, BM+1
     ([300, 0, 0, 2], 130, 384),
-    # at least 128 rows per expert on average: 256x256 tiles; segments ending at
-    # 1, 63/64/65 (one wave's rows), 255/256/257 (one tile)
+    # at least 128 rows per expert on average but too few tiles for the 256x256
+    # kernel (at most 15): 128x128 tiles, segments ending at 1, 63/64/65,
+    # 255/256/257
     ([0, 1, 255, 256, 257, 0, 64, 65, 300], 96, 256),
     ([700, 0, 129, 513, 63], 300, 384),
     ([1, 1100], 520, 128),
+    # enough tiles for the 256x256 kernel (19 tile rows x 8 columns, more than
+    # 128): segments ending at 1, 63/64/65 (one wave's rows), 255/256/257 (one
+    # tile) inside it
+    ([0, 1, 255, 256, 257, 0, 64, 65, 300, 63, 2300, 600, 513], 2048, 256),
 ])
 def test_segments_and_tails(lengths, N, K):
     d = require_gpu()
