@@ -446,3 +446,32 @@ def test_chunk_attention_of_one_token_is_the_decode_attention():
     c = bsb.attention_chunk_int8kv(q[:, None], *cache, dev(lens, d), 1088, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a, c[:, 0])
+
+
+def test_full_size_chunk_attention_sampled():
+    """Two query tokens per sequence over the benchmark's cache (32 sequences x 4096
+    tokens, 64 / 8 heads, written by the GPU write kernel), in the launch the benchmark
+    times (2 x 8 = 16 query columns); three sequences against the oracle."""
+    d = require_gpu()
+    c = synth.KV_CONFIG
+    B, Hq, Hkv, T, Qn = c["B"], c["Hq"], c["Hkv"], c["T"], 2
+    inp = synth.kv_inputs(B, Hq, Hkv, T, lens=np.full(B, T), seed=3)
+    say("full-size kv write + chunk attention (2 query tokens)")
+    kc, ks, vc, vs = bsb.kv_cache_empty(B, Hkv, T, d)
+    kt = dev_bf16(inp["k"], d).permute(0, 2, 1, 3).reshape(B * T, Hkv, D).contiguous()
+    vt = dev_bf16(inp["v"], d).permute(0, 2, 1, 3).reshape(B * T, Hkv, D).contiguous()
+    seq = torch.arange(B, dtype=torch.int32, device=d).repeat_interleave(T)
+    pos = torch.arange(T, dtype=torch.int32, device=d).repeat(B)
+    bsb.kv_cache_write(kt, vt, seq, pos, kc, ks, vc, vs)
+    rng = np.random.default_rng(11)
+    qb = f32_to_bf16_bits_ref(rng.standard_normal((B, Qn, Hq, D)).astype(np.float32))
+    lens = inp["lens"].copy()
+    lens[5] = 4000                                  # a shorter sequence among the full ones
+    out = bsb.attention_chunk_int8kv(dev_bf16(qb, d), kc, ks, vc, vs, dev(lens, d), T)
+    torch.cuda.synchronize()
+    y = bf16_bits_to_f32_ref(host(out)).astype(np.float64)
+    for b in (0, 5, 31):
+        qk, sk = kv_quantize_ref(inp["k"][b:b + 1])
+        qv, sv = kv_quantize_ref(inp["v"][b:b + 1])
+        o64, mag = attention_int8kv_chunk_ref(qb[b:b + 1], qk, sk, qv, sv, lens[b:b + 1])
+        _check(y[b:b + 1], o64, mag, True)
