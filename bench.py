@@ -746,13 +746,24 @@ def extra_rows(torch, L, stream, dev, steps):
     rows["moe_4096tok_top8_64e_gather"] = _rate(tga * 1e3, byts=T * K + R * K + 4 * T + 8 * R)
     rows["moe_4096tok_top8_64e_combine"] = _rate(
         tco * 1e3, byts=2 * R * N + 2 * T * N + 8 * T * topk)
+    # the grouped GEMM reading its rows through the token index (no gathered copy)
+    tgg = Row("moe grouped gather", [p], lambda p, st_: _ok(
+        L, L.bsb_grouped_gemm_w8a8_g128_gather(p["qt"], p["st"], p["tor"], T, p["qw"], p["sw"],
+                                               p["off"], E, R, N, K, p["y"], 0, st_))).time(
+        torch, stream, 20, 3)
+    rows["moe_4096tok_top8_64e_grouped_gather"] = _rate(
+        tgg * 1e3, ops=2 * R * N * K, byts=gbytes - R * K - 4 * R + T * K + 4 * T + 4 * R,
+        bound="mfma+hbm") | {"vs_gather_then_grouped": round(tgg / (tga + tg), 3)}
     rows["moe_4096tok_top8_64e_layer"] = {
-        "avg_us": round((tqt + tga + tg + tco) * 1e3, 2),
-        "parts": "quantize_act(tokens) + gather_rows + grouped GEMM + moe_combine",
+        "avg_us": round((tqt + tgg + tco) * 1e3, 2),
+        "parts": "quantize_act(tokens) + grouped GEMM gathering its rows + moe_combine",
+        "with_separate_gather_us": round((tqt + tga + tg + tco) * 1e3, 2),
         "quantise_after_gather_us": round((tq + tg) * 1e3, 2),
-        "note": "quantise_after_gather_us = quantize_act(gathered rows) + grouped GEMM, no combine"}
+        "note": "with_separate_gather_us: gather_rows then the grouped GEMM; "
+                "quantise_after_gather_us = quantize_act(gathered rows) + grouped GEMM, no combine"}
     log(f"moe glue: quant tokens {tqt * 1e3:.1f} us, gather {tga * 1e3:.1f} us, "
-        f"combine {tco * 1e3:.1f} us")
+        f"combine {tco * 1e3:.1f} us; grouped GEMM gathering its rows {tgg * 1e3:.1f} us "
+        f"(gather + grouped {(tga + tg) * 1e3:.1f} us)")
     del m, xs, qw, sw, off, q, sa, y, p, xt, qt, st, tor, rp, gate, out
     torch.cuda.empty_cache()
 

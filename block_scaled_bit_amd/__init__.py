@@ -7,7 +7,7 @@ raises if it has not been built.
 """
 from ._lib import (quantize_act, gemm_w8a8_g128, gemm_w8a8_g128_partials,  # noqa: F401
                    repack_weights_mfma, gemm_w8a8_g128_packed, decode_fp8_block_packed,
-                   grouped_gemm_w8a8_g128_packed,
+                   grouped_gemm_w8a8_g128_packed, grouped_gemm_w8a8_g128_gather,
                    gemm_w8a8_channel, gemm_w8a16_g128, gemm_bf16, dequant_fp8_block_bf16,
                    grouped_gemm_w8a8_g128, decode_fp8_block, decode_mxfp4, decode_mxfp4_packed,
                    gather_rows,

@@ -37,6 +37,8 @@ _SIGNATURES = {
                               _c_p],
     "bsb_grouped_gemm_w8a8_g128": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64,
                                    _c_p, _c_int, _c_p],
+    "bsb_grouped_gemm_w8a8_g128_gather": [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_p, _c_i64,
+                                          _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
     "bsb_decode_fp8_block": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_p],
     "bsb_dequant_fp8_block_bf16": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p],
     "bsb_decode_fp8_block_packed": [_c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_p],
@@ -281,6 +283,37 @@ def grouped_gemm_w8a8_g128(q: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, 
         _check(lib().bsb_grouped_gemm_w8a8_g128(_ptr(q), _ptr(sa), _ptr(qw), _ptr(sw),
                                                 _ptr(offsets), E, R, N, K, _ptr(out), code,
                                                 _stream(dev)), "bsb_grouped_gemm_w8a8_g128")
+    return out
+
+
+def grouped_gemm_w8a8_g128_gather(q: torch.Tensor, sa: torch.Tensor, index: torch.Tensor,
+                                  qw: torch.Tensor, sw: torch.Tensor, offsets: torch.Tensor,
+                                  out_dtype=torch.bfloat16,
+                                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """grouped_gemm_w8a8_g128 on rows gathered by the kernel: q [T,K] / sa [T] are the
+    quantised tokens and row r is token index[r] (index [R] int32, device); bit-identical
+    to gather_rows followed by grouped_gemm_w8a8_g128."""
+    _need(q, "q", (torch.int8,))
+    if q.dim() != 2 or qw.dim() != 3:
+        raise ValueError("q [T,K] and qw [E,N,K] required")
+    T, K = q.shape
+    E, N, _ = qw.shape
+    dev = q.device
+    _need(index, "index", (torch.int32,), None, dev)
+    if index.dim() != 1:
+        raise ValueError("index must be [R]")
+    R = index.shape[0]
+    _need(qw, "qw", (torch.int8,), (E, N, K), dev)
+    _need(sa, "sa", (torch.float32,), (T,), dev)
+    _need(sw, "sw", (torch.float32,), (E, N, K // 128), dev)
+    _need(offsets, "offsets", (torch.int32,), (E + 1,), dev)
+    code = _out_code(out_dtype)
+    out = torch.empty((R, N), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", (out_dtype,), (R, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().bsb_grouped_gemm_w8a8_g128_gather(
+            _ptr(q), _ptr(sa), _ptr(index), T, _ptr(qw), _ptr(sw), _ptr(offsets), E, R, N, K,
+            _ptr(out), code, _stream(dev)), "bsb_grouped_gemm_w8a8_g128_gather")
     return out
 
 

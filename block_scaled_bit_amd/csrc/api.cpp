@@ -212,6 +212,29 @@ bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa, const in
                                            as_stream(stream)));
 }
 
+bsb_status bsb_grouped_gemm_w8a8_g128_gather(const int8_t *q, const float *sa,
+                                             const int32_t *index, int64_t T, const int8_t *qw,
+                                             const float *sw, const int32_t *offsets, int64_t E,
+                                             int64_t R, int64_t N, int64_t K, void *y,
+                                             bsb_out_dtype out, void *stream) {
+    if (!dims_ok(R, N, K) || K >= kGemmKLimit || E < 1 || E >= (1 << 20) ||
+        !prod_le(E, N, K, kMaxElems))
+        return BSB_ERR_INVALID_ARG;
+    // the tokens are addressed through one 32-bit buffer range
+    if (T < 1 || T >= kMaxDim || T * K + 128 >= ((int64_t)1 << 31))
+        return BSB_ERR_INVALID_ARG;
+    if (out != BSB_OUT_BF16 && out != BSB_OUT_FP32) return BSB_ERR_INVALID_ARG;
+    if (R == 0) return BSB_OK;
+    if (!q || !sa || !index || !qw || !sw || !offsets || !y) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(sa) || !aligned16(index) || !aligned16(qw) ||
+        !aligned16(sw) || !aligned16(offsets) || !aligned16(y))
+        return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_grouped_gemm(q, sa, qw, sw, offsets, E, R, N, K, y, (int)out,
+                                           as_stream(stream), index, T));
+}
+
 bsb_status bsb_decode_fp8_block(const uint8_t *w, const uint8_t *bs, int64_t N, int64_t K,
                                 bsb_fp8_dialect dialect, int8_t *qw, float *sw, void *stream) {
     if (N < 128 || N % 128 || K < 128 || K % 128 || N >= kMaxDim || K >= kMaxDim ||

@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(64 * NW)
 gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                    const int8_t *__restrict__ qw, const float *__restrict__ sw, int M, int N,
                    int K, void *__restrict__ y, const int32_t *__restrict__ offsets,
-                   int sw_stride) {
+                   int sw_stride, const int32_t *__restrict__ gidx, int T) {
     constexpr int ROWS = 16 * MB;              // activation rows
     constexpr int WR = 16 * NW;                // weight rows per workgroup
     constexpr int RW = kGroup * (AM == AM_BF16 ? 2 : 1);   // bytes of a weight row per group
@@ -441,10 +441,37 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
         }
     };
 
+    // Row m of the problem: token gidx[m] of the T quantised tokens when
+    // gathering (grouped W8A8 only; an index outside [0, T) is a zero row with
+    // scale 0), else row m itself.
+    const bool gather = GROUPED && AM == AM_W8A8 && gidx != nullptr;
+    auto sa_of = [&](int m) {
+        if (!gather) return sa[m];
+        const int t = gidx[m];
+        return (t >= 0 && t < T) ? sa[t] : 0.0f;
+    };
+
     // One pass: rows r0 .. r0+rows-1 (rows <= 16*MB) against the whole K walk.
     auto pass = [&]() {
-        ra = make_rsrc_words(q + (int64_t)r0 * K * (RA / kGroup),
-                             (uint32_t)(rows * K * (RA / kGroup)));
+        if (gather) {
+            // the activation blocks' rows are this pass's gathered tokens
+            ra = make_rsrc_words(q, (uint32_t)(T * K));
+#pragma unroll
+            for (int i = 0; i < ABLK; ++i) {
+                constexpr int LPR = RA / 16, RPB = 1024 / RA;
+                const int blk = wv * ABLK + i;
+                const bool ok = blk < S * AT / 1024;
+                const int rb = blk % (AT / 1024);
+                const int row = rb * RPB + lane / LPR, pos = lane % LPR;
+                const int t = (ok && row < rows) ? gidx[r0 + row] : -1;
+                avo[i] = (t >= 0 && t < T)
+                             ? (uint32_t)(t * K + ((pos ^ chunk_swizzle<RA>(row)) << 4))
+                             : kOOB;
+            }
+        } else {
+            ra = make_rsrc_words(q + (int64_t)r0 * K * (RA / kGroup),
+                                 (uint32_t)(rows * K * (RA / kGroup)));
+        }
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
             iacc[i] = v4i{0, 0, 0, 0};
@@ -499,7 +526,7 @@ gemm_smallm_kernel(const int8_t *__restrict__ q, const float *__restrict__ sa,
                 for (int r = 0; r < 4; ++r) {
                     const int m = i * 16 + slot * 4 + r;
                     if (m < rows)
-                        store_out<OUT>(y, (int64_t)(r0 + m) * N + n, facc[i][r] * sa[r0 + m]);
+                        store_out<OUT>(y, (int64_t)(r0 + m) * N + n, facc[i][r] * sa_of(r0 + m));
                 }
         }
     };
@@ -539,7 +566,7 @@ constexpr int small_stage() {
 template <int MB, int NW, int OUT, bool GROUPED, int AM = AM_W8A8>
 hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                             int M, int N, int K, void *y, const int32_t *offsets, int E,
-                            hipStream_t stream, int sw_stride) {
+                            hipStream_t stream, int sw_stride, const int32_t *gidx, int T) {
     constexpr int S = small_stage<MB, NW, AM>();
     constexpr int D = small_depth<MB, NW, S, AM>();
     const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW)), GROUPED ? (unsigned)E : 1u);
@@ -549,10 +576,12 @@ hipError_t launch_smallm_mb(const int8_t *q, const float *sa, const int8_t *qw, 
     const bool nt = (int64_t)N * K * (GROUPED ? E : 1) * (AM == AM_BF16 ? 2 : 1) >= kNtMin;
     if (nt)
         gemm_smallm_kernel<MB, NW, OUT, S, D, GROUPED, true, AM>
-            <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets, sw_stride);
+            <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets, sw_stride, gidx,
+                                           T);
     else
         gemm_smallm_kernel<MB, NW, OUT, S, D, GROUPED, false, AM>
-            <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets, sw_stride);
+            <<<grid, 64 * NW, 0, stream>>>(q, sa, qw, sw, M, N, K, y, offsets, sw_stride, gidx,
+                                           T);
     return hipGetLastError();
 }
 
@@ -565,7 +594,8 @@ constexpr int kCUs = 256;
 template <int MB, int OUT, bool GROUPED, int AM = AM_W8A8>
 hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                             int M, int N, int K, void *y, const int32_t *offsets, int E,
-                            hipStream_t stream, int sw_stride = 1) {
+                            hipStream_t stream, int sw_stride = 1, const int32_t *gidx = nullptr,
+                            int T = 0) {
     const int64_t blocks16 = (int64_t)((N + 15) / 16) * (GROUPED ? E : 1);
     const int64_t rounds = (blocks16 + 8 * kCUs - 1) / (8 * kCUs);
     int nw = (int)((blocks16 + kCUs * rounds - 1) / (kCUs * rounds));
@@ -579,7 +609,7 @@ hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, 
 #define BSB_SMALLM_CASE(W)                                                                       \
     case W:                                                                                      \
         return launch_smallm_mb<MB, W, OUT, GROUPED, AM>(q, sa, qw, sw, M, N, K, y, offsets, E,   \
-                                                         stream, sw_stride);
+                                                         stream, sw_stride, gidx, T);
     switch (nw) {
         BSB_SMALLM_CASE(2)
         BSB_SMALLM_CASE(3)
@@ -588,7 +618,8 @@ hipError_t launch_smallm_nw(const int8_t *q, const float *sa, const int8_t *qw, 
         BSB_SMALLM_CASE(6)
         BSB_SMALLM_CASE(7)
         default: return launch_smallm_mb<MB, 8, OUT, GROUPED, AM>(q, sa, qw, sw, M, N, K, y,
-                                                                   offsets, E, stream, sw_stride);
+                                                                   offsets, E, stream, sw_stride,
+                                                                   gidx, T);
     }
 #undef BSB_SMALLM_CASE
 }
@@ -691,7 +722,10 @@ hipError_t launch_gemm_channel(const int8_t *q, const float *sa, const int8_t *q
 
 hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *qw,
                                const float *sw, const int32_t *offsets, int64_t E, int64_t R,
-                               int64_t N, int64_t K, void *y, int out, hipStream_t stream) {
+                               int64_t N, int64_t K, void *y, int out, hipStream_t stream,
+                               const int32_t *gidx, int64_t T) {
+    // gidx: every kernel below loads its activation rows through the index
+    // (same arithmetic, so the same bits as gathering the rows first)
     // Rows per expert are known only on the device; the mean decides. With
     // at least 128 rows per expert on average, and at least kBigMinTiles tiles
     // (counted without the experts' partial tiles, a lower bound), the 256x256
@@ -700,19 +734,19 @@ hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *q
     const int64_t big_tiles = ((R + 255) / 256) * ((N + 255) / 256);
     if (R >= 128 * E && big_tiles >= kBigMinTiles && big_gemm_fits(K))
         return launch_gemm_big(q, sa, qw, sw, (int)R, (int)N, (int)K, y, out, offsets, (int)E, 1,
-                               stream);
+                               stream, gidx, (int)T);
     // At most 32 rows per expert on average (decode-shaped MoE): stream each
     // expert's weights once per 32 of its rows.
     if (R <= 32 * E && E <= 65535 && (int64_t)128 * K < ((int64_t)1 << 31)) {
         if (out == OUT_BF16)
             return launch_smallm_nw<2, OUT_BF16, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y,
-                                                       offsets, (int)E, stream);
+                                                       offsets, (int)E, stream, 1, gidx, (int)T);
         return launch_smallm_nw<2, OUT_FP32, true>(q, sa, qw, sw, (int)R, (int)N, (int)K, y,
-                                                   offsets, (int)E, stream);
+                                                   offsets, (int)E, stream, 1, gidx, (int)T);
     }
     if (!mid_gemm_fits(K)) return hipErrorInvalidValue;   // excluded by the C ABI's checks
     return launch_gemm_mid(q, sa, qw, sw, (int)R, (int)N, (int)K, y, out, offsets, (int)E, 1,
-                           stream);
+                           stream, gidx, (int)T);
 }
 
 }  // namespace bsb

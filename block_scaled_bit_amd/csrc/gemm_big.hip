@@ -71,10 +71,14 @@ __device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
 // multiply expert e's weights qw[e] / sw[e]; tile rows are laid out expert
 // after expert (a tile never spans two experts) and the host sizes the grid
 // for the most tiles any split of R rows over E experts can need.
-template <int OUT, bool GROUPED>
+// GATHER (grouped only): q / sa are the T quantised tokens and row m of the
+// problem is token gidx[m] (the MoE gather done by the A-tile loads; an index
+// outside [0, T) reads a zero row with scale 0).
+template <int OUT, bool GROUPED, bool GATHER = false>
 __global__ void __launch_bounds__(512, 1)
 gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float *sw, int M, int N,
-                int K, void *y, TileGrid tiles, const int32_t *offsets, int E, int sw_stride) {
+                int K, void *y, TileGrid tiles, const int32_t *offsets, int E, int sw_stride,
+                const int32_t *gidx, int T) {
     constexpr bool CHN = per_channel<OUT>();             // one scale per row, applied at the end
     constexpr bool SCALES = !CHN && OUT != OUT_PARTIALS;   // per-group scales staged in LDS
     __shared__ __align__(16) int8_t lds[kBigLds];
@@ -98,7 +102,8 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     const int n0 = bn * kBigTN;
     const int mrows = min(kBigTM, row_end - m0), ncols = min(kBigTN, N - n0);
 
-    const v4i ra = make_rsrc_words(q + (int64_t)m0 * K, (uint32_t)(mrows * K));
+    const v4i ra = GATHER ? make_rsrc_words(q, (uint32_t)(T * K))
+                          : make_rsrc_words(q + (int64_t)m0 * K, (uint32_t)(mrows * K));
     const v4i rb = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(ncols * K));
     const v4i rs = make_rsrc_words(SCALES ? sw + (int64_t)n0 * G : nullptr,
                                    SCALES ? (uint32_t)(ncols * G * 4) : 0u);
@@ -118,6 +123,23 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     for (int j = 0; j < 2; ++j) {
         const int row = wave * 16 + 8 * j + (lane >> 3);
         dvoff[j] = (uint32_t)(row * K + (((lane & 7) ^ big_swz(row)) << 4));
+    }
+    // A rows of this lane's four A loads: 16w + 8j + lane/8 (j = 0, 1), and the
+    // same 128 rows further on (rows 128 apart share the swizzle). Gathered,
+    // each is its token's row; rows past the segment and invalid indices read
+    // zeros.
+    uint32_t aoff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (GATHER) {
+            const int row = wave * 16 + 8 * (j & 1) + (lane >> 3) + 128 * (j >> 1);
+            const int m = m0 + row;
+            const int t = m < row_end ? gidx[m] : -1;
+            aoff[j] = (t >= 0 && t < T) ? (uint32_t)(t * K + (((lane & 7) ^ big_swz(row)) << 4))
+                                        : kOOB;
+        } else {
+            aoff[j] = dvoff[j & 1];   // the second 128 rows through the scalar offset
+        }
     }
     const uint32_t boff01 = (uint32_t)((wave >= 4 ? 64 : 0) * K);
     const uint32_t boff23 = (uint32_t)((wave >= 4 ? 128 : 64) * K);
@@ -140,7 +162,7 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     auto dma_s = [&](int st, int g) {
         const bool in = g < G;
         const uint32_t so = in ? (uint32_t)g * kGroup : kOOB;
-        const uint32_t sa2 = in ? so + (uint32_t)(128 * K) : kOOB;
+        const uint32_t sa2 = in ? (GATHER ? so : so + (uint32_t)(128 * K)) : kOOB;
         const uint32_t sb = in ? so + boff01 : kOOB;
         const uint32_t ma = lbase + kBigLdsA + st * kBigStage + wave * 2048;
         const uint32_t mb = lbase + kBigLdsB01 + st * kBigHalf + wave * 2048;
@@ -148,13 +170,13 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
         asm volatile(
             "s_nop 4\n\t"
             "s_mov_b32 m0, %[a0]\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %[v0], %[ra], %[s0] offen lds\n\t"
+            "buffer_load_dwordx4 %[w0], %[ra], %[s0] offen lds\n\t"
             "s_mov_b32 m0, %[a1]\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %[v1], %[ra], %[s0] offen lds\n\t"
+            "buffer_load_dwordx4 %[w1], %[ra], %[s0] offen lds\n\t"
             "s_mov_b32 m0, %[a2]\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %[v0], %[ra], %[s1] offen lds\n\t"
+            "buffer_load_dwordx4 %[w2], %[ra], %[s1] offen lds\n\t"
             "s_mov_b32 m0, %[a3]\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %[v1], %[ra], %[s1] offen lds\n\t"
+            "buffer_load_dwordx4 %[w3], %[ra], %[s1] offen lds\n\t"
             "s_mov_b32 m0, %[b0]\n\ts_nop 0\n\t"
             "buffer_load_dwordx4 %[v0], %[rb], %[s2] offen lds\n\t"
             "s_mov_b32 m0, %[b1]\n\ts_nop 0\n\t"
@@ -162,6 +184,7 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             : "=&{m0}"(m0_out)
             : [a0] "s"(ma), [a1] "s"(ma + 1024), [a2] "s"(ma + 16384), [a3] "s"(ma + 17408),
               [b0] "s"(mb), [b1] "s"(mb + 1024), [v0] "v"(dvoff[0]), [v1] "v"(dvoff[1]),
+              [w0] "v"(aoff[0]), [w1] "v"(aoff[1]), [w2] "v"(aoff[2]), [w3] "v"(aoff[3]),
               [ra] "s"(ra), [rb] "s"(rb), [s0] "s"(so), [s1] "s"(sa2), [s2] "s"(sb)
             : "memory");
         (void)m0_out;
@@ -393,7 +416,13 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (m >= row_end) continue;
-                const float s = sa[m];
+                float s;
+                if (GATHER) {
+                    const int t = gidx[m];
+                    s = (t >= 0 && t < T) ? sa[t] : 0.0f;
+                } else {
+                    s = sa[m];
+                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int n = n0 + wn * 128 + j * 32 + l32;
@@ -403,17 +432,17 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     }
 }
 
-template <int OUT, bool GROUPED>
+template <int OUT, bool GROUPED, bool GATHER = false>
 hipError_t launch_big_t(const int8_t *q, const float *sa, const int8_t *qw, const float *sw, int M,
                         int N, int K, void *y, const int32_t *offsets, int E, int sw_stride,
-                        hipStream_t stream) {
+                        hipStream_t stream, const int32_t *gidx = nullptr, int T = 0) {
     // Grouped: sum over experts of ceil(rows_e / 256) <= ceil(R / 256) + E tile rows.
     const int64_t mt = (M + kBigTM - 1) / kBigTM + (GROUPED ? E : 0), nt = (N + kBigTN - 1) / kBigTN;
     const int64_t total = mt * nt;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const TileGrid t{(int)mt, (int)nt};
-    gemm_big_kernel<OUT, GROUPED><<<dim3((unsigned)total), 512, 0, stream>>>(
-        q, sa, qw, sw, M, N, K, y, t, offsets, E, sw_stride);
+    gemm_big_kernel<OUT, GROUPED, GATHER><<<dim3((unsigned)total), 512, 0, stream>>>(
+        q, sa, qw, sw, M, N, K, y, t, offsets, E, sw_stride, gidx, T);
     return hipGetLastError();
 }
 
@@ -426,7 +455,18 @@ bool big_gemm_fits(int64_t K) {
 
 hipError_t launch_gemm_big(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                            int M, int N, int K, void *y, int out, const int32_t *offsets, int E,
-                           int sw_stride, hipStream_t stream) {
+                           int sw_stride, hipStream_t stream, const int32_t *gidx, int T) {
+    if (offsets && gidx) {
+        switch (out) {
+            case OUT_BF16:
+                return launch_big_t<OUT_BF16, true, true>(q, sa, qw, sw, M, N, K, y, offsets, E, 1,
+                                                          stream, gidx, T);
+            case OUT_FP32:
+                return launch_big_t<OUT_FP32, true, true>(q, sa, qw, sw, M, N, K, y, offsets, E, 1,
+                                                          stream, gidx, T);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (offsets) {
         switch (out) {
             case OUT_BF16:

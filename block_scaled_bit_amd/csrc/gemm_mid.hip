@@ -49,10 +49,13 @@ constexpr int kMidLds = kMidStages * kMidStage;  // 139264 bytes of 160 KB
 
 __device__ __forceinline__ int mid_swz(int r) { return (r >> 1) & 7; }
 
-template <int OUT, bool GROUPED>
+// GATHER (grouped only): q / sa are the T quantised tokens and row m of the
+// problem is token gidx[m] (an index outside [0, T) reads a zero row, scale 0).
+template <int OUT, bool GROUPED, bool GATHER = false>
 __global__ void __launch_bounds__(512, 1)
 gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float *sw, int M, int N,
-                int K, void *y, TileGrid tiles, const int32_t *offsets, int E, int sw_stride) {
+                int K, void *y, TileGrid tiles, const int32_t *offsets, int E, int sw_stride,
+                const int32_t *gidx, int T) {
     constexpr bool CHN = per_channel<OUT>();             // one scale per row, applied at the end
     constexpr bool SCALES = !CHN && OUT != OUT_PARTIALS;   // per-group scales staged in LDS
     __shared__ __align__(16) int8_t lds[kMidLds];
@@ -76,7 +79,8 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     const int n0 = bn * kMidTN;
     const int mrows = min(kMidTM, row_end - m0), ncols = min(kMidTN, N - n0);
 
-    const v4i ra = make_rsrc_words(q + (int64_t)m0 * K, (uint32_t)(mrows * K));
+    const v4i ra = GATHER ? make_rsrc_words(q, (uint32_t)(T * K))
+                          : make_rsrc_words(q + (int64_t)m0 * K, (uint32_t)(mrows * K));
     const v4i rb = make_rsrc_words(qw + (int64_t)n0 * K, (uint32_t)(ncols * K));
     const v4i rs = make_rsrc_words(SCALES ? sw + (int64_t)n0 * G : nullptr,
                                    SCALES ? (uint32_t)(ncols * G * 4) : 0u);
@@ -93,6 +97,21 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     for (int j = 0; j < 2; ++j) {
         const int row = wave * 16 + 8 * j + (lane >> 3);
         dvoff[j] = (uint32_t)(row * K + (((lane & 7) ^ mid_swz(row)) << 4));
+    }
+    // A rows: the same tile rows; gathered, each its token's row (rows past the
+    // segment and invalid indices read zeros)
+    uint32_t aoff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (GATHER) {
+            const int row = wave * 16 + 8 * j + (lane >> 3);
+            const int m = m0 + row;
+            const int t = m < row_end ? gidx[m] : -1;
+            aoff[j] = (t >= 0 && t < T) ? (uint32_t)(t * K + (((lane & 7) ^ mid_swz(row)) << 4))
+                                        : kOOB;
+        } else {
+            aoff[j] = dvoff[j];
+        }
     }
     const uint32_t svoff = wave < 2 ? (uint32_t)((wave * 64 + lane) * G * 4) : 0u;
     const uint32_t lbase = (uint32_t)(uintptr_t)lds;
@@ -113,9 +132,9 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
         asm volatile(
             "s_nop 4\n\t"
             "s_mov_b32 m0, %[a0]\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %[v0], %[ra], %[so] offen lds\n\t"
+            "buffer_load_dwordx4 %[w0], %[ra], %[so] offen lds\n\t"
             "s_mov_b32 m0, %[a1]\n\ts_nop 0\n\t"
-            "buffer_load_dwordx4 %[v1], %[ra], %[so] offen lds\n\t"
+            "buffer_load_dwordx4 %[w1], %[ra], %[so] offen lds\n\t"
             "s_mov_b32 m0, %[b0]\n\ts_nop 0\n\t"
             "buffer_load_dwordx4 %[v0], %[rb], %[so] offen lds\n\t"
             "s_mov_b32 m0, %[b1]\n\ts_nop 0\n\t"
@@ -125,6 +144,7 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             : "=&{m0}"(m0_out)
             : [a0] "s"(ma), [a1] "s"(ma + 1024), [b0] "s"(mb), [b1] "s"(mb + 1024),
               [c0] "s"(ms), [v0] "v"(dvoff[0]), [v1] "v"(dvoff[1]), [vs] "v"(svoff),
+              [w0] "v"(aoff[0]), [w1] "v"(aoff[1]),
               [ra] "s"(ra), [rb] "s"(rb), [rs] "s"(rs), [so] "s"(so), [ss] "s"(ss)
             : "memory");
         (void)m0_out;
@@ -292,22 +312,30 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (m < row_end && n < N) store_out<OUT>(y, (int64_t)m * N + n, facc[i][r] * sa[m]);
+                if (m >= row_end || n >= N) continue;
+                float s;
+                if (GATHER) {
+                    const int t = gidx[m];
+                    s = (t >= 0 && t < T) ? sa[t] : 0.0f;
+                } else {
+                    s = sa[m];
+                }
+                store_out<OUT>(y, (int64_t)m * N + n, facc[i][r] * s);
             }
     }
 }
 
-template <int OUT, bool GROUPED>
+template <int OUT, bool GROUPED, bool GATHER = false>
 hipError_t launch_mid_t(const int8_t *q, const float *sa, const int8_t *qw, const float *sw, int M,
                         int N, int K, void *y, const int32_t *offsets, int E, int sw_stride,
-                        hipStream_t stream) {
+                        hipStream_t stream, const int32_t *gidx = nullptr, int T = 0) {
     // Grouped: sum over experts of ceil(rows_e / 128) <= ceil(R / 128) + E tile rows.
     const int64_t mt = (M + kMidTM - 1) / kMidTM + (GROUPED ? E : 0), nt = (N + kMidTN - 1) / kMidTN;
     const int64_t total = mt * nt;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const TileGrid t{(int)mt, (int)nt};
-    gemm_mid_kernel<OUT, GROUPED><<<dim3((unsigned)total), 512, 0, stream>>>(
-        q, sa, qw, sw, M, N, K, y, t, offsets, E, sw_stride);
+    gemm_mid_kernel<OUT, GROUPED, GATHER><<<dim3((unsigned)total), 512, 0, stream>>>(
+        q, sa, qw, sw, M, N, K, y, t, offsets, E, sw_stride, gidx, T);
     return hipGetLastError();
 }
 
@@ -320,7 +348,18 @@ bool mid_gemm_fits(int64_t K) {
 
 hipError_t launch_gemm_mid(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                            int M, int N, int K, void *y, int out, const int32_t *offsets, int E,
-                           int sw_stride, hipStream_t stream) {
+                           int sw_stride, hipStream_t stream, const int32_t *gidx, int T) {
+    if (offsets && gidx) {
+        switch (out) {
+            case OUT_BF16:
+                return launch_mid_t<OUT_BF16, true, true>(q, sa, qw, sw, M, N, K, y, offsets, E, 1,
+                                                          stream, gidx, T);
+            case OUT_FP32:
+                return launch_mid_t<OUT_FP32, true, true>(q, sa, qw, sw, M, N, K, y, offsets, E, 1,
+                                                          stream, gidx, T);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (offsets) {
         switch (out) {
             case OUT_BF16:

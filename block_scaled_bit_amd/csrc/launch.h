@@ -28,16 +28,20 @@ hipError_t launch_gemm(const int8_t *q, const float *sa, const int8_t *qw,
                        int out, hipStream_t stream);
 
 // gemm_big.hip: 256x256 tiles for prefill-shaped M. out as gemm_common.h's
-// OUT_* forms; offsets non-null selects the grouped form (BF16 / FP32 only).
+// OUT_* forms; offsets non-null selects the grouped form (BF16 / FP32 only);
+// with gidx non-null as well, q / sa are T tokens and row m is token gidx[m]
+// (T * K < 2^31).
 bool big_gemm_fits(int64_t K);
 hipError_t launch_gemm_big(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                            int M, int N, int K, void *y, int out, const int32_t *offsets, int E,
-                           int sw_stride, hipStream_t stream);
+                           int sw_stride, hipStream_t stream, const int32_t *gidx = nullptr,
+                           int T = 0);
 // gemm_mid.hip: 128x128 tiles for mid-sized M (same arguments and forms)
 bool mid_gemm_fits(int64_t K);
 hipError_t launch_gemm_mid(const int8_t *q, const float *sa, const int8_t *qw, const float *sw,
                            int M, int N, int K, void *y, int out, const int32_t *offsets, int E,
-                           int sw_stride, hipStream_t stream);
+                           int sw_stride, hipStream_t stream, const int32_t *gidx = nullptr,
+                           int T = 0);
 
 // gemm_a16.hip: BF16 activations beyond 64 rows, 128x128 tiles; am 1 = INT8
 // weights with group scales (W8A16), 2 = BF16 weights
@@ -67,10 +71,12 @@ hipError_t launch_gemm_channel(const int8_t *q, const float *sa, const int8_t *q
 hipError_t launch_gemm_a16(const uint16_t *x, const void *w, const float *sw, int64_t M,
                            int64_t N, int64_t K, void *y, int out, int am, hipStream_t stream);
 
+// gidx non-null: q / sa are T quantised tokens, row r of the grouped problem
+// is token gidx[r] (an index outside [0, T) reads a zero row with scale 0)
 hipError_t launch_grouped_gemm(const int8_t *q, const float *sa, const int8_t *qw,
                                const float *sw, const int32_t *offsets, int64_t E,
                                int64_t R, int64_t N, int64_t K, void *y, int out,
-                               hipStream_t stream);
+                               hipStream_t stream, const int32_t *gidx = nullptr, int64_t T = 0);
 
 hipError_t launch_gather_rows(const int8_t *q, const float *sa, const int32_t *index, int64_t R,
                               int64_t T, int64_t K, int8_t *q_out, float *sa_out,

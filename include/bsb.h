@@ -204,16 +204,39 @@ bsb_status bsb_gemm_w8a8_channel(const int8_t *q, const float *sa,
  *           y but never an out-of-bounds access.
  *   y       [R, N] BF16 bits or float32
  * The launch grid is sized from host values only (the row tiles any split of
- * R rows over E experts can need); with R >= 128*E (and a 256x256 tile per
- * CU) the kernel uses 256-row tiles, with R <= 32*E it walks each expert's
- * rows in passes of 32, otherwise it uses 128-row tiles. No choice changes a
- * result bit.
+ * R rows over E experts can need); with R >= 128*E (and more than 128 tiles
+ * of 256x256 without the experts' partial ones) the kernel uses 256-row
+ * tiles, with R <= 32*E it walks each expert's rows in passes of 32, otherwise
+ * it uses 128-row tiles. No choice changes a result bit.
  */
 bsb_status bsb_grouped_gemm_w8a8_g128(const int8_t *q, const float *sa,
                                       const int8_t *qw, const float *sw,
                                       const int32_t *offsets,
                                       int64_t E, int64_t R, int64_t N, int64_t K,
                                       void *y, bsb_out_dtype out, void *stream);
+
+/*
+ * The grouped GEMM with the MoE dispatch gather folded into its activation
+ * loads ([P3] sec. 1.3 / 4.4: each token runs through the experts it
+ * selected): row r of the grouped problem is token index[r] of the T
+ * quantised tokens, so the gathered rows are never written to memory. The
+ * result is bit-identical to bsb_gather_rows followed by
+ * bsb_grouped_gemm_w8a8_g128 (the same kernels and arithmetic; an index
+ * outside [0, T) reads a zero row with scale 0, as the gather writes it).
+ *   q       [T, K] int8, sa [T] float32 (bsb_quantize_act's outputs);
+ *           T >= 1 and T * K + 128 < 2^31
+ *   index   [R] int32, DEVICE memory, the token of each sorted row
+ *   qw, sw, offsets, E, R, N, K, y, out: as bsb_grouped_gemm_w8a8_g128
+ * Errors: as bsb_grouped_gemm_w8a8_g128, and BSB_ERR_INVALID_ARG for T out of
+ * range or a null index (R > 0), BSB_ERR_MISALIGNED for an index not on a
+ * 16-byte boundary.
+ */
+bsb_status bsb_grouped_gemm_w8a8_g128_gather(const int8_t *q, const float *sa,
+                                             const int32_t *index, int64_t T,
+                                             const int8_t *qw, const float *sw,
+                                             const int32_t *offsets,
+                                             int64_t E, int64_t R, int64_t N, int64_t K,
+                                             void *y, bsb_out_dtype out, void *stream);
 
 /*
  * The routes the pages run beside W8A8 ([P1] sec. 1-2): weight-only INT8

@@ -225,6 +225,33 @@ def test_kv_cache_argument_checks(L):
 
 
 @no_gpu
+def test_grouped_gather_argument_checks(L):
+    """Grouped GEMM with the rows gathered by the kernel: the grouped GEMM's checks plus
+    T >= 1, T * K + 128 < 2^31, a non-null 16-byte-aligned index; R = 0 is a no-op."""
+    f = L.bsb_grouped_gemm_w8a8_g128_gather
+    names = ["q", "sa", "index", "T", "qw", "sw", "off", "E", "R", "N", "K", "y", "out", "stream"]
+    ok = (A, A, A, 100, A, A, A, 4, 300, 64, 256, A, 0, None)
+
+    def call(**kw):
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+
+    assert call(T=0) == INVALID
+    assert call(T=(1 << 23), K=256) == INVALID          # T * K reaches 2^31
+    assert call(K=200) == INVALID
+    assert call(E=0) == INVALID
+    assert call(out=2) == INVALID
+    assert call(index=None) == INVALID
+    assert call(index=U) == MISALIGNED
+    assert call(q=U) == MISALIGNED
+    assert call(q=None, sa=None, index=None, qw=None, sw=None, off=None, y=None, R=0) == OK
+    if not torch.cuda.is_available():
+        assert call() == UNSUPPORTED
+        assert call(T=(1 << 23) - 1, K=256) == UNSUPPORTED
+
+
+@no_gpu
 def test_chunk_attention_argument_checks(L):
     """Attention of several query tokens per sequence: the decode attention's checks
     plus 1 <= Qn and Qn * Hq / Hkv <= 16, a workspace sized for B * Qn query heads;

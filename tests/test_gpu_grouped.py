@@ -140,3 +140,62 @@ def test_blockfmt_experts_decode_then_grouped(M):
         y64, mag = gemm_ref(q[rows], sa[rows], qw[e][cols], sw[e][cols])
         _, cb = gemm_fp32_ordered_ref(q[rows], sa[rows], qw[e][cols], sw[e][cols])
         check_bf16(yb[rows][:, cols], y64, mag, cb)
+
+
+@pytest.mark.parametrize("lengths,N,K,T", [
+    ([3, 0, 17, 32, 1, 0, 31], 200, 384, 40),         # <= 32 rows per expert: passes of 32 rows
+    ([0, 1, 127, 128, 129, 0, 5], 96, 256, 100),       # 128x128 tiles
+    ([0, 1, 255, 256, 257, 0, 64, 65, 300, 63, 2300, 600, 513], 2048, 256, 1000),   # 256x256
+])
+def test_rows_gathered_by_the_kernel(lengths, N, K, T):
+    """The grouped GEMM reading its rows through the token index: bit-identical to
+    gathering the rows first and running the grouped GEMM, and held to the same bar
+    against the oracle on the gathered rows; indices outside [0, T) read a zero row with
+    scale 0 (the gather's rule)."""
+    d = require_gpu()
+    R = sum(lengths)
+    say(f"grouped gather lengths={lengths} N={N} K={K} T={T}")
+    _, qw, sw, off = _case(lengths, N, K, R + N)
+    rng = np.random.default_rng(T + R)
+    q, sa = quantize_act_ref(synth.activations(rng, T, K, 0.01, 20.0))
+    index = rng.integers(0, T, size=R).astype(np.int32)
+    index[::97] = -1
+    index[5::101] = T
+    ok = (index >= 0) & (index < T)
+    qg = np.zeros((R, K), np.int8)
+    sg = np.zeros(R, np.float32)
+    qg[ok], sg[ok] = q[index[ok]], sa[index[ok]]
+    y64, mag = grouped_gemm_ref(qg, sg, qw, sw, off)
+    c32, cb = grouped_gemm_fp32_ordered_ref(qg, sg, qw, sw, off)
+    qd, sd, idd = dev(q, d), dev(sa, d), dev(index, d)
+    qwd, swd, offd = dev(qw, d), dev(sw, d), dev(off, d)
+    qs, ss = bsb.gather_rows(qd, sd, idd)
+    for dtype in (torch.float32, torch.bfloat16):
+        g = Guarded((R, N), dtype, d)
+        bsb.grouped_gemm_w8a8_g128_gather(qd, sd, idd, qwd, swd, offd, out_dtype=dtype,
+                                          out=g.view)
+        y2 = bsb.grouped_gemm_w8a8_g128(qs, ss, qwd, swd, offd, out_dtype=dtype)
+        torch.cuda.synchronize()
+        y = g.check()
+        assert np.array_equal(y.view(np.uint8), host(y2).view(np.uint8))
+        if dtype == torch.float32:
+            check_fp32(y, y64, mag, c32)
+        else:
+            check_bf16(y, y64, mag, cb)
+
+
+def test_moe_config_rows_gathered_by_the_kernel():
+    """The MoE layer's grouped GEMM (4096 tokens, top-8 of 64 experts) reading its 32768
+    rows through the token index, as the routed layer runs it: bit-identical to the
+    gather followed by the grouped GEMM."""
+    d = require_gpu()
+    say("moe config, rows gathered by the kernel")
+    m = synth.moe_inputs()
+    x = dev_bf16(m["x_tokens"], d)
+    qt, st = bsb.quantize_act(x)
+    idx, qw, sw, off = dev(m["token_of_row"], d), dev(m["qw"], d), dev(m["sw"], d), dev(m["offsets"], d)
+    qs, ss = bsb.gather_rows(qt, st, idx)
+    a = bsb.grouped_gemm_w8a8_g128(qs, ss, qw, sw, off)
+    b = bsb.grouped_gemm_w8a8_g128_gather(qt, st, idx, qw, sw, off)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
