@@ -693,7 +693,7 @@ def extra_rows(torch, L, stream, dev, steps):
     rows["moe_4096tok_top8_64e_grouped"] = _rate(tg * 1e3, ops=2 * R * N * K, byts=gbytes,
                                                  bound="mfma+hbm")
     rows["moe_4096tok_top8_64e_grouped"].update(rows=R, experts_nonempty=nonempty)
-    cs = counter_summary("gemm_big_kernel<0, true> [grid 786432]")
+    cs = counter_summary("gemm_big_kernel<0, true, false> [grid 786432]")
     if cs:
         rows["moe_4096tok_top8_64e_grouped"].update(counters=cs, mfma_util=cs.get("mfma_util"))
     log(f"moe: quant {tq * 1e3:.1f} us, grouped {tg * 1e3:.1f} us")
@@ -1140,9 +1140,9 @@ def main():
                               tops / peaks["mfma_i8_tops_workload"], 4),
                           "frac_of_measured_mfma_uniform": round(
                               tops / peaks["mfma_i8_tops_uniform"], 4),
-                          "kernel": "gemm_big_kernel<0, false> (256x256)",
+                          "kernel": "gemm_big_kernel<0, false, false> (256x256)",
                           "sclk": clk,
-                          "counters": counter_summary("gemm_big_kernel<0, false> [grid 262144]"),
+                          "counters": counter_summary("gemm_big_kernel<0, false, false> [grid 262144]"),
                           "traffic": measured_traffic("gemm_prefill")}
         if out["prefill"]["counters"]:
             out["prefill"]["mfma_util"] = out["prefill"]["counters"].get("mfma_util")
@@ -1158,11 +1158,13 @@ def main():
         # the committed counter runs of these rows' kernels (null once the sources change)
         for key, ck, tk in (
                 ("moe_4096tok_top8_64e_grouped", None, "moe_grouped"),
+                ("moe_4096tok_top8_64e_grouped_gather", "gemm_big_kernel<0, true, true> [grid 786432]",
+                 "moe_grouped_gather"),
                 ("w8a16_prefill_4096x8192x8192", "gemm_a16_kernel<0, 1> [grid 1048576]",
                  "w8a16_prefill"),
                 ("bf16_prefill_4096x8192x8192", "gemm_a16_kernel<0, 2> [grid 1048576]",
                  "bf16_prefill"),
-                ("blockfmt_gemm_m1024_4096x7168", "gemm_mid_kernel<0, false> [grid 131072]",
+                ("blockfmt_gemm_m1024_4096x7168", "gemm_mid_kernel<0, false, false> [grid 131072]",
                  "gemm_mid_m1024"),
                 ("blockfmt_decode_fp8_ocp_4096x7168", None, "decode_fp8"),
                 ("blockfmt_decode_fp8_ocp_16384x7168", None, "decode_fp8_layer"),

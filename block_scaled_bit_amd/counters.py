@@ -46,8 +46,8 @@ def sources_digest() -> str:
 
 
 def short_name(kernel: str) -> str:
-    """'void bsb::(anonymous namespace)::gemm_big_kernel<0, false>(signed char...)' ->
-    'gemm_big_kernel<0, false>'."""
+    """'void bsb::(anonymous namespace)::gemm_big_kernel<0, false, false>(signed char...)' ->
+    'gemm_big_kernel<0, false, false>'."""
     k = kernel.strip()
     if k.startswith("void "):
         k = k[5:]
@@ -103,11 +103,13 @@ TRAFFIC_KEYS = {
     "gemm_decode_packed": ("gemm_packed_kernel<2, 7, 0, true, false>", 114688, 244318336),
     "gemm_decode": ("gemm_smallm_kernel<2, 7, 0, 2, 4, false, true, 0>", 114688, 244318336),
     "quant_decode": ("quantize_act_kernel<4>", 8192, 786560),
-    "gemm_prefill": ("gemm_big_kernel<0, false>", 262144, 169885696),
-    "moe_grouped": ("gemm_big_kernel<0, true>", 786432, 787611908),
+    "gemm_prefill": ("gemm_big_kernel<0, false, false>", 262144, 169885696),
+    "moe_grouped": ("gemm_big_kernel<0, true, false>", 786432, 787611908),
+    # the same GEMM gathering its rows: the 4096 tokens and the row index instead of the rows
+    "moe_grouped_gather": ("gemm_big_kernel<0, true, true>", 786432, 670187780),
     "kv_attention": ("attn_split_kernel<0, 8, 1>", 131072, 277872640),
     "kv_attention_bf16": ("attn_split_kernel<1, 8, 1>", 131072, 537919488),
-    "gemm_mid_m1024": ("gemm_mid_kernel<0, false>", 131072, 46010368),
+    "gemm_mid_m1024": ("gemm_mid_kernel<0, false, false>", 131072, 46010368),
     "w8a16_prefill": ("gemm_a16_kernel<0, 1>", 1048576, 203423744),
     "bf16_prefill": ("gemm_a16_kernel<0, 2>", 1048576, 268435456),
     "decode_fp8": ("decode_fp8_block_kernel<false>", 917504, 59639552),
