@@ -63,7 +63,8 @@ constexpr int kBigLdsB01 = 2 * kBigStage;        // B01 halves of stages 0, 1
 constexpr int kBigLdsB23 = kBigLdsB01 + 2 * kBigHalf;   // B23 halves of stages 0, 1
 constexpr int kBigLdsS = kBigLdsB23 + 2 * kBigHalf;     // scales of stages 0, 1
 constexpr int kBigScaleStage = 512 * 4;          // 256 scales + 256 slots for the spare loads
-constexpr int kBigLds = kBigLdsS + 2 * kBigScaleStage;   // 135168 bytes of 160 KB
+constexpr int kBigLdsRowS = kBigLdsS + 2 * kBigScaleStage;   // the tile's 256 row scales
+constexpr int kBigLds = kBigLdsRowS + 256 * 4;   // 136192 bytes of 160 KB
 
 __device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
 
@@ -127,7 +128,10 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     // A rows of this lane's four A loads: 16w + 8j + lane/8 (j = 0, 1), and the
     // same 128 rows further on (rows 128 apart share the swizzle). Gathered,
     // each is its token's row; rows past the segment and invalid indices read
-    // zeros.
+    // zeros. One lane per row also stages the row's activation scale in LDS
+    // (published by the prologue's barrier) for the epilogue, which then reads
+    // no global memory before its stores (at the MoE layer with rows gathered
+    // through an index: 444.9 -> 400.8 us).
     uint32_t aoff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -135,10 +139,16 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             const int row = wave * 16 + 8 * (j & 1) + (lane >> 3) + 128 * (j >> 1);
             const int m = m0 + row;
             const int t = m < row_end ? gidx[m] : -1;
-            aoff[j] = (t >= 0 && t < T) ? (uint32_t)(t * K + (((lane & 7) ^ big_swz(row)) << 4))
-                                        : kOOB;
+            const bool tok = t >= 0 && t < T;
+            aoff[j] = tok ? (uint32_t)(t * K + (((lane & 7) ^ big_swz(row)) << 4)) : kOOB;
+            if (OUT != OUT_PARTIALS && (lane & 7) == 0)
+                reinterpret_cast<float *>(lds + kBigLdsRowS)[row] = tok ? sa[t] : 0.0f;
         } else {
             aoff[j] = dvoff[j & 1];   // the second 128 rows through the scalar offset
+            const int row = wave * 16 + 8 * (j & 1) + (lane >> 3) + 128 * (j >> 1);
+            if (OUT != OUT_PARTIALS && (lane & 7) == 0)
+                reinterpret_cast<float *>(lds + kBigLdsRowS)[row] =
+                    m0 + row < row_end ? sa[m0 + row] : 0.0f;
         }
     }
     const uint32_t boff01 = (uint32_t)((wave >= 4 ? 64 : 0) * K);
@@ -401,7 +411,7 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (m >= row_end) continue;
-                const float s = sa[m];
+                const float s = reinterpret_cast<const float *>(lds + kBigLdsRowS)[m - m0];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int n = n0 + wn * 128 + j * 32 + l32;
@@ -416,13 +426,7 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (m >= row_end) continue;
-                float s;
-                if (GATHER) {
-                    const int t = gidx[m];
-                    s = (t >= 0 && t < T) ? sa[t] : 0.0f;
-                } else {
-                    s = sa[m];
-                }
+                const float s = reinterpret_cast<const float *>(lds + kBigLdsRowS)[m - m0];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int n = n0 + wn * 128 + j * 32 + l32;
