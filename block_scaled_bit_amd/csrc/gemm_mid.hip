@@ -45,7 +45,8 @@ constexpr int kMidTile = 128 * kGroup;           // A or B tile of one K group (
 constexpr int kMidScales = 8 * 256;              // 128 scales + the spare waves' slots
 constexpr int kMidStage = 2 * kMidTile + kMidScales;
 constexpr int kMidStages = 4;
-constexpr int kMidLds = kMidStages * kMidStage;  // 139264 bytes of 160 KB
+constexpr int kMidLdsRowS = kMidStages * kMidStage;   // the tile's 128 row scales
+constexpr int kMidLds = kMidLdsRowS + 128 * 4;         // 139776 bytes of 160 KB
 
 __device__ __forceinline__ int mid_swz(int r) { return (r >> 1) & 7; }
 
@@ -100,18 +101,26 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     }
     // A rows: the same tile rows; gathered, each its token's row (rows past the
     // segment and invalid indices read zeros)
+    // One lane per row also stages the row's activation scale in LDS
+    // (published by the prologue's barrier) for the epilogue.
     uint32_t aoff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+        const int row = wave * 16 + 8 * j + (lane >> 3);
+        const int m = m0 + row;
+        int t = m;   // the row's source (its token when gathering); -1: none
         if (GATHER) {
-            const int row = wave * 16 + 8 * j + (lane >> 3);
-            const int m = m0 + row;
-            const int t = m < row_end ? gidx[m] : -1;
-            aoff[j] = (t >= 0 && t < T) ? (uint32_t)(t * K + (((lane & 7) ^ mid_swz(row)) << 4))
-                                        : kOOB;
+            t = m < row_end ? gidx[m] : -1;
+            const bool tok = t >= 0 && t < T;
+            aoff[j] = tok ? (uint32_t)(t * K + (((lane & 7) ^ mid_swz(row)) << 4)) : kOOB;
+            if (!tok) t = -1;
         } else {
             aoff[j] = dvoff[j];
+            if (m >= row_end) t = -1;
         }
+        // the partials form has no activation scales (sa may be null)
+        if (OUT != OUT_PARTIALS && (lane & 7) == 0)
+            reinterpret_cast<float *>(lds + kMidLdsRowS)[row] = t >= 0 ? sa[t] : 0.0f;
     }
     const uint32_t svoff = wave < 2 ? (uint32_t)((wave * 64 + lane) * G * 4) : 0u;
     const uint32_t lbase = (uint32_t)(uintptr_t)lds;
@@ -304,7 +313,10 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (m < row_end && n < N)
-                    store_out<OUT>(y, (int64_t)m * N + n, channel_value(pacc[i][r], swn, sa[m]));
+                    store_out<OUT>(y, (int64_t)m * N + n,
+                                   channel_value(pacc[i][r], swn,
+                                                 reinterpret_cast<const float *>(
+                                                     lds + kMidLdsRowS)[m - m0]));
             }
     } else if (OUT != OUT_PARTIALS) {
 #pragma unroll
@@ -313,13 +325,7 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (m >= row_end || n >= N) continue;
-                float s;
-                if (GATHER) {
-                    const int t = gidx[m];
-                    s = (t >= 0 && t < T) ? sa[t] : 0.0f;
-                } else {
-                    s = sa[m];
-                }
+                const float s = reinterpret_cast<const float *>(lds + kMidLdsRowS)[m - m0];
                 store_out<OUT>(y, (int64_t)m * N + n, facc[i][r] * s);
             }
     }
