@@ -128,28 +128,44 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     // A rows of this lane's four A loads: 16w + 8j + lane/8 (j = 0, 1), and the
     // same 128 rows further on (rows 128 apart share the swizzle). Gathered,
     // each is its token's row; rows past the segment and invalid indices read
-    // zeros. One lane per row also stages the row's activation scale in LDS
-    // (published by the prologue's barrier) for the epilogue, which then reads
-    // no global memory before its stores (at the MoE layer with rows gathered
-    // through an index: 444.9 -> 400.8 us).
+    // zeros. The index loads (and the row-scale one below) are issued together,
+    // unconditionally (rows past the segment read the segment's last entry,
+    // then dropped), and only then turned into offsets.
+    auto arow = [&](int j) { return wave * 16 + 8 * (j & 1) + (lane >> 3) + 128 * (j >> 1); };
+    int tix[5] = {0, 0, 0, 0, 0};
+    if (GATHER) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + arow(j);
+            tix[j] = gidx[m < row_end ? m : row_end - 1];
+        }
+        const int m = m0 + (wave & 3) * 64 + lane;
+        tix[4] = gidx[m < row_end ? m : row_end - 1];
+    }
     uint32_t aoff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if (GATHER) {
-            const int row = wave * 16 + 8 * (j & 1) + (lane >> 3) + 128 * (j >> 1);
-            const int m = m0 + row;
-            const int t = m < row_end ? gidx[m] : -1;
-            const bool tok = t >= 0 && t < T;
-            aoff[j] = tok ? (uint32_t)(t * K + (((lane & 7) ^ big_swz(row)) << 4)) : kOOB;
-            if (OUT != OUT_PARTIALS && (lane & 7) == 0)
-                reinterpret_cast<float *>(lds + kBigLdsRowS)[row] = tok ? sa[t] : 0.0f;
+            const int t = m0 + arow(j) < row_end ? tix[j] : -1;
+            const uint32_t o = (uint32_t)t * (uint32_t)K + (uint32_t)(((lane & 7) ^ big_swz(arow(j))) << 4);
+            aoff[j] = t >= 0 && t < T ? o : kOOB;
         } else {
             aoff[j] = dvoff[j & 1];   // the second 128 rows through the scalar offset
-            const int row = wave * 16 + 8 * (j & 1) + (lane >> 3) + 128 * (j >> 1);
-            if (OUT != OUT_PARTIALS && (lane & 7) == 0)
-                reinterpret_cast<float *>(lds + kBigLdsRowS)[row] =
-                    m0 + row < row_end ? sa[m0 + row] : 0.0f;
         }
+    }
+    // The tile's 256 activation scales go straight into LDS like the operands:
+    // waves 0-3 load rows 64w .. 64w+63, one per lane, ahead of the first stage
+    // (rows past the segment and invalid indices read zero). The epilogue then
+    // reads no global memory, and no load of the prologue waits for them (at the
+    // MoE layer with rows gathered through an index, scales read in the
+    // epilogue: 444.9 us; staged by the lanes before the first stage: 400.8 us).
+    const bool row_scales = OUT != OUT_PARTIALS && wave < 4;
+    const v4i rsa = GATHER ? make_rsrc_words(sa, (uint32_t)(T * 4))
+                           : make_rsrc_words(sa + m0, (uint32_t)(mrows * 4));
+    uint32_t saoff = (uint32_t)((wave * 64 + lane) * 4);
+    if (GATHER) {
+        const int t = m0 + (wave & 3) * 64 + lane < row_end ? tix[4] : -1;
+        saoff = t >= 0 && t < T ? (uint32_t)t * 4u : kOOB;
     }
     const uint32_t boff01 = (uint32_t)((wave >= 4 ? 64 : 0) * K);
     const uint32_t boff23 = (uint32_t)((wave >= 4 ? 128 : 64) * K);
@@ -222,6 +238,18 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             : "memory");
         (void)m0_out;
     };
+    auto dma_rows = [&]() {
+        const uint32_t mr = lbase + kBigLdsRowS + wave * 256;
+        uint32_t m0_out;
+        asm volatile(
+            "s_nop 4\n\t"
+            "s_mov_b32 m0, %[c0]\n\ts_nop 0\n\t"
+            "buffer_load_dword %[vo], %[rs], %[so] offen lds"
+            : "=&{m0}"(m0_out)
+            : [c0] "s"(mr), [vo] "v"(saoff), [rs] "s"(rsa), [so] "s"(0u)
+            : "memory");
+        (void)m0_out;
+    };
     // Loads per wave: 6 in an S batch, 3 in an M batch (scales first).
     // At S(g) B23[g] (end of the M batch of g-2) must have landed: the S and M
     // batches of g-1 (9 loads) may still be in flight. At M(g) the S batch of
@@ -271,8 +299,11 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
                 pacc[i][j][r] = 0;
             }
 
-    // prologue: groups 0 and 1 into stages 0 and 1; wait for A[0], B01[0]
-    // and the scales of group 0 (B23[0] and group 1 may stay in flight)
+    // prologue: the row scales (waves 0-3), then groups 0 and 1 into stages 0
+    // and 1; wait for the row scales, A[0], B01[0] and the scales of group 0
+    // (B23[0] and group 1 may stay in flight: the same count with or without
+    // the row-scale load in front)
+    if (row_scales) dma_rows();
     dma_s(0, 0);
     dma_m(0, 0);
     dma_s(1, 1);
@@ -396,7 +427,55 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     // loads past the last group still write (zeros) into LDS: let them land
     // before the workgroup's LDS can be handed to another one
     wait_vmem();
+    // BF16 results leave through LDS: the MFMA layout gives a lane one column of
+    // 16 rows per block, so direct stores write 2 bytes per lane (128 store
+    // instructions per lane, ~8.5 us per tile); transposed through the stages
+    // (free once every wave has passed this barrier) they leave as 16-byte
+    // rows, 16 instructions per lane (~5.5 us per tile; measured on the whole
+    // kernel: prefill 308 -> 304 us, the MoE grouped GEMM 423-430 -> 404-412 us).
+    constexpr bool LDS_OUT = OUT == OUT_BF16;
+    if (LDS_OUT) __syncthreads();
     if (!active) return;
+    if (LDS_OUT) {
+        // this wave's 64 x 128 outputs as 256-byte BF16 rows in the 16 KB at
+        // 16384 * wave, 16-byte chunk c of row r at c ^ (r & 7) (the two rows one
+        // write instruction covers, 4 apart, fall in different banks; a read of
+        // 4 rows x 16 chunks covers every bank once)
+        int8_t *wo = lds + wave * 16384;
+        const float *rsc = reinterpret_cast<const float *>(lds + kBigLdsRowS) + wm * 64;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ml = i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const float s = rsc[ml];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = j * 32 + l32;
+                    *reinterpret_cast<uint16_t *>(wo + ml * 256 + (((c >> 3) ^ (ml & 7)) << 4) +
+                                                  (c & 7) * 2) =
+                        (uint16_t)f32_to_bf16_rne(facc[i][j][r] * s);
+                }
+            }
+        const bool wide = (N & 7) == 0;   // 16-byte aligned rows of 8 outputs
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int row = 4 * k + (lane >> 4), c16 = lane & 15;
+            const v4i d = *reinterpret_cast<const v4i *>(wo + row * 256 + ((c16 ^ (row & 7)) << 4));
+            const int m = m0 + wm * 64 + row;
+            const int n = n0 + wn * 128 + c16 * 8;
+            if (m >= row_end) continue;
+            uint16_t *dst = reinterpret_cast<uint16_t *>(y) + (int64_t)m * N + n;
+            if (wide && n + 8 <= N) {
+                *reinterpret_cast<v4i *>(dst) = d;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) dst[e] = (uint16_t)((uint32_t)d[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+        return;
+    }
 
     if (CHN) {
         float swn[4];
