@@ -110,6 +110,23 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *offsets, int E, int 
         __syncthreads();
         return x + before;
     };
+    if (tid == 0) s_hit[0] = -1;   // published by the scans' barriers
+    if (E <= 512) {
+        // one expert per thread: one scan gives both the tile rows that exist and
+        // each expert's first tile row
+        const int c = tiles_of(tid);
+        int tot;
+        const int incl = block_scan(c, tot);
+        const int mt = tot < tiles.mt ? tot : tiles.mt;
+        if ((int64_t)blockIdx.x >= (int64_t)mt * tiles.nt) return false;
+        tiles.mt = mt;
+        xcd_tile_of(blockIdx.x, tiles, bm, bn);
+        if (c > 0 && incl - c <= bm && bm < incl) {
+            s_hit[0] = tid;
+            s_hit[1] = bm - (incl - c);
+        }
+        __syncthreads();
+    } else {
     int64_t mt = 0;
     for (int base = 0; base < E; base += 512) {
         int tot;
@@ -121,7 +138,6 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *offsets, int E, int 
     tiles.mt = (int)mt;
     xcd_tile_of(blockIdx.x, tiles, bm, bn);
     // tile row bm -> (expert, TM-row block)
-    if (tid == 0) s_hit[0] = -1;
     int run = 0;
     for (int base = 0; base < E; base += 512) {
         const int e = base + tid, c = tiles_of(e);
@@ -134,6 +150,7 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *offsets, int E, int 
         run += tot;
         __syncthreads();
         if (s_hit[0] >= 0 || run > bm) break;   // uniform: every thread reads the same
+    }
     }
     const int e = s_hit[0];
     if (e < 0) return false;   // unreachable: bm < mt
