@@ -100,27 +100,42 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
         dvoff[j] = (uint32_t)(row * K + (((lane & 7) ^ mid_swz(row)) << 4));
     }
     // A rows: the same tile rows; gathered, each its token's row (rows past the
-    // segment and invalid indices read zeros)
-    // One lane per row also stages the row's activation scale in LDS
-    // (published by the prologue's barrier) for the epilogue.
+    // segment and invalid indices read zeros). The index loads (and the
+    // row-scale one below) are issued together, unconditionally (rows past the
+    // segment read the segment's last entry, then dropped).
+    int tix[3] = {0, 0, 0};
+    if (GATHER) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int m = m0 + wave * 16 + 8 * j + (lane >> 3);
+            tix[j] = gidx[m < row_end ? m : row_end - 1];
+        }
+        const int m = m0 + (wave & 1) * 64 + lane;
+        tix[2] = gidx[m < row_end ? m : row_end - 1];
+    }
     uint32_t aoff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int row = wave * 16 + 8 * j + (lane >> 3);
-        const int m = m0 + row;
-        int t = m;   // the row's source (its token when gathering); -1: none
         if (GATHER) {
-            t = m < row_end ? gidx[m] : -1;
-            const bool tok = t >= 0 && t < T;
-            aoff[j] = tok ? (uint32_t)(t * K + (((lane & 7) ^ mid_swz(row)) << 4)) : kOOB;
-            if (!tok) t = -1;
+            const int t = m0 + row < row_end ? tix[j] : -1;
+            const uint32_t o = (uint32_t)t * (uint32_t)K + (uint32_t)(((lane & 7) ^ mid_swz(row)) << 4);
+            aoff[j] = t >= 0 && t < T ? o : kOOB;
         } else {
             aoff[j] = dvoff[j];
-            if (m >= row_end) t = -1;
         }
-        // the partials form has no activation scales (sa may be null)
-        if (OUT != OUT_PARTIALS && (lane & 7) == 0)
-            reinterpret_cast<float *>(lds + kMidLdsRowS)[row] = t >= 0 ? sa[t] : 0.0f;
+    }
+    // The tile's 128 activation scales go straight into LDS ahead of the first
+    // stage: waves 0-1 load rows 64w .. 64w+63, one per lane (rows past the
+    // segment and invalid indices read zero; the partials form has none, and sa
+    // may be null there).
+    const bool row_scales = OUT != OUT_PARTIALS && wave < 2;
+    const v4i rsa = GATHER ? make_rsrc_words(sa, (uint32_t)(T * 4))
+                           : make_rsrc_words(sa + m0, (uint32_t)(mrows * 4));
+    uint32_t saoff = (uint32_t)((wave * 64 + lane) * 4);
+    if (GATHER) {
+        const int t = m0 + (wave & 1) * 64 + lane < row_end ? tix[2] : -1;
+        saoff = t >= 0 && t < T ? (uint32_t)t * 4u : kOOB;
     }
     const uint32_t svoff = wave < 2 ? (uint32_t)((wave * 64 + lane) * G * 4) : 0u;
     const uint32_t lbase = (uint32_t)(uintptr_t)lds;
@@ -155,6 +170,18 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
               [c0] "s"(ms), [v0] "v"(dvoff[0]), [v1] "v"(dvoff[1]), [vs] "v"(svoff),
               [w0] "v"(aoff[0]), [w1] "v"(aoff[1]),
               [ra] "s"(ra), [rb] "s"(rb), [rs] "s"(rs), [so] "s"(so), [ss] "s"(ss)
+            : "memory");
+        (void)m0_out;
+    };
+    auto dma_rows = [&]() {
+        const uint32_t mr = lbase + kMidLdsRowS + wave * 256;
+        uint32_t m0_out;
+        asm volatile(
+            "s_nop 4\n\t"
+            "s_mov_b32 m0, %[c0]\n\ts_nop 0\n\t"
+            "buffer_load_dword %[vo], %[rs], %[so] offen lds"
+            : "=&{m0}"(m0_out)
+            : [c0] "s"(mr), [vo] "v"(saoff), [rs] "s"(rsa), [so] "s"(0u)
             : "memory");
         (void)m0_out;
     };
@@ -196,7 +223,10 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
             pacc[i][r] = 0;
         }
 
-    // prologue: groups 0..2 into stages 0..2; wait for group 0
+    // prologue: the row scales (waves 0-1), then groups 0..2 into stages 0..2;
+    // wait for the row scales and group 0 (the same count with or without the
+    // row-scale load in front)
+    if (row_scales) dma_rows();
     dma(0, 0);
     dma(1, 1);
     dma(2, 2);
@@ -302,6 +332,45 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     // loads past the last group still write (zeros) into LDS: let them land
     // before the workgroup's LDS can be handed to another one
     wait_vmem();
+    // BF16 results leave through LDS, as in the 256x256 kernel: the 128 x 128
+    // tile as 256-byte rows (16-byte chunk c of row r at c ^ (r & 7)) in the
+    // stages, free once every wave has passed the first barrier, then 16 bytes
+    // per lane and 4 rows per wave instruction.
+    if (OUT == OUT_BF16) {
+        __syncthreads();
+        if (active) {
+            const float *rsc = reinterpret_cast<const float *>(lds + kMidLdsRowS);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ml = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    const int c = wn * 32 + l32;
+                    *reinterpret_cast<uint16_t *>(lds + ml * 256 + (((c >> 3) ^ (ml & 7)) << 4) +
+                                                  (c & 7) * 2) =
+                        (uint16_t)f32_to_bf16_rne(facc[i][r] * rsc[ml]);
+                }
+        }
+        __syncthreads();
+        const bool wide = (N & 7) == 0;   // 16-byte aligned rows of 8 outputs
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int id = k * 512 + tid, row = id >> 4, c16 = id & 15;
+            const v4i d = *reinterpret_cast<const v4i *>(lds + row * 256 + ((c16 ^ (row & 7)) << 4));
+            const int m = m0 + row;
+            const int n = n0 + c16 * 8;
+            if (m >= row_end || row >= mrows) continue;
+            uint16_t *dst = reinterpret_cast<uint16_t *>(y) + (int64_t)m * N + n;
+            if (wide && n + 8 <= N) {
+                *reinterpret_cast<v4i *>(dst) = d;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) dst[e] = (uint16_t)((uint32_t)d[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+        return;
+    }
     if (!active) return;
 
     const int n = n0 + wn * 32 + l32;
