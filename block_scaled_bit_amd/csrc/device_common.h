@@ -25,6 +25,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
+// Two float32 values to BF16 in one instruction (v_cvt_pk_bf16_f32): lo in the
+// low half. Round to nearest even, the same bits as f32_to_bf16_rne for every
+// float32 that is not a NaN, denormals included (all 2^32 patterns compared on
+// the device, with the denormal-preserving mode this library is built with).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // The absmax INT8 rule of [P3] sec. 3.1 for one element, given the row's
 // scale s > 0: clamp(rint(x / s), -127, 127). The division is the IEEE
 // correctly rounded one (the library is built without fast-math), and rint

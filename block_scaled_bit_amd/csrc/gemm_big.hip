@@ -443,18 +443,23 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
         // 4 rows x 16 chunks covers every bank once)
         int8_t *wo = lds + wave * 16384;
         const float *rsc = reinterpret_cast<const float *>(lds + kBigLdsRowS) + wm * 64;
+        // rows ml and ml + 1 (r even, r + 1) converted as one pair
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 16; r += 2) {
                 const int ml = i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                const float s = rsc[ml];
+                const float s0 = rsc[ml], s1 = rsc[ml + 1];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int c = j * 32 + l32;
-                    *reinterpret_cast<uint16_t *>(wo + ml * 256 + (((c >> 3) ^ (ml & 7)) << 4) +
-                                                  (c & 7) * 2) =
-                        (uint16_t)f32_to_bf16_rne(facc[i][j][r] * s);
+                    const uint32_t h = bf16x2_rne(facc[i][j][r] * s0, facc[i][j][r + 1] * s1);
+                    const int co = (c & 7) * 2;
+                    *reinterpret_cast<uint16_t *>(wo + ml * 256 + (((c >> 3) ^ (ml & 7)) << 4) + co) =
+                        (uint16_t)h;
+                    *reinterpret_cast<uint16_t *>(wo + (ml + 1) * 256 +
+                                                  (((c >> 3) ^ ((ml + 1) & 7)) << 4) + co) =
+                        (uint16_t)(h >> 16);
                 }
             }
         const bool wide = (N & 7) == 0;   // 16-byte aligned rows of 8 outputs

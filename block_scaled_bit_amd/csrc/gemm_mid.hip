@@ -340,15 +340,19 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
         __syncthreads();
         if (active) {
             const float *rsc = reinterpret_cast<const float *>(lds + kMidLdsRowS);
+            // rows ml and ml + 1 (r even, r + 1) converted as one pair
+            const int c = wn * 32 + l32, co = (c & 7) * 2;
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
+                for (int r = 0; r < 16; r += 2) {
                     const int ml = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    const int c = wn * 32 + l32;
-                    *reinterpret_cast<uint16_t *>(lds + ml * 256 + (((c >> 3) ^ (ml & 7)) << 4) +
-                                                  (c & 7) * 2) =
-                        (uint16_t)f32_to_bf16_rne(facc[i][r] * rsc[ml]);
+                    const uint32_t h = bf16x2_rne(facc[i][r] * rsc[ml], facc[i][r + 1] * rsc[ml + 1]);
+                    *reinterpret_cast<uint16_t *>(lds + ml * 256 + (((c >> 3) ^ (ml & 7)) << 4) + co) =
+                        (uint16_t)h;
+                    *reinterpret_cast<uint16_t *>(lds + (ml + 1) * 256 +
+                                                  (((c >> 3) ^ ((ml + 1) & 7)) << 4) + co) =
+                        (uint16_t)(h >> 16);
                 }
         }
         __syncthreads();
