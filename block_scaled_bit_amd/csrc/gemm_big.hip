@@ -433,7 +433,7 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     // (free once every wave has passed this barrier) they leave as 16-byte
     // rows, 16 instructions per lane (~5.5 us per tile; measured on the whole
     // kernel: prefill 308 -> 304 us, the MoE grouped GEMM 423-430 -> 404-412 us).
-    constexpr bool LDS_OUT = OUT == OUT_BF16;
+    constexpr bool LDS_OUT = OUT == OUT_BF16 || OUT == OUT_BF16_CH;
     if (LDS_OUT) __syncthreads();
     if (!active) return;
     if (LDS_OUT) {
@@ -443,6 +443,17 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
         // 4 rows x 16 chunks covers every bank once)
         int8_t *wo = lds + wave * 16384;
         const float *rsc = reinterpret_cast<const float *>(lds + kBigLdsRowS) + wm * 64;
+        float swn[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // per-channel forms: the columns' scales
+        if (CHN) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = n0 + wn * 128 + j * 32 + l32;
+                swn[j] = n < N ? sw[(int64_t)n * sw_stride] : 0.0f;
+            }
+        }
+        auto val = [&](int i, int j, int r, float s) {
+            return CHN ? channel_value(pacc[i][j][r], swn[j], s) : facc[i][j][r] * s;
+        };
         // rows ml and ml + 1 (r even, r + 1) converted as one pair
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -453,7 +464,7 @@ gemm_big_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int c = j * 32 + l32;
-                    const uint32_t h = bf16x2_rne(facc[i][j][r] * s0, facc[i][j][r + 1] * s1);
+                    const uint32_t h = bf16x2_rne(val(i, j, r, s0), val(i, j, r + 1, s1));
                     const int co = (c & 7) * 2;
                     *reinterpret_cast<uint16_t *>(wo + ml * 256 + (((c >> 3) ^ (ml & 7)) << 4) + co) =
                         (uint16_t)h;

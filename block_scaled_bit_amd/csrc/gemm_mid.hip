@@ -336,10 +336,15 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     // tile as 256-byte rows (16-byte chunk c of row r at c ^ (r & 7)) in the
     // stages, free once every wave has passed the first barrier, then 16 bytes
     // per lane and 4 rows per wave instruction.
-    if (OUT == OUT_BF16) {
+    if (OUT == OUT_BF16 || OUT == OUT_BF16_CH) {
         __syncthreads();
         if (active) {
             const float *rsc = reinterpret_cast<const float *>(lds + kMidLdsRowS);
+            const int nc = n0 + wn * 32 + l32;
+            const float swn = CHN && nc < N ? sw[(int64_t)nc * sw_stride] : 0.0f;
+            auto val = [&](int i, int r, float s) {
+                return CHN ? channel_value(pacc[i][r], swn, s) : facc[i][r] * s;
+            };
             // rows ml and ml + 1 (r even, r + 1) converted as one pair
             const int c = wn * 32 + l32, co = (c & 7) * 2;
 #pragma unroll
@@ -347,7 +352,7 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     const int ml = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    const uint32_t h = bf16x2_rne(facc[i][r] * rsc[ml], facc[i][r + 1] * rsc[ml + 1]);
+                    const uint32_t h = bf16x2_rne(val(i, r, rsc[ml]), val(i, r + 1, rsc[ml + 1]));
                     *reinterpret_cast<uint16_t *>(lds + ml * 256 + (((c >> 3) ^ (ml & 7)) << 4) + co) =
                         (uint16_t)h;
                     *reinterpret_cast<uint16_t *>(lds + (ml + 1) * 256 +
