@@ -74,7 +74,7 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *offsets, int E, int 
                                              int &e_out, int &m0, int &row_end, int &bm,
                                              int &bn) {
     __shared__ int s_red[8];
-    __shared__ int s_hit[2];
+    __shared__ int s_hit[4];   // expert, block within it, its first row, its row end
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     auto seg = [&](int e, int &lo, int &hi) {   // expert e's rows, clamped to [0, R]
@@ -83,9 +83,10 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *offsets, int E, int 
         lo = lo < 0 ? 0 : (lo > R ? R : lo);
         hi = hi < lo ? lo : (hi > R ? R : hi);
     };
-    auto tiles_of = [&](int e) {
+    // tile rows of expert e (0 past E), with its clamped rows
+    auto tiles_of = [&](int e, int &lo, int &hi) {
+        lo = hi = 0;
         if (e >= E) return 0;
-        int lo, hi;
         seg(e, lo, hi);
         return (hi - lo + TM - 1) / TM;
     };
@@ -114,7 +115,8 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *offsets, int E, int 
     if (E <= 512) {
         // one expert per thread: one scan gives both the tile rows that exist and
         // each expert's first tile row
-        const int c = tiles_of(tid);
+        int lo, hi;
+        const int c = tiles_of(tid, lo, hi);
         int tot;
         const int incl = block_scan(c, tot);
         const int mt = tot < tiles.mt ? tot : tiles.mt;
@@ -124,13 +126,15 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *offsets, int E, int 
         if (c > 0 && incl - c <= bm && bm < incl) {
             s_hit[0] = tid;
             s_hit[1] = bm - (incl - c);
+            s_hit[2] = lo;
+            s_hit[3] = hi;
         }
         __syncthreads();
     } else {
     int64_t mt = 0;
     for (int base = 0; base < E; base += 512) {
-        int tot;
-        block_scan(tiles_of(base + tid), tot);
+        int tot, lo, hi;
+        block_scan(tiles_of(base + tid, lo, hi), tot);
         mt += tot;
     }
     mt = mt < tiles.mt ? mt : tiles.mt;
@@ -140,12 +144,15 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *offsets, int E, int 
     // tile row bm -> (expert, TM-row block)
     int run = 0;
     for (int base = 0; base < E; base += 512) {
-        const int e = base + tid, c = tiles_of(e);
+        int lo, hi;
+        const int e = base + tid, c = tiles_of(e, lo, hi);
         int tot;
         const int incl = block_scan(c, tot) + run;
         if (c > 0 && incl - c <= bm && bm < incl) {
             s_hit[0] = e;
             s_hit[1] = bm - (incl - c);
+            s_hit[2] = lo;
+            s_hit[3] = hi;
         }
         run += tot;
         __syncthreads();
@@ -154,11 +161,11 @@ __device__ __forceinline__ bool grouped_tile(const int32_t *offsets, int E, int 
     }
     const int e = s_hit[0];
     if (e < 0) return false;   // unreachable: bm < mt
-    int lo, hi;
-    seg(e, lo, hi);
+    // the expert's rows come from the thread that found it (no second load of
+    // the offsets after the scan)
     e_out = e;
-    m0 = lo + s_hit[1] * TM;
-    row_end = hi;
+    m0 = s_hit[2] + s_hit[1] * TM;
+    row_end = s_hit[3];
     return true;
 }
 
