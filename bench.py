@@ -296,10 +296,10 @@ def measured_peaks(torch, L, stream, dev, a_bytes=None, b_bytes=None):
     rounds = 512   # about a millisecond of matrix-core work per call
     ops = 2048 * rounds * 64 * 65536   # 131072 threads = 2048 waves of 64 MFMAs per round
 
-    def mfma_rate(a, b):
+    def mfma_rate(a, b, probe=None):
+        probe = probe or L.bsb_probe_mfma_i8
         def call():
-            _ok(L, L.bsb_probe_mfma_i8(a.data_ptr(), b.data_ptr(), a.numel(), rounds,
-                                       out.data_ptr(), stream))
+            _ok(L, probe(a.data_ptr(), b.data_ptr(), a.numel(), rounds, out.data_ptr(), stream))
         m = percall(torch, call, 10, 3)
         return round(ops / (m["median_us"] * 1e-6) / 1e12, 1)
     g = torch.Generator(device="cpu").manual_seed(0)
@@ -309,9 +309,14 @@ def measured_peaks(torch, L, stream, dev, a_bytes=None, b_bytes=None):
     res["mfma_i8_tops_uniform"] = mfma_rate(ua, ub)
     if a_bytes is not None and b_bytes is not None:
         n = min(u8, a_bytes.numel(), b_bytes.numel()) // 16 * 16
-        res["mfma_i8_tops_workload"] = mfma_rate(a_bytes.reshape(-1)[:n], b_bytes.reshape(-1)[:n])
+        wa, wb = a_bytes.reshape(-1)[:n], b_bytes.reshape(-1)[:n]
+        res["mfma_i8_tops_workload"] = mfma_rate(wa, wb)
+        # the same stream with the per-group epilogue beside it (4 conversions and
+        # 4 fused multiply-adds after every MFMA, as the W8A8-g128 kernels run)
+        res["mfma_i8_epilogue_tops_workload"] = mfma_rate(wa, wb, L.bsb_probe_mfma_i8_epilogue)
     res["mfma_probe"] = ("only v_mfma_i32_32x32x32_i8, 2 waves per SIMD on every CU, operands "
-                         "cycled over 8 register sets; median of 10 calls")
+                         "cycled over 8 register sets; median of 10 calls; the epilogue probe "
+                         "adds the per-group conversion and fused multiply-add work, no memory")
     return res
 
 
@@ -1140,6 +1145,8 @@ def main():
                               tops / peaks["mfma_i8_tops_workload"], 4),
                           "frac_of_measured_mfma_uniform": round(
                               tops / peaks["mfma_i8_tops_uniform"], 4),
+                          "frac_of_measured_mfma_epilogue": round(
+                              tops / peaks["mfma_i8_epilogue_tops_workload"], 4),
                           "kernel": "gemm_big_kernel<0, false, false> (256x256)",
                           "sclk": clk,
                           "counters": counter_summary("gemm_big_kernel<0, false, false> [grid 262144]"),

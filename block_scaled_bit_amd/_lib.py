@@ -59,6 +59,7 @@ _SIGNATURES = {
     "bsb_attention_decode_int8kv_noalloc": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64,
                                             _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_int, _c_p],
     "bsb_probe_mfma_i8": [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p],
+    "bsb_probe_mfma_i8_epilogue": [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p],
     "bsb_probe_hbm_read": [_c_p, _c_i64, _c_p, _c_p],
     "bsb_probe_hbm_copy": [_c_p, _c_p, _c_i64, _c_p],
     "bsb_kv_cache_write_bf16": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,

@@ -557,6 +557,18 @@ bsb_status bsb_probe_mfma_i8(const int8_t *a, const int8_t *b, int64_t bytes, in
     return finish(bsb::launch_probe_mfma_i8(a, b, bytes, rounds, out, as_stream(stream)));
 }
 
+bsb_status bsb_probe_mfma_i8_epilogue(const int8_t *a, const int8_t *b, int64_t bytes, int64_t rounds,
+                             int32_t *out, void *stream) {
+    if (bytes < 16 || bytes % 16 || bytes > ((int64_t)1 << 31) || rounds < 1 ||
+        rounds > ((int64_t)1 << 24))
+        return BSB_ERR_INVALID_ARG;
+    if (!a || !b || !out) return BSB_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out)) return BSB_ERR_MISALIGNED;
+    if (bsb_status s = check_device()) return s;
+    (void)hipGetLastError();
+    return finish(bsb::launch_probe_mfma_i8_epilogue(a, b, bytes, rounds, out, as_stream(stream)));
+}
+
 bsb_status bsb_probe_hbm_read(const void *src, int64_t bytes, int32_t *out, void *stream) {
     const int64_t sweep = (int64_t)16 * bsb::kProbeThreads;
     if (bytes < sweep || bytes % sweep || bytes > ((int64_t)1 << 40)) return BSB_ERR_INVALID_ARG;

@@ -119,6 +119,8 @@ hipError_t launch_attention_decode_noalloc(const uint16_t *q, const int8_t *kc, 
 constexpr int kProbeThreads = 131072;
 hipError_t launch_probe_mfma_i8(const int8_t *a, const int8_t *b, int64_t bytes, int64_t rounds,
                                 int32_t *out, hipStream_t stream);
+hipError_t launch_probe_mfma_i8_epilogue(const int8_t *a, const int8_t *b, int64_t bytes, int64_t rounds,
+                                int32_t *out, hipStream_t stream);
 hipError_t launch_probe_hbm_read(const void *src, int64_t bytes, int32_t *out,
                                  hipStream_t stream);
 hipError_t launch_probe_hbm_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);

@@ -7,6 +7,14 @@
 //    rate; uniform INT8 codes well below it), so the probe runs on the
 //    workload's own activation and weight bytes to give the INT8 rate those
 //    operands allow.
+//  * mfma_i8_epilogue_probe_kernel: the same MFMA stream with the GEMMs'
+//    per-group epilogue beside it: every block of four MFMAs (one 32x32 block
+//    over one 128-wide K group) is followed, next to the following block's
+//    MFMAs, by the previous block's 16 conversions and 16 fused multiply-adds
+//    into float32 totals (eight 32x32 blocks of them, as a GEMM wave holds),
+//    8 VALU instructions after each MFMA. No memory access in the loop: the
+//    rate the matrix cores keep while the VALU does the epilogue work that the
+//    per-group scales require.
 //  * hbm_read_probe_kernel: a streaming read of a buffer larger than the
 //    last-level cache, 16 bytes per lane, four loads in flight, non-temporal.
 //  * hbm_copy_probe_kernel: the same walk copying into a second buffer
@@ -54,6 +62,60 @@ mfma_i8_probe_kernel(const int8_t *a, const int8_t *b, uint32_t chunks, int roun
 #pragma unroll
         for (int r = 0; r < 16; ++r) x ^= c[j][r];
     out[gt] = x;
+}
+
+// Operands as the plain probe; rounds of 16 blocks of four MFMAs.
+__global__ void __launch_bounds__(512, 1)
+mfma_i8_epilogue_probe_kernel(const int8_t *a, const int8_t *b, uint32_t chunks, int rounds,
+                              int32_t *out) {
+    const uint32_t gt = blockIdx.x * 512u + threadIdx.x;
+    v4i ra[8], rb[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t c = (gt * 8u + (uint32_t)k) % chunks;
+        const uint4 x = reinterpret_cast<const uint4 *>(a)[c];
+        const uint4 y = reinterpret_cast<const uint4 *>(b)[(c * 7u + 3u) % chunks];
+        ra[k] = v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+        rb[k] = v4i{(int)y.x, (int)y.y, (int)y.z, (int)y.w};
+    }
+    const float s = 1.0f + (float)(gt & 7u) * 0x1p-10f;
+    v16f f[8];
+    v16i prev;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) f[j][r] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) prev[r] = 0;
+    for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+        for (int blk = 0; blk < 16; ++blk) {
+            v16i c;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c[r] = 0;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int k = (blk * 4 + ks) & 7;
+                c = __builtin_amdgcn_mfma_i32_32x32x32_i8(ra[k], rb[(k + (blk >> 1)) & 7], c, 0, 0,
+                                                          0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                const int pj = (blk + 7) & 7;
+#pragma unroll
+                for (int r = 4 * ks; r < 4 * ks + 4; ++r)
+                    f[pj][r] = __builtin_fmaf((float)prev[r], s, f[pj][r]);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            }
+            prev = c;
+        }
+    }
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x ^= __float_as_uint(f[j][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x ^= (uint32_t)prev[r];
+    out[gt] = (int32_t)x;
 }
 
 // 131072 threads; thread t reads chunks t, t + 131072, ... (16 bytes each),
@@ -122,6 +184,13 @@ hipError_t launch_probe_mfma_i8(const int8_t *a, const int8_t *b, int64_t bytes,
                                 int32_t *out, hipStream_t stream) {
     mfma_i8_probe_kernel<<<dim3(256), 512, 0, stream>>>(a, b, (uint32_t)(bytes / 16), (int)rounds,
                                                         out);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma_i8_epilogue(const int8_t *a, const int8_t *b, int64_t bytes,
+                                         int64_t rounds, int32_t *out, hipStream_t stream) {
+    mfma_i8_epilogue_probe_kernel<<<dim3(256), 512, 0, stream>>>(a, b, (uint32_t)(bytes / 16),
+                                                                 (int)rounds, out);
     return hipGetLastError();
 }
 

@@ -539,6 +539,13 @@ bsb_status bsb_attention_decode_bf16kv(const uint16_t *q_bf16,
  * `bytes` long), so the rate reflects those bytes (the matrix cores draw more
  * power on dense bit patterns and the clock follows).
  *   bytes a multiple of 16, 16 .. 2^31;  1 <= rounds <= 2^24
+ * bsb_probe_mfma_i8_epilogue: the same MFMA stream (same ops, same operand
+ * bytes and sizes) with the per-group epilogue of the W8A8-g128 GEMMs beside
+ * it ([P3] sec. 3.1: the INT32 group sum converted and scaled in float32 per
+ * 128-wide K group): after every MFMA, 4 conversions and 4 fused multiply-adds
+ * of the previous 32x32 block into float32 totals, with no memory traffic.
+ * Its rate is what the matrix cores keep beside the epilogue that the
+ * per-group scales require; out as bsb_probe_mfma_i8.
  * bsb_probe_hbm_read: reads `bytes` of src once, 16 bytes per lane, four
  * loads in flight per lane, non-temporal.
  *   bytes a multiple of 16 * BSB_PROBE_THREADS (2 MiB), at most 2^40
@@ -552,6 +559,9 @@ bsb_status bsb_attention_decode_bf16kv(const uint16_t *q_bf16,
 
 bsb_status bsb_probe_mfma_i8(const int8_t *a, const int8_t *b, int64_t bytes, int64_t rounds,
                              int32_t *out, void *stream);
+
+bsb_status bsb_probe_mfma_i8_epilogue(const int8_t *a, const int8_t *b, int64_t bytes,
+                                      int64_t rounds, int32_t *out, void *stream);
 
 bsb_status bsb_probe_hbm_read(const void *src, int64_t bytes, int32_t *out, void *stream);
 

@@ -325,12 +325,14 @@ def test_probe_argument_checks(L):
     """Measurement probes: sizes outside their stated ranges are refused before
     anything is launched; valid calls without a gfx950 device fail fast."""
     mf, hb = L.bsb_probe_mfma_i8, L.bsb_probe_hbm_read
-    assert mf(A, A, 8, 1, A, None) == INVALID            # under 16 bytes
-    assert mf(A, A, 24, 1, A, None) == INVALID           # not a multiple of 16
-    assert mf(A, A, 1024, 0, A, None) == INVALID         # no rounds
-    assert mf(A, A, (1 << 31) + 16, 1, A, None) == INVALID
-    assert mf(None, A, 1024, 1, A, None) == INVALID
-    assert mf(A, A, 1024, 1, U, None) == MISALIGNED
+    for m in (mf, L.bsb_probe_mfma_i8_epilogue):
+        assert m(A, A, 8, 1, A, None) == INVALID            # under 16 bytes
+        assert m(A, A, 24, 1, A, None) == INVALID           # not a multiple of 16
+        assert m(A, A, 1024, 0, A, None) == INVALID         # no rounds
+        assert m(A, A, 1024, (1 << 24) + 1, A, None) == INVALID
+        assert m(A, A, (1 << 31) + 16, 1, A, None) == INVALID
+        assert m(None, A, 1024, 1, A, None) == INVALID
+        assert m(A, A, 1024, 1, U, None) == MISALIGNED
     sweep = 16 * 131072
     assert hb(A, sweep - 16, A, None) == INVALID
     assert hb(A, sweep + 16, A, None) == INVALID
@@ -342,6 +344,7 @@ def test_probe_argument_checks(L):
     assert cp(A, U, sweep, None) == MISALIGNED
     if not torch.cuda.is_available():
         assert mf(A, A, 1024, 1, A, None) == UNSUPPORTED
+        assert L.bsb_probe_mfma_i8_epilogue(A, A, 1024, 1, A, None) == UNSUPPORTED
         assert hb(A, 2 * sweep, A, None) == UNSUPPORTED
         assert cp(A, A, 2 * sweep, None) == UNSUPPORTED
 

@@ -11,6 +11,7 @@ import torch
 
 import block_scaled_bit_amd as bsb
 from block_scaled_bit_amd import synth
+from block_scaled_bit_amd import _lib as bsb_lib
 from oracle import (quantize_act_ref, group_partials_ref, gemm_ref, gemm_fp32_ordered_ref,
                     decode_fp8_block_ref)
 from oracle.decode import OCP, FNUZ
@@ -214,3 +215,29 @@ def test_blockfmt_dense_decode_then_gemm(M):
     c32, cb = gemm_fp32_ordered_ref(q[rows], sa[rows], qw[cols], sw[cols])
     check_fp32(outs[OCP][1][rows][:, cols], y64, mag, c32)
     check_bf16(outs[OCP][0][rows][:, cols], y64, mag, cb)
+
+
+@pytest.mark.gpu
+def test_mfma_probes_run_and_repeat():
+    """The MFMA rate probes (plain, and with the per-group epilogue beside the MFMAs)
+    launch, write every thread's value, and give the same values on a second call
+    (the work is a fixed function of the operand bytes)."""
+    d = require_gpu()
+    say("mfma probes")
+    L = bsb_lib.lib()
+    g = torch.Generator(device="cpu").manual_seed(5)
+    a = torch.randint(-127, 128, (1 << 16,), dtype=torch.int8, generator=g).to(d)
+    b = torch.randint(-127, 128, (1 << 16,), dtype=torch.int8, generator=g).to(d)
+    st = torch.cuda.current_stream(d).cuda_stream
+    outs = []
+    for probe in (L.bsb_probe_mfma_i8, L.bsb_probe_mfma_i8_epilogue):
+        res = []
+        for _ in range(2):
+            o = torch.full((131072,), 0x5A5A5A5A, dtype=torch.int32, device=d)
+            assert probe(a.data_ptr(), b.data_ptr(), a.numel(), 2, o.data_ptr(), st) == 0
+            torch.cuda.synchronize(d)
+            res.append(o.cpu())
+        assert torch.equal(res[0], res[1])
+        assert (res[0] != 0x5A5A5A5A).float().mean() > 0.99
+        outs.append(res[0])
+    assert not torch.equal(outs[0], outs[1])
