@@ -130,8 +130,9 @@ gemm_mid_kernel(const int8_t *q, const float *sa, const int8_t *qw, const float 
     // segment and invalid indices read zero; the partials form has none, and sa
     // may be null there).
     const bool row_scales = OUT != OUT_PARTIALS && wave < 2;
-    const v4i rsa = GATHER ? make_rsrc_words(sa, (uint32_t)(T * 4))
-                           : make_rsrc_words(sa + m0, (uint32_t)(mrows * 4));
+    const v4i rsa = OUT == OUT_PARTIALS ? make_rsrc_words(nullptr, 0u)
+                    : GATHER            ? make_rsrc_words(sa, (uint32_t)(T * 4))
+                                        : make_rsrc_words(sa + m0, (uint32_t)(mrows * 4));
     uint32_t saoff = (uint32_t)((wave * 64 + lane) * 4);
     if (GATHER) {
         const int t = m0 + (wave & 1) * 64 + lane < row_end ? tix[2] : -1;
