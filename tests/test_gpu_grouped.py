@@ -55,6 +55,10 @@ def _gpu_grouped(q, sa, qw, sw, off, dtype, d):
     # 128): segments ending at 1, 63/64/65 (one wave's rows), 255/256/257 (one
     # tile) inside it
     ([0, 1, 255, 256, 257, 0, 64, 65, 300, 63, 2300, 600, 513], 2048, 256),
+    # the same with a ragged last tile column: N not a multiple of 8 (outputs stored
+    # one by one at the end of each row) and a multiple of 8 that is not one of 256
+    ([0, 1, 255, 256, 257, 0, 64, 65, 300, 63, 2300, 600, 513], 2053, 256),
+    ([0, 1, 255, 256, 257, 0, 64, 65, 300, 63, 2300, 600, 513], 2056, 256),
 ])
 def test_segments_and_tails(lengths, N, K):
     d = require_gpu()
@@ -146,6 +150,8 @@ def test_blockfmt_experts_decode_then_grouped(M):
     ([3, 0, 17, 32, 1, 0, 31], 200, 384, 40),         # <= 32 rows per expert: passes of 32 rows
     ([0, 1, 127, 128, 129, 0, 5], 96, 256, 100),       # 128x128 tiles
     ([0, 1, 255, 256, 257, 0, 64, 65, 300, 63, 2300, 600, 513], 2048, 256, 1000),   # 256x256
+    ([0, 1, 255, 256, 257, 0, 64, 65, 300, 63, 2300, 600, 513], 2053, 256, 1000),   # ragged N
+    ([0, 1, 127, 128, 129, 0, 5], 99, 256, 100),       # 128x128 tiles, ragged N
 ])
 def test_rows_gathered_by_the_kernel(lengths, N, K, T):
     """The grouped GEMM reading its rows through the token index: bit-identical to
